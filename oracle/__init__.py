@@ -1,0 +1,173 @@
+"""fp64 CPU oracle for the DSA layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP product path never does, and
+shares no code with it. The arithmetic lives in ``dsa_oracle.c`` (plain C,
+double precision, OpenMP over independent outputs); this module only builds
+that file with gcc and marshals numpy arrays into it.
+
+Inputs are numpy arrays in their storage type: ``float32`` for fp32 data or
+``uint16`` holding bf16 bit patterns. Outputs are float64 (scores, attention)
+or int32 (top-k indices).
+
+Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
+  index_scores  pinned: einsum/matmul closed forms, |u| and identity
+                constructions for the per-head ReLU, causal -inf triangle.
+  topk          pinned: brute-force subset enumeration, numpy lexsort,
+                constant rows, signed-zero and -inf handling.
+  sparse_attn   pinned: full selection equals torch's dense causal SDPA
+                (float64), top-1 closed form, set semantics, convexity, gate
+                limits.
+  swa_attn      pinned: window >= context equals dense causal SDPA, window 1
+                closed form, buffer-offset equivalence.
+Parity unpinned by the pages (fixed by convention, tested in every mode):
+ReLU placement (per head by default), the two scale constants, and the
+inclusive window boundary.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "libdsa_oracle.so")
+
+F32 = 0
+BF16 = 1
+RELU_PER_HEAD = 0
+RELU_NONE = 1
+RELU_POST_SUM = 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile dsa_oracle.c into libdsa_oracle.so with gcc (OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+             "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            dbl, i32, vp]
+        lib.oracle_index_scores.restype = None
+        lib.oracle_topk.argtypes = [vp, i64, i64, i32, vp]
+        lib.oracle_topk.restype = None
+        lib.oracle_sparse_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, i32, i32, dbl, i32, vp]
+        lib.oracle_sparse_attn.restype = None
+        lib.oracle_swa_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, i32, i32, dbl, i32, vp]
+        lib.oracle_swa_attn.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _dtype_of(*arrs) -> int:
+    kinds = {a.dtype for a in arrs if a is not None}
+    if kinds == {np.dtype(np.float32)}:
+        return F32
+    if kinds == {np.dtype(np.uint16)}:
+        return BF16
+    raise TypeError(f"oracle inputs must all be float32 or all uint16 (bf16 bits), got {kinds}")
+
+
+def _c(a):
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def index_scores(q_idx, k_idx, w, past_len: int, scale: float | None = None,
+                 relu_mode: int = RELU_PER_HEAD) -> np.ndarray:
+    """q_idx [B,S,HI,DI], k_idx [B,T,DI], w [B,S,HI] -> scores [B,S,T] float64."""
+    q_idx, k_idx, w = _c(q_idx), _c(k_idx), _c(w)
+    B, S, HI, DI = q_idx.shape
+    T = k_idx.shape[1]
+    assert k_idx.shape == (B, T, DI) and w.shape == (B, S, HI)
+    if scale is None:
+        scale = DI ** -0.5
+    out = np.empty((B, S, T), np.float64)
+    _load().oracle_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), _dtype_of(q_idx, k_idx, w),
+                                B, S, T, past_len, HI, DI, float(scale), relu_mode, _ptr(out))
+    return out
+
+
+def topk(scores, k: int) -> np.ndarray:
+    """scores [..., T] float32 -> indices [..., k] int32 (score desc, t asc; -1 pads)."""
+    scores = _c(np.asarray(scores, dtype=np.float32))
+    lead, T = scores.shape[:-1], scores.shape[-1]
+    R = int(np.prod(lead)) if lead else 1
+    out = np.empty(lead + (k,), np.int32)
+    _load().oracle_topk(_ptr(scores), R, T, k, _ptr(out))
+    return out
+
+
+def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: int,
+                qk_rope_dim: int, sm_scale: float | None = None, gate_dim: int = 1) -> np.ndarray:
+    """q [B,S,H,Dqk], caches [B,T,H,D], indices [B,S,k] int32, gate [B,S,H(,Dv)] or None
+    -> out [B,S,H,Dv] float64."""
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    indices = _c(np.asarray(indices, dtype=np.int32))
+    B, S, H, Dqk = q.shape
+    assert Dqk == qk_nope_dim + qk_rope_dim
+    T = k_cache.shape[1]
+    Dv = v_cache.shape[3]
+    topk_ = indices.shape[2]
+    if gate is None:
+        gate_dim = 0
+    else:
+        gate = _c(gate)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    out = np.empty((B, S, H, Dv), np.float64)
+    _load().oracle_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate),
+                               _dtype_of(q, k_cache, v_cache, gate), B, S, T, past_len, H, Dqk,
+                               Dv, topk_, float(sm_scale), gate_dim, _ptr(out))
+    return out
+
+
+def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
+             qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+             gate_dim: int = 1) -> np.ndarray:
+    """q [B,S,H,Dqk], buffers [B,T_buf,H,D] (row j = position kv_offset + j)
+    -> out [B,S,H,Dv] float64."""
+    q, k_buf, v_buf = _c(q), _c(k_buf), _c(v_buf)
+    B, S, H, Dqk = q.shape
+    assert Dqk == qk_nope_dim + qk_rope_dim
+    T_buf = k_buf.shape[1]
+    Dv = v_buf.shape[3]
+    if gate is None:
+        gate_dim = 0
+    else:
+        gate = _c(gate)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    out = np.empty((B, S, H, Dv), np.float64)
+    _load().oracle_swa_attn(_ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate),
+                            _dtype_of(q, k_buf, v_buf, gate), B, S, T_buf, past_len, kv_offset,
+                            H, Dqk, Dv, window, float(sm_scale), gate_dim, _ptr(out))
+    return out

@@ -1,0 +1,301 @@
+/*
+ * dsa_oracle.c -- plain, slow, fp64 CPU reference for one DeepSeek-Sparse-
+ * Attention (DSA) layer and its sliding-window (SWA) sibling.
+ *
+ * THIS IS TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it. The product path (the HIP library)
+ * never calls it, and the two share no source, header, table or helper.
+ *
+ * Every function is the plain definition of its result, written out in the
+ * order the pages give it:
+ *   oracle_index_scores  -- lightning-indexer score with causal mask
+ *                           [A.X-K2 page, "Sparse Gated Attention (SGA)"]
+ *   oracle_topk          -- per-query top-k of a score row
+ *                           [A.X-K2 page, SGA bullets and "index_topk"]
+ *   oracle_sparse_attn   -- attention under the additive sparse mask AND the
+ *                           causal mask, then the sigmoid output gate
+ *                           [A.X-K2 page, "MLA + explicit sparse mask" steps
+ *                           4-5 and "Attention output gate"; Spark-X2.5 page,
+ *                           "forward pass" steps 1-3]
+ *   oracle_swa_attn      -- sliding-window attention, window W keys
+ *                           [Spark-X2.5 page, "why the gate" (sliding_window
+ *                           512); openPangu-2.0 page §3.2]
+ * Decode is the same functions with S = 1 and past_len = T - 1.
+ *
+ * Arithmetic is IEEE double throughout; inputs are read in their storage type
+ * (fp32, or bf16 bit patterns) and widened exactly. No blocking, fusion or
+ * reordering beyond what the definitions state. Loops over independent
+ * outputs are split across OpenMP threads; each output is computed by one
+ * thread in a fixed order, so results do not depend on the thread count.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - ReLU placement in the indexer: per head, before the weighted sum
+ *    (relu_mode 0). Mode 1 applies none (the formula as printed), mode 2
+ *    applies it after the weighted sum.
+ *  - Query s of a call sits at absolute position p = past_len + s and sees
+ *    keys t <= p, itself included.
+ *  - Top-k: order by (score descending, t ascending); -0.0 equals +0.0; slots
+ *    whose score is -inf, or beyond the row, are emitted as -1.
+ *  - Attention index lists are sets: negative entries, entries > p and
+ *    entries >= T are ignored; a repeated entry selects its key once.
+ *  - SWA window: the W keys p-W+1 .. p.
+ *  - Gate: sigmoid(x) = 1 / (1 + exp(-x)), one scalar per (token, head)
+ *    (gate_dim 1) or one per output element (gate_dim = v_dim).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Storage types of the inputs. */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Indexer ReLU placement. */
+#define ORACLE_RELU_PER_HEAD 0
+#define ORACLE_RELU_NONE 1
+#define ORACLE_RELU_POST_SUM 2
+
+/* Read element i of an fp32 or bf16 array as an exact double. A bf16 value is
+ * the upper 16 bits of the fp32 with the same value. */
+static double rd(const void *base, int dtype, int64_t i) {
+  if (dtype == ORACLE_F32) return (double)((const float *)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Lightning-indexer scores [A.X-K2 page, SGA: the score formula and the
+ * causal mask]:
+ *   score[b,s,t] = sum_h w[b,s,h] * relu(scale * q[b,s,h,:] . k[b,t,:])
+ * for t <= p = past_len + s, and -inf for t > p.
+ *   q_idx [B,S,HI,DI], k_idx [B,T,DI], w [B,S,HI]  (dtype)
+ *   out   [B,S,T] double
+ */
+void oracle_index_scores(const void *q_idx, const void *k_idx, const void *w,
+                         int dtype, int B, int S, int T, int past_len, int HI,
+                         int DI, double scale, int relu_mode, double *out) {
+  int64_t n = (int64_t)B * S * T;
+#pragma omp parallel for schedule(dynamic, 256)
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t t = e % T;
+    int64_t bs = e / T; /* b*S + s */
+    int64_t s = bs % S;
+    int64_t b = bs / S;
+    int64_t p = (int64_t)past_len + s;
+    if (t > p) {
+      out[e] = -INFINITY;
+      continue;
+    }
+    double total = 0.0;
+    for (int h = 0; h < HI; ++h) {
+      double dot = 0.0;
+      for (int d = 0; d < DI; ++d)
+        dot += rd(q_idx, dtype, (bs * HI + h) * DI + d) *
+               rd(k_idx, dtype, (b * T + t) * DI + d);
+      double u = scale * dot;
+      double wh = rd(w, dtype, bs * HI + h);
+      if (relu_mode == ORACLE_RELU_PER_HEAD)
+        total += wh * (u > 0.0 ? u : 0.0);
+      else
+        total += wh * u;
+    }
+    if (relu_mode == ORACLE_RELU_POST_SUM && !(total > 0.0)) total = 0.0;
+    out[e] = total;
+  }
+}
+
+/* One candidate of a top-k row. */
+typedef struct {
+  float score;
+  int32_t t;
+} cand_t;
+
+/* Order: higher score first, then lower position. -0.0 and +0.0 compare equal
+ * under IEEE comparison, so they fall through to the position rule. */
+static int cand_cmp(const void *pa, const void *pb) {
+  const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  if (a->t < b->t) return -1;
+  if (a->t > b->t) return 1;
+  return 0;
+}
+
+/*
+ * Per-row top-k [A.X-K2 page, SGA: keep the top index_topk positions, int32
+ * [B,S,topk]]. Rows are fp32 (what the indexer stores); NaN is outside the
+ * contract. The whole row is sorted by (score desc, t asc) and the first k
+ * entries are emitted: t when its score is above -inf, else -1. Slots past
+ * the end of the row are -1 as well.
+ *   scores [R,T] float -> out [R,k] int32
+ */
+void oracle_topk(const float *scores, int64_t R, int64_t T, int k,
+                 int32_t *out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < R; ++r) {
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(T > 0 ? T : 1));
+    for (int64_t t = 0; t < T; ++t) {
+      c[t].score = scores[r * T + t];
+      c[t].t = (int32_t)t;
+    }
+    qsort(c, (size_t)T, sizeof(cand_t), cand_cmp);
+    for (int j = 0; j < k; ++j) {
+      int32_t v = -1;
+      if (j < T && c[j].score > -INFINITY) v = c[j].t;
+      out[r * k + j] = v;
+    }
+    free(c);
+  }
+}
+
+/* sigmoid(x) = 1 / (1 + e^-x): exactly 0 at -inf, 1 at +inf, 1/2 at 0. */
+static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/*
+ * Softmax attention of one (b, s, h) query over the keys marked in sel[0..T),
+ * followed by the gate. Shared by the DSA and SWA functions below (both are
+ * the same masked softmax, they differ only in which keys are marked).
+ *   qrow [Dqk] at q + qoff; key t row at kc + ((b*T + t)*H + h)*Dqk, likewise
+ *   vc with Dv. o [Dv] receives the result.
+ */
+static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
+                               const void *vc, int dtype, int64_t b, int64_t T,
+                               int H, int h, int Dqk, int Dv, double sm_scale,
+                               const unsigned char *sel, double *logit,
+                               double *o) {
+  double mx = -INFINITY;
+  int64_t nsel = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (!sel[t]) continue;
+    double dot = 0.0;
+    for (int d = 0; d < Dqk; ++d)
+      dot += rd(q, dtype, qoff + d) *
+             rd(kc, dtype, ((b * T + t) * H + h) * (int64_t)Dqk + d);
+    logit[t] = sm_scale * dot;
+    if (logit[t] > mx) mx = logit[t];
+    ++nsel;
+  }
+  for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+  if (nsel == 0) return; /* no visible selected key: output 0 */
+  double den = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (!sel[t]) continue;
+    double e = exp(logit[t] - mx);
+    den += e;
+    for (int d = 0; d < Dv; ++d)
+      o[d] += e * rd(vc, dtype, ((b * T + t) * H + h) * (int64_t)Dv + d);
+  }
+  for (int d = 0; d < Dv; ++d) o[d] /= den;
+}
+
+/* Multiply the head output by its gate [A.X-K2 page, "Attention output gate";
+ * Spark-X2.5 page, forward-pass steps 2-3]. gate_dim 0: no gate; 1: one logit
+ * per (token, head), broadcast over v_dim; Dv: one logit per element. */
+static void apply_gate(const void *gate, int dtype, int gate_dim, int64_t bs,
+                       int H, int h, int Dv, double *o) {
+  if (gate_dim == 0 || gate == NULL) return;
+  if (gate_dim == 1) {
+    double g = sigm(rd(gate, dtype, bs * H + h));
+    for (int d = 0; d < Dv; ++d) o[d] *= g;
+  } else {
+    for (int d = 0; d < Dv; ++d)
+      o[d] *= sigm(rd(gate, dtype, (bs * H + h) * (int64_t)Dv + d));
+  }
+}
+
+/*
+ * Sparse MLA attention [A.X-K2 page, "MLA + explicit sparse mask" step 4:
+ * positions not chosen by the indexer get -inf, combined with the causal
+ * mask; step 5 and "Attention output gate": output times sigmoid gate].
+ *   q [B,S,H,Dqk] (nope slice then rope slice; the split does not change the
+ *     dot product), k_cache [B,T,H,Dqk], v_cache [B,T,H,Dv] (expanded K/V),
+ *   indices [B,S,topk] int32, gate [B,S,H] or [B,S,H,Dv] or NULL
+ *   out [B,S,H,Dv] double
+ */
+void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *indices, const void *gate, int dtype,
+                        int B, int S, int T, int past_len, int H, int Dqk,
+                        int Dv, int topk, double sm_scale, int gate_dim,
+                        double *out) {
+  int64_t n = (int64_t)B * S * H;
+#pragma omp parallel
+  {
+    unsigned char *sel = (unsigned char *)malloc((size_t)T);
+    double *logit = (double *)malloc(sizeof(double) * (size_t)T);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t e = 0; e < n; ++e) {
+      int h = (int)(e % H);
+      int64_t bs = e / H;
+      int64_t s = bs % S;
+      int64_t b = bs / S;
+      int64_t p = (int64_t)past_len + s;
+      /* additive sparse mask AND causal mask */
+      memset(sel, 0, (size_t)T);
+      for (int j = 0; j < topk; ++j) {
+        int64_t t = indices[bs * topk + j];
+        if (t >= 0 && t <= p && t < T) sel[t] = 1;
+      }
+      double *o = out + e * Dv;
+      masked_softmax_row(q, e * Dqk, k_cache, v_cache, dtype, b, T, H, h, Dqk,
+                         Dv, sm_scale, sel, logit, o);
+      apply_gate(gate, dtype, gate_dim, bs, H, h, Dv, o);
+    }
+    free(logit);
+    free(sel);
+  }
+}
+
+/*
+ * Sliding-window attention [Spark-X2.5 page: sliding_window 512;
+ * openPangu-2.0 page §3.2: SWA layers see a fixed 512-token local window].
+ * Query at p sees keys max(0, p-W+1) .. p. The K/V buffers hold T_buf rows;
+ * buffer row j is absolute position kv_offset + j.
+ *   q [B,S,H,Dqk], k_buf [B,T_buf,H,Dqk], v_buf [B,T_buf,H,Dv], gate as above
+ *   out [B,S,H,Dv] double
+ */
+void oracle_swa_attn(const void *q, const void *k_buf, const void *v_buf,
+                     const void *gate, int dtype, int B, int S, int T_buf,
+                     int past_len, int kv_offset, int H, int Dqk, int Dv,
+                     int window, double sm_scale, int gate_dim, double *out) {
+  int64_t n = (int64_t)B * S * H;
+#pragma omp parallel
+  {
+    unsigned char *sel = (unsigned char *)malloc((size_t)T_buf);
+    double *logit = (double *)malloc(sizeof(double) * (size_t)T_buf);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t e = 0; e < n; ++e) {
+      int h = (int)(e % H);
+      int64_t bs = e / H;
+      int64_t s = bs % S;
+      int64_t b = bs / S;
+      int64_t p = (int64_t)past_len + s;
+      int64_t lo = p - window + 1;
+      if (lo < 0) lo = 0;
+      for (int64_t j = 0; j < T_buf; ++j) {
+        int64_t t = (int64_t)kv_offset + j;
+        sel[j] = (t >= lo && t <= p) ? 1 : 0;
+      }
+      double *o = out + e * Dv;
+      masked_softmax_row(q, e * Dqk, k_buf, v_buf, dtype, b, T_buf, H, h, Dqk,
+                         Dv, sm_scale, sel, logit, o);
+      apply_gate(gate, dtype, gate_dim, bs, H, h, Dv, o);
+    }
+    free(logit);
+    free(sel);
+  }
+}

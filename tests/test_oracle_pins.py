@@ -1,0 +1,360 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a closed form, a library routine for a
+special case, a brute-force enumeration or an invariant, chosen so that a
+plausible slip (a dropped term, a wrong sign or index, a transposed operand,
+an off-by-one in the causal or window boundary) fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+RNG = np.random.default_rng(1234)
+
+
+def f32(*shape, scale=1.0):
+    return (RNG.standard_normal(shape) * scale).astype(np.float32)
+
+
+def sdpa_masked(q, k, v, mask, scale):
+    """torch SDPA in float64 with an explicit boolean mask (True = attend).
+    q [B,S,H,E], k [B,T,H,E], v [B,T,H,Ev], mask [B,S,T] -> [B,S,H,Ev]."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3).contiguous()
+    m = torch.from_numpy(mask)[:, None, :, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def causal_mask(B, S, T, past_len):
+    p = past_len + np.arange(S)[:, None]
+    t = np.arange(T)[None, :]
+    return np.broadcast_to(t <= p, (B, S, T)).copy()
+
+
+def sigmoid64(x):
+    return torch.sigmoid(torch.from_numpy(np.asarray(x, np.float64))).numpy()
+
+
+# ------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("past_len", [0, 5])
+def test_index_none_equals_collapsed_matmul(past_len):
+    # With no ReLU, sum_h w_h (q_h . k) = (sum_h w_h q_h) . k: a single matmul.
+    B, S, HI, DI = 2, 7, 3, 16
+    T = past_len + S
+    q, k, w = f32(B, S, HI, DI), f32(B, T, DI), f32(B, S, HI)
+    sc = 0.37
+    got = oracle.index_scores(q, k, w, past_len, scale=sc, relu_mode=oracle.RELU_NONE)
+    qeff = (w.astype(np.float64)[..., None] * q.astype(np.float64)).sum(2)
+    ref = sc * (torch.from_numpy(qeff) @ torch.from_numpy(k.astype(np.float64)).transpose(1, 2)).numpy()
+    vis = causal_mask(B, S, T, past_len)
+    np.testing.assert_allclose(got[vis], ref[vis], rtol=1e-12, atol=1e-12)
+    assert np.all(np.isneginf(got[~vis]))
+
+
+def test_index_single_head_plain_matmul():
+    # H_I = 1, w = 1: the score is the scaled matmul q k^T (ReLU'd per head).
+    B, S, DI = 1, 9, 32
+    q, k, w = f32(B, S, 1, DI), f32(B, S, DI), np.ones((B, S, 1), np.float32)
+    got = oracle.index_scores(q, k, w, 0)  # default scale DI^-1/2, per-head ReLU
+    ref = (q[:, :, 0].astype(np.float64) @ k.astype(np.float64).transpose(0, 2, 1)) / math.sqrt(DI)
+    ref = np.maximum(ref, 0.0)
+    vis = causal_mask(B, S, S, 0)
+    np.testing.assert_allclose(got[vis], ref[vis], rtol=1e-12, atol=1e-13)
+
+
+def test_index_per_head_relu_abs_construction():
+    # heads q, -q, 2q with weights 1, 2, 0.5: relu(u)+2relu(-u)+0.5relu(2u) = 2|u|.
+    B, S, DI = 1, 11, 8
+    x = f32(B, S, DI)
+    q = np.stack([x, -x, 2 * x], axis=2)
+    w = np.broadcast_to(np.array([1.0, 2.0, 0.5], np.float32), (B, S, 3)).copy()
+    k = f32(B, S, DI)
+    got = oracle.index_scores(q, k, w, 0, scale=1.0)
+    u = x.astype(np.float64) @ k.astype(np.float64).transpose(0, 2, 1)
+    vis = causal_mask(B, S, S, 0)
+    np.testing.assert_allclose(got[vis], 2 * np.abs(u)[vis], rtol=1e-12, atol=1e-13)
+
+
+def test_index_per_head_relu_identity_construction():
+    # heads q, -q with weights 1, -1: relu(u) - relu(-u) = u.
+    B, S, DI = 2, 6, 16
+    x = f32(B, S, DI)
+    q = np.stack([x, -x], axis=2)
+    w = np.broadcast_to(np.array([1.0, -1.0], np.float32), (B, S, 2)).copy()
+    k = f32(B, S, DI)
+    got = oracle.index_scores(q, k, w, 0, scale=0.25)
+    u = 0.25 * (x.astype(np.float64) @ k.astype(np.float64).transpose(0, 2, 1))
+    vis = causal_mask(B, S, S, 0)
+    np.testing.assert_allclose(got[vis], u[vis], rtol=1e-12, atol=1e-13)
+
+
+def test_index_per_head_equals_none_for_nonnegative_products():
+    B, S, HI, DI = 1, 8, 4, 16
+    q, k, w = np.abs(f32(B, S, HI, DI)), np.abs(f32(B, S, DI)), f32(B, S, HI)
+    a = oracle.index_scores(q, k, w, 0, relu_mode=oracle.RELU_PER_HEAD)
+    b = oracle.index_scores(q, k, w, 0, relu_mode=oracle.RELU_NONE)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_index_post_sum_is_relu_of_collapsed():
+    B, S, HI, DI = 1, 10, 3, 8
+    q, k, w = f32(B, S, HI, DI), f32(B, S, DI), f32(B, S, HI)
+    got = oracle.index_scores(q, k, w, 0, scale=1.0, relu_mode=oracle.RELU_POST_SUM)
+    qeff = (w.astype(np.float64)[..., None] * q.astype(np.float64)).sum(2)
+    ref = np.maximum(qeff @ k.astype(np.float64).transpose(0, 2, 1), 0.0)
+    vis = causal_mask(B, S, S, 0)
+    np.testing.assert_allclose(got[vis], ref[vis], rtol=1e-12, atol=1e-13)
+
+
+def test_index_causal_boundary_with_past_len():
+    # query s of a chunk at past_len P sees t <= P + s exactly (itself included).
+    B, S, P, HI, DI = 1, 4, 3, 2, 8
+    q, k, w = np.abs(f32(B, S, HI, DI)), np.abs(f32(B, P + S, DI)), np.abs(f32(B, S, HI))
+    got = oracle.index_scores(q, k, w, P)
+    for s in range(S):
+        assert np.all(np.isfinite(got[0, s, : P + s + 1])) and np.all(got[0, s, : P + s + 1] > 0)
+        assert np.all(np.isneginf(got[0, s, P + s + 1:]))
+
+
+def test_index_bf16_inputs_widen_exactly():
+    # bf16 bit patterns must give the same scores as their exact fp32 values.
+    B, S, HI, DI = 1, 5, 2, 16
+    qf, kf, wf = f32(B, S, HI, DI), f32(B, S, DI), f32(B, S, HI)
+    tb = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    qb, kb, wb = tb(qf), tb(kf), tb(wf)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    a = oracle.index_scores(bits(qb), bits(kb), bits(wb), 0)
+    b = oracle.index_scores(qb.float().numpy(), kb.float().numpy(), wb.float().numpy(), 0)
+    np.testing.assert_array_equal(a, b)
+
+
+# -------------------------------------------------------------------- top-k
+def brute_topk(row, k):
+    """Enumerate every k-subset; the winner has the lexicographically largest
+    list of (score, -t) sorted descending. Positions with -inf are only
+    chosen when nothing else is left, and are reported as -1."""
+    T = len(row)
+    keyed = [(float(row[t]) + 0.0, -t) for t in range(T)]
+    best = None
+    for sub in itertools.combinations(range(T), min(k, T)):
+        cand = sorted((keyed[t] for t in sub), reverse=True)
+        if best is None or cand > best:
+            best = cand
+    out = [(-nt if s > -math.inf else -1) for s, nt in best]
+    return out + [-1] * (k - len(out))
+
+
+def test_topk_brute_force_small_rows():
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        T = int(rng.integers(1, 10))
+        k = int(rng.integers(1, 10))
+        row = rng.integers(-2, 3, size=T).astype(np.float32)  # many ties
+        row[rng.random(T) < 0.2] = -np.inf
+        row[(row == 0) & (rng.random(T) < 0.5)] = -0.0
+        got = oracle.topk(row[None, :], k)[0].tolist()
+        assert got == brute_topk(row, k), (row, k)
+
+
+def test_topk_matches_lexsort():
+    rng = np.random.default_rng(8)
+    R, T, k = 6, 300, 37
+    s = (rng.integers(-20, 20, size=(R, T)) / 4).astype(np.float32)
+    s[:, ::7] = -np.inf
+    got = oracle.topk(s, k)
+    for r in range(R):
+        order = np.lexsort((np.arange(T), -s[r].astype(np.float64)))[:k]
+        exp = np.where(np.isneginf(s[r, order]), -1, order)
+        np.testing.assert_array_equal(got[r], exp)
+
+
+def test_topk_constant_row_and_signed_zero():
+    assert oracle.topk(np.full((1, 50), 3.5, np.float32), 10)[0].tolist() == list(range(10))
+    row = np.array([-0.0, 0.0, -0.0, 1.0, -0.0], np.float32)
+    assert oracle.topk(row[None], 5)[0].tolist() == [3, 0, 1, 2, 4]
+
+
+def test_topk_pads_with_minus_one():
+    row = np.array([0.5, -np.inf, 2.0, -np.inf], np.float32)
+    assert oracle.topk(row[None], 3)[0].tolist() == [2, 0, -1]
+    assert oracle.topk(row[None], 6)[0].tolist() == [2, 0, -1, -1, -1, -1]
+
+
+# ------------------------------------------------------- sparse attention
+def _attn_inputs(B, S, T, H, Dqk, Dv):
+    return f32(B, S, H, Dqk), f32(B, T, H, Dqk), f32(B, T, H, Dv), f32(B, S, H)
+
+
+@pytest.mark.parametrize("past_len", [0, 6])
+def test_attn_full_selection_is_dense_causal_sdpa(past_len):
+    B, S, H, nope, rope, Dv = 2, 9, 3, 8, 4, 6
+    T = past_len + S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, nope + rope, Dv)
+    idx = np.broadcast_to(np.arange(T, dtype=np.int32), (B, S, T)).copy()  # topk >= T
+    sc = 0.3
+    got = oracle.sparse_attn(q, kc, vc, idx, None, past_len, nope, rope, sm_scale=sc)
+    ref = sdpa_masked(q, kc, vc, causal_mask(B, S, T, past_len), sc)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attn_subset_matches_sdpa_with_boolean_mask():
+    B, S, H, nope, rope, Dv, k = 1, 12, 2, 8, 8, 5, 4
+    T = S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, nope + rope, Dv)
+    rng = np.random.default_rng(3)
+    idx = np.full((B, S, k), -1, np.int32)
+    mask = np.zeros((B, S, T), bool)
+    for s in range(S):
+        pick = rng.permutation(s + 1)[: min(k, s + 1)]
+        idx[0, s, : len(pick)] = pick
+        mask[0, s, pick] = True
+    got = oracle.sparse_attn(q, kc, vc, idx, g, 0, nope, rope, gate_dim=1)
+    ref = sdpa_masked(q, kc, vc, mask, (nope + rope) ** -0.5) * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attn_top1_closed_form():
+    # one selected key: softmax weight 1, output = V row times the gate.
+    B, S, H, Dqk, Dv = 1, 5, 3, 12, 7
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    idx = np.array([[[0], [0], [2], [1], [4]]], np.int32)
+    got = oracle.sparse_attn(q, kc, vc, idx, g, 0, 6, 6)
+    for s in range(S):
+        t = idx[0, s, 0]
+        np.testing.assert_allclose(got[0, s], vc[0, t].astype(np.float64) * sigmoid64(g[0, s])[:, None],
+                                   rtol=1e-14)
+
+
+def test_attn_gate_limits():
+    B, S, H, Dqk, Dv = 1, 6, 4, 8, 5
+    q, kc, vc, _ = _attn_inputs(B, S, S, H, Dqk, Dv)
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (B, S, S)).copy()
+    g = np.zeros((B, S, H), np.float32)
+    g[..., 0], g[..., 1], g[..., 2] = -np.inf, np.inf, 0.0
+    g[..., 3] = 1.5
+    ung = oracle.sparse_attn(q, kc, vc, idx, None, 0, 4, 4)
+    got = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4)
+    assert np.all(got[:, :, 0] == 0.0)
+    np.testing.assert_array_equal(got[:, :, 1], ung[:, :, 1])
+    np.testing.assert_array_equal(got[:, :, 2], 0.5 * ung[:, :, 2])
+    np.testing.assert_allclose(got[:, :, 3], ung[:, :, 3] / (1 + math.exp(-1.5)), rtol=1e-15)
+
+
+def test_attn_elementwise_gate():
+    B, S, H, Dqk, Dv = 1, 5, 2, 8, 4
+    q, kc, vc, _ = _attn_inputs(B, S, S, H, Dqk, Dv)
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (B, S, S)).copy()
+    g = f32(B, S, H, Dv)
+    got = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4, gate_dim=Dv)
+    ref = sdpa_masked(q, kc, vc, causal_mask(B, S, S, 0), Dqk ** -0.5) * sigmoid64(g)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attn_set_semantics():
+    # permuting an index row, or adding -1 / future / repeated entries, changes nothing.
+    B, S, H, Dqk, Dv = 1, 10, 2, 8, 4
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    rng = np.random.default_rng(5)
+    base = np.full((B, S, 3), -1, np.int32)
+    for s in range(S):
+        pick = rng.permutation(s + 1)[:3]
+        base[0, s, : len(pick)] = pick
+    a = oracle.sparse_attn(q, kc, vc, base, g, 0, 4, 4)
+    perm = base[:, :, ::-1].copy()
+    extra = np.concatenate([base, np.full((B, S, 1), -1, np.int32),
+                            np.minimum(np.arange(S)[None, :, None] + 1, S - 1).astype(np.int32),
+                            base[:, :, :1]], axis=2)
+    # the "+1" column is a future key except on the last row where it is the row itself
+    extra[0, S - 1, 4] = -1
+    np.testing.assert_array_equal(oracle.sparse_attn(q, kc, vc, perm, g, 0, 4, 4), a)
+    np.testing.assert_array_equal(oracle.sparse_attn(q, kc, vc, extra, g, 0, 4, 4), a)
+
+
+def test_attn_convexity_and_empty_selection():
+    B, S, H, Dqk, Dv = 1, 8, 3, 8, 6
+    q, kc, vc, _ = _attn_inputs(B, S, S, H, Dqk, Dv)
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (B, S, S)).copy()
+    o = oracle.sparse_attn(q, kc, vc, idx, None, 0, 4, 4)
+    for s in range(S):
+        lo = vc[0, : s + 1].min(0)
+        hi = vc[0, : s + 1].max(0)
+        assert np.all(o[0, s] >= lo - 1e-12) and np.all(o[0, s] <= hi + 1e-12)
+    none = np.full((B, S, 2), -1, np.int32)
+    assert np.all(oracle.sparse_attn(q, kc, vc, none, None, 0, 4, 4) == 0.0)
+
+
+def test_attn_chunk_and_decode_consistency():
+    # one prefill of S rows == two calls of S/2 (second at past_len S/2) and
+    # the decode call at p == the last prefill row.
+    B, S, H, Dqk, Dv, k = 2, 10, 2, 8, 4, 4
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    rng = np.random.default_rng(9)
+    idx = np.full((B, S, k), -1, np.int32)
+    for b in range(B):
+        for s in range(S):
+            pick = rng.permutation(s + 1)[:k]
+            idx[b, s, : len(pick)] = pick
+    full = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4)
+    h = S // 2
+    first = oracle.sparse_attn(q[:, :h], kc[:, :h], vc[:, :h], idx[:, :h], g[:, :h], 0, 4, 4)
+    second = oracle.sparse_attn(q[:, h:], kc, vc, idx[:, h:], g[:, h:], h, 4, 4)
+    np.testing.assert_array_equal(np.concatenate([first, second], 1), full)
+    dec = oracle.sparse_attn(q[:, -1:], kc, vc, idx[:, -1:], g[:, -1:], S - 1, 4, 4)
+    np.testing.assert_array_equal(dec, full[:, -1:])
+
+
+# -------------------------------------------------------------------- SWA
+def test_swa_wide_window_is_dense_causal():
+    B, S, H, Dqk, Dv = 1, 9, 2, 8, 4
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    got = oracle.swa_attn(q, kc, vc, g, 0, 0, S + 3, 4, 4)
+    ref = sdpa_masked(q, kc, vc, causal_mask(B, S, S, 0), Dqk ** -0.5) * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_swa_window_one_closed_form():
+    B, S, H, Dqk, Dv = 1, 6, 3, 8, 5
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    got = oracle.swa_attn(q, kc, vc, g, 0, 0, 1, 4, 4)
+    ref = vc[0].astype(np.float64) * sigmoid64(g[0])[..., None]
+    np.testing.assert_allclose(got[0], ref, rtol=1e-14)
+
+
+@pytest.mark.parametrize("W", [2, 3, 5])
+def test_swa_band_matches_sdpa_band_mask(W):
+    B, S, P, H, Dqk, Dv = 1, 7, 4, 2, 8, 4
+    T = P + S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, Dqk, Dv)
+    p = P + np.arange(S)[:, None]
+    t = np.arange(T)[None, :]
+    band = ((t <= p) & (t >= p - W + 1))[None]
+    got = oracle.swa_attn(q, kc, vc, None, P, 0, W, 4, 4)
+    ref = sdpa_masked(q, kc, vc, band, Dqk ** -0.5)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_swa_buffer_offset_equivalence():
+    # a window buffer starting at kv_offset gives the same result as the full cache.
+    B, S, P, H, Dqk, Dv, W = 1, 5, 9, 2, 8, 4, 4
+    T = P + S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, Dqk, Dv)
+    full = oracle.swa_attn(q, kc, vc, g, P, 0, W, 4, 4)
+    off = P - W + 1
+    part = oracle.swa_attn(q, kc[:, off:], vc[:, off:], g, P, off, W, 4, 4)
+    np.testing.assert_array_equal(part, full)
+
+
+def test_swa_equals_sparse_attn_with_window_indices():
+    B, S, H, Dqk, Dv, W = 1, 8, 2, 8, 4, 3
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    idx = np.array([[[s - j if s - j >= 0 else -1 for j in range(W)] for s in range(S)]], np.int32)
+    a = oracle.swa_attn(q, kc, vc, g, 0, 0, W, 4, 4)
+    b = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4)
+    np.testing.assert_array_equal(a, b)
