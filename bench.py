@@ -1,0 +1,364 @@
+"""Benchmark of the DSA layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic
+inputs already resident in HBM:
+  prefill workloads  indexer scores -> top-k -> sparse attention (+ gate)
+  decode workloads   indexer scores (S = 1) -> top-k -> split-K decode
+  hybrid-512k        DSA chunk (indexer, top-k, attention) + 2 SWA chunk
+                     layers, then one decode token through the DSA layer and
+                     both SWA layers
+Every stage is a C-ABI call of libdsa.so; stage times come from HIP events
+recorded on the same stream the library launches on.
+
+Prints ONE JSON line. `value` is prefill tokens/s of the named workload
+(default mla-s4k, the DeepSeek-V2-shaped 4096-token prefill); the other
+workloads are measured in the same run and reported under "also".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA layer prefill tokens/s + decode µs/step; % MFMA / HBM roofline"
+PEAK_BF16 = 2.5e15
+PEAK_HBM = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mla-s4k")
+    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k",
+                    help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--also-steps", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+class Layer:
+    """Device buffers and the stage list of one workload."""
+
+    def __init__(self, wl, torch, dsa, datagen):
+        self.wl, self.torch, self.dsa = wl, torch, dsa
+        dev = torch.device("cuda")
+        tdt = torch.bfloat16 if wl.dtype == 1 else torch.float32
+        B, S, P, T = wl.B, wl.S, wl.past_len, wl.T
+        H, Dqk, Dv, HI, DI, k = wl.H, wl.Dqk, wl.v, wl.HI, wl.DI, wl.topk
+        self.T_alloc = T + (1 if wl.decode_after else 0)
+        Ta = self.T_alloc
+        E = lambda *shape: torch.empty(*shape, dtype=tdt, device=dev)
+        gen = lambda t, tid, sc, start=0: datagen.normal_device(t, wl.seed, tid, sc, start)
+        # caches (B rows of T_alloc tokens) and query-side tensors
+        self.k = gen(E(B, Ta, H, Dqk), datagen.TID_K, wl.scale_k)
+        self.v = gen(E(B, Ta, H, Dv), datagen.TID_V, wl.scale_v)
+        self.k_idx = gen(E(B, Ta, DI), datagen.TID_KIDX, wl.scale_kidx)
+        self.q = gen(E(B, S, H, Dqk), datagen.TID_Q, wl.scale_q)
+        self.q_idx = gen(E(B, S, HI, DI), datagen.TID_QIDX, wl.scale_qidx)
+        self.w = gen(E(B, S, HI), datagen.TID_W, wl.scale_w)
+        self.gate = gen(E(B, S, H), datagen.TID_GATE, wl.scale_gate)
+        self.scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(B, S, k, dtype=torch.int32, device=dev)
+        self.out = E(B, S, H, Dv)
+        if S > 1:
+            nb = dsa.dsa_sparse_attn_prefill_workspace_size(B, S, T, H, Dqk, Dv, k, wl.dtype)
+        else:
+            nb = dsa.dsa_sparse_attn_decode_workspace_size(B, H, Dv, k)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.tk_ws = torch.empty(max(dsa.dsa_topk_workspace_size(B, S, T, k), 1), dtype=torch.uint8,
+                                 device=dev)
+        # hybrid: decode token + SWA layers
+        self.swa = []
+        if wl.decode_after:
+            st = S  # the decode query is row S of the query streams
+            self.qd = gen(E(B, 1, H, Dqk), datagen.TID_Q, wl.scale_q, st * H * Dqk)
+            self.qd_idx = gen(E(B, 1, HI, DI), datagen.TID_QIDX, wl.scale_qidx, st * HI * DI)
+            self.wd = gen(E(B, 1, HI), datagen.TID_W, wl.scale_w, st * HI)
+            self.gd = gen(E(B, 1, H), datagen.TID_GATE, wl.scale_gate, st * H)
+            self.sd = torch.empty(B, 1, T + 1, dtype=torch.float32, device=dev)
+            self.idd = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+            self.od = E(B, 1, H, Dv)
+            self.wsd = torch.empty(dsa.dsa_sparse_attn_decode_workspace_size(B, H, Dv, k),
+                                   dtype=torch.uint8, device=dev)
+            W = wl.window
+            for j in range(1, wl.n_swa + 1):
+                off = max(0, P - W + 1)
+                Tb = P + S - off
+                offd = max(0, P + S - W + 1)
+                Tbd = P + S + 1 - offd
+                tid = lambda base: base + datagen.SWA_TID_STRIDE * j
+                lay = {
+                    # buffer row r = absolute position off + r (B = 1 in this workload)
+                    "k": gen(E(B, Tb + 1, H, Dqk), tid(datagen.TID_K), wl.scale_k, off * H * Dqk),
+                    "v": gen(E(B, Tb + 1, H, Dv), tid(datagen.TID_V), wl.scale_v, off * H * Dv),
+                    "q": gen(E(B, S, H, Dqk), tid(datagen.TID_Q), wl.scale_q),
+                    "g": gen(E(B, S, H), tid(datagen.TID_GATE), wl.scale_gate),
+                    "qd": gen(E(B, 1, H, Dqk), tid(datagen.TID_Q), wl.scale_q, S * H * Dqk),
+                    "gd": gen(E(B, 1, H), tid(datagen.TID_GATE), wl.scale_gate, S * H),
+                    "o": E(B, S, H, Dv), "od": E(B, 1, H, Dv),
+                    "off": off, "Tb": Tb, "offd": offd, "Tbd": Tbd,
+                }
+                nbw = dsa.swa_attn_workspace_size(B, S, H, Dqk, Dv, W, wl.dtype)
+                lay["ws"] = torch.empty(max(nbw, 1), dtype=torch.uint8, device=dev)
+                lay["wsd"] = torch.empty(dsa.swa_attn_workspace_size(B, 1, H, Dqk, Dv, W, wl.dtype),
+                                         dtype=torch.uint8, device=dev)
+                self.swa.append(lay)
+        torch.cuda.synchronize()
+
+    # each stage: (name, callable)
+    def stages(self):
+        wl, dsa = self.wl, self.dsa
+        P, S = wl.past_len, wl.S
+        st = [
+            ("K1 index_scores", lambda: dsa.dsa_index_scores(self.q_idx, self.k_idx[:, : wl.T] if wl.B == 1 else self.k_idx, self.w, self.scores, P)),
+            ("K2 topk", lambda: dsa.dsa_topk(self.scores, self.idx, self.tk_ws)),
+        ]
+        kc = self.k if self.T_alloc == wl.T else self.k[:, : wl.T]
+        vc = self.v if self.T_alloc == wl.T else self.v[:, : wl.T]
+        if S > 1:
+            st.append(("K3 sparse_attn_prefill", lambda: dsa.dsa_sparse_attn_prefill(
+                self.q, kc, vc, self.idx, self.gate, self.out, P, wl.nope, wl.rope, workspace=self.ws)))
+        else:
+            st.append(("K4 sparse_attn_decode", lambda: dsa.dsa_sparse_attn_decode(
+                self.q, kc, vc, self.idx, self.gate, self.out, wl.nope, wl.rope, workspace=self.ws)))
+        for j, L in enumerate(self.swa):
+            st.append((f"K5 swa_attn chunk L{j + 1}", lambda L=L: dsa.swa_attn(
+                L["q"], L["k"][:, : L["Tb"]], L["v"][:, : L["Tb"]], L["g"], L["o"], P, L["off"],
+                wl.window, wl.nope, wl.rope, workspace=L["ws"])))
+        if wl.decode_after:
+            Td = wl.T + 1
+            st += [
+                ("D K1 index_scores", lambda: dsa.dsa_index_scores(self.qd_idx, self.k_idx, self.wd, self.sd, Td - 1)),
+                ("D K2 topk", lambda: dsa.dsa_topk(self.sd, self.idd, self.tk_ws)),
+                ("D K4 sparse_attn_decode", lambda: dsa.dsa_sparse_attn_decode(
+                    self.qd, self.k, self.v, self.idd, self.gd, self.od, wl.nope, wl.rope,
+                    workspace=self.wsd)),
+            ]
+            for j, L in enumerate(self.swa):
+                st.append((f"D K5 swa_attn L{j + 1}", lambda L=L: dsa.swa_attn(
+                    L["qd"], L["k"][:, L["offd"] - L["off"]:L["offd"] - L["off"] + L["Tbd"]],
+                    L["v"][:, L["offd"] - L["off"]:L["offd"] - L["off"] + L["Tbd"]], L["gd"],
+                    L["od"], Td - 1, L["offd"], wl.window, wl.nope, wl.rope, workspace=L["wsd"])))
+        return st
+
+
+def contiguous_view(t):
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def time_layer(layer, steps, warmup, torch):
+    stages = layer.stages()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for s in range(steps):
+        for (name, fn), (a, b) in zip(stages, ev[s]):
+            a.record(stream)
+            fn()
+            b.record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_stage = {}
+    for i, (name, _) in enumerate(stages):
+        ts = [ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3 for s in range(steps)]
+        per_stage[name] = {"mean_us": float(np.mean(ts)), "min_us": float(np.min(ts)),
+                           "median_us": float(np.median(ts))}
+    total_ms = t_all0.elapsed_time(t_all1) / steps
+    return per_stage, total_ms, wall
+
+
+# ------------------------------------------------------ algorithmic work
+def work(wl):
+    """Algorithmic flops / bytes per stage (the dense work DSA avoids is not counted)."""
+    B, S, P, T, k = wl.B, wl.S, wl.past_len, wl.T, wl.topk
+    esz = 2 if wl.dtype == 1 else 4
+    pos = P + np.arange(S, dtype=np.float64)
+    vis = float(B * np.sum(pos + 1))                 # visible (s, t) pairs
+    sel = float(B * np.sum(np.minimum(k, pos + 1)))  # selected pairs
+    out = {
+        "K1": {"flops": 2.0 * wl.HI * wl.DI * vis,
+               "bytes": esz * (B * S * wl.HI * wl.DI + B * T * wl.DI + B * S * wl.HI) + 4.0 * B * S * T},
+        "K2": {"bytes": 4.0 * B * S * T + 4.0 * B * S * k},
+        "attn": {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * sel,
+                 "dense_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * vis,
+                 "bytes_once": esz * (B * T * wl.H * (wl.Dqk + wl.v) + B * S * wl.H * (wl.Dqk + 2 * wl.v)),
+                 "bytes_gather": esz * sel * wl.H * (wl.Dqk + wl.v)},
+    }
+    if wl.decode_after:
+        Td = T + 1
+        out["D"] = {"K1_bytes": esz * (B * Td * wl.DI) + 4.0 * B * Td,
+                    "K4_bytes": esz * B * k * wl.H * (wl.Dqk + wl.v),
+                    "K4_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * B * k}
+    if wl.n_swa:
+        W = wl.window
+        win = float(B * np.sum(np.minimum(W, pos + 1)))
+        out["K5"] = {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * win}
+    return out
+
+
+def summarize(wl, per_stage, total_ms):
+    w = work(wl)
+    g = lambda name: per_stage[name]["mean_us"] * 1e-6
+    r = {"workload": wl.name, "ms_per_step": total_ms,
+         "stages_us": {k: round(v["mean_us"], 2) for k, v in per_stage.items()}}
+    t1, t2 = g("K1 index_scores"), g("K2 topk")
+    r["K1_mfma_frac"] = w["K1"]["flops"] / t1 / PEAK_BF16
+    r["K1_tflops"] = w["K1"]["flops"] / t1 / 1e12
+    r["K2_hbm_frac"] = w["K2"]["bytes"] / t2 / PEAK_HBM
+    if wl.S > 1:
+        t3 = g("K3 sparse_attn_prefill")
+        r["K3_useful_mfma_frac"] = w["attn"]["flops"] / t3 / PEAK_BF16
+        r["K3_issued_mfma_frac"] = w["attn"]["dense_flops"] / t3 / PEAK_BF16
+        pre = sum(v["mean_us"] for k_, v in per_stage.items() if not k_.startswith("D ")) * 1e-6
+        r["prefill_tokens_per_s"] = wl.B * wl.S / pre
+        r["prefill_us"] = pre * 1e6
+    else:
+        t4 = g("K4 sparse_attn_decode")
+        r["decode_us_per_step"] = total_ms * 1e3
+        r["K4_hbm_frac"] = w["attn"]["bytes_gather"] / t4 / PEAK_HBM
+        r["K4_GBps"] = w["attn"]["bytes_gather"] / t4 / 1e9
+        r["K1_hbm_frac"] = w["K1"]["bytes"] / t1 / PEAK_HBM
+    if wl.decode_after:
+        dec = sum(v["mean_us"] for k_, v in per_stage.items() if k_.startswith("D ")) * 1e-6
+        r["decode_us_per_step"] = dec * 1e6
+        r["D_K4_hbm_frac"] = w["D"]["K4_bytes"] / g("D K4 sparse_attn_decode") / PEAK_HBM
+    return r
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of query rows of the
+    same workload, timed on this host's cores: indexer -> top-k -> attention
+    for blocks of consecutive query rows spread over the sequence."""
+    import datagen
+    import oracle
+
+    oracle.build(force=False)
+    B, S, P = wl.B, wl.S, wl.past_len
+    T = wl.T
+    dt = wl.dtype_name
+    g = lambda shape, tid, sc, start=0: datagen.normal_host(shape, dt, wl.seed, tid, sc, start)
+    k_idx = g((1, T, wl.DI), datagen.TID_KIDX, wl.scale_kidx)
+    kc = g((1, T, wl.H, wl.Dqk), datagen.TID_K, wl.scale_k)
+    vc = g((1, T, wl.H, wl.v), datagen.TID_V, wl.scale_v)
+    block = 8
+    starts = np.linspace(0, S - block, 16).astype(int) if S > block else [0]
+    rows = 0
+    t0 = time.perf_counter()
+    for s0 in starts:
+        n = min(block, S - s0)
+        q_idx = g((1, n, wl.HI, wl.DI), datagen.TID_QIDX, wl.scale_qidx, s0 * wl.HI * wl.DI)
+        w = g((1, n, wl.HI), datagen.TID_W, wl.scale_w, s0 * wl.HI)
+        q = g((1, n, wl.H, wl.Dqk), datagen.TID_Q, wl.scale_q, s0 * wl.H * wl.Dqk)
+        gate = g((1, n, wl.H), datagen.TID_GATE, wl.scale_gate, s0 * wl.H)
+        Tn = P + s0 + n
+        sc = oracle.index_scores(q_idx, k_idx[:, :Tn], w, P + s0)
+        idx = oracle.topk(sc.astype(np.float32), wl.topk)
+        oracle.sparse_attn(q, kc[:, :Tn], vc[:, :Tn], idx, gate, P + s0, wl.nope, wl.rope)
+        rows += n
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows} query rows of {wl.name} (blocks of {block} spread over the "
+                      f"{S}-token prefill, B=1): indexer + top-k + sparse attention + gate in "
+                      f"fp64, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by query rows / key ranges, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import datagen
+    import sparse_attention_11_amd as dsa
+    from datagen.configs import WORKLOADS
+
+    dsa.lib()
+    torch.cuda.init()
+    wl = WORKLOADS[args.workload]
+    layer = Layer(wl, torch, dsa, datagen)
+    per_stage, total_ms, wall = time_layer(layer, args.steps, args.warmup, torch)
+    main_r = summarize(wl, per_stage, total_ms)
+    del layer
+    torch.cuda.empty_cache()
+
+    also = {}
+    for name in [s for s in args.also.split(",") if s]:
+        if name == wl.name:
+            continue
+        lay = Layer(WORKLOADS[name], torch, dsa, datagen)
+        ps, tm, _ = time_layer(lay, args.also_steps, 2, torch)
+        also[name] = summarize(WORKLOADS[name], ps, tm)
+        del lay
+        torch.cuda.empty_cache()
+        print(f"# {name}: {tm:.3f} ms/step", file=sys.stderr, flush=True)
+
+    w = work(wl)
+    t3 = per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6 if wl.S > 1 else None
+    if t3 is not None:
+        ach = w["attn"]["flops"] / t3 / 1e12
+        roof = {"kernel": "K3 sparse_attn_prefill (bitmap + MFMA flash)", "bound": "mfma",
+                "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
+                "algorithmic_flops_per_launch": w["attn"]["flops"],
+                "issued_dense_flops_per_launch": w["attn"]["dense_flops"],
+                "mean_launch_us": t3 * 1e6}
+    else:
+        t4 = per_stage["K4 sparse_attn_decode"]["mean_us"] * 1e-6
+        ach = w["attn"]["bytes_gather"] / t4 / 1e9
+        roof = {"kernel": "K4 sparse_attn_decode", "bound": "hbm", "achieved": ach,
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM,
+                "traffic": None, "mean_launch_us": t4 * 1e6}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": main_r.get("prefill_tokens_per_s", 1e6 / main_r.get("decode_us_per_step", 1.0)),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype_name, "data": "synthetic (seeded Irwin-Hall normal inputs in HBM)",
+        "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "past_len": wl.past_len,
+                   "heads": wl.H, "qk_nope": wl.nope, "qk_rope": wl.rope, "v": wl.v,
+                   "index_heads": wl.HI, "index_dim": wl.DI, "topk": wl.topk,
+                   "parallelism": "single GPU"},
+        "decode_us_per_step": main_r.get("decode_us_per_step"),
+        "stages": main_r,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,91 @@
+"""The five workloads, as shapes plus the distribution of every input tensor.
+
+Every tensor is drawn from the seeded generator in this package: a normal
+N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
+
+  tiny-fp32     B 1, S = T = 256 causal prefill; 4 heads (nope 32, rope 16,
+                v 32); indexer 2 heads x 32; top-k 64; fp32; all N(0,1),
+                index weights / sqrt(2), gate logits N(0,1).
+  mla-s4k       B 1, S = T = 4096; 20 heads (64, 64, v 128); indexer 4 x 64;
+                top-k 512; bf16; every tensor N(0,1) / sqrt(d) where d is its
+                innermost size (q, K: 128; V: 128; q_idx, k_idx: 64), index
+                weights / sqrt(4); gate logits unscaled N(0,1).
+  dsa-s32k      B 1, S = T = 32768; 128 heads (128, 64, v 128); indexer 64 x
+                128; top-k 2048; bf16; N(0,1), index weights / sqrt(64), gate
+                logits N(0,1).
+  decode-b8     B 8 x 131072 cached tokens, one new query each (S 1, past_len
+                131071); heads and indexer as dsa-s32k; top-k 2048.
+  hybrid-512k   B 1; 524288 cached tokens; DSA layer with 32 heads (128, 64,
+                v 128), indexer 32 x 128, top-k 2048; two SWA layers, window
+                512; a 4096-token chunk (past_len 524288) then one decode
+                token (position 528384); index weights / sqrt(32).
+
+Element (b, t, h, d) of a cache is element ((b*T_alloc + t)*H + h)*D + d of
+its stream, so a window buffer starting at absolute position kv_offset is the
+stream from kv_offset*H*D on (B = 1).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+F32, BF16 = 0, 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: int
+    B: int
+    S: int
+    past_len: int
+    H: int
+    nope: int
+    rope: int
+    v: int
+    HI: int
+    DI: int
+    topk: int
+    seed: int
+    window: int = 512
+    n_swa: int = 0            # SWA layers in the stack (hybrid: 2)
+    decode_after: bool = False  # hybrid: one decode token after the chunk
+    scale_q: float = 1.0
+    scale_k: float = 1.0
+    scale_v: float = 1.0
+    scale_qidx: float = 1.0
+    scale_kidx: float = 1.0
+    scale_w: float = 1.0
+    scale_gate: float = 1.0
+    notes: str = ""
+
+    @property
+    def T(self) -> int:
+        return self.past_len + self.S
+
+    @property
+    def Dqk(self) -> int:
+        return self.nope + self.rope
+
+    @property
+    def dtype_name(self) -> str:
+        return "f32" if self.dtype == F32 else "bf16"
+
+
+WORKLOADS = {
+    "tiny-fp32": Workload("tiny-fp32", F32, B=1, S=256, past_len=0, H=4, nope=32, rope=16, v=32,
+                          HI=2, DI=32, topk=64, seed=0, scale_w=1 / math.sqrt(2)),
+    "mla-s4k": Workload("mla-s4k", BF16, B=1, S=4096, past_len=0, H=20, nope=64, rope=64, v=128,
+                        HI=4, DI=64, topk=512, seed=1, scale_q=1 / math.sqrt(128),
+                        scale_k=1 / math.sqrt(128), scale_v=1 / math.sqrt(128),
+                        scale_qidx=1 / 8.0, scale_kidx=1 / 8.0, scale_w=0.5),
+    "dsa-s32k": Workload("dsa-s32k", BF16, B=1, S=32768, past_len=0, H=128, nope=128, rope=64,
+                         v=128, HI=64, DI=128, topk=2048, seed=2, scale_w=1 / 8.0),
+    "decode-b8": Workload("decode-b8", BF16, B=8, S=1, past_len=131071, H=128, nope=128, rope=64,
+                          v=128, HI=64, DI=128, topk=2048, seed=3, scale_w=1 / 8.0),
+    "hybrid-512k": Workload("hybrid-512k", BF16, B=1, S=4096, past_len=524288, H=32, nope=128,
+                            rope=64, v=128, HI=32, DI=128, topk=2048, seed=4, n_swa=2,
+                            decode_after=True, scale_w=1 / math.sqrt(32)),
+}
+
+ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k"]

@@ -1,0 +1,186 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: one DeepSeek-Sparse-Attention (DSA) layer and
+ * its sliding-window (SWA) sibling on an AMD Instinct MI355X (gfx950).
+ *
+ * Pages defining the operations (cited by title and section):
+ *  [AXK2]    "Transformers 中的 AXK2 架构解析" (A.X-K2 in HF Transformers):
+ *            "注意力前向的骨架：MLA + 显式稀疏掩码" (MLA forward with an explicit
+ *            sparse mask), "三大改进" §1 Sparse Gated Attention (lightning
+ *            indexer), §3 Attention output gate, and the AXK2Config section
+ *            (index_topk, index_head_dim, index_n_heads).
+ *  [SPARK]   Spark-X2.5-1.7B headwise attention output gate: "前向流程" steps
+ *            1-3 and "为什么要加这一层门控" (sliding_window 512).
+ *  [DSV2]    DeepSeek-V2 attention constructor parameters: items 4-6
+ *            (qk_nope_head_dim, qk_rope_head_dim, v_head_dim).
+ *  [PANGU]   openPangu-2.0 technical-report walkthrough: §3.2 (DSA-SWA-SWA,
+ *            window 512), §3.3 (lightning indexer, fixed top-K), §3.5 Table 1.
+ *
+ * Conventions shared by every entry point
+ *  - Dtypes: DSA_F32 or DSA_BF16 applies to every floating input and to the
+ *    attention output. Scores are always fp32, indices always int32.
+ *  - Layouts are dense row-major with no padding. Caches are token-major:
+ *    k_cache [B,T,H,Dqk], v_cache [B,T,H,Dv]; q [B,S,H,Dqk]. The last
+ *    dimension of q and K is the nope slice followed by the rope slice
+ *    ([DSV2] items 4-5); v_dim is separate ([DSV2] item 6).
+ *  - Positions: query s of a call sits at absolute position p = past_len + s
+ *    and may see keys t <= p (itself included). The caller has already
+ *    appended this call's K/V rows and index keys to the caches
+ *    ([AXK2] cache note), so T >= past_len + S.
+ *  - Ownership: the caller allocates every buffer (inputs, outputs and the
+ *    workspace) in device memory. The library never allocates or frees
+ *    memory and keeps no pointer after a call returns.
+ *  - Streams: every call only enqueues work on `stream` (0 = the default
+ *    stream) and returns; outputs are valid once the stream reaches that
+ *    point. Inputs must stay unchanged until then. Outputs must not alias
+ *    inputs. Calls on different streams may run concurrently as long as they
+ *    do not share a workspace.
+ *  - Errors: every call validates its arguments on the host before touching
+ *    the device and returns a status code (DSA_OK = 0). On error nothing is
+ *    enqueued, and dsa_last_error() returns a message for the calling thread.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DSA_OK 0
+#define DSA_ERR_INVALID_ARG 1 /* null pointer, bad size, bad enum, T < past_len + S, ... */
+#define DSA_ERR_UNSUPPORTED 2 /* valid but not implemented (head dims, topk > DSA_MAX_TOPK) */
+#define DSA_ERR_WORKSPACE 3   /* workspace pointer null or smaller than the *_workspace_size */
+#define DSA_ERR_HIP 4         /* a HIP launch failed; dsa_last_error() holds the message */
+
+/* dtype */
+#define DSA_F32 0
+#define DSA_BF16 1
+
+/* relu_mode of the indexer: where the ReLU sits relative to the head sum */
+#define DSA_RELU_PER_HEAD 0 /* sum_h w_h * relu(u_h)  (default) */
+#define DSA_RELU_NONE 1     /* sum_h w_h * u_h        (the printed formula) */
+#define DSA_RELU_POST_SUM 2 /* relu(sum_h w_h * u_h) */
+
+/* limits */
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_HEAD_DIM 256
+
+/*
+ * Lightning-indexer scores with causal mask ([AXK2] §1: per-head dot products
+ * of the index query with the shared index key, weighted by the learned
+ * per-head weights and summed; causality by an upper-triangle mask;
+ * [PANGU] §3.3).
+ *   score[b,s,t] = sum_h w[b,s,h] * relu(scale * q_idx[b,s,h,:] . k_idx[b,t,:])
+ *   for t <= p = past_len + s, and -inf for p < t < T.
+ * q_idx  [B,S,n_idx_heads,idx_dim]   dtype
+ * k_idx  [B,T,idx_dim]               dtype (the indexer's own key cache)
+ * w      [B,S,n_idx_heads]           dtype (per-head weights)
+ * scores [B,S,T] fp32, written in full (every element, including the -inf
+ *        triangle).
+ * scale  > 0 and finite; the conventional value is idx_dim^-1/2.
+ * relu_mode one of DSA_RELU_*.
+ * Supported: idx_dim in {32, 64, 128}; any n_idx_heads >= 1.
+ */
+int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
+                     int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
+                     int relu_mode, int dtype, hipStream_t stream);
+
+/*
+ * Per-query top-k of the score rows ([AXK2] §1: the indexer returns the top
+ * index_topk positions as int32 [B,S,topk]; AXK2Config: index_topk, clamped
+ * to the number of keys by the caller).
+ * indices[b,s,j] lists the topk positions with the largest scores, ordered by
+ * score descending and, among equal scores, position ascending (-0.0 equals
+ * +0.0). A slot whose score is -inf (a causally invisible key) holds -1.
+ * Every row is independent; results are bit-identical from run to run.
+ * scores  [B,S,T] fp32, finite or -inf (NaN is outside the contract)
+ * indices [B,S,topk] int32
+ * 1 <= topk <= min(T, DSA_MAX_TOPK).
+ * workspace: at least dsa_topk_workspace_size(...) bytes (may be 0 bytes, in
+ * which case workspace may be NULL).
+ */
+size_t dsa_topk_workspace_size(int B, int S, int T, int topk);
+int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sparse MLA attention over the selected expanded K/V rows, prefill
+ * ([AXK2] "MLA + explicit sparse mask" steps 3-5: the cache holds expanded
+ * K/V; the indexer's positions form an additive mask, combined with the
+ * causal mask, so each query attends only to its selected, visible keys;
+ * the result is multiplied by a sigmoid gate; [SPARK] steps 2-3: the gate is
+ * one scalar per token and head, sigmoid taken in fp32).
+ * For each (b, s, h), with Sel = { t in indices[b,s,:] : 0 <= t <= p }:
+ *   out[b,s,h,:] = sigmoid(g) * sum_{t in Sel} softmax_t(sm_scale * q.K[t]) V[t]
+ * where g = gate[b,s,h] (gate_dim 1) or gate[b,s,h,:] (gate_dim = v_dim), or
+ * no gate (gate_dim 0, gate may be NULL). An empty Sel gives 0. Index lists
+ * are sets: -1 and out-of-range entries are ignored; a position may appear at
+ * most once per row (dsa_topk never repeats one).
+ * q [B,S,H,Dqk], k_cache [B,T,H,Dqk], v_cache [B,T,H,Dv], indices
+ * [B,S,topk] int32, gate as above, out [B,S,H,Dv]; Dqk = qk_nope_dim +
+ * qk_rope_dim. sm_scale > 0 and finite (conventionally Dqk^-1/2).
+ * Supported: Dqk and v_dim multiples of 16, at most DSA_MAX_HEAD_DIM;
+ * topk <= DSA_MAX_TOPK.
+ * workspace: at least dsa_sparse_attn_prefill_workspace_size(...) bytes, with
+ * qk_dim = Dqk (a per-query selection bitmap for the MFMA path; per-split
+ * partial softmax states when S is small or dtype is fp32).
+ */
+size_t dsa_sparse_attn_prefill_workspace_size(int B, int S, int T, int H, int qk_dim, int v_dim,
+                                              int topk, int dtype);
+int dsa_sparse_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* indices, const void* gate, void* out, int B, int S,
+                            int T, int past_len, int H, int qk_nope_dim, int qk_rope_dim,
+                            int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The same attention for one new token per sequence (decode): S = 1 and
+ * past_len = T - 1, so every cached key is causally visible.
+ * q [B,1,H,Dqk], caches [B,T,H,*], indices [B,1,topk], gate [B,1,H(,Dv)],
+ * out [B,1,H,Dv].
+ * workspace: at least dsa_sparse_attn_decode_workspace_size(...) bytes
+ * (per-split partial softmax states).
+ */
+size_t dsa_sparse_attn_decode_workspace_size(int B, int H, int v_dim, int topk);
+int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* indices, const void* gate, void* out, int B, int T,
+                           int H, int qk_nope_dim, int qk_rope_dim, int v_dim, int topk,
+                           float sm_scale, int gate_dim, int dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sliding-window attention ([SPARK] sliding_window 512; [PANGU] §3.2: SWA
+ * layers see a fixed local window of 512 tokens). Query at p attends to the
+ * keys max(0, p-window+1) .. p, then the same gate as above.
+ * The K/V buffers may hold only a suffix of the sequence: buffer row j is
+ * absolute position kv_offset + j, and T_buf = past_len + S - kv_offset
+ * rows are present. kv_offset must satisfy
+ *   0 <= kv_offset <= max(0, past_len - window + 1)
+ * so that every query's window lies inside the buffer.
+ * q [B,S,H,Dqk], k_buf [B,T_buf,H,Dqk], v_buf [B,T_buf,H,Dv], gate, out as
+ * above. Both prefill (S > 1) and decode (S = 1) shapes are accepted.
+ * workspace: at least swa_attn_workspace_size(...) bytes, with qk_dim = Dqk
+ * (0 for the MFMA path: bf16 with S >= 16).
+ */
+size_t swa_attn_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                               int dtype);
+int swa_attn(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,
+             int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
+             int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text of a status code (static storage). */
+const char* dsa_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

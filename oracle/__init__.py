@@ -126,10 +126,19 @@ def topk(scores, k: int) -> np.ndarray:
     return out
 
 
+def _gate_dim(gate, Dv, gate_dim):
+    if gate is None:
+        return 0
+    if gate_dim is None:
+        return 1 if gate.ndim == 3 else Dv
+    return gate_dim
+
+
 def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: int,
-                qk_rope_dim: int, sm_scale: float | None = None, gate_dim: int = 1) -> np.ndarray:
-    """q [B,S,H,Dqk], caches [B,T,H,D], indices [B,S,k] int32, gate [B,S,H(,Dv)] or None
-    -> out [B,S,H,Dv] float64."""
+                qk_rope_dim: int, sm_scale: float | None = None,
+                gate_dim: int | None = None) -> np.ndarray:
+    """q [B,S,H,Dqk], caches [B,T,H,D], indices [B,S,k] int32, gate [B,S,H] (one logit
+    per head) or [B,S,H,Dv] (one per element) or None -> out [B,S,H,Dv] float64."""
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     indices = _c(np.asarray(indices, dtype=np.int32))
     B, S, H, Dqk = q.shape
@@ -137,9 +146,8 @@ def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: 
     T = k_cache.shape[1]
     Dv = v_cache.shape[3]
     topk_ = indices.shape[2]
-    if gate is None:
-        gate_dim = 0
-    else:
+    gate_dim = _gate_dim(gate, Dv, gate_dim)
+    if gate is not None:
         gate = _c(gate)
     if sm_scale is None:
         sm_scale = Dqk ** -0.5
@@ -152,7 +160,7 @@ def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: 
 
 def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
              qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
-             gate_dim: int = 1) -> np.ndarray:
+             gate_dim: int | None = None) -> np.ndarray:
     """q [B,S,H,Dqk], buffers [B,T_buf,H,D] (row j = position kv_offset + j)
     -> out [B,S,H,Dv] float64."""
     q, k_buf, v_buf = _c(q), _c(k_buf), _c(v_buf)
@@ -160,9 +168,8 @@ def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
     assert Dqk == qk_nope_dim + qk_rope_dim
     T_buf = k_buf.shape[1]
     Dv = v_buf.shape[3]
-    if gate is None:
-        gate_dim = 0
-    else:
+    gate_dim = _gate_dim(gate, Dv, gate_dim)
+    if gate is not None:
         gate = _c(gate)
     if sm_scale is None:
         sm_scale = Dqk ** -0.5

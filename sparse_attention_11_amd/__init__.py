@@ -1,0 +1,232 @@
+"""Python binding of libdsa.so: one DeepSeek-Sparse-Attention layer on MI355X.
+
+Every function here has the name of a C entry point in ``include/dsa.h`` and
+does argument marshalling only: it checks that tensors are contiguous, on the
+GPU and of the expected dtype, turns them into raw pointers plus the current
+HIP stream, calls the library, and raises ``DsaError`` on a non-zero status.
+All computation happens in the HIP kernels behind the C ABI; there is no
+fallback of any kind. If the library is not built, importing works but every
+call raises.
+
+Tensors (torch, device ``cuda``) follow the layouts of ``include/dsa.h``:
+q [B,S,H,Dqk], k_cache [B,T,H,Dqk], v_cache [B,T,H,Dv], q_idx [B,S,HI,DI],
+k_idx [B,T,DI], w [B,S,HI], scores [B,S,T] float32, indices [B,S,topk] int32,
+gate [B,S,H] or [B,S,H,Dv].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_F32, DSA_BF16 = 0, 1
+RELU_PER_HEAD, RELU_NONE, RELU_POST_SUM = 0, 1, 2
+MAX_TOPK = 2048
+
+_EXPORTS = [
+    "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk",
+    "dsa_sparse_attn_prefill_workspace_size", "dsa_sparse_attn_prefill",
+    "dsa_sparse_attn_decode_workspace_size", "dsa_sparse_attn_decode",
+    "swa_attn_workspace_size", "swa_attn", "dsa_status_string", "dsa_last_error",
+]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() or "
+                               "python sparse_attention_11_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.dsa_index_scores.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                       i32, vp]
+        L.dsa_topk_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.dsa_topk_workspace_size.restype = sz
+        L.dsa_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
+        L.dsa_sparse_attn_prefill_workspace_size.argtypes = [i32] * 8
+        L.dsa_sparse_attn_prefill_workspace_size.restype = sz
+        L.dsa_sparse_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                              i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+        L.dsa_sparse_attn_decode_workspace_size.argtypes = [i32] * 4
+        L.dsa_sparse_attn_decode_workspace_size.restype = sz
+        L.dsa_sparse_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             i32, f32, i32, i32, vp, sz, vp]
+        L.swa_attn_workspace_size.argtypes = [i32] * 7
+        L.swa_attn_workspace_size.restype = sz
+        L.swa_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                               i32, f32, i32, i32, vp, sz, vp]
+        for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
+                   "dsa_sparse_attn_decode", "swa_attn"):
+            getattr(L, fn).restype = i32
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        L.dsa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn: str, st: int):
+    if st != DSA_OK:
+        L = lib()
+        raise DsaError(fn, st, f"{L.dsa_status_string(st).decode()}: {L.dsa_last_error().decode()}")
+
+
+def _workspace(nbytes: int, like):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+# ------------------------------------------------------------- entry points
+def dsa_index_scores(q_idx, k_idx, w, scores, past_len: int, scale: float | None = None,
+                     relu_mode: int = RELU_PER_HEAD, stream=None):
+    B, S, HI, DI = q_idx.shape
+    T = k_idx.shape[1]
+    if scale is None:
+        scale = DI ** -0.5
+    _check("dsa_index_scores", lib().dsa_index_scores(
+        _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, S, T, past_len, HI, DI, scale,
+        relu_mode, _dtype(q_idx), _stream(stream)))
+    return scores
+
+
+def dsa_topk_workspace_size(B: int, S: int, T: int, topk: int) -> int:
+    return int(lib().dsa_topk_workspace_size(B, S, T, topk))
+
+
+def dsa_topk(scores, indices, workspace=None, stream=None):
+    B, S, T = scores.shape
+    topk = indices.shape[-1]
+    need = dsa_topk_workspace_size(B, S, T, topk)
+    if workspace is None:
+        workspace = _workspace(need, scores)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_topk", lib().dsa_topk(_ptr(scores), _ptr(indices), B, S, T, topk,
+                                      _ptr(workspace), nbytes, _stream(stream)))
+    return indices
+
+
+def dsa_sparse_attn_prefill_workspace_size(B, S, T, H, qk_dim, v_dim, topk, dtype) -> int:
+    return int(lib().dsa_sparse_attn_prefill_workspace_size(B, S, T, H, qk_dim, v_dim, topk, dtype))
+
+
+def _gate_dim(gate, Dv):
+    if gate is None:
+        return 0
+    return 1 if gate.dim() == 3 else Dv
+
+
+def dsa_sparse_attn_prefill(q, k_cache, v_cache, indices, gate, out, past_len: int,
+                            qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+                            workspace=None, stream=None):
+    B, S, H, Dqk = q.shape
+    T, Dv = k_cache.shape[1], v_cache.shape[3]
+    topk = indices.shape[-1]
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    dt = _dtype(q)
+    if workspace is None:
+        workspace = _workspace(dsa_sparse_attn_prefill_workspace_size(B, S, T, H, Dqk, Dv, topk, dt), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_attn_prefill", lib().dsa_sparse_attn_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate), _ptr(out), B, S, T,
+        past_len, H, qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale, _gate_dim(gate, Dv), dt,
+        _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def dsa_sparse_attn_decode_workspace_size(B, H, v_dim, topk) -> int:
+    return int(lib().dsa_sparse_attn_decode_workspace_size(B, H, v_dim, topk))
+
+
+def dsa_sparse_attn_decode(q, k_cache, v_cache, indices, gate, out, qk_nope_dim: int,
+                           qk_rope_dim: int, sm_scale: float | None = None, workspace=None,
+                           stream=None):
+    B, _, H, Dqk = q.shape
+    T, Dv = k_cache.shape[1], v_cache.shape[3]
+    topk = indices.shape[-1]
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    if workspace is None:
+        workspace = _workspace(dsa_sparse_attn_decode_workspace_size(B, H, Dv, topk), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_attn_decode", lib().dsa_sparse_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate), _ptr(out), B, T, H,
+        qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale, _gate_dim(gate, Dv), _dtype(q),
+        _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def swa_attn_workspace_size(B, S, H, qk_dim, v_dim, window, dtype) -> int:
+    return int(lib().swa_attn_workspace_size(B, S, H, qk_dim, v_dim, window, dtype))
+
+
+def swa_attn(q, k_buf, v_buf, gate, out, past_len: int, kv_offset: int, window: int,
+             qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None, workspace=None,
+             stream=None):
+    B, S, H, Dqk = q.shape
+    T_buf, Dv = k_buf.shape[1], v_buf.shape[3]
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    dt = _dtype(q)
+    if workspace is None:
+        workspace = _workspace(swa_attn_workspace_size(B, S, H, Dqk, Dv, window, dt), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("swa_attn", lib().swa_attn(
+        _ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate), _ptr(out), B, S, T_buf, past_len,
+        kv_offset, H, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale, _gate_dim(gate, Dv), dt,
+        _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def dsa_status_string(status: int) -> str:
+    return lib().dsa_status_string(status).decode()
+
+
+def dsa_last_error() -> str:
+    return lib().dsa_last_error().decode()

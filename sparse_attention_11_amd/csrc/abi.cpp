@@ -1,0 +1,255 @@
+// abi.cpp -- the C ABI of libdsa.so: argument validation, status codes and
+// dispatch to the HIP launchers. Validation is pure host code and runs before
+// any HIP call, so argument errors are reported even where no GPU exists.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+bool head_dim_ok(int d) { return d >= 16 && d <= DSA_MAX_HEAD_DIM && d % 16 == 0; }
+
+// Common checks of the attention entry points. Returns DSA_OK or a status.
+int check_attn(const char* fn, const void* q, const void* k, const void* v, const void* gate,
+               const void* out, int B, int S, int T, int H, int nope, int rope, int v_dim,
+               float sm_scale, int gate_dim, int dtype) {
+  if (!q || !k || !v || !out) return fail(DSA_ERR_INVALID_ARG, "%s: null input/output pointer", fn);
+  if (B < 1 || S < 1 || T < 1 || H < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: B, S, T and H must be >= 1 (got %d, %d, %d, %d)", fn, B,
+                S, T, H);
+  if (nope < 0 || rope < 0 || nope + rope < 1 || v_dim < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad head dims (nope %d, rope %d, v %d)", fn, nope, rope,
+                v_dim);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: dtype must be DSA_F32 or DSA_BF16 (got %d)", fn, dtype);
+  if (!finite_pos(sm_scale))
+    return fail(DSA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
+  if (gate_dim != 0 && gate_dim != 1 && gate_dim != v_dim)
+    return fail(DSA_ERR_INVALID_ARG, "%s: gate_dim must be 0, 1 or v_dim (got %d)", fn, gate_dim);
+  if (gate_dim != 0 && !gate) return fail(DSA_ERR_INVALID_ARG, "%s: gate is NULL", fn);
+  if (!head_dim_ok(nope + rope) || !head_dim_ok(v_dim))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "%s: head dims must be multiples of 16 in [16, %d] (qk %d, v %d)", fn,
+                DSA_MAX_HEAD_DIM, nope + rope, v_dim);
+  return DSA_OK;
+}
+
+int check_ws(const char* fn, void* ws, size_t have, size_t need) {
+  if (need == 0) return DSA_OK;
+  if (!ws || have < need)
+    return fail(DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given%s", fn, need, have,
+                ws ? "" : " (NULL)");
+  return DSA_OK;
+}
+
+size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, int dtype) {
+  if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return dsa::bitmap_bytes(B, S, T);
+  return dsa::gather_workspace_bytes(B * S, H, v_dim, topk);
+}
+
+size_t swa_ws(int B, int S, int H, int qk_dim, int v_dim, int window, int dtype) {
+  if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return 0;
+  return dsa::gather_workspace_bytes(B * S, H, v_dim, window);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    default: return "DSA_ERR_UNKNOWN";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
+                     int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
+                     int relu_mode, int dtype, hipStream_t stream) {
+  const char* fn = "dsa_index_scores";
+  g_err.clear();
+  if (!q_idx || !k_idx || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || S < 1 || T < 1 || n_idx_heads < 1 || idx_dim < 1 || past_len < 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1 and past_len >= 0", fn);
+  if ((long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T (%d) < past_len + S (%d + %d)", fn, T, past_len, S);
+  if (!finite_pos(scale)) return fail(DSA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (relu_mode < DSA_RELU_PER_HEAD || relu_mode > DSA_RELU_POST_SUM)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad relu_mode %d", fn, relu_mode);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (idx_dim != 32 && idx_dim != 64 && idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: idx_dim must be 32, 64 or 128 (got %d)", fn, idx_dim);
+  if ((long long)B * S > 65535 && dtype == DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: fp32 path limited to B*S <= 65535", fn);
+  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  return hip_status(dsa::launch_index_scores(q_idx, k_idx, w, scores, B, S, T, past_len,
+                                             n_idx_heads, idx_dim, scale, relu_mode, dtype,
+                                             stream),
+                    fn);
+}
+
+size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
+  if (B < 1 || S < 1 || T < 1 || topk < 1) return 0;
+  return dsa::topk_workspace_bytes(B, S, T, topk);
+}
+
+int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_topk";
+  g_err.clear();
+  if (!scores || !indices) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || S < 1 || T < 1) return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  int st = check_ws(fn, workspace, workspace_bytes, dsa::topk_workspace_bytes(B, S, T, topk));
+  if (st) return st;
+  return hip_status(dsa::launch_topk(scores, indices, B, S, T, topk, workspace, stream), fn);
+}
+
+size_t dsa_sparse_attn_prefill_workspace_size(int B, int S, int T, int H, int qk_dim, int v_dim,
+                                              int topk, int dtype) {
+  if (B < 1 || S < 1 || T < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || topk < 1) return 0;
+  return prefill_ws(B, S, T, H, qk_dim, v_dim, topk, dtype);
+}
+
+int dsa_sparse_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* indices, const void* gate, void* out, int B, int S,
+                            int T, int past_len, int H, int qk_nope_dim, int qk_rope_dim,
+                            int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_sparse_attn_prefill";
+  g_err.clear();
+  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, S, T, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
+  if (past_len < 0 || (long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: need 0 <= past_len and past_len + S <= T", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  const int dqk = qk_nope_dim + qk_rope_dim;
+  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
+  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
+  st = check_ws(fn, workspace, workspace_bytes,
+                prefill_ws(B, S, T, H, dqk, v_dim, topk, dtype));
+  if (st) return st;
+  hipError_t e;
+  if (mfma)
+    e = dsa::launch_prefill_mfma(q, k_cache, v_cache, indices, gate, out, B, S, T, past_len, 0, H,
+                                 dqk, v_dim, topk, 0, sm_scale, gate_dim, workspace, stream);
+  else
+    e = dsa::launch_gather(q, k_cache, v_cache, indices, gate, out, B, S, T, past_len, 0, H, dqk,
+                           v_dim, topk, 0, sm_scale, gate_dim, dtype, workspace, stream);
+  return hip_status(e, fn);
+}
+
+size_t dsa_sparse_attn_decode_workspace_size(int B, int H, int v_dim, int topk) {
+  if (B < 1 || H < 1 || v_dim < 1 || topk < 1) return 0;
+  return dsa::gather_workspace_bytes(B, H, v_dim, topk);
+}
+
+int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* indices, const void* gate, void* out, int B, int T,
+                           int H, int qk_nope_dim, int qk_rope_dim, int v_dim, int topk,
+                           float sm_scale, int gate_dim, int dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_sparse_attn_decode";
+  g_err.clear();
+  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, 1, T, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  st = check_ws(fn, workspace, workspace_bytes, dsa::gather_workspace_bytes(B, H, v_dim, topk));
+  if (st) return st;
+  return hip_status(dsa::launch_gather(q, k_cache, v_cache, indices, gate, out, B, 1, T, T - 1, 0,
+                                       H, qk_nope_dim + qk_rope_dim, v_dim, topk, 0, sm_scale,
+                                       gate_dim, dtype, workspace, stream),
+                    fn);
+}
+
+size_t swa_attn_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                               int dtype) {
+  if (B < 1 || S < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || window < 1) return 0;
+  return swa_ws(B, S, H, qk_dim, v_dim, window, dtype);
+}
+
+int swa_attn(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,
+             int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
+             int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "swa_attn";
+  g_err.clear();
+  int st = check_attn(fn, q, k_buf, v_buf, gate, out, B, S, T_buf, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if (window < 1) return fail(DSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
+  if (past_len < 0 || kv_offset < 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: past_len and kv_offset must be >= 0", fn);
+  const long long lim = std::max(0LL, (long long)past_len - window + 1);
+  if (kv_offset > lim)
+    return fail(DSA_ERR_INVALID_ARG,
+                "%s: kv_offset %d > max(0, past_len - window + 1) = %lld (window not in buffer)",
+                fn, kv_offset, lim);
+  if ((long long)T_buf != (long long)past_len + S - kv_offset)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T_buf (%d) must equal past_len + S - kv_offset (%lld)",
+                fn, T_buf, (long long)past_len + S - kv_offset);
+  const int dqk = qk_nope_dim + qk_rope_dim;
+  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
+  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
+  st = check_ws(fn, workspace, workspace_bytes, swa_ws(B, S, H, dqk, v_dim, window, dtype));
+  if (st) return st;
+  hipError_t e;
+  if (mfma)
+    e = dsa::launch_prefill_mfma(q, k_buf, v_buf, nullptr, gate, out, B, S, T_buf, past_len,
+                                 kv_offset, H, dqk, v_dim, 0, window, sm_scale, gate_dim, nullptr,
+                                 stream);
+  else
+    e = dsa::launch_gather(q, k_buf, v_buf, nullptr, gate, out, B, S, T_buf, past_len, kv_offset,
+                           H, dqk, v_dim, 0, window, sm_scale, gate_dim, dtype, workspace, stream);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// attn_gather.hip -- split-K row-gather attention + merge (gfx950).
+//
+// For few queries (decode: one token per sequence) the work is a stream of
+// whole selected cache rows: with token-major caches one selected position is
+// one contiguous [H, D] row (A.X-K2 page: the cache holds expanded K/V; the
+// indexer's positions are shared by all heads). The selection is split into
+// chunks; a workgroup takes one chunk for 32 heads, keeps an online softmax
+// per head and writes a partial state (m, l, o[Dv]); the merge kernel
+// combines the chunks, applies the sigmoid gate (A.X-K2 page, "Attention
+// output gate"; Spark-X2.5 page, forward pass) and stores the output.
+//
+// Lane layout: 8 lanes per head, 8 heads per wave, 4 waves = 32 heads. A
+// head's K row (Dqk elements) is read as 16-byte chunks, lane j of the head
+// taking chunks j, j+8, ...; each load instruction therefore covers 128
+// contiguous bytes per head and 1 KiB per wave. The per-head dot product is
+// reduced over the 8 lanes with three xor-swaps. Four tokens are in flight
+// per step.
+//
+// The same kernels serve the fp32 path and sliding-window attention (the
+// window is an implicit list p, p-1, ..., p-W+1).
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kG = 4;          // tokens in flight per step
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<0> {  // fp32
+  static constexpr int kPer16 = 4;
+  static constexpr int kMaxChunks = 8;  // 16-byte chunks per lane per row (head dim <= 256)
+  __device__ static void unpack(const u32x4_t& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+};
+template <>
+struct Elem<1> {  // bf16
+  static constexpr int kPer16 = 8;
+  static constexpr int kMaxChunks = 4;
+  __device__ static void unpack(const u32x4_t& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+// WIN 0: indices list; WIN 1: window p, p-1, ..., p-window+1.
+template <int DT, int WIN>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
+    const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
+    int kv_offset, int H, int DQK, int DV, int nent, int per_split, int nsplit, int window,
+    float scale_log2) {
+  using E = Elem<DT>;
+  constexpr int EP = E::kPer16;
+  constexpr int esz = DT ? 2 : 4;
+  constexpr int kMaxChunks = E::kMaxChunks;
+  const int split = (int)(blockIdx.x % (unsigned)nsplit);
+  const int64_t row = blockIdx.x / (unsigned)nsplit;
+  const int b = (int)(row / S), s = (int)(row % S);
+  const int p = P + s;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 7;
+  const int h = 32 * blockIdx.y + 8 * wave + (lane >> 3);
+  const bool hvalid = h < H;
+  const int hh = hvalid ? h : H - 1;
+  const int nck = DQK / EP, ncv = DV / EP;
+
+  const char* qb = (const char*)qv;
+  const char* kb = (const char*)kv;
+  const char* vb = (const char*)vv;
+
+  float qf[kMaxChunks][EP];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = sub + 8 * i;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) qf[i][e] = 0.0f;
+    if (c < nck) {
+      const u32x4_t x = load16(qb + ((row * H + hh) * (int64_t)DQK + c * EP) * esz);
+      E::unpack(x, qf[i]);
+#pragma unroll
+      for (int e = 0; e < EP; ++e) qf[i][e] *= scale_log2;
+    }
+  }
+
+  float m = -INFINITY, l = 0.0f;
+  float o[kMaxChunks][EP];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
+
+  const int e0 = split * per_split;
+  const int e1 = min(nent, e0 + per_split);
+  const int32_t* irow = idx + row * (int64_t)nent;
+  const int64_t kvrow0 = (int64_t)b * Tbuf;
+
+  for (int base = e0; base < e1; base += kG) {
+    int jrow[kG];
+    bool ok[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const int ent = base + g;
+      int t;
+      if (WIN)
+        t = p - ent;
+      else
+        t = (ent < e1) ? irow[ent] : -1;
+      const int j = t - kv_offset;
+      ok[g] = (ent < e1) && t >= 0 && t <= p && j >= 0 && j < Tbuf;
+      if (WIN) ok[g] = ok[g] && ent < window;
+      jrow[g] = ok[g] ? j : 0;
+    }
+    // logits
+    float x[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const char* kr = kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = sub + 8 * i;
+        if (c < nck) {
+          float kf[EP];
+          E::unpack(load16(kr + (int64_t)c * EP * esz), kf);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) dot = fmaf(qf[i][e], kf[e], dot);
+        }
+      }
+      dot += shfl_xor_f(dot, 1);
+      dot += shfl_xor_f(dot, 2);
+      dot += shfl_xor_f(dot, 4);
+      x[g] = ok[g] ? dot : -INFINITY;
+    }
+    float mx = m;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) mx = fmaxf(mx, x[g]);
+    const float muse = (mx == -INFINITY) ? 0.0f : mx;
+    const float alpha = exp2f(m - muse);
+    m = mx;
+    float pg[kG];
+    float ps = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      pg[g] = exp2f(x[g] - muse);
+      ps += pg[g];
+    }
+    l = l * alpha + ps;
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) o[i][e] *= alpha;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      if (!ok[g]) continue;
+      const char* vr = vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
+#pragma unroll
+      for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = sub + 8 * i;
+        if (c < ncv) {
+          float vf[EP];
+          E::unpack(load16(vr + (int64_t)c * EP * esz), vf);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) o[i][e] = fmaf(pg[g], vf[e], o[i][e]);
+        }
+      }
+    }
+  }
+
+  if (!hvalid) return;
+  // partial state: [row][split][h][DV + 2] = o[0..DV), m, l
+  float* pr = part + ((row * nsplit + split) * H + h) * (int64_t)(DV + 2);
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = sub + 8 * i;
+    if (c < ncv) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e) pr[c * EP + e] = o[i][e];
+    }
+  }
+  if (sub == 0) {
+    pr[DV] = m;
+    pr[DV + 1] = l;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part,
+                                                    const void* __restrict__ gate,
+                                                    void* __restrict__ out, int H, int DV,
+                                                    int nsplit, int gate_dim) {
+  const int64_t rh = blockIdx.x;  // row * H + h
+  const int64_t row = rh / H;
+  const int h = (int)(rh % H);
+  const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 2);
+  const int64_t sstride = (int64_t)H * (DV + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pbase[sp * sstride + DV]);
+  const float Muse = (M == -INFINITY) ? 0.0f : M;
+  float L = 0.0f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* ps = pbase + sp * sstride;
+    L += ps[DV + 1] * exp2f(ps[DV] - Muse);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  float g1 = 1.0f;
+  if (gate_dim == 1)
+    g1 = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
+  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
+    float acc = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* ps = pbase + sp * sstride;
+      acc = fmaf(ps[d], exp2f(ps[DV] - Muse), acc);
+    }
+    float gg = g1;
+    if (gate_dim > 1) {
+      const int64_t gi = rh * DV + d;
+      gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[gi]) : ((const float*)gate)[gi]);
+    }
+    const float r = acc * inv * gg;
+    if (DT)
+      ((uint16_t*)out)[rh * DV + d] = f32_to_bf16(r);
+    else
+      ((float*)out)[rh * DV + d] = r;
+  }
+}
+
+struct Plan {
+  int nsplit, per_split;
+};
+
+Plan make_plan(int64_t rows, int H, int nent) {
+  const int64_t hgroups = (H + 31) / 32;
+  const int64_t base = rows * hgroups;
+  int nsplit = (int)std::max<int64_t>(1, (2048 + base - 1) / base);
+  const int max_split = std::max(1, (nent + 15) / 16);  // at least 16 entries per split
+  nsplit = std::min(nsplit, max_split);
+  int per = (nent + nsplit - 1) / nsplit;
+  per = (per + kG - 1) / kG * kG;
+  nsplit = (nent + per - 1) / per;
+  return {nsplit, per};
+}
+
+}  // namespace
+
+size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries) {
+  const Plan pl = make_plan(rows, H, nentries);
+  return (size_t)rows * pl.nsplit * H * (size_t)(Dv + 2) * sizeof(float);
+}
+
+hipError_t launch_gather(const void* q, const void* k, const void* v, const int32_t* indices,
+                         const void* gate, void* out, int B, int S, int T, int past_len,
+                         int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                         float sm_scale, int gate_dim, int dtype, void* workspace,
+                         hipStream_t st) {
+  const int64_t rows = (int64_t)B * S;
+  const int nent = window > 0 ? window : topk;
+  const Plan pl = make_plan(rows, H, nent);
+  float* part = (float*)workspace;
+  const dim3 grid((unsigned)(rows * pl.nsplit), (H + 31) / 32);
+  if (rows * pl.nsplit > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const float sl2 = sm_scale * DSA_LOG2E;
+#define DSA_GATHER(DT, WIN)                                                                      \
+  hipLaunchKernelGGL((gather_kernel<DT, WIN>), grid, dim3(256), 0, st, q, k, v, indices, part, S, \
+                     T, past_len, kv_offset, H, Dqk, Dv, nent, pl.per_split, pl.nsplit, window,  \
+                     sl2)
+  if (dtype == 1) {
+    if (window > 0)
+      DSA_GATHER(1, 1);
+    else
+      DSA_GATHER(1, 0);
+  } else {
+    if (window > 0)
+      DSA_GATHER(0, 1);
+    else
+      DSA_GATHER(0, 0);
+  }
+#undef DSA_GATHER
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nrh = rows * H;
+  if (dtype == 1)
+    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)nrh), dim3(128), 0, st, part, gate, out, H,
+                       Dv, pl.nsplit, gate_dim);
+  else
+    hipLaunchKernelGGL(merge_kernel<0>, dim3((unsigned)nrh), dim3(128), 0, st, part, gate, out, H,
+                       Dv, pl.nsplit, gate_dim);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,338 @@
+// attn_prefill.hip -- sparse (or sliding-window) MLA attention for many
+// queries at once, bf16 MFMA on gfx950.
+//
+// DSA: each query attends only to its selected, causally visible keys; the
+// selection acts as an additive 0/-inf mask on the attention logits (A.X-K2
+// page, "MLA + explicit sparse mask", steps 4-5), followed by the sigmoid
+// output gate (same page, "Attention output gate"; Spark-X2.5 page, forward
+// pass steps 2-3). SWA: the mask is the window p-W+1 .. p instead (Spark-X2.5
+// page: sliding_window 512; openPangu-2.0 page §3.2).
+//
+// Cost structure. The caches hold expanded per-head K/V and selections are
+// per query, so gathering selected rows per query is a ~1 flop/byte stream.
+// Dense flash tiles over the causal range, masked by a per-query selection
+// bitmap, run at MFMA rate instead; every unselected logit is -inf and
+// contributes exactly 0, so the result is the masked softmax itself.
+//
+// Layout of the work. One workgroup = one head, 128 queries (32 per wave).
+// Logits are produced transposed, S^T = K Q^T (keys on the MFMA M axis), so a
+// lane owns one query column: the softmax max/sum stay in registers except
+// for one swap with the other half-wave. The 32x32 accumulator layout then
+// holds keys {8g + 4*half + r}; the P.V product uses exactly that key order
+// as its contraction index, and V is staged in LDS transposed with the same
+// permutation (bits 2 and 3 of the key offset swapped within each 16 keys),
+// so P never leaves registers. Q^T stays in registers for the whole key loop.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBN = 64;   // keys per step
+
+// --------------------------------------------------------- selection bitmap
+// bitmap[(b*S + s) * W32 + w] bit j  <=>  key 32w + j is selected and t <= p.
+__global__ __launch_bounds__(256) void bitmap_lds_kernel(const int32_t* __restrict__ idx,
+                                                         uint32_t* __restrict__ bm, int S, int T,
+                                                         int P, int topk, int W32) {
+  extern __shared__ uint32_t sbits[];
+  const int64_t row = blockIdx.x;
+  const int p = P + (int)(row % S);
+  for (int i = threadIdx.x; i < W32; i += blockDim.x) sbits[i] = 0;
+  __syncthreads();
+  const int32_t* ir = idx + row * topk;
+  for (int j = threadIdx.x; j < topk; j += blockDim.x) {
+    const int t = ir[j];
+    if (t >= 0 && t <= p && t < T) atomicOr(&sbits[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  uint32_t* br = bm + row * W32;
+  for (int i = threadIdx.x; i < W32; i += blockDim.x) br[i] = sbits[i];
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void bitmap_global_kernel(const int32_t* __restrict__ idx,
+                                                            uint32_t* __restrict__ bm, int S,
+                                                            int T, int P, int topk, int W32) {
+  const int64_t row = blockIdx.x;
+  const int p = P + (int)(row % S);
+  const int32_t* ir = idx + row * topk;
+  uint32_t* br = bm + row * W32;
+  for (int j = threadIdx.x; j < topk; j += blockDim.x) {
+    const int t = ir[j];
+    if (t >= 0 && t <= p && t < T) atomicOr(&br[t >> 5], 1u << (t & 31));
+  }
+}
+
+// ------------------------------------------------------------ flash kernel
+// MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA).
+template <int DQK, int DV, int MASK>
+__global__ __launch_bounds__(256) void prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
+    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int S, int Tbuf, int P,
+    int kv_offset, int H, int W32, int window, float scale_log2, int gate_dim) {
+  constexpr int KSQ = DQK / 16;
+  constexpr int NDB = DV / 32;
+  constexpr int KPAD = DQK + 8;  // bf16 elements per K row in LDS
+  constexpr int VPAD = kBN + 8;  // bf16 elements per V^T row in LDS
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VPAD];
+
+  const int qt = gridDim.x - 1 - blockIdx.x;  // long (late) query tiles first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+  const int q0 = qt * kBQ;
+  const int s = q0 + 32 * wave + ln;
+  const bool svalid = s < S;
+  const int sc = svalid ? s : S - 1;
+  const int p = P + sc;  // absolute position of this lane's query
+  const int64_t qrow = (int64_t)b * S + sc;
+
+  bf16x8_t bq[KSQ];
+  {
+    const uint16_t* qp = q + (qrow * H + h) * DQK + 8 * lh;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = as_bf16x8(load16(qp + 16 * ks));
+  }
+
+  // key range of the tile, in buffer rows (row j = absolute position kv_offset + j)
+  const int pmax = P + min(q0 + kBQ - 1, S - 1);
+  int tlo = 0;
+  if (MASK == 1) tlo = max(kv_offset, P + q0 - window + 1);
+  const int jlo = ((tlo - kv_offset) / kBN) * kBN;
+  const int jhi = min(pmax - kv_offset, Tbuf - 1);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) o[d] = zero16();
+
+  const uint32_t* bmrow = bm + qrow * (int64_t)W32;
+  const int64_t kvrow0 = (int64_t)b * Tbuf;
+
+  for (int jb = jlo; jb <= jhi; jb += kBN) {
+    __syncthreads();
+    // ---- stage K rows jb..jb+63 -> Ks[row][dim]
+    constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
+    for (int u = tid; u < kBN * KCH; u += 256) {
+      const int r = u / KCH, c = u - r * KCH;
+      const int j = jb + r;
+      u32x4_t val = u32x4_t{0, 0, 0, 0};
+      if (j < Tbuf) val = load16(k + ((kvrow0 + j) * H + h) * DQK + 8 * c);
+      *(u32x4_t*)(&Ks[r * KPAD + 8 * c]) = val;
+    }
+    // ---- stage V rows jb..jb+63 -> Vt[dv][perm(key)], 4 keys x 8 dv per unit
+    constexpr int VCH = DV / 8;
+    for (int u = tid; u < (kBN / 4) * VCH; u += 256) {
+      const int kg = u / VCH, dg = u - kg * VCH;
+      uint32_t w[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + 4 * kg + r;
+        u32x4_t val = u32x4_t{0, 0, 0, 0};
+        if (j < Tbuf) val = load16(v + ((kvrow0 + j) * H + h) * DV + 8 * dg);
+        w[r][0] = val[0];
+        w[r][1] = val[1];
+        w[r][2] = val[2];
+        w[r][3] = val[3];
+      }
+      const int o16 = (4 * kg) & 15;  // 0, 4, 8, 12 within the 16-key chunk
+      const int pos = ((4 * kg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        // dv 8*dg + 2*mm (low halves) and 8*dg + 2*mm + 1 (high halves)
+        const uint32_t lo01 = (w[0][mm] & 0xFFFFu) | (w[1][mm] << 16);
+        const uint32_t lo23 = (w[2][mm] & 0xFFFFu) | (w[3][mm] << 16);
+        const uint32_t hi01 = (w[0][mm] >> 16) | (w[1][mm] & 0xFFFF0000u);
+        const uint32_t hi23 = (w[2][mm] >> 16) | (w[3][mm] & 0xFFFF0000u);
+        uint32_t* d0 = (uint32_t*)&Vt[(8 * dg + 2 * mm) * VPAD + pos];
+        uint32_t* d1 = (uint32_t*)&Vt[(8 * dg + 2 * mm + 1) * VPAD + pos];
+        d0[0] = lo01;
+        d0[1] = lo23;
+        d1[0] = hi01;
+        d1[1] = hi23;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 64 keys x this wave's 32 queries
+    f32x16_t st[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      st[i] = zero16();
+      const uint16_t* kr = &Ks[(32 * i + ln) * KPAD + 8 * lh];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks)
+        st[i] = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(kr + 16 * ks)), bq[ks], st[i]);
+    }
+
+    // ---- mask, online softmax (log2 domain)
+    uint32_t bits[2] = {0u, 0u};
+    if (MASK == 0) {
+      const int w0 = (jb >> 5);
+      bits[0] = (w0 < W32) ? bmrow[w0] : 0u;
+      bits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int off = 8 * (e >> 2) + 4 * lh + (e & 3);
+        bool ok;
+        if (MASK == 0) {
+          ok = (bits[i] >> off) & 1u;
+        } else {
+          const int j = jb + 32 * i + off;
+          const int t = kv_offset + j;
+          ok = (j < Tbuf) && (t <= p) && (t > p - window);
+        }
+        const float x = ok ? st[i][e] * scale_log2 : -INFINITY;
+        st[i][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
+    const float alpha = exp2f(m - muse);
+    m = mnew;
+    float psum = 0.0f;
+    uint32_t pk[2][2][4];  // [key block][half of 16 keys][packed pair]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = exp2f(st[i][e] - muse);
+        const float p1 = exp2f(st[i][e + 1] - muse);
+        psum += p0 + p1;
+        pk[i][e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t pb =
+            as_bf16x8(u32x4_t{pk[i][c][0], pk[i][c][1], pk[i][c][2], pk[i][c][3]});
+        const int kcol = 32 * i + 16 * c + 8 * lh;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const bf16x8_t va = as_bf16x8(*(const u32x4_t*)(&Vt[(32 * d + ln) * VPAD + kcol]));
+          o[d] = mfma32x32x16(va, pb, o[d]);
+        }
+      }
+    }
+  }
+
+  // ---- normalise, gate, store
+  const float ltot = l + shfl_xor_f(l, 32);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (!svalid) return;
+  float g1 = 1.0f;
+  if (gate_dim == 1) g1 = sigmoid_f32(bf16_to_f32(gate[qrow * H + h]));
+  uint16_t* orow = out + (qrow * H + h) * DV;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dv0 = 32 * d + 8 * g + 4 * lh;
+      float r4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float gg = g1;
+        if (gate_dim > 1) gg = sigmoid_f32(bf16_to_f32(gate[(qrow * H + h) * DV + dv0 + r]));
+        r4[r] = o[d][4 * g + r] * inv * gg;
+      }
+      uint2 pkd;
+      pkd.x = pack_bf16x2(r4[0], r4[1]);
+      pkd.y = pack_bf16x2(r4[2], r4[3]);
+      *(uint2*)(orow + dv0) = pkd;
+    }
+  }
+}
+
+template <int DQK, int DV>
+hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint32_t* bm, const uint16_t* gate, uint16_t* out, int B, int S,
+                       int Tbuf, int P, int kv_offset, int H, int W32, int window,
+                       float scale_log2, int gate_dim, hipStream_t st) {
+  const dim3 grid((S + kBQ - 1) / kBQ, H, B);
+  if (window > 0)
+    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, bm, gate,
+                       out, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, bm, gate,
+                       out, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim);
+  return hipGetLastError();
+}
+
+constexpr int kBitmapLdsMaxWords = 12288;  // 48 KiB of LDS
+
+}  // namespace
+
+bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv) {
+  if (dtype != 1 || S < 16) return false;
+  return (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128) ||
+         (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64);
+}
+
+size_t bitmap_bytes(int B, int S, int T) {
+  return (size_t)B * (size_t)S * (size_t)((T + 31) / 32) * sizeof(uint32_t);
+}
+
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
+                               const void* gate, void* out, int B, int S, int T, int past_len,
+                               int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                               float sm_scale, int gate_dim, void* workspace, hipStream_t st) {
+  const int W32 = (T + 31) / 32;
+  uint32_t* bm = (uint32_t*)workspace;
+  const int64_t rows = (int64_t)B * S;
+  if (window <= 0) {
+    if (W32 <= kBitmapLdsMaxWords) {
+      hipLaunchKernelGGL(bitmap_lds_kernel, dim3((unsigned)rows), dim3(256),
+                         W32 * sizeof(uint32_t), st, indices, bm, S, T, past_len, topk, W32);
+    } else {
+      const int64_t n = rows * W32;
+      const int64_t g = std::min<int64_t>((n + 255) / 256, 65536);
+      hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)g), dim3(256), 0, st, bm, n);
+      hipLaunchKernelGGL(bitmap_global_kernel, dim3((unsigned)rows), dim3(256), 0, st, indices,
+                         bm, S, T, past_len, topk, W32);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const float sl2 = sm_scale * DSA_LOG2E;
+  const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v,
+                 *gg = (const uint16_t*)gate;
+  uint16_t* oo = (uint16_t*)out;
+#define DSA_PREFILL_CASE(A, C)                                                                    \
+  if (Dqk == A && Dv == C)                                                                        \
+    return launch_dims<A, C>(qq, kk, vv, bm, gg, oo, B, S, T, past_len, kv_offset, H, W32, window, \
+                             sl2, gate_dim, st);
+  DSA_PREFILL_CASE(64, 64)
+  DSA_PREFILL_CASE(128, 64)
+  DSA_PREFILL_CASE(128, 128)
+  DSA_PREFILL_CASE(192, 128)
+  DSA_PREFILL_CASE(256, 128)
+#undef DSA_PREFILL_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

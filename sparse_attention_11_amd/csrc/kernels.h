@@ -1,0 +1,38 @@
+// kernels.h -- host launchers of the libdsa kernels. Arguments are validated
+// by the C-ABI layer (abi.cpp) before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Lightning-indexer scores (index_scores.hip).
+hipError_t launch_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores,
+                               int B, int S, int T, int past_len, int HI, int DI, float scale,
+                               int relu_mode, int dtype, hipStream_t stream);
+
+// Per-row top-k (topk.hip).
+size_t topk_workspace_bytes(int B, int S, int T, int topk);
+hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+                       void* workspace, hipStream_t stream);
+
+// Selection bitmap + MFMA flash attention with a bitmap or window mask
+// (attn_prefill.hip). Requires bf16, Dqk % 16 == 0, Dv % 32 == 0.
+size_t bitmap_bytes(int B, int S, int T);
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
+                               const void* gate, void* out, int B, int S, int T, int past_len,
+                               int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                               float sm_scale, int gate_dim, void* workspace, hipStream_t stream);
+bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv);
+
+// Split-K row-gather attention + merge (attn_gather.hip); any dtype, any S.
+// window > 0 selects the implicit window list, else `indices` is used.
+size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries);
+hipError_t launch_gather(const void* q, const void* k, const void* v, const int32_t* indices,
+                         const void* gate, void* out, int B, int S, int T, int past_len,
+                         int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                         float sm_scale, int gate_dim, int dtype, void* workspace,
+                         hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports what include/dsa.h declares, and rejects
+invalid arguments on the host with the documented status codes (CPU only:
+validation runs before any HIP call, so no GPU is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_11_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+P = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dsa._EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(dsa.lib(), n)
+
+
+def test_status_strings():
+    L = dsa.lib()
+    assert L.dsa_status_string(0) == b"DSA_OK"
+    assert L.dsa_status_string(1) == b"DSA_ERR_INVALID_ARG"
+    assert L.dsa_status_string(2) == b"DSA_ERR_UNSUPPORTED"
+    assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
+    assert L.dsa_status_string(4) == b"DSA_ERR_HIP"
+
+
+def idx(**kw):
+    a = dict(q=P, k=P, w=P, s=P, B=1, S=4, T=8, past=0, HI=2, DI=64, scale=0.125, relu=0, dt=1)
+    a.update(kw)
+    return dsa.lib().dsa_index_scores(a["q"], a["k"], a["w"], a["s"], a["B"], a["S"], a["T"],
+                                      a["past"], a["HI"], a["DI"], a["scale"], a["relu"], a["dt"],
+                                      None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(s=None), 1), (dict(B=0), 1), (dict(S=0), 1), (dict(HI=0), 1),
+    (dict(past=-1), 1), (dict(T=3), 1), (dict(past=5), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1), (dict(relu=3), 1),
+    (dict(dt=2), 1), (dict(DI=48), 2), (dict(DI=256), 2),
+])
+def test_index_scores_validation(kw, code):
+    assert idx(**kw) == code
+    assert dsa.dsa_last_error().startswith("dsa_index_scores")
+
+
+def topk(**kw):
+    a = dict(s=P, i=P, B=1, S=2, T=100, k=10, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_topk(a["s"], a["i"], a["B"], a["S"], a["T"], a["k"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s=None), 1), (dict(i=None), 1), (dict(k=0), 1), (dict(k=101), 1), (dict(T=0), 1),
+    (dict(T=5000, k=2049), 2),
+])
+def test_topk_validation(kw, code):
+    assert topk(**kw) == code
+
+
+def prefill(**kw):
+    a = dict(q=P, k=P, v=P, i=P, g=P, o=P, B=1, S=32, T=64, past=0, H=2, nope=64, rope=64, v_dim=128,
+             topk=16, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_sparse_attn_prefill(a["q"], a["k"], a["v"], a["i"], a["g"], a["o"], a["B"],
+                                             a["S"], a["T"], a["past"], a["H"], a["nope"],
+                                             a["rope"], a["v_dim"], a["topk"], a["sc"], a["gd"],
+                                             a["dt"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(i=None), 1), (dict(g=None), 1), (dict(gd=7), 1), (dict(sc=-1.0), 1),
+    (dict(past=40), 1), (dict(topk=0), 1), (dict(topk=65), 1), (dict(dt=5), 1), (dict(H=0), 1),
+    (dict(nope=60), 2), (dict(v_dim=300), 2), (dict(T=5000, topk=4096), 2),
+    (dict(), 3),  # a workspace (selection bitmap) is required and none is given
+    (dict(nb=1, ws=P), 3),
+])
+def test_prefill_validation(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_without_gate_is_valid_until_workspace():
+    # gate may be NULL with gate_dim 0; the next failing check is the workspace
+    assert prefill(g=None, gd=0) == 3
+
+
+def test_workspace_sizes():
+    L = dsa.lib()
+    # bf16, many queries: one bit per (query, key) rounded up to 32-bit words
+    assert L.dsa_sparse_attn_prefill_workspace_size(1, 4096, 4096, 20, 128, 128, 512, 1) == 4096 * 128 * 4
+    assert L.dsa_sparse_attn_decode_workspace_size(8, 128, 128, 2048) > 0
+    assert L.dsa_topk_workspace_size(1, 1, 100, 10) == 0
+    assert L.swa_attn_workspace_size(1, 4096, 32, 192, 128, 512, 1) == 0
+    assert L.swa_attn_workspace_size(1, 1, 32, 192, 128, 512, 1) > 0
+
+
+def swa(**kw):
+    a = dict(q=P, k=P, v=P, g=P, o=P, B=1, S=10, Tb=10, past=0, off=0, H=2, nope=64, rope=64, v_dim=128,
+             W=4, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().swa_attn(a["q"], a["k"], a["v"], a["g"], a["o"], a["B"], a["S"], a["Tb"], a["past"],
+                              a["off"], a["H"], a["nope"], a["rope"], a["v_dim"], a["W"], a["sc"],
+                              a["gd"], a["dt"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=0), 1), (dict(off=-1), 1), (dict(past=100, Tb=110, off=98), 1),
+    (dict(past=100, Tb=50, off=97), 1), (dict(Tb=11), 1), (dict(nope=8, rope=0), 2),
+])
+def test_swa_validation(kw, code):
+    assert swa(**kw) == code
+
+
+def decode(**kw):
+    a = dict(q=P, k=P, v=P, i=P, g=P, o=P, B=2, T=100, H=2, nope=64, rope=64, v_dim=128, topk=16,
+             sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_sparse_attn_decode(a["q"], a["k"], a["v"], a["i"], a["g"], a["o"], a["B"],
+                                            a["T"], a["H"], a["nope"], a["rope"], a["v_dim"],
+                                            a["topk"], a["sc"], a["gd"], a["dt"], a["ws"], a["nb"],
+                                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(i=None), 1), (dict(topk=101), 1), (dict(B=0), 1), (dict(), 3),
+])
+def test_decode_validation(kw, code):
+    assert decode(**kw) == code

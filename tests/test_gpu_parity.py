@@ -1,0 +1,332 @@
+"""Parity of every C-ABI entry point against the fp64 oracle (GPU).
+
+Inputs come from the seeded generator (host twin for the oracle, identical
+bytes uploaded for the GPU). Top-k is compared bit-exactly on the same fp32
+score tensor (the oracle's own scores rounded to fp32); attention is compared
+on the same index tensor (the oracle's top-k or a generated index set).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import sparse_attention_11_amd as dsa
+from datagen.configs import WORKLOADS, F32
+from tests._helpers import assert_rows_close, host_inputs, to_dev, from_dev, widen, RTOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- generator
+def test_device_generator_matches_host():
+    for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        t = torch.empty(1 << 20, dtype=tdt, device=DEV)
+        datagen.normal_device(t, 3, 2, 0.7, start=12345)
+        h = datagen.normal_host((1 << 20,), dt, 3, 2, 0.7, start=12345)
+        _sync()
+        got = t.cpu().view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.cpu().numpy()
+        assert np.array_equal(got.view(np.uint8), h.view(np.uint8))
+    ti = torch.empty(300, 64, dtype=torch.int32, device=DEV)
+    datagen.indices_device(ti, 100, 400, 50, seed=2)
+    _sync()
+    assert np.array_equal(ti.cpu().numpy(), datagen.indices_host(100, 300, 400, 50, 64, seed=2))
+    for mode in (0, 1, 2):
+        ts = torch.empty(70, 333, dtype=torch.float32, device=DEV)
+        datagen.scores_device(ts, 5, 80, 200, seed=4, mode=mode)
+        _sync()
+        ref = datagen.scores_host(5, 70, 80, 333, 200, seed=4, mode=mode)
+        assert np.array_equal(ts.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------- indexer
+def _run_index(hi, past_len, mode=dsa.RELU_PER_HEAD, scale=None):
+    B, S, HI, DI = hi["q_idx"].shape
+    T = hi["k_idx"].shape[1]
+    sc = torch.empty(B, S, T, dtype=torch.float32, device=DEV)
+    sc.fill_(float("nan"))
+    dsa.dsa_index_scores(to_dev(hi["q_idx"]), to_dev(hi["k_idx"]), to_dev(hi["w"]), sc, past_len,
+                         scale=scale, relu_mode=mode)
+    _sync()
+    return sc.cpu().numpy()
+
+
+def test_index_scores_tiny_fp32():
+    wl = WORKLOADS["tiny-fp32"]
+    hi = host_inputs(wl, with_attn=False)
+    got = _run_index(hi, 0)
+    ref = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0)
+    assert_rows_close(got, ref, RTOL[F32], what="tiny-fp32 scores")
+
+
+def test_index_scores_mla_s4k():
+    wl = WORKLOADS["mla-s4k"]
+    hi = host_inputs(wl, with_attn=False)
+    got = _run_index(hi, 0)
+    ref = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0)
+    assert_rows_close(got, ref, 2e-2, what="mla-s4k scores")
+
+
+# (B, S, P, HI, DI, mode): tile path (S >= 32) and head-major rows path (S < 32)
+INDEX_CASES = [
+    (1, 200, 0, 3, 32, 0), (1, 200, 0, 3, 32, 1), (1, 200, 0, 3, 32, 2),
+    (2, 130, 73, 5, 128, 0), (1, 257, 0, 64, 128, 0), (1, 64, 1000, 16, 64, 2),
+    (2, 1, 999, 64, 128, 0), (3, 5, 300, 40, 64, 0), (1, 3, 40, 130, 32, 0),
+    (1, 7, 0, 32, 128, 1), (2, 1, 4095, 4, 64, 2),
+]
+
+
+@pytest.mark.parametrize("B,S,P,HI,DI,mode", INDEX_CASES)
+def test_index_scores_bf16_cases(B, S, P, HI, DI, mode):
+    T = P + S
+    seed = 100 + S + HI
+    g = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", seed, tid, sc)
+    hi = {"q_idx": g((B, S, HI, DI), 4, DI ** -0.5), "k_idx": g((B, T, DI), 5, 1.0),
+          "w": g((B, S, HI), 6, HI ** -0.5)}
+    got = _run_index(hi, P, mode=mode)
+    ref = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], P, relu_mode=mode)
+    assert_rows_close(got, ref, 2e-2, what=f"scores {B, S, P, HI, DI, mode}")
+
+
+def test_index_scores_custom_scale_and_longer_cache():
+    # T larger than past_len + S (keys beyond the last position are masked)
+    B, S, P, HI, DI = 1, 40, 10, 4, 64
+    T = 100
+    g = lambda shape, tid: datagen.normal_host(shape, "bf16", 9, tid, 0.5)
+    hi = {"q_idx": g((B, S, HI, DI), 4), "k_idx": g((B, T, DI), 5), "w": g((B, S, HI), 6)}
+    got = _run_index(hi, P, scale=0.3)
+    ref = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], P, scale=0.3)
+    assert_rows_close(got, ref, 2e-2, what="scores T > P+S")
+
+
+# ----------------------------------------------------------------- top-k
+def _run_topk(scores32: np.ndarray, k: int) -> np.ndarray:
+    B, S, T = scores32.shape
+    idx = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(to_dev(scores32), idx)
+    _sync()
+    return idx.cpu().numpy()
+
+
+def test_topk_on_oracle_scores_tiny_and_mla():
+    for name in ("tiny-fp32", "mla-s4k"):
+        wl = WORKLOADS[name]
+        hi = host_inputs(wl, with_attn=False)
+        sc = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0).astype(np.float32)
+        got = _run_topk(sc, wl.topk)
+        np.testing.assert_array_equal(got, oracle.topk(sc, wl.topk), err_msg=name)
+
+
+@pytest.mark.parametrize("T,P,k,mode", [
+    (100, 60, 1, 0), (100, 60, 17, 1), (256, 0, 64, 2), (5000, 4000, 2048, 1),
+    (5000, 4500, 512, 2), (2048, 2000, 2048, 0), (33000, 32900, 2048, 1), (40000, 39990, 300, 2),
+    (8192, 8100, 8, 1),
+])
+def test_topk_synthetic_rows(T, P, k, mode):
+    S = T - P
+    rows = min(S, 24)
+    sc = datagen.scores_host(0, rows, S, T, P, seed=T + k, mode=mode)
+    got = _run_topk(sc[None], k)[0]
+    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+
+
+def test_topk_constant_and_all_masked_tail():
+    T, k = 3000, 2048
+    sc = np.zeros((2, T), np.float32)
+    sc[1, 5:] = -np.inf
+    sc[0, ::2] = -0.0
+    got = _run_topk(sc[None], k)[0]
+    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+    assert got[1, 5:].tolist() == [-1] * (k - 5)
+
+
+# ----------------------------------------------------- sparse attention
+def _attn_dev(hi):
+    return {k_: to_dev(v_) for k_, v_ in hi.items()}
+
+
+def _run_prefill(hi, idx, past_len, nope, rope, gate=None, gate_dim=1):
+    B, S, H, Dqk = hi["q"].shape
+    Dv = hi["v"].shape[3]
+    dt = torch.bfloat16 if hi["q"].dtype == np.uint16 else torch.float32
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=dt, device=DEV)
+    g = None if gate is None else to_dev(gate)
+    dsa.dsa_sparse_attn_prefill(to_dev(hi["q"]), to_dev(hi["k"]), to_dev(hi["v"]), to_dev(idx), g,
+                                out, past_len, nope, rope)
+    _sync()
+    return from_dev(out)
+
+
+def _cmp_attn(got, ref, rtol, what):
+    Dv = ref.shape[-1]
+    assert_rows_close(got.reshape(-1, Dv), ref.reshape(-1, Dv), rtol, what=what)
+
+
+def test_prefill_tiny_fp32_chain_indices():
+    wl = WORKLOADS["tiny-fp32"]
+    hi = host_inputs(wl)
+    sc = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0).astype(np.float32)
+    idx = oracle.topk(sc, wl.topk)
+    got = _run_prefill(hi, idx, 0, wl.nope, wl.rope, hi["gate"])
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], 0, wl.nope, wl.rope)
+    _cmp_attn(got, ref, RTOL[F32], "tiny-fp32 prefill")
+
+
+def test_prefill_mla_s4k_chain_indices():
+    wl = WORKLOADS["mla-s4k"]
+    hi = host_inputs(wl)
+    sc = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0).astype(np.float32)
+    idx = oracle.topk(sc, wl.topk)
+    got = _run_prefill(hi, idx, 0, wl.nope, wl.rope, hi["gate"])
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], 0, wl.nope, wl.rope)
+    _cmp_attn(got, ref, 2e-2, "mla-s4k prefill")
+
+
+def _attn_case(B, S, P, H, nope, rope, Dv, seed, dt="bf16"):
+    T = P + S
+    Dqk = nope + rope
+    g = lambda shape, tid, sc: datagen.normal_host(shape, dt, seed, tid, sc)
+    return {"q": g((B, S, H, Dqk), 1, Dqk ** -0.25), "k": g((B, T, H, Dqk), 2, Dqk ** -0.25),
+            "v": g((B, T, H, Dv), 3, 1.0), "gate": g((B, S, H), 7, 1.0)}
+
+
+# (B, S, P, H, nope, rope, Dv, topk): MFMA path for bf16 S >= 16, gather otherwise
+PREFILL_CASES = [
+    (1, 200, 50, 3, 128, 64, 128, 64), (2, 130, 100, 2, 64, 64, 128, 200), (1, 77, 300, 4, 32, 32, 64, 33),
+    (1, 64, 0, 2, 128, 128, 128, 64), (1, 96, 10, 2, 64, 64, 64, 16), (2, 8, 500, 5, 128, 64, 128, 128),
+    (1, 1, 40, 3, 64, 64, 128, 41), (1, 300, 1800, 1, 128, 64, 128, 2048),
+]
+
+
+@pytest.mark.parametrize("B,S,P,H,nope,rope,Dv,k", PREFILL_CASES)
+def test_prefill_bf16_cases(B, S, P, H, nope, rope, Dv, k):
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=S + H)
+    idx = datagen.indices_host(0, B * S, S, P, k, seed=S + k).reshape(B, S, k)
+    got = _run_prefill(hi, idx, P, nope, rope, hi["gate"])
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], P, nope, rope)
+    _cmp_attn(got, ref, 2e-2, f"prefill {B, S, P, H, nope, rope, Dv, k}")
+
+
+@pytest.mark.parametrize("gate_kind", ["none", "elementwise", "limits"])
+def test_prefill_gate_modes(gate_kind):
+    B, S, P, H, nope, rope, Dv, k = 1, 150, 20, 3, 128, 64, 128, 48
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=5)
+    idx = datagen.indices_host(0, S, S, P, k, seed=6).reshape(B, S, k)
+    if gate_kind == "none":
+        gate = None
+    elif gate_kind == "elementwise":
+        gate = datagen.normal_host((B, S, H, Dv), "bf16", 5, 8, 1.0)
+    else:
+        gf = np.zeros((B, S, H), np.float32)
+        gf[..., 0], gf[..., 1], gf[..., 2] = -np.inf, np.inf, 0.0
+        gate = torch.from_numpy(gf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = _run_prefill(hi, idx, P, nope, rope, gate)
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, gate, P, nope, rope)
+    _cmp_attn(got, ref, 2e-2, f"gate {gate_kind}")
+    if gate_kind == "limits":
+        assert np.all(got[:, :, 0] == 0.0)
+        ung = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, None, P, nope, rope)
+        _cmp_attn(got[:, :, 1], ung[:, :, 1], 2e-2, "gate +inf")
+
+
+def test_prefill_set_semantics_on_gpu():
+    # -1 padding, future and out-of-range entries are ignored by the GPU too
+    B, S, P, H, nope, rope, Dv, k = 1, 100, 0, 2, 64, 64, 128, 24
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=8)
+    base = datagen.indices_host(0, S, S, P, k, seed=9).reshape(B, S, k)
+    junk = base.copy()
+    junk[:, :, -4] = -1
+    junk[:, :, -3] = np.arange(S)[None, :] + 1  # future position (ignored)
+    junk[:, :, -2] = S + 1000                     # beyond T (ignored)
+    got = _run_prefill(hi, junk, P, nope, rope, hi["gate"])
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], junk, hi["gate"], P, nope, rope)
+    _cmp_attn(got, ref, 2e-2, "junk indices")
+
+
+def test_prefill_fp32_gather_path():
+    hi = _attn_case(2, 40, 30, 3, 32, 16, 32, seed=12, dt="f32")
+    idx = datagen.indices_host(0, 80, 40, 30, 20, seed=13).reshape(2, 40, 20)
+    got = _run_prefill(hi, idx, 30, 32, 16, hi["gate"])
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], 30, 32, 16)
+    _cmp_attn(got, ref, 1e-5, "fp32 prefill")
+
+
+# ---------------------------------------------------------------- decode
+@pytest.mark.parametrize("B,T,H,nope,rope,Dv,k,dt", [
+    (3, 3000, 16, 128, 64, 128, 256, "bf16"), (2, 700, 4, 64, 64, 128, 700, "bf16"),
+    (1, 5000, 8, 128, 64, 128, 2048, "bf16"), (2, 300, 4, 32, 16, 32, 64, "f32"),
+])
+def test_decode_cases(B, T, H, nope, rope, Dv, k, dt):
+    P = T - 1
+    hi = _attn_case(B, 1, P, H, nope, rope, Dv, seed=T + k, dt=dt)
+    idx = np.stack([datagen.indices_host(0, 1, 1, P, k, seed=T + b) for b in range(B)])
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, 1, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.dsa_sparse_attn_decode(to_dev(hi["q"]), to_dev(hi["k"]), to_dev(hi["v"]), to_dev(idx),
+                               to_dev(hi["gate"]), out, nope, rope)
+    _sync()
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], P, nope, rope)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"decode {B, T, k, dt}")
+
+
+# ------------------------------------------------------------------- SWA
+@pytest.mark.parametrize("B,S,P,W,H,nope,rope,Dv,dt,offset", [
+    (1, 300, 700, 128, 2, 128, 64, 128, "bf16", True), (2, 200, 0, 64, 3, 64, 64, 128, "bf16", False),
+    (1, 150, 40, 512, 2, 128, 64, 128, "bf16", True), (1, 1, 900, 512, 4, 128, 64, 128, "bf16", True),
+    (2, 6, 100, 32, 3, 64, 64, 64, "bf16", True), (1, 50, 20, 16, 2, 32, 16, 32, "f32", True),
+])
+def test_swa_cases(B, S, P, W, H, nope, rope, Dv, dt, offset):
+    kv_off = max(0, P - W + 1) if offset else 0
+    T = P + S
+    full = _attn_case(B, S, P, H, nope, rope, Dv, seed=W + S, dt=dt)
+    kb, vb = full["k"][:, kv_off:].copy(), full["v"][:, kv_off:].copy()
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.swa_attn(to_dev(full["q"]), to_dev(kb), to_dev(vb), to_dev(full["gate"]), out, P, kv_off, W,
+                 nope, rope)
+    _sync()
+    ref = oracle.swa_attn(full["q"], kb, vb, full["gate"], P, kv_off, W, nope, rope)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"swa {B, S, P, W}")
+
+
+# ------------------------------------------------------------ full chain
+def test_chain_mla_s4k_end_to_end():
+    """GPU indexer -> GPU top-k -> GPU attention vs the oracle's own chain.
+
+    Index sets may differ only at near-ties of the k-th score; rows whose
+    sets agree must match the oracle's attention output."""
+    wl = WORKLOADS["mla-s4k"]
+    hi = host_inputs(wl)
+    d = _attn_dev(hi)
+    S, T, k = wl.S, wl.T, wl.topk
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], sc, 0)
+    idx = torch.empty(1, S, k, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(sc, idx)
+    out = torch.empty(1, S, wl.H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_prefill(d["q"], d["k"], d["v"], idx, d["gate"], out, 0, wl.nope, wl.rope)
+    _sync()
+    g_idx = idx.cpu().numpy()[0]
+    ref_sc = oracle.index_scores(hi["q_idx"], hi["k_idx"], hi["w"], 0)[0]
+    o_idx = oracle.topk(ref_sc.astype(np.float32), k)
+    same = np.array([set(g_idx[s]) == set(o_idx[s]) for s in range(S)])
+    for s in np.nonzero(~same)[0]:
+        kth = np.sort(ref_sc[s][np.isfinite(ref_sc[s])])[::-1][min(k, s + 1) - 1]
+        fin = ref_sc[s][np.isfinite(ref_sc[s])]
+        rms = math.sqrt(float(np.mean(fin ** 2)))
+        for t in set(g_idx[s]) ^ set(o_idx[s]):
+            assert abs(ref_sc[s, t] - kth) <= 2e-2 * (abs(kth) + rms), (s, t)
+    assert same.mean() > 0.95
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], o_idx[None], hi["gate"], 0, wl.nope, wl.rope)
+    got = from_dev(out)
+    rows = np.nonzero(same)[0]
+    _cmp_attn(got[0, rows], ref[0, rows], 2e-2, "chain mla-s4k")
