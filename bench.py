@@ -92,6 +92,8 @@ class Layer:
             self.od = E(B, 1, H, Dv)
             self.wsd = torch.empty(dsa.dsa_sparse_attn_decode_workspace_size(B, H, Dv, k),
                                    dtype=torch.uint8, device=dev)
+            self.tk_wsd = torch.empty(max(dsa.dsa_topk_workspace_size(B, 1, T + 1, k), 1),
+                                      dtype=torch.uint8, device=dev)
             W = wl.window
             for j in range(1, wl.n_swa + 1):
                 off = max(0, P - W + 1)
@@ -141,7 +143,7 @@ class Layer:
             Td = wl.T + 1
             st += [
                 ("D K1 index_scores", lambda: dsa.dsa_index_scores(self.qd_idx, self.k_idx, self.wd, self.sd, Td - 1)),
-                ("D K2 topk", lambda: dsa.dsa_topk(self.sd, self.idd, self.tk_ws)),
+                ("D K2 topk", lambda: dsa.dsa_topk(self.sd, self.idd, self.tk_wsd)),
                 ("D K4 sparse_attn_decode", lambda: dsa.dsa_sparse_attn_decode(
                     self.qd, self.k, self.v, self.idd, self.gd, self.od, wl.nope, wl.rope,
                     workspace=self.wsd)),

@@ -30,7 +30,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kBN = 64;   // keys per step
 
 // --------------------------------------------------------- selection bitmap
@@ -73,16 +73,28 @@ __global__ __launch_bounds__(256) void bitmap_global_kernel(const int32_t* __res
 
 // ------------------------------------------------------------ flash kernel
 // MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA).
+//
+// One workgroup = one head x 128 queries, wave w owning queries 32w..32w+31.
+// Register budget is held to 256 per wave so two workgroups share a CU: one
+// computes while the other waits on its barrier or loads. Inside a
+// workgroup the next 64-key block is loaded into registers while the current
+// block is computed (software pipelining) and written to LDS after a barrier.
 template <int DQK, int DV, int MASK>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
     const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int S, int Tbuf, int P,
     int kv_offset, int H, int W32, int window, float scale_log2, int gate_dim) {
   constexpr int KSQ = DQK / 16;
   constexpr int NDB = DV / 32;
-  constexpr int KPAD = DQK + 8;  // bf16 elements per K row in LDS
-  constexpr int VPAD = kBN + 8;  // bf16 elements per V^T row in LDS
+  constexpr int KPAD = DQK + 8;           // bf16 elements per K row in LDS
+  constexpr int VPAD = kBN + 8;           // bf16 elements per V^T row in LDS
+  constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
+  constexpr int KLD = kBN * KCH / 256;    // K chunks per thread per block
+  constexpr int VCH = DV / 8;             // 8-dv groups per V row
+  constexpr int VUN = (kBN / 4) * VCH;    // (4 keys x 8 dv) units per block
+  constexpr int VLD = (VUN + 255) / 256;  // units per thread
+  static_assert((kBN * KCH) % 256 == 0, "K block must split evenly over 256 threads");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VPAD];
 
@@ -110,127 +122,138 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   if (MASK == 1) tlo = max(kv_offset, P + q0 - window + 1);
   const int jlo = ((tlo - kv_offset) / kBN) * kBN;
   const int jhi = min(pmax - kv_offset, Tbuf - 1);
+  const int64_t kvrow0 = (int64_t)b * Tbuf;
+
+  // ---- register prefetch of one key block
+  u32x4_t kpre[KLD];
+  u32x4_t vpre[VLD][4];
+  auto load_block = [&](int jb) {
+#pragma unroll
+    for (int r = 0; r < KLD; ++r) {
+      const int u = tid + 256 * r;
+      const int row = u / KCH, c = u - row * KCH;
+      const int j = jb + row;
+      kpre[r] = u32x4_t{0, 0, 0, 0};
+      if (j < Tbuf) kpre[r] = load16(k + ((kvrow0 + j) * H + h) * DQK + 8 * c);
+    }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int u = tid + 256 * r;
+      const int kg = u / VCH, dg = u - kg * VCH;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jb + 4 * kg + e;
+        vpre[r][e] = u32x4_t{0, 0, 0, 0};
+        if (u < VUN && j < Tbuf) vpre[r][e] = load16(v + ((kvrow0 + j) * H + h) * DV + 8 * dg);
+      }
+    }
+  };
+  // ---- registers -> LDS: K row-major, V transposed with bits 2/3 of the key
+  // offset swapped inside each 16-key chunk (the order the P^T operand uses)
+  auto store_block = [&]() {
+#pragma unroll
+    for (int r = 0; r < KLD; ++r) {
+      const int u = tid + 256 * r;
+      const int row = u / KCH, c = u - row * KCH;
+      *(u32x4_t*)(&Ks[row * KPAD + 8 * c]) = kpre[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int u = tid + 256 * r;
+      if (u < VUN) {
+        const int kg = u / VCH, dg = u - kg * VCH;
+        const int o16 = (4 * kg) & 15;
+        const int pos = ((4 * kg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const uint32_t a0 = vpre[r][0][mm], a1 = vpre[r][1][mm];
+          const uint32_t a2 = vpre[r][2][mm], a3 = vpre[r][3][mm];
+          uint2 lo, hi;
+          lo.x = (a0 & 0xFFFFu) | (a1 << 16);
+          lo.y = (a2 & 0xFFFFu) | (a3 << 16);
+          hi.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
+          hi.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
+          *(uint2*)(&Vt[(8 * dg + 2 * mm) * VPAD + pos]) = lo;
+          *(uint2*)(&Vt[(8 * dg + 2 * mm + 1) * VPAD + pos]) = hi;
+        }
+      }
+    }
+  };
 
   float m = -INFINITY, l = 0.0f;
   f32x16_t o[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) o[d] = zero16();
-
   const uint32_t* bmrow = bm + qrow * (int64_t)W32;
-  const int64_t kvrow0 = (int64_t)b * Tbuf;
 
+  if (jlo <= jhi) load_block(jlo);
   for (int jb = jlo; jb <= jhi; jb += kBN) {
-    __syncthreads();
-    // ---- stage K rows jb..jb+63 -> Ks[row][dim]
-    constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
-    for (int u = tid; u < kBN * KCH; u += 256) {
-      const int r = u / KCH, c = u - r * KCH;
-      const int j = jb + r;
-      u32x4_t val = u32x4_t{0, 0, 0, 0};
-      if (j < Tbuf) val = load16(k + ((kvrow0 + j) * H + h) * DQK + 8 * c);
-      *(u32x4_t*)(&Ks[r * KPAD + 8 * c]) = val;
-    }
-    // ---- stage V rows jb..jb+63 -> Vt[dv][perm(key)], 4 keys x 8 dv per unit
-    constexpr int VCH = DV / 8;
-    for (int u = tid; u < (kBN / 4) * VCH; u += 256) {
-      const int kg = u / VCH, dg = u - kg * VCH;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jb + 4 * kg + r;
-        u32x4_t val = u32x4_t{0, 0, 0, 0};
-        if (j < Tbuf) val = load16(v + ((kvrow0 + j) * H + h) * DV + 8 * dg);
-        w[r][0] = val[0];
-        w[r][1] = val[1];
-        w[r][2] = val[2];
-        w[r][3] = val[3];
-      }
-      const int o16 = (4 * kg) & 15;  // 0, 4, 8, 12 within the 16-key chunk
-      const int pos = ((4 * kg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        // dv 8*dg + 2*mm (low halves) and 8*dg + 2*mm + 1 (high halves)
-        const uint32_t lo01 = (w[0][mm] & 0xFFFFu) | (w[1][mm] << 16);
-        const uint32_t lo23 = (w[2][mm] & 0xFFFFu) | (w[3][mm] << 16);
-        const uint32_t hi01 = (w[0][mm] >> 16) | (w[1][mm] & 0xFFFF0000u);
-        const uint32_t hi23 = (w[2][mm] >> 16) | (w[3][mm] & 0xFFFF0000u);
-        uint32_t* d0 = (uint32_t*)&Vt[(8 * dg + 2 * mm) * VPAD + pos];
-        uint32_t* d1 = (uint32_t*)&Vt[(8 * dg + 2 * mm + 1) * VPAD + pos];
-        d0[0] = lo01;
-        d0[1] = lo23;
-        d1[0] = hi01;
-        d1[1] = hi23;
-      }
-    }
+    __syncthreads();  // every wave is done reading the previous block
+    store_block();
     __syncthreads();
 
-    // ---- S^T = K Q^T for 64 keys x this wave's 32 queries
-    f32x16_t st[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      st[i] = zero16();
-      const uint16_t* kr = &Ks[(32 * i + ln) * KPAD + 8 * lh];
-#pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks)
-        st[i] = mfma32x32x16(as_bf16x8(*(const u32x4_t*)(kr + 16 * ks)), bq[ks], st[i]);
-    }
-
-    // ---- mask, online softmax (log2 domain)
     uint32_t bits[2] = {0u, 0u};
     if (MASK == 0) {
-      const int w0 = (jb >> 5);
+      const int w0 = jb >> 5;
       bits[0] = (w0 < W32) ? bmrow[w0] : 0u;
       bits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
     }
-    float mx = -INFINITY;
+
+    // the next block's loads overlap this block's MFMA and softmax work
+    if (jb + kBN <= jhi) load_block(jb + kBN);
+
+    // two 32-key halves in sequence: S^T, masked online softmax, O^T += V^T P^T
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      f32x16_t st = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) {
+        const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Ks[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
+        st = mfma32x32x16(a, bq[ks], st);
+      }
+      // mask, then the running max on raw logits (scale > 0 keeps the order)
+      float mx = -INFINITY;
+      const uint32_t wbits = (MASK == 0) ? (bits[i] >> (4 * lh)) : 0u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int off = 8 * (e >> 2) + 4 * lh + (e & 3);
         bool ok;
         if (MASK == 0) {
-          ok = (bits[i] >> off) & 1u;
+          ok = (wbits >> (8 * (e >> 2) + (e & 3))) & 1u;
         } else {
-          const int j = jb + 32 * i + off;
-          const int t = kv_offset + j;
-          ok = (j < Tbuf) && (t <= p) && (t > p - window);
+          const int jj = jb + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+          const int t = kv_offset + jj;
+          ok = (jj < Tbuf) && (t <= p) && (t > p - window);
         }
-        const float x = ok ? st[i][e] * scale_log2 : -INFINITY;
-        st[i][e] = x;
+        const float x = ok ? st[e] : -INFINITY;
+        st[e] = x;
         mx = fmaxf(mx, x);
       }
-    }
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float muse = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = exp2f(m - muse);
-    m = mnew;
-    float psum = 0.0f;
-    uint32_t pk[2][2][4];  // [key block][half of 16 keys][packed pair]
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      // p = 2^(scale*log2e*(x - m)) as one fma + exp2; masked x = -inf gives 0
+      const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
+      const float alpha = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * scale_log2);
+      const bool changed = mnew != m;
+      m = mnew;
+      uint32_t pk[2][4];  // [16-key half][packed pair]
+      float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = exp2f(st[i][e] - muse);
-        const float p1 = exp2f(st[i][e + 1] - muse);
+        const float p0 = exp2f(fmaf(st[e], scale_log2, nms));
+        const float p1 = exp2f(fmaf(st[e + 1], scale_log2, nms));
         psum += p0 + p1;
-        pk[i][e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+        pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
       }
-    }
-    l = l * alpha + psum;
+      l = l * alpha + psum;
+      if (__any(changed)) {
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+        for (int d = 0; d < NDB; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8_t pb =
-            as_bf16x8(u32x4_t{pk[i][c][0], pk[i][c][1], pk[i][c][2], pk[i][c][3]});
+        const bf16x8_t pb = as_bf16x8(u32x4_t{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
         const int kcol = 32 * i + 16 * c + 8 * lh;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {

@@ -5,200 +5,443 @@
 // positions), ordered by score descending and position ascending; -inf
 // slots are reported as -1.
 //
-// Every element becomes a unique 64-bit key
+// Every finite score becomes a unique non-zero 64-bit key
 //     key = orderable(score) << 32 | (0xFFFFFFFF - t)
 // (orderable() is monotone in the float order and folds -0.0 onto +0.0), so
 // "largest k keys" is exactly the required selection including the
-// lower-position tie rule. A radix select over 8-bit digits, most significant
-// first, finds the k-th largest key; it stops as soon as every key sharing the
-// current prefix is needed. Keys >= that threshold are compacted into LDS and
-// sorted with a bitonic network. Histograms are per wave (LDS atomics), the
-// digit search is a wave-level suffix scan. One 1024-thread workgroup per
-// row; rows up to 32768 elements stay in registers, longer rows are re-read
-// from memory on every pass.
+// lower-position tie rule. -inf scores become key 0 and are never selected:
+// if a row has only n < k finite scores, its last k - n slots are -1, which is
+// what selecting -inf entries would print anyway. (Skipping them also keeps
+// the causal half of every prefill row out of the histograms, where its
+// identical keys would serialise the LDS atomics.)
+//
+// One 256-thread workgroup per (row, segment):
+//  1. count the valid keys; k' = min(k, count);
+//  2. radix select of the k'-th largest key, most significant digit first,
+//     11/11/10-bit digits per 32-bit half, one shared LDS histogram per
+//     pass, a block suffix scan to pick the digit; it stops as soon as every
+//     key sharing the current prefix is needed (normally after two or three
+//     passes over the high half);
+//  3. the k' keys >= threshold are compacted into LDS;
+//  4. either a bitonic sort (descending; strides inside a thread run in
+//     registers, inside a wave via lane swaps, only the widest through LDS)
+//     and the index output, or, for the first stage of a long row, the
+//     unsorted keys of the segment (padded with 0) for a second pass.
+// Long rows with few rows per call are split: segments of 16384 scores are
+// reduced to k candidate keys each, then one workgroup per row selects the
+// final k among the candidates.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 2048;
+constexpr int kBins = 2048;
+constexpr int kSegLen = 16384;   // segment length of the first stage (long rows)
+constexpr int kSegMinRows = 512; // rows per call below which long rows are segmented
 
-__device__ __forceinline__ uint64_t make_key(float sc, int t) {
+__device__ __forceinline__ uint64_t score_key(float sc, int t) {
+  if (sc == -INFINITY) return 0ull;
   return ((uint64_t)orderable_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
 }
 
-// EPT > 0: T <= kThreads * EPT, elements held in registers; EPT == 0: streamed.
-template <int EPT>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
-                                                        int32_t* __restrict__ out, int T, int k,
-                                                        int k2) {
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ uint32_t total[256];
-  __shared__ uint64_t sel[kMaxK];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_krem;
-  __shared__ int s_done;
-  __shared__ uint32_t s_cnt;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const float* srow = scores + row * (int64_t)T;
+// digit layout: pass 0..2 on the high word, 3..5 on the low word
+__device__ __forceinline__ int digit_shift(int pass) {
+  const int lo = (pass >= 3) ? 0 : 32;
+  const int pp = pass % 3;
+  return lo + (pp == 0 ? 21 : (pp == 1 ? 10 : 0));
+}
+__device__ __forceinline__ uint32_t digit_mask(int pass) { return (pass % 3 == 2) ? 0x3FFu : 0x7FFu; }
 
-  uint32_t kreg[EPT > 0 ? EPT : 1];
-  if (EPT > 0) {
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int t = tid + j * kThreads;
-      kreg[j] = t < T ? orderable_key(srow[t]) : 0u;
-    }
-  }
-
-  uint64_t prefix = 0, mask = 0;
-  int krem = k;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    if (EPT > 0) {
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) {
-        const int t = tid + j * kThreads;
-        if (t < T) {
-          const uint64_t key = ((uint64_t)kreg[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
-          if ((key & mask) == prefix) atomicAdd(&hist[wave][(uint32_t)(key >> shift) & 255u], 1u);
-        }
-      }
-    } else {
-      for (int t = tid; t < T; t += kThreads) {
-        const uint64_t key = make_key(srow[t], t);
-        if ((key & mask) == prefix) atomicAdd(&hist[wave][(uint32_t)(key >> shift) & 255u], 1u);
-      }
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) c += hist[w][tid];
-      total[tid] = c;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins 4l..4l+3; suffix sums over lanes (high digits first)
-      const uint32_t b0 = total[4 * lane], b1 = total[4 * lane + 1], b2 = total[4 * lane + 2],
-                     b3 = total[4 * lane + 3];
-      const uint32_t local = b0 + b1 + b2 + b3;
-      uint32_t x = local;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += y;
-      }
-      const uint64_t ball = __ballot(x >= (uint32_t)krem);
-      const int L = __popcll(ball) - 1;  // highest lane whose suffix reaches krem
-      if (lane == L) {
-        uint32_t cum = x - local;  // elements in digits above this lane's bins
-        const uint32_t bins[4] = {b0, b1, b2, b3};
-        int digit = 4 * lane;
-        uint32_t above = cum;
-        for (int q = 3; q >= 0; --q) {
-          if (cum + bins[q] >= (uint32_t)krem) {
-            digit = 4 * lane + q;
-            above = cum;
-            break;
-          }
-          cum += bins[q];
-        }
-        const int kr = krem - (int)above;
-        s_prefix = prefix | ((uint64_t)digit << shift);
-        s_krem = kr;
-        s_done = (total[digit] == (uint32_t)kr) ? 1 : 0;
-      }
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    mask |= (uint64_t)0xFF << shift;
-    krem = s_krem;
-    const int done = s_done;
-    __syncthreads();
-    if (done) break;
-  }
-
-  // compact keys >= threshold (exactly k of them)
-  if (tid == 0) s_cnt = 0;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  const uint64_t thr = prefix;
-  if (EPT > 0) {
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int t = tid + j * kThreads;
-      if (t < T) {
-        const uint64_t key = ((uint64_t)kreg[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
-        if (key >= thr) {
-          const uint32_t pos = atomicAdd(&s_cnt, 1u);
-          if (pos < (uint32_t)kMaxK) sel[pos] = key;
-        }
-      }
-    }
-  } else {
-    for (int t = tid; t < T; t += kThreads) {
-      const uint64_t key = make_key(srow[t], t);
-      if (key >= thr) {
-        const uint32_t pos = atomicAdd(&s_cnt, 1u);
-        if (pos < (uint32_t)kMaxK) sel[pos] = key;
-      }
-    }
-  }
-  for (int i = k + tid; i < k2; i += kThreads) sel[i] = 0;  // pad to a power of two
+  if (lane == 0) red[wave] = v;
   __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s += red[w];
+  return s;
+}
 
-  // bitonic sort, descending
-  for (int size = 2; size <= k2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (k2 >> 1); i += kThreads) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const uint64_t a = sel[lo], c = sel[hi];
-        const bool desc = (lo & size) == 0;
-        if (desc ? (a < c) : (a > c)) {
-          sel[lo] = c;
-          sel[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
+// After a histogram pass: find the digit holding the krem-th largest key.
+// Thread t owns bins 8t..8t+7; a block suffix scan over threads (high digits
+// first) locates the bin. Writes the digit, the count still needed inside
+// it, and whether that bin is taken whole.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, int krem, int tid,
+                                           int lane, int wave, int* s_krem, int* s_done,
+                                           int* s_digit) {
+  uint32_t bins[8];
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    bins[q] = hist[8 * tid + q];
+    local += bins[q];
   }
-
-  int32_t* orow = out + row * (int64_t)k;
-  for (int i = tid; i < k; i += kThreads) {
-    const uint64_t key = sel[i];
-    const uint32_t hi = (uint32_t)(key >> 32);
-    orow[i] = (hi == DSA_NEG_INF_KEY) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+  uint32_t x = local;  // inclusive suffix sum within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  uint32_t above_waves = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w > wave) above_waves += red[w];
+  const uint32_t suf = x + above_waves;   // keys in bins >= 8*tid
+  const uint32_t suf_next = suf - local;  // keys in bins >= 8*tid + 8
+  if (suf >= (uint32_t)krem && suf_next < (uint32_t)krem) {
+    uint32_t cum = suf_next;
+    int q = 7;
+    for (; q > 0; --q) {
+      if (cum + bins[q] >= (uint32_t)krem) break;
+      cum += bins[q];
+    }
+    const int kr = krem - (int)cum;
+    *s_digit = 8 * tid + q;
+    *s_krem = kr;
+    *s_done = (bins[q] == (uint32_t)kr) ? 1 : 0;
   }
 }
 
+// SRC 0: fp32 scores, element range [seg*seg_len, min(T, (seg+1)*seg_len)) of
+//        row blockIdx.x / nseg (seg = blockIdx.x % nseg);
+// SRC 1: 64-bit candidate keys, row blockIdx.x holds T keys.
+// DST 0: sorted indices to out_idx[row, 0..k); DST 1: unsorted keys of this
+//        segment to out_keys[(row*nseg + seg)*k ...], padded with 0.
+// EPT > 0 keeps the elements in registers (range <= 256*EPT); EPT == 0 streams.
+// E: sort elements per thread (the sort covers max(k, 256) = 256*E keys).
+template <int SRC, int DST, int EPT, int E>
+__global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__ src,
+                                                        int32_t* __restrict__ out_idx,
+                                                        uint64_t* __restrict__ out_keys, int T,
+                                                        int k, int seg_len, int nseg) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t sel[kMaxK > 256 * E ? kMaxK : 256 * E];
+  __shared__ uint32_t s_red[kWaves];
+  __shared__ uint32_t s_col[(EPT > 0 ? EPT : 1) * kWaves];
+  __shared__ int s_krem, s_done, s_digit;
+  __shared__ uint32_t s_cnt;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t row;
+  int seg, t0, n;
+  if (SRC == 0) {
+    row = blockIdx.x / nseg;
+    seg = (int)(blockIdx.x % nseg);
+    t0 = seg * seg_len;
+    n = min(T - t0, seg_len);
+  } else {
+    row = blockIdx.x;
+    seg = 0;
+    t0 = 0;
+    n = T;
+  }
+  const float* srow = (const float*)src + row * (int64_t)T;
+  const uint64_t* krow = (const uint64_t*)src + row * (int64_t)T;
+  auto load_key = [&](int j) -> uint64_t {
+    if (SRC == 0) return score_key(srow[t0 + j], t0 + j);
+    return krow[j];
+  };
+  // registers hold the high word only for score input (the low word is the
+  // position, known from the slot), the whole key for candidate input
+  using KT = typename std::conditional<SRC == 0, uint32_t, uint64_t>::type;
+  KT kreg[EPT > 0 ? EPT : 1];
+  auto reg_key = [&](int j) -> uint64_t {
+    if (SRC == 1) return (uint64_t)kreg[j];
+    const int t = t0 + tid + j * kThreads;
+    return kreg[j] ? (((uint64_t)kreg[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t)) : 0ull;
+  };
+  uint32_t valid = 0;
+  if (EPT > 0) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + j * kThreads;
+      const uint64_t key = e < n ? load_key(e) : 0ull;
+      kreg[j] = (SRC == 0) ? (KT)(key >> 32) : (KT)key;
+      valid += key != 0ull;
+    }
+  } else {
+    for (int e = tid; e < n; e += kThreads) valid += load_key(e) != 0ull;
+  }
+  const int nvalid = (int)block_sum(valid, s_red);
+  const int kk = min(k, nvalid);
+
+  // Register path on score input: the selection is decided on the 32-bit
+  // score key alone; ties at the threshold are resolved by position rank.
+  if (EPT > 0 && SRC == 0) {
+    uint32_t prefix = 0, mask = 0;
+    int krem = kk;
+    bool done = kk == 0;
+    for (int pass = 0; pass < 3 && !done; ++pass) {
+      const int shift = (pass == 0) ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = (pass == 2) ? 0x3FFu : 0x7FFu;
+      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const uint32_t hi = (uint32_t)kreg[j];
+        if (hi != 0u && (hi & mask) == prefix) atomicAdd(&hist[(hi >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      pick_digit(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= dmask << shift;
+      krem = s_krem;
+      done = s_done != 0;
+    }
+    // done: every key >= prefix is taken. Otherwise the score key is fully
+    // determined (prefix), all larger keys are taken, and among the keys equal
+    // to it the krem lowest positions.
+    if (tid == 0) s_cnt = 0;
+    if (!done) {
+      // positions t = t0 + 256 j + 64 wave + lane are ordered (j, wave, lane)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const uint64_t b = __ballot((uint32_t)kreg[j] == prefix);
+        if (lane == 0) s_col[j * kWaves + wave] = (uint32_t)__popcll(b);
+      }
+      __syncthreads();
+      if (wave == 0) {  // exclusive prefix over the EPT*4 column counts
+        constexpr int PER = EPT > 0 ? (EPT * kWaves + 63) / 64 : 1;
+        uint32_t v[PER];
+        uint32_t loc = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          v[q] = i < EPT * kWaves ? s_col[i] : 0u;
+          loc += v[q];
+        }
+        uint32_t x = loc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        uint32_t run = x - loc;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int i = lane * PER + q;
+          if (i < EPT * kWaves) s_col[i] = run;
+          run += v[q];
+        }
+      }
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const uint32_t hi = (uint32_t)kreg[j];
+      bool take;
+      if (done) {
+        take = hi != 0u && hi >= prefix;
+      } else {
+        const bool tie = hi == prefix;
+        const uint64_t b = __ballot(tie);
+        const uint32_t rank = s_col[j * kWaves + wave] + (uint32_t)__popcll(b & lt_mask);
+        take = hi > prefix || (tie && rank < (uint32_t)krem);
+      }
+      if (take) {
+        const uint32_t t = (uint32_t)(t0 + tid + j * kThreads);
+        const uint32_t pos = atomicAdd(&s_cnt, 1u);
+        if (pos < (uint32_t)kMaxK) sel[pos] = ((uint64_t)hi << 32) | (0xFFFFFFFFu - t);
+      }
+    }
+    __syncthreads();
+  } else {
+    // 64-bit keys (candidate input, or streamed rows): radix select on both halves
+    uint64_t prefix = 0, mask = 0;
+    if (kk > 0) {
+      int krem = kk;
+      for (int pass = 0; pass < 6; ++pass) {
+        const int shift = digit_shift(pass);
+        const uint32_t dmask = digit_mask(pass);
+        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        if (EPT > 0) {
+#pragma unroll
+          for (int j = 0; j < EPT; ++j) {
+            const uint64_t key = reg_key(j);
+            if (key != 0ull && (key & mask) == prefix)
+              atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
+          }
+        } else {
+          for (int e = tid; e < n; e += kThreads) {
+            const uint64_t key = load_key(e);
+            if (key != 0ull && (key & mask) == prefix)
+              atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
+          }
+        }
+        __syncthreads();
+        pick_digit(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+        __syncthreads();
+        prefix |= (uint64_t)s_digit << shift;
+        mask |= (uint64_t)dmask << shift;
+        krem = s_krem;
+        if (s_done) break;
+      }
+    }
+    // compact the kk keys >= threshold
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    if (kk > 0) {
+      const uint64_t thr = prefix;
+      if (EPT > 0) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          const uint64_t key = reg_key(j);
+          if (key != 0ull && key >= thr) {
+            const uint32_t pos = atomicAdd(&s_cnt, 1u);
+            if (pos < (uint32_t)kMaxK) sel[pos] = key;
+          }
+        }
+      } else {
+        for (int e = tid; e < n; e += kThreads) {
+          const uint64_t key = load_key(e);
+          if (key != 0ull && key >= thr) {
+            const uint32_t pos = atomicAdd(&s_cnt, 1u);
+            if (pos < (uint32_t)kMaxK) sel[pos] = key;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (DST == 1) {  // first stage of a long row: unsorted candidates
+    uint64_t* o = out_keys + ((int64_t)row * nseg + seg) * k;
+    for (int i = tid; i < k; i += kThreads) o[i] = (i < kk) ? sel[i] : 0ull;
+    return;
+  }
+
+  // ---- bitonic sort (descending) of N = 256*E keys, padded with 0
+  constexpr int N = 256 * E;
+  uint64_t a[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    a[e] = (i < kk) ? sel[i] : 0ull;
+  }
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pe = e ^ stride;
+          if (pe > e) {
+            const int i = tid * E + e;
+            const bool desc = (i & size) == 0;
+            const uint64_t lo = a[e], hi = a[pe];
+            const bool sw = desc ? (lo < hi) : (lo > hi);
+            a[e] = sw ? hi : lo;
+            a[pe] = sw ? lo : hi;
+          }
+        }
+      } else if (stride < 64 * E) {
+        const int lm = stride / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          const uint64_t other = shfl_xor_u64(a[e], lm);
+          const bool desc = (i & size) == 0;
+          const bool low = (i & stride) == 0;  // lower index of its pair
+          const bool keep_max = (low == desc);
+          a[e] = keep_max ? (a[e] > other ? a[e] : other) : (a[e] < other ? a[e] : other);
+        }
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) sel[tid * E + e] = a[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          const uint64_t other = sel[i ^ stride];
+          const bool desc = (i & size) == 0;
+          const bool low = (i & stride) == 0;
+          const bool keep_max = (low == desc);
+          a[e] = keep_max ? (a[e] > other ? a[e] : other) : (a[e] < other ? a[e] : other);
+        }
+      }
+    }
+  }
+
+  int32_t* orow = out_idx + row * (int64_t)k;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < k) orow[i] = (a[e] == 0ull) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)a[e]);
+  }
+}
+
+template <int SRC, int DST, int EPT>
+hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T, int k,
+                    int seg_len, int nseg, hipStream_t st) {
+  const dim3 g((unsigned)blocks), b(kThreads);
+  if (DST == 1 || k <= 256)
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else if (k <= 512)
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else if (k <= 1024)
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else
+    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  return hipGetLastError();
+}
+
+// rows of length T processed whole (one workgroup per row)
+hipError_t launch_rows(const float* scores, int32_t* idx, int64_t rows, int T, int k, hipStream_t st) {
+  if (T <= kThreads * 16) return launch_e<0, 0, 16>(scores, idx, nullptr, rows, T, k, T, 1, st);
+  if (T <= kThreads * 64) return launch_e<0, 0, 64>(scores, idx, nullptr, rows, T, k, T, 1, st);
+  if (T <= kThreads * 128) return launch_e<0, 0, 128>(scores, idx, nullptr, rows, T, k, T, 1, st);
+  return launch_e<0, 0, 0>(scores, idx, nullptr, rows, T, k, T, 1, st);
+}
+
+bool segmented(int64_t rows, int T) { return T > 4 * kSegLen && rows < kSegMinRows; }
+
 }  // namespace
 
-size_t topk_workspace_bytes(int, int, int, int) { return 0; }
+size_t topk_workspace_bytes(int B, int S, int T, int topk) {
+  const int64_t rows = (int64_t)B * S;
+  if (!segmented(rows, T)) return 0;
+  const int64_t nseg = (T + kSegLen - 1) / kSegLen;
+  return (size_t)(rows * nseg * topk) * sizeof(uint64_t);
+}
 
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void*, hipStream_t stream) {
-  int k2 = 1;
-  while (k2 < topk) k2 <<= 1;
+                       void* workspace, hipStream_t stream) {
   const int64_t rows = (int64_t)B * S;
-  if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (T <= kThreads * 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
-                       indices, T, topk, k2);
-  else if (T <= kThreads * 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
-                       indices, T, topk, k2);
-  else
-    hipLaunchKernelGGL(topk_kernel<0>, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
-                       indices, T, topk, k2);
-  return hipGetLastError();
+  if (!segmented(rows, T)) {
+    if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    return launch_rows(scores, indices, rows, T, topk, stream);
+  }
+  // stage 1: k candidate keys per 16384-score segment
+  const int nseg = (T + kSegLen - 1) / kSegLen;
+  uint64_t* cand = (uint64_t*)workspace;
+  hipError_t e = launch_e<0, 1, kSegLen / kThreads>(scores, nullptr, cand, rows * nseg, T, topk,
+                                                    kSegLen, nseg, stream);
+  if (e != hipSuccess) return e;
+  // stage 2: final selection and sort among nseg * k candidates per row
+  const int C = nseg * topk;
+  if (C <= kThreads * 64)
+    return launch_e<1, 0, 64>(cand, indices, nullptr, rows, C, topk, C, 1, stream);
+  return launch_e<1, 0, 0>(cand, indices, nullptr, rows, C, topk, C, 1, stream);
 }
 
 }  // namespace dsa

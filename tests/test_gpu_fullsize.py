@@ -1,0 +1,267 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times, on sampled outputs the oracle computes one by one (GPU).
+
+Inputs are generated in HBM by the device twin of the seeded generator; the
+oracle gets the same values from the host twin. For sampled attention rows
+the oracle receives only the selected cache rows (a compact cache whose
+position j holds the j-th selected key, with index list 0..n-1): attention
+is a function of the selected set, so this is the same result.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import sparse_attention_11_amd as dsa
+from datagen.configs import WORKLOADS
+from tests._helpers import assert_rows_close, from_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sample_rows(S, k, n=12, seed=0):
+    rng = np.random.default_rng(seed)
+    base = {0, min(k - 1, S - 1), min(k, S - 1), S - 1}
+    extra = rng.choice(S, size=min(n, S), replace=False).tolist()
+    return sorted(base | set(extra))
+
+
+def dev_normal(shape, wl, tid, scale, start=0):
+    t = torch.empty(*shape, dtype=torch.bfloat16, device=DEV)
+    return datagen.normal_device(t, wl.seed, tid, scale, start)
+
+
+def host_row(wl, tid, scale, row, width):
+    """Row `row` (elements row*width ... +width) of a bf16 stream."""
+    return datagen.normal_host((width,), "bf16", wl.seed, tid, scale, start=row * width)
+
+
+def compact_cache(wl, positions, b, T_alloc, H, D, tid, scale):
+    """[1, n, H, D] rows of cache b at the given absolute positions."""
+    rows = [host_row(wl, tid, scale, b * T_alloc + int(t), H * D) for t in positions]
+    return np.stack(rows).reshape(1, len(positions), H, D)
+
+
+def check_attn_rows(wl, out, idx, rows, b, T_alloc, qtid=datagen.TID_Q, gtid=datagen.TID_GATE,
+                    S_stream=None, ktid=datagen.TID_K, vtid=datagen.TID_V):
+    """Compare out[b, s] for s in rows against the oracle on compact caches."""
+    S_stream = wl.S if S_stream is None else S_stream
+    H, Dqk, Dv = wl.H, wl.Dqk, wl.v
+    for s in rows:
+        sel = [int(t) for t in idx[s] if t >= 0]
+        kc = compact_cache(wl, sel, b, T_alloc, H, Dqk, ktid, wl.scale_k)
+        vc = compact_cache(wl, sel, b, T_alloc, H, Dv, vtid, wl.scale_v)
+        r = b * S_stream + s
+        q = host_row(wl, qtid, wl.scale_q, r, H * Dqk).reshape(1, 1, H, Dqk)
+        g = host_row(wl, gtid, wl.scale_gate, r, H).reshape(1, 1, H)
+        n = len(sel)
+        ci = np.arange(n, dtype=np.int32).reshape(1, 1, n)
+        ref = oracle.sparse_attn(q, kc, vc, ci, g, n - 1, wl.nope, wl.rope)[0, 0]
+        assert_rows_close(out[s].reshape(H, Dv), ref, 2e-2, what=f"{wl.name} attn row {s}")
+
+
+# ------------------------------------------------------------ dsa-s32k
+def test_dsa_s32k_indexer_sampled_rows():
+    wl = WORKLOADS["dsa-s32k"]
+    S, T = wl.S, wl.T
+    q_idx = dev_normal((1, S, wl.HI, wl.DI), wl, datagen.TID_QIDX, wl.scale_qidx)
+    k_idx = dev_normal((1, T, wl.DI), wl, datagen.TID_KIDX, wl.scale_kidx)
+    w = dev_normal((1, S, wl.HI), wl, datagen.TID_W, wl.scale_w)
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(q_idx, k_idx, w, sc, 0)
+    rows = sample_rows(S, wl.topk, n=10, seed=1)
+    got = sc[0, rows].cpu().numpy()
+    del sc, q_idx, w
+    _free()
+    kh = datagen.normal_host((1, T, wl.DI), "bf16", wl.seed, datagen.TID_KIDX, wl.scale_kidx)
+    for i, s in enumerate(rows):
+        qh = host_row(wl, datagen.TID_QIDX, wl.scale_qidx, s, wl.HI * wl.DI).reshape(1, 1, wl.HI, wl.DI)
+        wh = host_row(wl, datagen.TID_W, wl.scale_w, s, wl.HI).reshape(1, 1, wl.HI)
+        ref = oracle.index_scores(qh, kh, wh, s)[0, 0]
+        assert_rows_close(got[i], ref, 2e-2, what=f"dsa-s32k scores row {s}")
+
+
+def _topk_full(wl, S, T, P, k, mode, rows, seed_off=0):
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    datagen.scores_device(sc.view(S, T), 0, S, P, wl.seed + seed_off, mode=mode)
+    idx = torch.empty(1, S, k, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(sc, idx)
+    got = idx[0, rows].cpu().numpy()
+    del sc, idx
+    _free()
+    for i, s in enumerate(rows):
+        ref_sc = datagen.scores_host(s, 1, S, T, P, wl.seed + seed_off, mode=mode)
+        np.testing.assert_array_equal(got[i], oracle.topk(ref_sc, k)[0], err_msg=f"row {s}")
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_dsa_s32k_topk_full_tensor(mode):
+    wl = WORKLOADS["dsa-s32k"]
+    _topk_full(wl, wl.S, wl.T, 0, wl.topk, mode, sample_rows(wl.S, wl.topk, n=12, seed=2))
+
+
+def test_dsa_s32k_prefill_sampled_rows():
+    wl = WORKLOADS["dsa-s32k"]
+    S, T, H = wl.S, wl.T, wl.H
+    q = dev_normal((1, S, H, wl.Dqk), wl, datagen.TID_Q, wl.scale_q)
+    k = dev_normal((1, T, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)
+    v = dev_normal((1, T, H, wl.v), wl, datagen.TID_V, wl.scale_v)
+    g = dev_normal((1, S, H), wl, datagen.TID_GATE, wl.scale_gate)
+    idx = torch.empty(1, S, wl.topk, dtype=torch.int32, device=DEV)
+    datagen.indices_device(idx.view(S, wl.topk), 0, S, 0, seed=wl.seed)
+    out = torch.empty(1, S, H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_prefill(q, k, v, idx, g, out, 0, wl.nope, wl.rope)
+    rows = sample_rows(S, wl.topk, n=8, seed=3)
+    got = from_dev(out[0, rows])
+    idx_h = datagen.indices_host(0, S, S, 0, wl.topk, seed=wl.seed)
+    del q, k, v, g, idx, out
+    _free()
+    check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, T)
+
+
+# ----------------------------------------------------------- decode-b8
+def test_decode_b8_full_layer():
+    wl = WORKLOADS["decode-b8"]
+    B, T, H, P = wl.B, wl.T, wl.H, wl.past_len
+    q_idx = dev_normal((B, 1, wl.HI, wl.DI), wl, datagen.TID_QIDX, wl.scale_qidx)
+    k_idx = dev_normal((B, T, wl.DI), wl, datagen.TID_KIDX, wl.scale_kidx)
+    w = dev_normal((B, 1, wl.HI), wl, datagen.TID_W, wl.scale_w)
+    sc = torch.empty(B, 1, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(q_idx, k_idx, w, sc, P)
+    got_sc = sc.cpu().numpy()
+    del q_idx, k_idx, w, sc
+    _free()
+    kh = datagen.normal_host((B, T, wl.DI), "bf16", wl.seed, datagen.TID_KIDX, wl.scale_kidx)
+    qh = datagen.normal_host((B, 1, wl.HI, wl.DI), "bf16", wl.seed, datagen.TID_QIDX, wl.scale_qidx)
+    wh = datagen.normal_host((B, 1, wl.HI), "bf16", wl.seed, datagen.TID_W, wl.scale_w)
+    ref = oracle.index_scores(qh, kh, wh, P)
+    assert_rows_close(got_sc, ref, 2e-2, what="decode-b8 scores")
+    del kh
+
+    # top-k on a synthetic full-size score tensor
+    scs = torch.empty(B, 1, T, dtype=torch.float32, device=DEV)
+    datagen.scores_device(scs.view(B, T), 0, 1, P, wl.seed, mode=1)
+    idx = torch.empty(B, 1, wl.topk, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(scs, idx)
+    got_i = idx.cpu().numpy()[:, 0]
+    ref_i = oracle.topk(datagen.scores_host(0, B, 1, T, P, wl.seed, mode=1), wl.topk)
+    np.testing.assert_array_equal(got_i, ref_i)
+    del scs, idx
+    _free()
+
+    # decode attention over 8 x 131072 expanded rows with generated selections
+    k = dev_normal((B, T, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)
+    v = dev_normal((B, T, H, wl.v), wl, datagen.TID_V, wl.scale_v)
+    q = dev_normal((B, 1, H, wl.Dqk), wl, datagen.TID_Q, wl.scale_q)
+    g = dev_normal((B, 1, H), wl, datagen.TID_GATE, wl.scale_gate)
+    idx = torch.empty(B, 1, wl.topk, dtype=torch.int32, device=DEV)
+    datagen.indices_device(idx.view(B, wl.topk), 0, 1, P, seed=wl.seed)
+    out = torch.empty(B, 1, H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_decode(q, k, v, idx, g, out, wl.nope, wl.rope)
+    got = from_dev(out)
+    del k, v, q, g, idx, out
+    _free()
+    idx_h = datagen.indices_host(0, B, 1, P, wl.topk, seed=wl.seed)
+    for b in range(B):
+        check_attn_rows(wl, {0: got[b, 0]}, idx_h[b:b + 1], [0], b, T, S_stream=1)
+
+
+# --------------------------------------------------------- hybrid-512k
+def test_hybrid_512k_chunk_and_decode():
+    wl = WORKLOADS["hybrid-512k"]
+    S, P, T, H = wl.S, wl.past_len, wl.T, wl.H
+    Ta = T + 1
+    # indexer over the chunk and for the decode token (row S of the query streams)
+    k_idx = dev_normal((1, Ta, wl.DI), wl, datagen.TID_KIDX, wl.scale_kidx)
+    q_idx = dev_normal((1, S + 1, wl.HI, wl.DI), wl, datagen.TID_QIDX, wl.scale_qidx)
+    w = dev_normal((1, S + 1, wl.HI), wl, datagen.TID_W, wl.scale_w)
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(q_idx[:, :S], k_idx[:, :T].contiguous(), w[:, :S], sc, P)
+    rows = [0, 1, S // 2, S - 1]
+    got = sc[0, rows].cpu().numpy()
+    del sc
+    scd = torch.empty(1, 1, Ta, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(q_idx[:, S:].contiguous(), k_idx, w[:, S:].contiguous(), scd, T)
+    got_d = scd[0, 0].cpu().numpy()
+    del scd, q_idx, k_idx, w
+    _free()
+    kh = datagen.normal_host((1, Ta, wl.DI), "bf16", wl.seed, datagen.TID_KIDX, wl.scale_kidx)
+    for i, s in enumerate(rows + [S]):
+        qh = host_row(wl, datagen.TID_QIDX, wl.scale_qidx, s, wl.HI * wl.DI).reshape(1, 1, wl.HI, wl.DI)
+        wh = host_row(wl, datagen.TID_W, wl.scale_w, s, wl.HI).reshape(1, 1, wl.HI)
+        if s < S:
+            ref = oracle.index_scores(qh, kh[:, :T], wh, P + s)[0, 0]
+            assert_rows_close(got[i], ref, 2e-2, what=f"hybrid chunk scores row {s}")
+        else:
+            ref = oracle.index_scores(qh, kh, wh, T)[0, 0]
+            assert_rows_close(got_d, ref, 2e-2, what="hybrid decode scores")
+    del kh
+
+    # top-k on synthetic chunk-shaped and decode-shaped score rows
+    _topk_full(wl, S, T, P, wl.topk, 1, [0, 7, S - 1], seed_off=50)
+    _topk_full(wl, 1, Ta, T, wl.topk, 2, [0], seed_off=51)
+
+    # DSA attention: chunk (MFMA path) and decode (gather path)
+    k = dev_normal((1, Ta, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)
+    v = dev_normal((1, Ta, H, wl.v), wl, datagen.TID_V, wl.scale_v)
+    q = dev_normal((1, S + 1, H, wl.Dqk), wl, datagen.TID_Q, wl.scale_q)
+    g = dev_normal((1, S + 1, H), wl, datagen.TID_GATE, wl.scale_gate)
+    idx = torch.empty(1, S + 1, wl.topk, dtype=torch.int32, device=DEV)
+    datagen.indices_device(idx.view(S + 1, wl.topk), 0, S + 1, P, seed=wl.seed)
+    out = torch.empty(1, S, H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_prefill(q[:, :S], k[:, :T], v[:, :T], idx[:, :S], g[:, :S], out, P,
+                                wl.nope, wl.rope)
+    od = torch.empty(1, 1, H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_decode(q[:, S:].contiguous(), k, v, idx[:, S:].contiguous(),
+                               g[:, S:].contiguous(), od, wl.nope, wl.rope)
+    got = from_dev(out[0, rows])
+    got_d = from_dev(od[0, 0])
+    del k, v, q, g, idx, out, od
+    _free()
+    idx_h = datagen.indices_host(0, S + 1, S + 1, P, wl.topk, seed=wl.seed)
+    check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, Ta, S_stream=0)
+    check_attn_rows(wl, {S: got_d}, idx_h, [S], 0, Ta, S_stream=0)
+
+
+def test_hybrid_512k_swa_layers():
+    wl = WORKLOADS["hybrid-512k"]
+    S, P, H, W = wl.S, wl.past_len, wl.H, wl.window
+    for j in (1, 2):
+        tid = lambda base: base + datagen.SWA_TID_STRIDE * j
+        off = P - W + 1
+        Tb = P + S - off
+        # buffer row r = absolute position off + r; one extra row for the decode token
+        kb = dev_normal((1, Tb + 1, H, wl.Dqk), wl, tid(datagen.TID_K), wl.scale_k, off * H * wl.Dqk)
+        vb = dev_normal((1, Tb + 1, H, wl.v), wl, tid(datagen.TID_V), wl.scale_v, off * H * wl.v)
+        q = dev_normal((1, S + 1, H, wl.Dqk), wl, tid(datagen.TID_Q), wl.scale_q)
+        g = dev_normal((1, S + 1, H), wl, tid(datagen.TID_GATE), wl.scale_gate)
+        out = torch.empty(1, S, H, wl.v, dtype=torch.bfloat16, device=DEV)
+        dsa.swa_attn(q[:, :S], kb[:, :Tb], vb[:, :Tb], g[:, :S], out, P, off, W, wl.nope, wl.rope)
+        offd = P + S - W + 1
+        od = torch.empty(1, 1, H, wl.v, dtype=torch.bfloat16, device=DEV)
+        dsa.swa_attn(q[:, S:].contiguous(), kb[:, offd - off:].contiguous(),
+                     vb[:, offd - off:].contiguous(), g[:, S:].contiguous(), od, P + S, offd, W,
+                     wl.nope, wl.rope)
+        rows = [0, 1, 511, 2047, S - 1]
+        got = from_dev(out[0, rows])
+        got_d = from_dev(od[0, 0])
+        del kb, vb, q, g, out, od
+        _free()
+        for s, o in list(zip(rows, got)) + [(S, got_d)]:
+            p = P + s
+            pos = list(range(p - W + 1, p + 1))
+            kc = compact_cache(wl, pos, 0, 0, H, wl.Dqk, tid(datagen.TID_K), wl.scale_k)
+            vc = compact_cache(wl, pos, 0, 0, H, wl.v, tid(datagen.TID_V), wl.scale_v)
+            qh = host_row(wl, tid(datagen.TID_Q), wl.scale_q, s, H * wl.Dqk).reshape(1, 1, H, wl.Dqk)
+            gh = host_row(wl, tid(datagen.TID_GATE), wl.scale_gate, s, H).reshape(1, 1, H)
+            ref = oracle.swa_attn(qh, kc, vc, gh, p, p - W + 1, W, wl.nope, wl.rope)[0, 0]
+            assert_rows_close(o.reshape(H, wl.v), ref, 2e-2, what=f"swa layer {j} row {s}")
