@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -304,6 +306,12 @@ def main():
 
     dsa.lib()
     torch.cuda.init()
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = WORKLOADS[args.workload]
     layer = Layer(wl, torch, dsa, datagen)
     per_stage, total_ms, wall = time_layer(layer, args.steps, args.warmup, torch)

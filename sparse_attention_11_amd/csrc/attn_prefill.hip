@@ -71,6 +71,15 @@ __global__ __launch_bounds__(256) void bitmap_global_kernel(const int32_t* __res
   }
 }
 
+// Column of key position `pos` in row `row` of the transposed V tile: the
+// 16-byte chunk index (8 keys) is XORed with bits 4..6 of the row. The 16
+// rows 8 apart that one store instruction writes then fall into distinct
+// LDS banks, while the 16 consecutive rows one operand read covers share the
+// same swizzle and stay conflict-free as well.
+__device__ __forceinline__ int vt_col(int row, int pos) {
+  return ((((pos >> 3) ^ (row >> 4)) & 7) << 3) | (pos & 7);
+}
+
 // ------------------------------------------------------------ flash kernel
 // MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA).
 //
@@ -173,8 +182,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           lo.y = (a2 & 0xFFFFu) | (a3 << 16);
           hi.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
           hi.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
-          *(uint2*)(&Vt[(8 * dg + 2 * mm) * VPAD + pos]) = lo;
-          *(uint2*)(&Vt[(8 * dg + 2 * mm + 1) * VPAD + pos]) = hi;
+          const int r0 = 8 * dg + 2 * mm, r1 = r0 + 1;
+          *(uint2*)(&Vt[r0 * VPAD + vt_col(r0, pos)]) = lo;
+          *(uint2*)(&Vt[r1 * VPAD + vt_col(r1, pos)]) = hi;
         }
       }
     }
@@ -186,21 +196,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   for (int d = 0; d < NDB; ++d) o[d] = zero16();
   const uint32_t* bmrow = bm + qrow * (int64_t)W32;
 
-  if (jlo <= jhi) load_block(jlo);
+  // selection-bitmap words of a block, loaded one block ahead like K and V
+  uint32_t nbits[2] = {0u, 0u};
+  auto load_bits = [&](int jb) {
+    if (MASK == 0) {
+      const int w0 = jb >> 5;
+      nbits[0] = (w0 < W32) ? bmrow[w0] : 0u;
+      nbits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
+    }
+  };
+
+  if (jlo <= jhi) {
+    load_block(jlo);
+    load_bits(jlo);
+  }
   for (int jb = jlo; jb <= jhi; jb += kBN) {
     __syncthreads();  // every wave is done reading the previous block
     store_block();
     __syncthreads();
-
-    uint32_t bits[2] = {0u, 0u};
-    if (MASK == 0) {
-      const int w0 = jb >> 5;
-      bits[0] = (w0 < W32) ? bmrow[w0] : 0u;
-      bits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
-    }
+    const uint32_t bits[2] = {nbits[0], nbits[1]};
 
     // the next block's loads overlap this block's MFMA and softmax work
-    if (jb + kBN <= jhi) load_block(jb + kBN);
+    if (jb + kBN <= jhi) {
+      load_block(jb + kBN);
+      load_bits(jb + kBN);
+    }
 
     // two 32-key halves in sequence: S^T, masked online softmax, O^T += V^T P^T
 #pragma unroll
@@ -257,7 +277,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         const int kcol = 32 * i + 16 * c + 8 * lh;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
-          const bf16x8_t va = as_bf16x8(*(const u32x4_t*)(&Vt[(32 * d + ln) * VPAD + kcol]));
+          const int vr = 32 * d + ln;
+          const bf16x8_t va = as_bf16x8(*(const u32x4_t*)(&Vt[vr * VPAD + vt_col(vr, kcol)]));
           o[d] = mfma32x32x16(va, pb, o[d]);
         }
       }

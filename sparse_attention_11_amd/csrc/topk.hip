@@ -27,9 +27,10 @@
 //     registers, inside a wave via lane swaps, only the widest through LDS)
 //     and the index output, or, for the first stage of a long row, the
 //     unsorted keys of the segment (padded with 0) for a second pass.
-// Long rows with few rows per call are split: segments of 16384 scores are
-// reduced to k candidate keys each, then one workgroup per row selects the
-// final k among the candidates.
+// Rows longer than 16384 are split: segments of 16384 scores are reduced to
+// k candidate keys each, groups of 16384 candidates are reduced again until
+// at most 16384 remain, then one workgroup per row selects and sorts the
+// final k. Every stage keeps its elements in registers.
 #include <type_traits>
 
 #include "common.h"
@@ -42,8 +43,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 2048;
 constexpr int kBins = 2048;
-constexpr int kSegLen = 16384;   // segment length of the first stage (long rows)
-constexpr int kSegMinRows = 512; // rows per call below which long rows are segmented
+constexpr int kSegLen = 16384;  // segment length of the first stage (long rows)
 
 __device__ __forceinline__ uint64_t score_key(float sc, int t) {
   if (sc == -INFINITY) return 0ull;
@@ -119,9 +119,9 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
   }
 }
 
-// SRC 0: fp32 scores, element range [seg*seg_len, min(T, (seg+1)*seg_len)) of
-//        row blockIdx.x / nseg (seg = blockIdx.x % nseg);
-// SRC 1: 64-bit candidate keys, row blockIdx.x holds T keys.
+// Workgroup blockIdx.x handles elements [seg*seg_len, min(T, (seg+1)*seg_len))
+// of row blockIdx.x / nseg (seg = blockIdx.x % nseg), where a row holds
+// SRC 0: T fp32 scores; SRC 1: T 64-bit candidate keys (0 = empty).
 // DST 0: sorted indices to out_idx[row, 0..k); DST 1: unsorted keys of this
 //        segment to out_keys[(row*nseg + seg)*k ...], padded with 0.
 // EPT > 0 keeps the elements in registers (range <= 256*EPT); EPT == 0 streams.
@@ -139,24 +139,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   __shared__ uint32_t s_cnt;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t row;
-  int seg, t0, n;
-  if (SRC == 0) {
-    row = blockIdx.x / nseg;
-    seg = (int)(blockIdx.x % nseg);
-    t0 = seg * seg_len;
-    n = min(T - t0, seg_len);
-  } else {
-    row = blockIdx.x;
-    seg = 0;
-    t0 = 0;
-    n = T;
-  }
+  const int64_t row = blockIdx.x / nseg;
+  const int seg = (int)(blockIdx.x % nseg);
+  const int t0 = seg * seg_len;
+  const int n = min(T - t0, seg_len);
   const float* srow = (const float*)src + row * (int64_t)T;
   const uint64_t* krow = (const uint64_t*)src + row * (int64_t)T;
   auto load_key = [&](int j) -> uint64_t {
     if (SRC == 0) return score_key(srow[t0 + j], t0 + j);
-    return krow[j];
+    return krow[t0 + j];
   };
   // registers hold the high word only for score input (the low word is the
   // position, known from the slot), the whole key for candidate input
@@ -405,43 +396,63 @@ hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t block
   return hipGetLastError();
 }
 
-// rows of length T processed whole (one workgroup per row)
-hipError_t launch_rows(const float* scores, int32_t* idx, int64_t rows, int T, int k, hipStream_t st) {
-  if (T <= kThreads * 16) return launch_e<0, 0, 16>(scores, idx, nullptr, rows, T, k, T, 1, st);
-  if (T <= kThreads * 64) return launch_e<0, 0, 64>(scores, idx, nullptr, rows, T, k, T, 1, st);
-  if (T <= kThreads * 128) return launch_e<0, 0, 128>(scores, idx, nullptr, rows, T, k, T, 1, st);
-  return launch_e<0, 0, 0>(scores, idx, nullptr, rows, T, k, T, 1, st);
-}
+constexpr int kCand = kThreads * 64;  // candidate keys one register-resident workgroup takes
 
-bool segmented(int64_t rows, int T) { return T > 4 * kSegLen && rows < kSegMinRows; }
+// number of candidate-reduction passes and their group counts for a row of T scores
+int stage_groups(int T, int k, int* groups, int max_levels) {
+  const int nseg = (T + kSegLen - 1) / kSegLen;
+  int C = nseg * k, lv = 0;
+  groups[lv++] = nseg;
+  while (C > kCand && lv < max_levels) {
+    const int g = (C + kCand - 1) / kCand;
+    groups[lv++] = g;
+    C = g * k;
+  }
+  return lv;
+}
 
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int S, int T, int topk) {
+  if (T <= kSegLen) return 0;
   const int64_t rows = (int64_t)B * S;
-  if (!segmented(rows, T)) return 0;
-  const int64_t nseg = (T + kSegLen - 1) / kSegLen;
-  return (size_t)(rows * nseg * topk) * sizeof(uint64_t);
+  int groups[8];
+  const int lv = stage_groups(T, topk, groups, 8);
+  // two ping-pong candidate buffers: the first stage output and the largest later one
+  const int64_t a = rows * groups[0] * (int64_t)topk;
+  const int64_t b = lv > 1 ? rows * groups[1] * (int64_t)topk : 0;
+  return (size_t)(a + b) * sizeof(uint64_t);
 }
 
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void* workspace, hipStream_t stream) {
+                       void* workspace, hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
-  if (!segmented(rows, T)) {
-    if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    return launch_rows(scores, indices, rows, T, topk, stream);
+  if (T <= kSegLen) {  // one register-resident workgroup per row
+    if (T <= kThreads * 16) return launch_e<0, 0, 16>(scores, indices, nullptr, rows, T, topk, T, 1, st);
+    return launch_e<0, 0, 64>(scores, indices, nullptr, rows, T, topk, T, 1, st);
   }
+  int groups[8];
+  const int lv = stage_groups(T, topk, groups, 8);
+  uint64_t* bufa = (uint64_t*)workspace;
+  uint64_t* bufb = bufa + rows * groups[0] * (int64_t)topk;
+  if (rows * groups[0] > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   // stage 1: k candidate keys per 16384-score segment
-  const int nseg = (T + kSegLen - 1) / kSegLen;
-  uint64_t* cand = (uint64_t*)workspace;
-  hipError_t e = launch_e<0, 1, kSegLen / kThreads>(scores, nullptr, cand, rows * nseg, T, topk,
-                                                    kSegLen, nseg, stream);
+  hipError_t e = launch_e<0, 1, kSegLen / kThreads>(scores, nullptr, bufa, rows * groups[0], T,
+                                                    topk, kSegLen, groups[0], st);
   if (e != hipSuccess) return e;
-  // stage 2: final selection and sort among nseg * k candidates per row
-  const int C = nseg * topk;
-  if (C <= kThreads * 64)
-    return launch_e<1, 0, 64>(cand, indices, nullptr, rows, C, topk, C, 1, stream);
-  return launch_e<1, 0, 0>(cand, indices, nullptr, rows, C, topk, C, 1, stream);
+  // candidate reductions: groups of kCand candidates -> k each
+  int C = groups[0] * topk;
+  uint64_t *in = bufa, *outb = bufb;
+  for (int l = 1; l < lv; ++l) {
+    e = launch_e<1, 1, 64>(in, nullptr, outb, rows * groups[l], C, topk, kCand, groups[l], st);
+    if (e != hipSuccess) return e;
+    C = groups[l] * topk;
+    uint64_t* tmp = in;
+    in = outb;
+    outb = tmp;
+  }
+  // final selection and sort among at most kCand candidates per row
+  return launch_e<1, 0, 64>(in, indices, nullptr, rows, C, topk, C, 1, st);
 }
 
 }  // namespace dsa
