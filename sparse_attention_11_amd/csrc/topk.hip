@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
                                                         int32_t* __restrict__ out_idx,
                                                         uint64_t* __restrict__ out_keys, int T,
                                                         int k, int seg_len, int nseg) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
   __shared__ uint64_t sel[kMaxK > 256 * E ? kMaxK : 256 * E];
   __shared__ uint32_t s_red[kWaves];
   __shared__ uint32_t s_col[(EPT > 0 ? EPT : 1) * kWaves];
@@ -159,12 +159,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     return kreg[j] ? (((uint64_t)kreg[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t)) : 0ull;
   };
   uint32_t valid = 0;
-  if (EPT > 0) {
+  if (EPT > 0 && SRC == 0) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + j * kThreads;
+      const float sc = e < n ? srow[t0 + e] : -INFINITY;
+      const uint32_t hi = (sc == -INFINITY) ? 0u : orderable_key(sc);
+      kreg[j] = (KT)hi;
+      valid += hi != 0u;
+    }
+  } else if (EPT > 0) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = tid + j * kThreads;
       const uint64_t key = e < n ? load_key(e) : 0ull;
-      kreg[j] = (SRC == 0) ? (KT)(key >> 32) : (KT)key;
+      kreg[j] = (KT)key;
       valid += key != 0ull;
     }
   } else {
@@ -186,8 +195,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
+        // non-matching keys count into a per-lane spare bin instead of branching
         const uint32_t hi = (uint32_t)kreg[j];
-        if (hi != 0u && (hi & mask) == prefix) atomicAdd(&hist[(hi >> shift) & dmask], 1u);
+        const bool m = hi != 0u && (hi & mask) == prefix;
+        atomicAdd(&hist[m ? ((hi >> shift) & dmask) : (uint32_t)(kBins + lane)], 1u);
       }
       __syncthreads();
       pick_digit(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
@@ -236,6 +247,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     }
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // which of this thread's keys are taken (bit j), then an ordered compaction
+    uint64_t takebits = 0;
+    uint32_t ntake = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const uint32_t hi = (uint32_t)kreg[j];
@@ -248,10 +262,27 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
         const uint32_t rank = s_col[j * kWaves + wave] + (uint32_t)__popcll(b & lt_mask);
         take = hi > prefix || (tie && rank < (uint32_t)krem);
       }
-      if (take) {
+      takebits |= (uint64_t)take << j;
+      ntake += take;
+    }
+    uint32_t x = ntake;  // inclusive prefix over the block
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_red[wave] = x;
+    __syncthreads();
+    uint32_t base = x - ntake;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (w < wave) base += s_red[w];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      if ((takebits >> j) & 1ull) {
         const uint32_t t = (uint32_t)(t0 + tid + j * kThreads);
-        const uint32_t pos = atomicAdd(&s_cnt, 1u);
-        if (pos < (uint32_t)kMaxK) sel[pos] = ((uint64_t)hi << 32) | (0xFFFFFFFFu - t);
+        if (base < (uint32_t)kMaxK) sel[base] = ((uint64_t)kreg[j] << 32) | (0xFFFFFFFFu - t);
+        ++base;
       }
     }
     __syncthreads();
