@@ -67,7 +67,8 @@ int check_ws(const char* fn, void* ws, size_t have, size_t need) {
 }
 
 size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, int dtype) {
-  if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return dsa::bitmap_bytes(B, S, T);
+  if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim))
+    return dsa::prefill_mfma_workspace_bytes(B, S, T, H, v_dim);
   return dsa::gather_workspace_bytes(B * S, H, v_dim, topk);
 }
 

@@ -80,6 +80,44 @@ __device__ __forceinline__ int vt_col(int row, int pos) {
   return ((((pos >> 3) ^ (row >> 4)) & 7) << 3) | (pos & 7);
 }
 
+// Buffer-row range [jlo, jhi] (64-aligned start) of the keys a 128-query tile
+// can see: the causal range for the bitmap mask, the window range otherwise.
+__host__ __device__ __forceinline__ void tile_range(int qt, int S, int P, int Tbuf, int kv_offset,
+                                                    int window, int* jlo, int* jhi) {
+  const int q0 = qt * kBQ;
+  const int pmax = P + min(q0 + kBQ - 1, S - 1);
+  int tlo = 0;
+  if (window > 0) tlo = max(kv_offset, P + q0 - window + 1);
+  *jlo = ((tlo - kv_offset) / kBN) * kBN;
+  *jhi = min(pmax - kv_offset, Tbuf - 1);
+}
+
+__host__ __device__ __forceinline__ int tile_blocks(int qt, int S, int P, int Tbuf, int kv_offset,
+                                                     int window) {
+  int jlo, jhi;
+  tile_range(qt, S, P, Tbuf, kv_offset, window, &jlo, &jhi);
+  return jhi >= jlo ? (jhi - jlo) / kBN + 1 : 0;
+}
+
+// Work item -> (query tile, split, number of splits). Items run from the
+// longest tile down; a tile of nb key blocks is cut into ceil(nb / M) splits.
+__device__ __forceinline__ bool item_tile(int item, int nqt, int M, int S, int P, int Tbuf,
+                                          int kv_offset, int window, int* qt, int* split,
+                                          int* nsplit) {
+  for (int t = nqt - 1; t >= 0; --t) {
+    const int nb = tile_blocks(t, S, P, Tbuf, kv_offset, window);
+    const int c = nb > M ? (nb + M - 1) / M : 1;
+    if (item < c) {
+      *qt = t;
+      *split = item;
+      *nsplit = c;
+      return true;
+    }
+    item -= c;
+  }
+  return false;
+}
+
 // ------------------------------------------------------------ flash kernel
 // MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA).
 //
@@ -92,8 +130,9 @@ template <int DQK, int DV, int MASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
-    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int S, int Tbuf, int P,
-    int kv_offset, int H, int W32, int window, float scale_log2, int gate_dim) {
+    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ part,
+    int S, int Tbuf, int P, int kv_offset, int H, int W32, int window, float scale_log2,
+    int gate_dim, int nqt, int M) {
   constexpr int KSQ = DQK / 16;
   constexpr int NDB = DV / 32;
   constexpr int KPAD = DQK + 8;           // bf16 elements per K row in LDS
@@ -107,7 +146,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VPAD];
 
-  const int qt = gridDim.x - 1 - blockIdx.x;  // long (late) query tiles first
+  int qt, split, nsplit;
+  if (!item_tile(blockIdx.x, nqt, M, S, P, Tbuf, kv_offset, window, &qt, &split, &nsplit)) return;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
@@ -125,12 +165,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     for (int ks = 0; ks < KSQ; ++ks) bq[ks] = as_bf16x8(load16(qp + 16 * ks));
   }
 
-  // key range of the tile, in buffer rows (row j = absolute position kv_offset + j)
-  const int pmax = P + min(q0 + kBQ - 1, S - 1);
-  int tlo = 0;
-  if (MASK == 1) tlo = max(kv_offset, P + q0 - window + 1);
-  const int jlo = ((tlo - kv_offset) / kBN) * kBN;
-  const int jhi = min(pmax - kv_offset, Tbuf - 1);
+  // key range of this split of the tile, in buffer rows (row j = position kv_offset + j)
+  int tjlo, tjhi;
+  tile_range(qt, S, P, Tbuf, kv_offset, MASK == 1 ? window : 0, &tjlo, &tjhi);
+  // (64-bit: M is INT_MAX when tiles are not split)
+  const int jlo = (int)((int64_t)tjlo + (int64_t)split * M * kBN);
+  const int jhi = (int)std::min<int64_t>(tjhi, (int64_t)jlo + (int64_t)M * kBN - 1);
   const int64_t kvrow0 = (int64_t)b * Tbuf;
 
   // ---- register prefetch of one key block
@@ -287,6 +327,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   // ---- normalise, gate, store
   const float ltot = l + shfl_xor_f(l, 32);
+  if (nsplit > 1) {  // partial state (unnormalised O, max, sum) for the merge kernel
+    float* pp = part + ((((int64_t)b * H + h) * gridDim.x + blockIdx.x) * kBQ + 32 * wave + ln) *
+                           (DV + 4);
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(pp + 32 * d + 8 * g + 4 * lh) =
+            make_float4(o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]);
+    if (lh == 0) {
+      pp[DV] = m;
+      pp[DV + 1] = ltot;
+    }
+    return;
+  }
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if (!svalid) return;
   float g1 = 1.0f;
@@ -312,18 +367,110 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
 }
 
+// Combines the splits of each split tile: out = sum_s 2^(c(m_s - M)) O_s /
+// sum_s 2^(c(m_s - M)) l_s, then the gate. One workgroup per (tile, head, b).
+template <int DV>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part,
+                                                           const uint16_t* __restrict__ gate,
+                                                           uint16_t* __restrict__ out, int S,
+                                                           int P, int Tbuf, int H, int items,
+                                                           int nqt, int M, float scale_log2,
+                                                           int gate_dim) {
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // first item of this tile and its number of splits
+  int base = 0, c = 1;
+  for (int t = nqt - 1; t >= qt; --t) {
+    const int nb = tile_blocks(t, S, P, Tbuf, 0, 0);
+    c = nb > M ? (nb + M - 1) / M : 1;
+    if (t > qt) base += c;
+  }
+  if (c <= 1) return;
+  const float* pt = part + (((int64_t)b * H + h) * items + base) * kBQ * (DV + 4);
+  const int64_t split_stride = (int64_t)kBQ * (DV + 4);
+  for (int i = threadIdx.x; i < kBQ * (DV / 4); i += blockDim.x) {
+    const int qi = i / (DV / 4), dv0 = 4 * (i % (DV / 4));
+    const int s = qt * kBQ + qi;
+    if (s >= S) continue;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < c; ++sp) mx = fmaxf(mx, pt[sp * split_stride + qi * (DV + 4) + DV]);
+    float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < c; ++sp) {
+      const float* q = pt + sp * split_stride + qi * (DV + 4);
+      const float w = (q[DV] == -INFINITY) ? 0.0f : exp2f((q[DV] - mx) * scale_log2);
+      L += w * q[DV + 1];
+      const float4 o4 = *(const float4*)(q + dv0);
+      acc[0] += w * o4.x;
+      acc[1] += w * o4.y;
+      acc[2] += w * o4.z;
+      acc[3] += w * o4.w;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int64_t qrow = (int64_t)b * S + s;
+    float g1 = 1.0f;
+    if (gate_dim == 1) g1 = sigmoid_f32(bf16_to_f32(gate[qrow * H + h]));
+    float r4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float gg = g1;
+      if (gate_dim > 1) gg = sigmoid_f32(bf16_to_f32(gate[(qrow * H + h) * DV + dv0 + r]));
+      r4[r] = acc[r] * inv * gg;
+    }
+    uint2 pkd;
+    pkd.x = pack_bf16x2(r4[0], r4[1]);
+    pkd.y = pack_bf16x2(r4[2], r4[3]);
+    *(uint2*)(out + (qrow * H + h) * DV + dv0) = pkd;
+  }
+}
+
+struct SplitPlan {
+  int nqt, M, items;
+};
+
+// Splits long query tiles when the plain grid is too small to fill the GPU:
+// at most M key blocks per work item, about 1024 items in total. The bound
+// uses past_len = T - S (the longest tiles a call with this T can have).
+// Only selection-mask (DSA) calls split: there kv_offset = 0 and T >= P + S,
+// so T - S bounds past_len and the bound plan covers every actual call.
+// Window (SWA) tiles are short by construction and never split.
+SplitPlan make_split_plan(int B, int S, int T, int P, int H, int kv_offset, int window) {
+  SplitPlan pl;
+  pl.nqt = (S + kBQ - 1) / kBQ;
+  pl.M = 0x7FFFFFFF;  // no split
+  if (window <= 0 && kv_offset == 0 && (int64_t)B * H * pl.nqt < 1024) {
+    int64_t total_bound = 0;
+    for (int t = 0; t < pl.nqt; ++t) total_bound += tile_blocks(t, S, T - S, T, 0, 0);
+    total_bound *= (int64_t)B * H;
+    const int64_t m = (total_bound + 1023) / 1024;
+    pl.M = (int)std::max<int64_t>(16, m);
+  }
+  pl.items = 0;
+  for (int t = 0; t < pl.nqt; ++t) {
+    const int nb = tile_blocks(t, S, P, T, kv_offset, window);
+    pl.items += nb > pl.M ? (nb + pl.M - 1) / pl.M : 1;
+  }
+  return pl;
+}
+
 template <int DQK, int DV>
 hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint32_t* bm, const uint16_t* gate, uint16_t* out, int B, int S,
                        int Tbuf, int P, int kv_offset, int H, int W32, int window,
-                       float scale_log2, int gate_dim, hipStream_t st) {
-  const dim3 grid((S + kBQ - 1) / kBQ, H, B);
+                       float scale_log2, int gate_dim, float* part, hipStream_t st) {
+  const SplitPlan pl = make_split_plan(B, S, Tbuf, P, H, kv_offset, window);
+  if (pl.items != pl.nqt && part == nullptr) return hipErrorInvalidValue;  // no partial buffer
+  const dim3 grid(pl.items, H, B);
   if (window > 0)
     hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, bm, gate,
-                       out, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim);
+                       out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
+                       pl.nqt, pl.M);
   else
     hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, bm, gate,
-                       out, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim);
+                       out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
+                       pl.nqt, pl.M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.items == pl.nqt) return e;
+  hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt, H, B), dim3(256), 0, st, part, gate,
+                     out, S, P, Tbuf, H, pl.items, pl.nqt, pl.M, scale_log2, gate_dim);
   return hipGetLastError();
 }
 
@@ -341,12 +488,25 @@ size_t bitmap_bytes(int B, int S, int T) {
   return (size_t)B * (size_t)S * (size_t)((T + 31) / 32) * sizeof(uint32_t);
 }
 
+size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv) {
+  // bitmap, 256-byte aligned, then partial states if long tiles get split
+  const size_t bmb = (bitmap_bytes(B, S, T) + 255) / 256 * 256;
+  const SplitPlan pl = make_split_plan(B, S, T, T - S, H, 0, 0);
+  if (pl.items == pl.nqt) return bmb;
+  return bmb + (size_t)B * H * pl.items * kBQ * (Dv + 4) * sizeof(float);
+}
+
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
                                int kv_offset, int H, int Dqk, int Dv, int topk, int window,
                                float sm_scale, int gate_dim, void* workspace, hipStream_t st) {
   const int W32 = (T + 31) / 32;
   uint32_t* bm = (uint32_t*)workspace;
+  // partial states follow the (256-byte aligned) bitmap; only DSA calls have them
+  float* part = nullptr;
+  if (window <= 0 && prefill_mfma_workspace_bytes(B, S, T, H, Dv) >
+                         (bitmap_bytes(B, S, T) + 255) / 256 * 256)
+    part = (float*)((char*)workspace + (bitmap_bytes(B, S, T) + 255) / 256 * 256);
   const int64_t rows = (int64_t)B * S;
   if (window <= 0) {
     if (W32 <= kBitmapLdsMaxWords) {
@@ -369,7 +529,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
 #define DSA_PREFILL_CASE(A, C)                                                                    \
   if (Dqk == A && Dv == C)                                                                        \
     return launch_dims<A, C>(qq, kk, vv, bm, gg, oo, B, S, T, past_len, kv_offset, H, W32, window, \
-                             sl2, gate_dim, st);
+                             sl2, gate_dim, part, st);
   DSA_PREFILL_CASE(64, 64)
   DSA_PREFILL_CASE(128, 64)
   DSA_PREFILL_CASE(128, 128)

@@ -20,6 +20,7 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
 // Selection bitmap + MFMA flash attention with a bitmap or window mask
 // (attn_prefill.hip). Requires bf16, Dqk % 16 == 0, Dv % 32 == 0.
 size_t bitmap_bytes(int B, int S, int T);
+size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv);
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
                                int kv_offset, int H, int Dqk, int Dv, int topk, int window,

@@ -102,8 +102,11 @@ def test_prefill_without_gate_is_valid_until_workspace():
 
 def test_workspace_sizes():
     L = dsa.lib()
-    # bf16, many queries: one bit per (query, key) rounded up to 32-bit words
-    assert L.dsa_sparse_attn_prefill_workspace_size(1, 4096, 4096, 20, 128, 128, 512, 1) == 4096 * 128 * 4
+    # bf16, many queries: one bit per (query, key) in 32-bit words, plus partial softmax
+    # states when the grid is small enough that long query tiles are split
+    bitmap = 4096 * 128 * 4
+    assert L.dsa_sparse_attn_prefill_workspace_size(1, 4096, 4096, 20, 128, 128, 512, 1) > bitmap
+    assert L.dsa_sparse_attn_prefill_workspace_size(1, 32768, 32768, 128, 192, 128, 2048, 1) == 32768 * 1024 * 4
     assert L.dsa_sparse_attn_decode_workspace_size(8, 128, 128, 2048) > 0
     assert L.dsa_topk_workspace_size(1, 1, 100, 10) == 0
     assert L.swa_attn_workspace_size(1, 4096, 32, 192, 128, 512, 1) == 0
