@@ -27,13 +27,13 @@ namespace dsa {
 namespace {
 
 constexpr int kG = 4;          // tokens in flight per step
+constexpr int kMaxSplit = 256;  // splits of one row's selection (merge weights live in LDS)
 
 template <int DT>
 struct Elem;
 template <>
 struct Elem<0> {  // fp32
   static constexpr int kPer16 = 4;
-  static constexpr int kMaxChunks = 8;  // 16-byte chunks per lane per row (head dim <= 256)
   __device__ static void unpack(const u32x4_t& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
@@ -42,7 +42,6 @@ struct Elem<0> {  // fp32
 template <>
 struct Elem<1> {  // bf16
   static constexpr int kPer16 = 8;
-  static constexpr int kMaxChunks = 4;
   __device__ static void unpack(const u32x4_t& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -53,7 +52,9 @@ struct Elem<1> {  // bf16
 };
 
 // WIN 0: indices list; WIN 1: window p, p-1, ..., p-window+1.
-template <int DT, int WIN>
+// KC / VC: 16-byte chunks per lane of a head's K / V row (chunk c of a row
+// belongs to lane c % 8 of the head's 8 lanes).
+template <int DT, int WIN, int KC, int VC>
 __global__ __launch_bounds__(256) void gather_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
     const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
@@ -62,7 +63,6 @@ __global__ __launch_bounds__(256) void gather_kernel(
   using E = Elem<DT>;
   constexpr int EP = E::kPer16;
   constexpr int esz = DT ? 2 : 4;
-  constexpr int kMaxChunks = E::kMaxChunks;
   const int split = (int)(blockIdx.x % (unsigned)nsplit);
   const int64_t row = blockIdx.x / (unsigned)nsplit;
   const int b = (int)(row / S), s = (int)(row % S);
@@ -78,9 +78,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
   const char* kb = (const char*)kv;
   const char* vb = (const char*)vv;
 
-  float qf[kMaxChunks][EP];
+  float qf[KC][EP];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < KC; ++i) {
     const int c = sub + 8 * i;
 #pragma unroll
     for (int e = 0; e < EP; ++e) qf[i][e] = 0.0f;
@@ -93,9 +93,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 
   float m = -INFINITY, l = 0.0f;
-  float o[kMaxChunks][EP];
+  float o[VC][EP];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i)
+  for (int i = 0; i < VC; ++i)
 #pragma unroll
     for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
 
@@ -104,37 +104,57 @@ __global__ __launch_bounds__(256) void gather_kernel(
   const int32_t* irow = idx + row * (int64_t)nent;
   const int64_t kvrow0 = (int64_t)b * Tbuf;
 
+  auto pos_of = [&](int ent) -> int {
+    if (WIN) return p - ent;
+    return (ent < e1) ? irow[ent] : -1;
+  };
+  int tn[kG];  // positions of the next group (index loads run one group ahead)
+#pragma unroll
+  for (int g = 0; g < kG; ++g) tn[g] = pos_of(e0 + g);
+
   for (int base = e0; base < e1; base += kG) {
     int jrow[kG];
     bool ok[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
       const int ent = base + g;
-      int t;
-      if (WIN)
-        t = p - ent;
-      else
-        t = (ent < e1) ? irow[ent] : -1;
+      const int t = tn[g];
       const int j = t - kv_offset;
       ok[g] = (ent < e1) && t >= 0 && t <= p && j >= 0 && j < Tbuf;
       if (WIN) ok[g] = ok[g] && ent < window;
       jrow[g] = ok[g] ? j : 0;
     }
+    // all K and V chunks of the group in flight at once
+    u32x4_t kr[kG][KC], vr[kG][VC];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const char* krow = kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
+      const char* vrow = vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const int c = sub + 8 * i;
+        kr[g][i] = (c < nck) ? load16(krow + (int64_t)c * EP * esz) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < VC; ++i) {
+        const int c = sub + 8 * i;
+        vr[g][i] = (c < ncv) ? load16(vrow + (int64_t)c * EP * esz) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kG; ++g) tn[g] = pos_of(base + kG + g);
+
     // logits
     float x[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      const char* kr = kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
       float dot = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kMaxChunks; ++i) {
-        const int c = sub + 8 * i;
-        if (c < nck) {
-          float kf[EP];
-          E::unpack(load16(kr + (int64_t)c * EP * esz), kf);
+      for (int i = 0; i < KC; ++i) {
+        float kf[EP];
+        E::unpack(kr[g][i], kf);
 #pragma unroll
-          for (int e = 0; e < EP; ++e) dot = fmaf(qf[i][e], kf[e], dot);
-        }
+        for (int e = 0; e < EP; ++e) dot = fmaf(qf[i][e], kf[e], dot);
       }
       dot += shfl_xor_f(dot, 1);
       dot += shfl_xor_f(dot, 2);
@@ -151,27 +171,23 @@ __global__ __launch_bounds__(256) void gather_kernel(
     float ps = 0.0f;
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      pg[g] = exp2f(x[g] - muse);
+      pg[g] = exp2f(x[g] - muse);  // 0 for a skipped slot (x = -inf)
       ps += pg[g];
     }
     l = l * alpha + ps;
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i)
+    for (int i = 0; i < VC; ++i)
 #pragma unroll
       for (int e = 0; e < EP; ++e) o[i][e] *= alpha;
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      if (!ok[g]) continue;
-      const char* vr = vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
+      if (!ok[g]) continue;  // never multiply a skipped row (it may hold anything)
 #pragma unroll
-      for (int i = 0; i < kMaxChunks; ++i) {
-        const int c = sub + 8 * i;
-        if (c < ncv) {
-          float vf[EP];
-          E::unpack(load16(vr + (int64_t)c * EP * esz), vf);
+      for (int i = 0; i < VC; ++i) {
+        float vf[EP];
+        E::unpack(vr[g][i], vf);
 #pragma unroll
-          for (int e = 0; e < EP; ++e) o[i][e] = fmaf(pg[g], vf[e], o[i][e]);
-        }
+        for (int e = 0; e < EP; ++e) o[i][e] = fmaf(pg[g], vf[e], o[i][e]);
       }
     }
   }
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
   // partial state: [row][split][h][DV + 2] = o[0..DV), m, l
   float* pr = part + ((row * nsplit + split) * H + h) * (int64_t)(DV + 2);
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < VC; ++i) {
     const int c = sub + 8 * i;
     if (c < ncv) {
 #pragma unroll
@@ -193,34 +209,44 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 }
 
+// One wave per (row, head): split weights w_s = 2^(m_s - M) are computed once
+// into LDS, then every lane accumulates its dv columns over the splits.
 template <int DT>
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
                                                     const void* __restrict__ gate,
-                                                    void* __restrict__ out, int H, int DV,
-                                                    int nsplit, int gate_dim) {
-  const int64_t rh = blockIdx.x;  // row * H + h
+                                                    void* __restrict__ out, int64_t nrh, int H,
+                                                    int DV, int nsplit, int gate_dim) {
+  __shared__ float wsh[4][kMaxSplit];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;  // row * H + h
+  if (rh >= nrh) return;
   const int64_t row = rh / H;
   const int h = (int)(rh % H);
   const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 2);
   const int64_t sstride = (int64_t)H * (DV + 2);
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pbase[sp * sstride + DV]);
+  for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, pbase[sp * sstride + DV]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   const float Muse = (M == -INFINITY) ? 0.0f : M;
   float L = 0.0f;
-  for (int sp = 0; sp < nsplit; ++sp) {
+  for (int sp = lane; sp < nsplit; sp += 64) {
     const float* ps = pbase + sp * sstride;
-    L += ps[DV + 1] * exp2f(ps[DV] - Muse);
+    const float w = exp2f(ps[DV] - Muse);
+    wsh[wave][sp] = w;
+    L += w * ps[DV + 1];
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float g1 = 1.0f;
   if (gate_dim == 1)
     g1 = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
-  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
+  for (int d = lane; d < DV; d += 64) {
     float acc = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* ps = pbase + sp * sstride;
-      acc = fmaf(ps[d], exp2f(ps[DV] - Muse), acc);
-    }
+    for (int sp = 0; sp < nsplit; ++sp) acc = fmaf(pbase[sp * sstride + d], wsh[wave][sp], acc);
     float gg = g1;
     if (gate_dim > 1) {
       const int64_t gi = rh * DV + d;
@@ -243,7 +269,7 @@ Plan make_plan(int64_t rows, int H, int nent) {
   const int64_t base = rows * hgroups;
   int nsplit = (int)std::max<int64_t>(1, (2048 + base - 1) / base);
   const int max_split = std::max(1, (nent + 15) / 16);  // at least 16 entries per split
-  nsplit = std::min(nsplit, max_split);
+  nsplit = std::min(std::min(nsplit, max_split), kMaxSplit);
   int per = (nent + nsplit - 1) / nsplit;
   per = (per + kG - 1) / kG * kG;
   nsplit = (nent + per - 1) / per;
@@ -269,31 +295,59 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const int3
   const dim3 grid((unsigned)(rows * pl.nsplit), (H + 31) / 32);
   if (rows * pl.nsplit > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float sl2 = sm_scale * DSA_LOG2E;
-#define DSA_GATHER(DT, WIN)                                                                      \
-  hipLaunchKernelGGL((gather_kernel<DT, WIN>), grid, dim3(256), 0, st, q, k, v, indices, part, S, \
-                     T, past_len, kv_offset, H, Dqk, Dv, nent, pl.per_split, pl.nsplit, window,  \
-                     sl2)
-  if (dtype == 1) {
-    if (window > 0)
-      DSA_GATHER(1, 1);
-    else
-      DSA_GATHER(1, 0);
-  } else {
-    if (window > 0)
-      DSA_GATHER(0, 1);
-    else
-      DSA_GATHER(0, 0);
+#define DSA_GATHER(DT, WIN, KC, VC)                                                            \
+  hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC>), grid, dim3(256), 0, st, q, k, v, indices,  \
+                     part, S, T, past_len, kv_offset, H, Dqk, Dv, nent, pl.per_split, pl.nsplit,  \
+                     window, sl2)
+#define DSA_GATHER_VC(DT, WIN, KC)            \
+  switch (vc) {                               \
+    case 1: DSA_GATHER(DT, WIN, KC, 1); break; \
+    case 2: DSA_GATHER(DT, WIN, KC, 2); break; \
+    case 3: DSA_GATHER(DT, WIN, KC, 3); break; \
+    default: DSA_GATHER(DT, WIN, KC, 4); break; \
   }
+#define DSA_GATHER_KC(DT, WIN)                  \
+  switch (kc) {                                 \
+    case 1: DSA_GATHER_VC(DT, WIN, 1); break;   \
+    case 2: DSA_GATHER_VC(DT, WIN, 2); break;   \
+    case 3: DSA_GATHER_VC(DT, WIN, 3); break;   \
+    default: DSA_GATHER_VC(DT, WIN, 4); break;  \
+  }
+  // chunks per lane: bf16 rows carry 8 values per 16 bytes, fp32 rows 4
+  const int per = dtype == 1 ? 64 : 32;
+  const int kc = (Dqk + per - 1) / per, vc = (Dv + per - 1) / per;
+  if (dtype == 1) {
+    if (window > 0) {
+      DSA_GATHER_KC(1, 1)
+    } else {
+      DSA_GATHER_KC(1, 0)
+    }
+  } else if (kc > 4 || vc > 4) {  // fp32 head dims above 128
+    if (window > 0) {
+      DSA_GATHER(0, 1, 8, 8);
+    } else {
+      DSA_GATHER(0, 0, 8, 8);
+    }
+  } else {
+    if (window > 0) {
+      DSA_GATHER_KC(0, 1)
+    } else {
+      DSA_GATHER_KC(0, 0)
+    }
+  }
+#undef DSA_GATHER_KC
+#undef DSA_GATHER_VC
 #undef DSA_GATHER
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nrh = rows * H;
+  const unsigned mg = (unsigned)((nrh + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)nrh), dim3(128), 0, st, part, gate, out, H,
-                       Dv, pl.nsplit, gate_dim);
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(mg), dim3(256), 0, st, part, gate, out, nrh, H, Dv,
+                       pl.nsplit, gate_dim);
   else
-    hipLaunchKernelGGL(merge_kernel<0>, dim3((unsigned)nrh), dim3(128), 0, st, part, gate, out, H,
-                       Dv, pl.nsplit, gate_dim);
+    hipLaunchKernelGGL(merge_kernel<0>, dim3(mg), dim3(256), 0, st, part, gate, out, nrh, H, Dv,
+                       pl.nsplit, gate_dim);
   return hipGetLastError();
 }
 

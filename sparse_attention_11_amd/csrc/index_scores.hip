@@ -19,7 +19,7 @@
 //                    pair costs the same, pairs dealt to XCDs round-robin.
 //  idx_fill_kernel   -inf for the key tiles above the diagonal.
 //  idx_rows_kernel   few-query calls (decode): the index heads become the
-//                    MFMA M axis; a wave streams 64 keys of k per step.
+//                    MFMA M axis; a wave streams 256 keys of k in blocks of 32.
 //  idx_f32_kernel    fp32 inputs: plain fp32 loops (parity-size workloads).
 #include "common.h"
 #include "kernels.h"
@@ -153,6 +153,10 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(float* __restrict__ score
 }
 
 // Few queries per call: MFMA M = index heads (NHB blocks of 32), N = 32 keys.
+// A wave streams kRowsKeys keys in blocks of 32; the query operand is loaded
+// once per wave and the next block's keys are loaded during the current
+// block's MFMAs.
+constexpr int kRowsKeys = 256;  // keys per wave
 template <int DI, int NHB, int MODE>
 __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
@@ -160,16 +164,18 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
                                                        float* __restrict__ scores, int S, int T,
                                                        int P, int HI, float scale) {
   constexpr int KS = DI / 16;
+  constexpr int NB = kRowsKeys / 32;
   const int64_t row = blockIdx.y;
   const int b = (int)(row / S), s = (int)(row % S);
   const int p = P + s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 31, lh = lane >> 5;
-  const int tbase = blockIdx.x * 256 + wave * 64;
+  const int tbase = (blockIdx.x * 4 + wave) * kRowsKeys;
   float* orow = scores + row * T;
+  if (tbase >= T) return;
 
-  if (tbase > p) {  // whole wave above the diagonal
-    for (int kb = 0; kb < 2; ++kb) {
+  if (tbase > p) {  // the whole wave is above the diagonal
+    for (int kb = 0; kb < NB; ++kb) {
       const int t = tbase + 32 * kb + ln;
       if (lh == 0 && t < T) orow[t] = -INFINITY;
     }
@@ -195,34 +201,45 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
     }
   }
 
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  auto load_keys = [&](int kb, bf16x8_t* bk) {
     const int t = tbase + 32 * kb + ln;
     const bool tv = t < T && t <= p;
     const uint16_t* kp = k + ((int64_t)b * T + (tv ? t : 0)) * DI + 8 * lh;
-    bf16x8_t bk[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t v = load16(kp + 16 * ks);
       if (!tv) v = u32x4_t{0, 0, 0, 0};
       bk[ks] = as_bf16x8(v);
     }
+  };
+  bf16x8_t bk[KS], bn[KS];
+  load_keys(0, bk);
+  for (int kb = 0; kb < NB; ++kb) {
+    const int t = tbase + 32 * kb + ln;
+    const bool more = kb + 1 < NB && tbase + 32 * (kb + 1) <= p && tbase + 32 * (kb + 1) < T;
+    if (more) load_keys(kb + 1, bn);
     float part = 0.0f;
+    if (tbase + 32 * kb <= p) {
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      f32x16_t acc = zero16();
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x16_t acc = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[hb][ks], bk[ks], acc);
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[hb][ks], bk[ks], acc);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = acc[e];
-        if (MODE == 0) x = fmaxf(x, 0.0f);
-        part = fmaf(wv[hb][e], x, part);
+        for (int e = 0; e < 16; ++e) {
+          float x = acc[e];
+          if (MODE == 0) x = fmaxf(x, 0.0f);
+          part = fmaf(wv[hb][e], x, part);
+        }
       }
+      part += shfl_xor_f(part, 32);
+      if (MODE == 2) part = fmaxf(part, 0.0f);
     }
-    part += shfl_xor_f(part, 32);
-    if (MODE == 2) part = fmaxf(part, 0.0f);
     if (lh == 0 && t < T) orow[t] = (t <= p) ? part : -INFINITY;
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bk[ks] = bn[ks];
+    }
   }
 }
 
@@ -287,8 +304,8 @@ hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w,
 template <int DI, int NHB, int MODE>
 hipError_t launch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
                        int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
-  hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE>), dim3((T + 255) / 256, B * S), dim3(256), 0,
-                     st, q, k, w, scores, S, T, P, HI, scale);
+  hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE>), dim3((T + 4 * kRowsKeys - 1) / (4 * kRowsKeys), B * S),
+                     dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale);
   return hipGetLastError();
 }
 

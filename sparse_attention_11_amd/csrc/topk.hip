@@ -324,13 +324,33 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     __syncthreads();
     if (kk > 0) {
       const uint64_t thr = prefix;
-      if (EPT > 0) {
+      if (EPT > 0) {  // ordered compaction: block prefix scan of per-thread counts
+        uint64_t takebits = 0;
+        uint32_t ntake = 0;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
           const uint64_t key = reg_key(j);
-          if (key != 0ull && key >= thr) {
-            const uint32_t pos = atomicAdd(&s_cnt, 1u);
-            if (pos < (uint32_t)kMaxK) sel[pos] = key;
+          const bool take = key != 0ull && key >= thr;
+          takebits |= (uint64_t)take << j;
+          ntake += take;
+        }
+        uint32_t x = ntake;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        if (lane == 63) s_red[wave] = x;
+        __syncthreads();
+        uint32_t base = x - ntake;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (w < wave) base += s_red[w];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          if ((takebits >> j) & 1ull) {
+            if (base < (uint32_t)kMaxK) sel[base] = reg_key(j);
+            ++base;
           }
         }
       } else {
