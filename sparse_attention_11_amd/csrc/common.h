@@ -47,6 +47,14 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// max(x, 0) as a single v_max_f32 (fmaxf also emits a NaN-quieting max, and
+// the compiler folds med3(x, 0, inf) back into fmaxf). Pure VALU op, no memory.
+__device__ __forceinline__ float relu_f32(float x) {
+  float r;
+  asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // sigmoid in fp32 as 1 / (1 + e^-x): exactly 0 at -inf, 1 at +inf, 1/2 at 0.
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + __expf(-x)); }
 

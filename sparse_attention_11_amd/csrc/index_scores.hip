@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void idx_tile_kernel(const uint16_t* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x = acc[e];
-        if (MODE == 0) x = fmaxf(x, 0.0f);
+        if (MODE == 0) x = relu_f32(x);
         sc[i][e] = fmaf(wh, x, sc[i][e]);
       }
     }
