@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kBN = 64;   // keys per step
+constexpr float kLazyLog2 = 8.0f;  // largest exponent of an unnormalised weight p
 
 // --------------------------------------------------------- selection bitmap
 // bitmap[(b*S + s) * W32 + w] bit j  <=>  key 32w + j is selected and t <= p.
@@ -173,64 +174,67 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int jhi = (int)std::min<int64_t>(tjhi, (int64_t)jlo + (int64_t)M * kBN - 1);
   const int64_t kvrow0 = (int64_t)b * Tbuf;
 
-  // ---- register prefetch of one key block
+  // ---- register prefetch of one key block. A K row of KCH 16-byte chunks is
+  // covered by one or two power-of-two parts (24 = 16 + 8), so that a thread
+  // keeps one byte offset per part and successive loads of a part add a
+  // fixed row step. Loads go through a buffer resource that ends at the
+  // last row of this batch's buffer: rows past it read as zeros.
+  constexpr int KP1 = (KCH == 24) ? 16 : KCH;  // chunks per row, part 1
+  constexpr int KP2 = KCH - KP1;               // part 2 (0 or 8)
+  constexpr int R1 = 256 / KP1, N1 = kBN / R1;  // rows per load, loads
+  constexpr int R2 = KP2 ? 256 / KP2 : 1, N2 = KP2 ? kBN / R2 : 0;
+  static_assert(N1 + N2 == KLD && VLD == 1, "load split");
+  const int krow1 = tid / KP1, kc1 = tid % KP1;
+  const int krow2 = KP2 ? tid / KP2 : 0, kc2 = KP2 ? KP1 + tid % KP2 : 0;
+  const uint32_t rowb = (uint32_t)H * DQK * 2u;  // bytes between key rows
+  const uint32_t kbo1 = krow1 * rowb + 16u * kc1, kbo2 = krow2 * rowb + 16u * kc2;
+  const int vkg = tid / VCH, vdg = tid - vkg * VCH;
+  const uint32_t vrowb = (uint32_t)H * DV * 2u;
+  const uint32_t vbo = 4 * vkg * vrowb + 16u * vdg;
   u32x4_t kpre[KLD];
-  u32x4_t vpre[VLD][4];
+  u32x4_t vpre[4];
   auto load_block = [&](int jb) {
+    const int64_t rows = (int64_t)Tbuf - jb;  // rows of the buffer from jb on
+    const auto kr = make_rsrc(k + ((kvrow0 + jb) * H + h) * DQK, rows * rowb - (int64_t)h * DQK * 2);
+    const auto vr = make_rsrc(v + ((kvrow0 + jb) * H + h) * DV, rows * vrowb - (int64_t)h * DV * 2);
 #pragma unroll
-    for (int r = 0; r < KLD; ++r) {
-      const int u = tid + 256 * r;
-      const int row = u / KCH, c = u - row * KCH;
-      const int j = jb + row;
-      kpre[r] = u32x4_t{0, 0, 0, 0};
-      if (j < Tbuf) kpre[r] = load16(k + ((kvrow0 + j) * H + h) * DQK + 8 * c);
-    }
+    for (int n = 0; n < N1; ++n) kpre[n] = buffer_load16(kr, kbo1 + n * R1 * rowb);
 #pragma unroll
-    for (int r = 0; r < VLD; ++r) {
-      const int u = tid + 256 * r;
-      const int kg = u / VCH, dg = u - kg * VCH;
+    for (int n = 0; n < N2; ++n) kpre[N1 + n] = buffer_load16(kr, kbo2 + n * R2 * rowb);
+    if (tid < VUN) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jb + 4 * kg + e;
-        vpre[r][e] = u32x4_t{0, 0, 0, 0};
-        if (u < VUN && j < Tbuf) vpre[r][e] = load16(v + ((kvrow0 + j) * H + h) * DV + 8 * dg);
-      }
+      for (int e = 0; e < 4; ++e) vpre[e] = buffer_load16(vr, vbo + e * vrowb);
     }
   };
   // ---- registers -> LDS: K row-major, V transposed with bits 2/3 of the key
   // offset swapped inside each 16-key chunk (the order the P^T operand uses)
   auto store_block = [&]() {
 #pragma unroll
-    for (int r = 0; r < KLD; ++r) {
-      const int u = tid + 256 * r;
-      const int row = u / KCH, c = u - row * KCH;
-      *(u32x4_t*)(&Ks[row * KPAD + 8 * c]) = kpre[r];
-    }
+    for (int n = 0; n < N1; ++n) *(u32x4_t*)(&Ks[(krow1 + n * R1) * KPAD + 8 * kc1]) = kpre[n];
 #pragma unroll
-    for (int r = 0; r < VLD; ++r) {
-      const int u = tid + 256 * r;
-      if (u < VUN) {
-        const int kg = u / VCH, dg = u - kg * VCH;
-        const int o16 = (4 * kg) & 15;
-        const int pos = ((4 * kg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
+    for (int n = 0; n < N2; ++n) *(u32x4_t*)(&Ks[(krow2 + n * R2) * KPAD + 8 * kc2]) = kpre[N1 + n];
+    if (tid < VUN) {
+      const int o16 = (4 * vkg) & 15;
+      const int pos = ((4 * vkg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const uint32_t a0 = vpre[r][0][mm], a1 = vpre[r][1][mm];
-          const uint32_t a2 = vpre[r][2][mm], a3 = vpre[r][3][mm];
-          uint2 lo, hi;
-          lo.x = (a0 & 0xFFFFu) | (a1 << 16);
-          lo.y = (a2 & 0xFFFFu) | (a3 << 16);
-          hi.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
-          hi.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
-          const int r0 = 8 * dg + 2 * mm, r1 = r0 + 1;
-          *(uint2*)(&Vt[r0 * VPAD + vt_col(r0, pos)]) = lo;
-          *(uint2*)(&Vt[r1 * VPAD + vt_col(r1, pos)]) = hi;
-        }
+      for (int mm = 0; mm < 4; ++mm) {
+        const uint32_t a0 = vpre[0][mm], a1 = vpre[1][mm];
+        const uint32_t a2 = vpre[2][mm], a3 = vpre[3][mm];
+        // even dv of the four keys, then odd dv
+        uint2 lo, hi;
+        lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+        const int r0 = 8 * vdg + 2 * mm, r1 = r0 + 1;
+        *(uint2*)(&Vt[r0 * VPAD + vt_col(r0, pos)]) = lo;
+        *(uint2*)(&Vt[r1 * VPAD + vt_col(r1, pos)]) = hi;
       }
     }
   };
 
   float m = -INFINITY, l = 0.0f;
+  const float lazy_thr = kLazyLog2 / scale_log2;  // raw-logit units
   f32x16_t o[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) o[d] = zero16();
@@ -276,36 +280,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       const uint32_t wbits = (MASK == 0) ? (bits[i] >> (4 * lh)) : 0u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        bool ok;
+        float x;
         if (MASK == 0) {
-          ok = (wbits >> (8 * (e >> 2) + (e & 3))) & 1u;
+          x = keep_or_neg_inf(st[e], wbits, 8 * (e >> 2) + (e & 3));
         } else {
           const int jj = jb + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
           const int t = kv_offset + jj;
-          ok = (jj < Tbuf) && (t <= p) && (t > p - window);
+          x = ((jj < Tbuf) && (t <= p) && (t > p - window)) ? st[e] : -INFINITY;
         }
-        const float x = ok ? st[e] : -INFINITY;
         st[e] = x;
         mx = fmaxf(mx, x);
       }
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      // p = 2^(scale*log2e*(x - m)) as one fma + exp2; masked x = -inf gives 0
+      // The reference max m only moves when the block max exceeds it by more
+      // than kLazyLog2 in log2 units, so p = 2^(c(x - m)) stays below
+      // 2^kLazyLog2 and O, l are rescaled rarely. Any m gives the same O / l.
+      const bool bump = mx > m + lazy_thr;
+      const bool resc = bump && (m != -INFINITY);  // m = -inf: O and l are still 0
+      const float mnew = bump ? mx : m;
       const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
-      const float alpha = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * scale_log2);
-      const bool changed = mnew != m;
+      const float alpha = resc ? exp2_hw((m - mnew) * scale_log2) : 1.0f;
       m = mnew;
       uint32_t pk[2][4];  // [16-key half][packed pair]
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = exp2f(fmaf(st[e], scale_log2, nms));
-        const float p1 = exp2f(fmaf(st[e + 1], scale_log2, nms));
+        const float p0 = exp2_hw(fmaf(st[e], scale_log2, nms));
+        const float p1 = exp2_hw(fmaf(st[e + 1], scale_log2, nms));
         psum += p0 + p1;
         pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
       }
       l = l * alpha + psum;
-      if (__any(changed)) {
+      if (__any(resc)) {
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll

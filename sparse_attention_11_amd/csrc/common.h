@@ -36,6 +36,18 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *(const u32x4_t*)p; }
 
+// Raw buffer resource over [base, base + bytes) (bytes clamped to 32 bits):
+// a buffer load whose range lies past the end returns zeros instead of
+// touching memory. The third dword is the gfx9-family untyped-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n,
+                                          0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -53,6 +65,17 @@ __device__ __forceinline__ float relu_f32(float x) {
   float r;
   asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
   return r;
+}
+
+// 2^x as the bare hardware instruction (no denormal-range fix-up): results
+// below 2^-126 may flush to zero, which only ever drops negligible weights.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x where bit `pos` of `bits` is set, else -inf: one bit-field extract that
+// replicates the bit, then one bitwise select.
+__device__ __forceinline__ float keep_or_neg_inf(float x, uint32_t bits, int pos) {
+  const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)bits, pos, 1);
+  return __uint_as_float((__float_as_uint(x) & sel) | (0xFF800000u & ~sel));
 }
 
 // sigmoid in fp32 as 1 / (1 + e^-x): exactly 0 at -inf, 1 at +inf, 1/2 at 0.
