@@ -6,6 +6,7 @@
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // MFMA bf16 operand (16 B / lane)
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;    // 16x16 MFMA accumulator
 
 #define DSA_LOG2E 1.4426950408889634f
 
@@ -51,6 +52,11 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// D(16x16) += A(16x32) B(32x16): lane l holds A[l%16][8(l/16)+i] and
+// B[8(l/16)+i][l%16] (i = 0..7); acc[j] = D[4(l/16)+j][l%16].
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
@@ -65,6 +71,11 @@ __device__ __forceinline__ float relu_f32(float x) {
   float r;
   asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
   return r;
+}
+// max(x, 0) as one signed-integer max on the bit pattern: every float with
+// the sign bit set (negatives, -0) maps to +0, everything else is unchanged.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 // 2^x as the bare hardware instruction (no denormal-range fix-up): results

@@ -6,18 +6,19 @@
 // causal upper-triangle mask).
 //
 // The index key is shared by all index heads, so it is the stationary MFMA
-// operand: a workgroup keeps a 128-key tile of k in registers and streams the
-// per-head query tiles through the bf16 MFMA, one K = idx_dim product per
+// operand: each wave keeps 128 keys of k in registers and streams the
+// per-head query operands through the bf16 MFMA, one K = idx_dim product per
 // head followed by the per-head ReLU and weighted accumulation in fp32.
 // Scores are produced transposed (keys on the MFMA M axis) so that each lane
 // owns one query column: the head weight is then a per-lane scalar.
 //
 // Kernels
-//  idx_tile_kernel   prefill tiles of 128 queries x 128 keys, 4 waves, each
-//                    wave 128 keys x 32 queries; only tiles on or below the
-//                    causal diagonal are launched, paired (j, last-j) so every
-//                    pair costs the same, pairs dealt to XCDs round-robin.
-//  idx_fill_kernel   -inf for the key tiles above the diagonal.
+//  idx_tile_kernel   prefill tiles of 16 queries x 512 keys, 4 waves, each
+//                    wave 128 keys x 16 queries with its keys held in
+//                    registers and the queries' operands shared through LDS;
+//                    only tiles on or below the causal diagonal are launched,
+//                    paired (j, last-j) so every pair costs the same, pairs
+//                    dealt to XCDs round-robin.
 //  idx_rows_kernel   few-query calls (decode): the index heads become the
 //                    MFMA M axis; a wave streams 256 keys of k in blocks of 32.
 //  idx_f32_kernel    fp32 inputs: plain fp32 loops (parity-size workloads).
@@ -27,8 +28,11 @@
 namespace dsa {
 namespace {
 
-constexpr int kTileQ = 128;
-constexpr int kTileK = 128;
+constexpr int kQG = 1;                 // 16-query groups per wave
+constexpr int kTileQ = 16 * kQG;       // queries per workgroup (MFMA N axis)
+constexpr int kWaveK = 128;            // keys per wave (8 MFMA M blocks of 16)
+constexpr int kTileK = 4 * kWaveK;     // keys per workgroup
+constexpr int kStageBytes = 16384;     // query operands staged in LDS per step
 
 // Key tiles a query tile needs (the causal triangle).
 __host__ __device__ __forceinline__ int tiles_for_qtile(int qt, int S, int P, int nkt) {
@@ -37,16 +41,30 @@ __host__ __device__ __forceinline__ int tiles_for_qtile(int qt, int S, int P, in
   return c < nkt ? c : nkt;
 }
 
+// One workgroup = kTileQ queries x 512 keys; wave w keeps keys 128w..128w+127
+// of the tile in registers as 16x16x32 MFMA A operands for the whole kernel.
+// The queries' per-head operands are shared by the four waves: they are
+// copied global -> LDS by the LDS-DMA path (no register staging), one stage
+// of G heads at a time, double-buffered so that stage g+1 lands while stage
+// g is multiplied. The LDS image of a stage is laid out exactly in operand
+// lane order (1 KB per head, 32-dim step and 16-query group), so each B
+// operand is one conflict-free 16-byte read per lane.
 template <int DI, int MODE>
-__global__ __launch_bounds__(256) void idx_tile_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ w,
-                                                       float* __restrict__ scores, int S, int T,
-                                                       int P, int HI, float scale, int nqt,
-                                                       int nkt, int npairs, int maxlen) {
-  constexpr int KS = DI / 16;
+__global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ w,
+                                                          float* __restrict__ scores, int S,
+                                                          int T, int P, int HI, float scale,
+                                                          int nqt, int nkt, int npairs,
+                                                          int maxlen) {
+  constexpr int KS = DI / 32;                          // 32-dim steps per head
+  constexpr int G = kStageBytes / (kTileQ * DI * 2);   // heads per stage
+  static_assert(G * KS * kQG == 16, "a stage is 16 one-KB operand blocks, 4 per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t qs[2][kStageBytes];
+
   const int b = blockIdx.y;
-  // block -> (query tile, key tile)
+  // block -> (query tile, key tile); tiles paired (j, nqt-1-j), pairs dealt
+  // round-robin to the 8 XCDs
   const int pid = blockIdx.x;
   const int xcd = pid & 7;
   const int n = pid >> 3;
@@ -56,6 +74,8 @@ __global__ __launch_bounds__(256) void idx_tile_kernel(const uint16_t* __restric
   if (j >= npairs) return;
   const int qa = j, qb = nqt - 1 - j;
   const int ca = tiles_for_qtile(qa, S, P, nkt);
+  const int cb = qb == qa ? 0 : tiles_for_qtile(qb, S, P, nkt);
+  const int v = u;  // index of this workgroup among the pair's ca + cb
   int qt, kt;
   if (u < ca) {
     qt = qa;
@@ -63,93 +83,173 @@ __global__ __launch_bounds__(256) void idx_tile_kernel(const uint16_t* __restric
   } else {
     if (qb == qa) return;
     u -= ca;
-    if (u >= tiles_for_qtile(qb, S, P, nkt)) return;
+    if (u >= cb) return;
     qt = qb;
     kt = u;
   }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ln = lane & 31, lh = lane >> 5;
-  const int q0 = qt * kTileQ, k0 = kt * kTileK;
-
-  // stationary A operands: key rows (MFMA M), 8 dims per lane per k-step
-  bf16x8_t a[4][KS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int lq = lane & 15, lg = lane >> 4;
+  const int q0 = qt * kTileQ;
+  const int kw0 = kt * kTileK + wave * kWaveK;  // first key of this wave
+  int64_t row[kQG];  // this lane's query row of each group (clamped to S-1)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = k0 + 32 * i + ln;
-    const uint16_t* kp = k + ((int64_t)b * T + (t < T ? t : T - 1)) * DI + 8 * lh;
+  for (int qg = 0; qg < kQG; ++qg) row[qg] = (int64_t)b * S + min(q0 + 16 * qg + lq, S - 1);
+  // waves whose keys all lie above the tile's last query skip the products
+  const bool active = kw0 <= P + min(q0 + kTileQ, S) - 1;
+
+  bf16x8_t a[8][KS];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const int t = kw0 + 16 * kb + lq;
+    const uint16_t* kp = k + ((int64_t)b * T + (t < T ? t : T - 1)) * DI + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = load16(kp + 16 * ks);
-      if (t >= T) v = u32x4_t{0, 0, 0, 0};
-      a[i][ks] = as_bf16x8(v);
+      u32x4_t v = u32x4_t{0, 0, 0, 0};
+      if (active && t < T) v = load16(kp + 32 * ks);
+      a[kb][ks] = as_bf16x8(v);
     }
   }
 
-  const int s = q0 + 32 * wave + ln;
-  const int sc_ = s < S ? s : S - 1;
-  const int64_t row = (int64_t)b * S + sc_;
-  const uint16_t* qp = q + row * HI * DI + 8 * lh;
-  const uint16_t* wp = w + row * HI;
+  // operand block n of a stage = (head n / (KS kQG), dims 32((n / kQG) % KS)
+  // + 8 lg .. +8, query group n % kQG) of query lq; wave w copies 4w..4w+3
+  const int nst = (HI + G - 1) / G;
+  auto issue_stage = [&](int st, int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int blk = 4 * wave + r;
+      const int qg = blk % kQG, ks = (blk / kQG) % KS;
+      // heads past HI copy the last head (finite operands for the zero
+      // weight they get), so every stage runs G heads without branches
+      const int h = min(st * G + blk / (KS * kQG), HI - 1);
+      const uint16_t* src = q + (row[qg] * HI + h) * DI + 32 * ks + 8 * lg;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src, (__attribute__((address_space(3))) void*)(&qs[buf][blk * 1024]), 16, 0,
+          0);
+    }
+  };
+  // head weights of the next stage as raw bf16 bits (heads past HI read the
+  // last head's), converted and masked only when their stage runs so that
+  // nothing waits on these loads before then
+  uint16_t wn[kQG][G];
+  auto load_weights = [&](int st) {
+#pragma unroll
+    for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+      for (int g = 0; g < G; ++g) wn[qg][g] = w[row[qg] * HI + min(st * G + g, HI - 1)];
+  };
 
-  f32x16_t sc[4];
+  f32x4_t sc[kQG][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sc[i] = zero16();
+  for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) sc[qg][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int h = 0; h < HI; ++h) {
-    bf16x8_t bq[KS];
+  issue_stage(0, 0);
+  load_weights(0);
+  for (int st = 0; st < nst; ++st) {
+    uint16_t wc[kQG][G];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bq[ks] = as_bf16x8(load16(qp + h * DI + 16 * ks));
-    const float wh = bf16_to_f32(wp[h]) * scale;
+    for (int qg = 0; qg < kQG; ++qg)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x16_t acc = zero16();
+      for (int g = 0; g < G; ++g) wc[qg][g] = wn[qg][g];
+    // stage st has landed (each wave drains its own copies, vmcnt(0), before
+    // the barrier) and every wave is done with the buffer stage st+1 overwrites
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const int buf = st & 1;
+    if (st + 1 < nst) {
+      issue_stage(st + 1, buf ^ 1);
+      load_weights(st + 1);
+    }
+    if (active) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[i][ks], bq[ks], acc);
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = acc[e];
-        if (MODE == 0) x = relu_f32(x);
-        sc[i][e] = fmaf(wh, x, sc[i][e]);
+        for (int qg = 0; qg < kQG; ++qg) {
+          bf16x8_t bq[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            bq[ks] = as_bf16x8(
+                *(const u32x4_t*)(&qs[buf][((g * KS + ks) * kQG + qg) * 1024 + 16 * lane]));
+          f32x4_t acc[8];
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) acc[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) acc[kb] = mfma16x16x32(a[kb][ks], bq[ks], acc[kb]);
+          const float wh = (st * G + g < HI) ? bf16_to_f32(wc[qg][g]) * scale : 0.0f;
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = acc[kb][e];
+              if (MODE == 0) x = relu_bits(x);
+              sc[qg][kb][e] = fmaf(wh, x, sc[qg][kb][e]);
+            }
+        }
       }
     }
   }
-  if (s >= S) return;
 
-  const int p = P + s;
-  float* orow = scores + ((int64_t)b * S + s) * T;
+  // lane (lq, lg) holds keys kw0 + 16 kb + 4 lg + e of query q0 + 16 qg + lq
   const bool vec = (T & 3) == 0;
+  // Key tiles above the diagonal get -inf. The pair's (nkt - ca) + (nkt - cb)
+  // such (query tile, key tile) units are dealt round-robin to its ca + cb
+  // workgroups, whose counts nearly match, so the fill rides along with the
+  // products instead of a separate pass over HBM.
+  {
+    const int na = nkt - ca, nunits = na + (qb == qa ? 0 : nkt - cb);
+    for (int un = v; un < nunits; un += ca + cb) {
+      const int fq = un < na ? qa : qb;
+      const int fk = un < na ? ca + un : cb + (un - na);
+      const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int rr = 0; rr < kTileQ; rr += 16) {
+        const int fs = fq * kTileQ + rr + tid / 16;
+        if (fs >= S) continue;
+        float* frow = scores + ((int64_t)b * S + fs) * T;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int t0 = k0 + 32 * i + 8 * g + 4 * lh;
+        for (int i = 0; i < kTileK / 64; ++i) {
+          const int t0 = fk * kTileK + 4 * (tid % 16 + 16 * i);
+          if (vec && t0 + 3 < T) {
+            *(float4*)(frow + t0) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + e < T) frow[t0 + e] = -INFINITY;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int qg = 0; qg < kQG; ++qg) {
+    const int s = q0 + 16 * qg + lq;
+    if (s >= S) continue;
+    const int p = P + s;
+    float* orow = scores + ((int64_t)b * S + s) * T;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const int t0 = kw0 + 16 * kb + 4 * lg;
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = sc[i][4 * g + r];
-        if (MODE == 2) x = fmaxf(x, 0.0f);
-        v[r] = (t0 + r <= p) ? x : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        float x = sc[qg][kb][e];
+        if (MODE == 2) x = relu_bits(x);
+        v[e] = (t0 + e <= p) ? x : -INFINITY;
       }
       if (vec && t0 + 3 < T) {
         *(float4*)(orow + t0) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t0 + r < T) orow[t0 + r] = v[r];
+        for (int e = 0; e < 4; ++e)
+          if (t0 + e < T) orow[t0 + e] = v[e];
       }
     }
   }
-}
-
-// -inf for every key tile above the causal diagonal of its query tile.
-__global__ __launch_bounds__(256) void idx_fill_kernel(float* __restrict__ scores, int S, int T,
-                                                       int P, int nkt) {
-  const int64_t row = blockIdx.x;  // b*S + s
-  const int s = (int)(row % S);
-  const int start = tiles_for_qtile(s / kTileQ, S, P, nkt) * kTileK;
-  float* orow = scores + row * T;
-  for (int t = start + threadIdx.x; t < T; t += blockDim.x) orow[t] = -INFINITY;
 }
 
 // Few queries per call: MFMA M = index heads (NHB blocks of 32), N = 32 keys.
@@ -290,15 +390,7 @@ hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w,
   if (gx > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((idx_tile_kernel<DI, MODE>), dim3((unsigned)gx, B), dim3(256), 0, st, q, k,
                      w, scores, S, T, P, HI, scale, nqt, nkt, npairs, maxlen);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // rows whose query tile does not reach the last key tile get -inf past it
-  if (tiles_for_qtile(0, S, P, nkt) < nkt) {
-    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)((int64_t)B * S)), dim3(256), 0, st, scores,
-                       S, T, P, nkt);
-    e = hipGetLastError();
-  }
-  return e;
+  return hipGetLastError();
 }
 
 template <int DI, int NHB, int MODE>

@@ -82,6 +82,8 @@ INDEX_CASES = [
     (2, 130, 73, 5, 128, 0), (1, 257, 0, 64, 128, 0), (1, 64, 1000, 16, 64, 2),
     (2, 1, 999, 64, 128, 0), (3, 5, 300, 40, 64, 0), (1, 3, 40, 130, 32, 0),
     (1, 7, 0, 32, 128, 1), (2, 1, 4095, 4, 64, 2),
+    # several 512-key tiles, head counts that leave a partial last LDS stage
+    (1, 600, 0, 9, 64, 0), (1, 1000, 500, 13, 128, 2), (2, 333, 1200, 17, 32, 1),
 ]
 
 
