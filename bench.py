@@ -236,8 +236,10 @@ def summarize(wl, per_stage, total_ms):
         r["K3_useful_mfma_frac"] = w["attn"]["flops"] / t3 / PEAK_BF16
         r["K3_issued_mfma_frac"] = w["attn"]["dense_flops"] / t3 / PEAK_BF16
         pre = sum(v["mean_us"] for k_, v in per_stage.items() if not k_.startswith("D ")) * 1e-6
-        r["prefill_tokens_per_s"] = wl.B * wl.S / pre
+        r["prefill_tokens_per_s"] = wl.B * wl.S / pre  # sum of the prefill stages' times
         r["prefill_us"] = pre * 1e6
+        if not wl.decode_after:  # whole timed step, launch gaps included
+            r["step_tokens_per_s"] = wl.B * wl.S / (total_ms * 1e-3)
     else:
         t4 = g("K4 sparse_attn_decode")
         r["decode_us_per_step"] = total_ms * 1e3
@@ -249,6 +251,23 @@ def summarize(wl, per_stage, total_ms):
         r["decode_us_per_step"] = dec * 1e6
         r["D_K4_hbm_frac"] = w["D"]["K4_bytes"] / g("D K4 sparse_attn_decode") / PEAK_HBM
     return r
+
+
+# --------------------------------------------------- counted HBM traffic
+def counted_traffic(wl_name):
+    """HBM bytes per launch of the dominant stage from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when
+    there is none or the kernel source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm-bytes_{wl_name}.json")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["kernel_source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest() if os.path.exists(src) else ""
+    if sha != rec["kernel_source_sha256"]:
+        return None, f"counters in {os.path.relpath(path, ROOT)} predate the current {rec['kernel_source']}"
+    return rec["traffic_bytes_per_launch"], os.path.relpath(path, ROOT)
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -267,11 +286,17 @@ def cpu_baseline(wl, budget_s):
     k_idx = g((1, T, wl.DI), datagen.TID_KIDX, wl.scale_kidx)
     kc = g((1, T, wl.H, wl.Dqk), datagen.TID_K, wl.scale_k)
     vc = g((1, T, wl.H, wl.v), datagen.TID_V, wl.scale_v)
-    block = 8
-    starts = np.linspace(0, S - block, 16).astype(int) if S > block else [0]
-    rows = 0
+    # blocks of 8 consecutive query rows; visited in bit-reversed order of a
+    # 256-block grid over the sequence so that any prefix of the visit order
+    # samples early and late rows (short and long causal contexts) alike.
+    # Passes over the grid repeat until the time budget is spent.
+    block, nblk = 8, 256
+    grid = np.linspace(0, max(S - block, 0), nblk).astype(int)
+    order = [int(format(i, "08b")[::-1], 2) for i in range(nblk)]
+    rows, nb_done = 0, 0
     t0 = time.perf_counter()
-    for s0 in starts:
+    for oi in order * 64:
+        s0 = int(grid[oi])
         n = min(block, S - s0)
         q_idx = g((1, n, wl.HI, wl.DI), datagen.TID_QIDX, wl.scale_qidx, s0 * wl.HI * wl.DI)
         w = g((1, n, wl.HI), datagen.TID_W, wl.scale_w, s0 * wl.HI)
@@ -282,13 +307,14 @@ def cpu_baseline(wl, budget_s):
         idx = oracle.topk(sc.astype(np.float32), wl.topk)
         oracle.sparse_attn(q, kc[:, :Tn], vc[:, :Tn], idx, gate, P + s0, wl.nope, wl.rope)
         rows += n
-        if time.perf_counter() - t0 > budget_s:
+        nb_done += 1
+        if time.perf_counter() - t0 > budget_s or S <= block:
             break
     el = time.perf_counter() - t0
     return {"value": rows / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows} query rows of {wl.name} (blocks of {block} spread over the "
-                      f"{S}-token prefill, B=1): indexer + top-k + sparse attention + gate in "
-                      f"fp64, {el:.1f} s"}
+            "sample": f"{rows} query rows of {wl.name} ({nb_done} blocks of {block} consecutive "
+                      f"rows spread over the {S}-token prefill, B=1): indexer + top-k + sparse "
+                      f"attention + gate in fp64, {el:.1f} s"}
 
 
 def main():
@@ -346,12 +372,14 @@ def main():
         roof = {"kernel": "K4 sparse_attn_decode", "bound": "hbm", "achieved": ach,
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM,
                 "traffic": None, "mean_launch_us": t4 * 1e6}
+    roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, args.cpu_seconds)
     line = {
         "metric": METRIC,
-        "value": main_r.get("prefill_tokens_per_s", 1e6 / main_r.get("decode_us_per_step", 1.0)),
+        "value": main_r.get("step_tokens_per_s", main_r.get("prefill_tokens_per_s",
+                                                            1e6 / main_r.get("decode_us_per_step", 1.0))),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_ms,
