@@ -100,23 +100,36 @@ __host__ __device__ __forceinline__ int tile_blocks(int qt, int S, int P, int Tb
   return jhi >= jlo ? (jhi - jlo) / kBN + 1 : 0;
 }
 
-// Work item -> (query tile, split, number of splits). Items run from the
-// longest tile down; a tile of nb key blocks is cut into ceil(nb / M) splits.
-__device__ __forceinline__ bool item_tile(int item, int nqt, int M, int S, int P, int Tbuf,
-                                          int kv_offset, int window, int* qt, int* split,
-                                          int* nsplit) {
-  for (int t = nqt - 1; t >= 0; --t) {
-    const int nb = tile_blocks(t, S, P, Tbuf, kv_offset, window);
-    const int c = nb > M ? (nb + M - 1) / M : 1;
-    if (item < c) {
-      *qt = t;
-      *split = item;
-      *nsplit = c;
-      return true;
-    }
-    item -= c;
+// Work items run from the longest query tile down. When long tiles are split
+// (at most M key blocks per item), start[o] is the first item of the o-th
+// longest tile (tile nqt-1-o) and start[nqt] the item count; the table is
+// built on the host and passed by value, so no kernel walks the tiles.
+constexpr int kMaxSplitTiles = 128;  // calls with more query tiles never split
+struct SplitTable {
+  int start[kMaxSplitTiles + 1];
+};
+
+// Work item -> (query tile, split, number of splits).
+__device__ __forceinline__ bool item_tile(int item, int nqt, int M, const SplitTable& tab, int* qt,
+                                          int* split, int* nsplit) {
+  if (M == 0x7FFFFFFF) {  // one item per tile
+    if (item >= nqt) return false;
+    *qt = nqt - 1 - item;
+    *split = 0;
+    *nsplit = 1;
+    return true;
   }
-  return false;
+  if (item >= tab.start[nqt]) return false;
+  int lo = 0, hi = nqt;  // largest o with start[o] <= item
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tab.start[mid] <= item) lo = mid;
+    else hi = mid;
+  }
+  *qt = nqt - 1 - lo;
+  *split = item - tab.start[lo];
+  *nsplit = tab.start[lo + 1] - tab.start[lo];
+  return true;
 }
 
 // ------------------------------------------------------------ flash kernel
@@ -133,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
     const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ part,
     int S, int Tbuf, int P, int kv_offset, int H, int W32, int window, float scale_log2,
-    int gate_dim, int nqt, int M) {
+    int gate_dim, int nqt, int M, const SplitTable tab) {
   constexpr int KSQ = DQK / 16;
   constexpr int NDB = DV / 32;
   constexpr int KPAD = DQK + 8;           // bf16 elements per K row in LDS
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VPAD];
 
   int qt, split, nsplit;
-  if (!item_tile(blockIdx.x, nqt, M, S, P, Tbuf, kv_offset, window, &qt, &split, &nsplit)) return;
+  if (!item_tile(blockIdx.x, nqt, M, tab, &qt, &split, &nsplit)) return;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
@@ -374,62 +387,84 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 }
 
 // Combines the splits of each split tile: out = sum_s 2^(c(m_s - M)) O_s /
-// sum_s 2^(c(m_s - M)) l_s, then the gate. One workgroup per (tile, head, b).
+// sum_s 2^(c(m_s - M)) l_s, then the gate. A workgroup covers 8 query rows
+// of one (tile, head, b), 32 threads per row and 4 output dims per thread,
+// and issues every split's loads before combining them (up to kMergeUnroll
+// splits in flight; longer lists run in chunks).
+constexpr int kMergeRows = 8;
+constexpr int kMergeUnroll = 8;
 template <int DV>
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part,
                                                            const uint16_t* __restrict__ gate,
                                                            uint16_t* __restrict__ out, int S,
-                                                           int P, int Tbuf, int H, int items,
-                                                           int nqt, int M, float scale_log2,
-                                                           int gate_dim) {
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+                                                           int H, int items, int nqt,
+                                                           float scale_log2, int gate_dim,
+                                                           const SplitTable tab) {
+  constexpr int TPR = DV / 4;  // threads per query row
+  static_assert(TPR * kMergeRows <= 256, "row group must fit the workgroup");
+  const int qt = blockIdx.x / (kBQ / kMergeRows);
+  const int rg = blockIdx.x % (kBQ / kMergeRows);
+  const int h = blockIdx.y, b = blockIdx.z;
   // first item of this tile and its number of splits
-  int base = 0, c = 1;
-  for (int t = nqt - 1; t >= qt; --t) {
-    const int nb = tile_blocks(t, S, P, Tbuf, 0, 0);
-    c = nb > M ? (nb + M - 1) / M : 1;
-    if (t > qt) base += c;
-  }
-  if (c <= 1) return;
-  const float* pt = part + (((int64_t)b * H + h) * items + base) * kBQ * (DV + 4);
+  const int base = tab.start[nqt - 1 - qt];
+  const int c = tab.start[nqt - qt] - base;
+  if (c <= 1 || (int)threadIdx.x >= TPR * kMergeRows) return;
+  const int qi = rg * kMergeRows + threadIdx.x / TPR, dv0 = 4 * (threadIdx.x % TPR);
+  const int s = qt * kBQ + qi;
+  if (s >= S) return;
   const int64_t split_stride = (int64_t)kBQ * (DV + 4);
-  for (int i = threadIdx.x; i < kBQ * (DV / 4); i += blockDim.x) {
-    const int qi = i / (DV / 4), dv0 = 4 * (i % (DV / 4));
-    const int s = qt * kBQ + qi;
-    if (s >= S) continue;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < c; ++sp) mx = fmaxf(mx, pt[sp * split_stride + qi * (DV + 4) + DV]);
-    float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp = 0; sp < c; ++sp) {
-      const float* q = pt + sp * split_stride + qi * (DV + 4);
-      const float w = (q[DV] == -INFINITY) ? 0.0f : exp2f((q[DV] - mx) * scale_log2);
-      L += w * q[DV + 1];
-      const float4 o4 = *(const float4*)(q + dv0);
-      acc[0] += w * o4.x;
-      acc[1] += w * o4.y;
-      acc[2] += w * o4.z;
-      acc[3] += w * o4.w;
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const int64_t qrow = (int64_t)b * S + s;
-    float g1 = 1.0f;
-    if (gate_dim == 1) g1 = sigmoid_f32(bf16_to_f32(gate[qrow * H + h]));
-    float r4[4];
+  const float* pt = part + (((int64_t)b * H + h) * items + base) * split_stride + qi * (DV + 4);
+  const int64_t qrow = (int64_t)b * S + s;
+  const uint16_t g1raw = gate_dim == 1 ? gate[qrow * H + h] : (uint16_t)0;  // issued early
+  // loads are unconditional (split indices past the last one re-read it and
+  // get weight 0) so that every load of a chunk is in flight at once
+  float mx = -INFINITY;
+  for (int s0 = 0; s0 < c; s0 += kMergeUnroll) {
+    float ms[kMergeUnroll];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float gg = g1;
-      if (gate_dim > 1) gg = sigmoid_f32(bf16_to_f32(gate[(qrow * H + h) * DV + dv0 + r]));
-      r4[r] = acc[r] * inv * gg;
-    }
-    uint2 pkd;
-    pkd.x = pack_bf16x2(r4[0], r4[1]);
-    pkd.y = pack_bf16x2(r4[2], r4[3]);
-    *(uint2*)(out + (qrow * H + h) * DV + dv0) = pkd;
+    for (int u = 0; u < kMergeUnroll; ++u) ms[u] = pt[min(s0 + u, c - 1) * split_stride + DV];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) mx = fmaxf(mx, ms[u]);
   }
+  float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < c; s0 += kMergeUnroll) {
+    float2 ml[kMergeUnroll];
+    float4 o4[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float* q = pt + min(s0 + u, c - 1) * split_stride;
+      ml[u] = *(const float2*)(q + DV);
+      o4[u] = *(const float4*)(q + dv0);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float w = (s0 + u >= c || ml[u].x == -INFINITY) ? 0.0f : exp2f((ml[u].x - mx) * scale_log2);
+      L += w * ml[u].y;
+      acc[0] += w * o4[u].x;
+      acc[1] += w * o4[u].y;
+      acc[2] += w * o4[u].z;
+      acc[3] += w * o4[u].w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  float g1 = 1.0f;
+  if (gate_dim == 1) g1 = sigmoid_f32(bf16_to_f32(g1raw));
+  float r4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float gg = g1;
+    if (gate_dim > 1) gg = sigmoid_f32(bf16_to_f32(gate[(qrow * H + h) * DV + dv0 + r]));
+    r4[r] = acc[r] * inv * gg;
+  }
+  uint2 pkd;
+  pkd.x = pack_bf16x2(r4[0], r4[1]);
+  pkd.y = pack_bf16x2(r4[2], r4[3]);
+  *(uint2*)(out + (qrow * H + h) * DV + dv0) = pkd;
 }
 
 struct SplitPlan {
   int nqt, M, items;
+  SplitTable tab;
 };
 
 // Splits long query tiles when the plain grid is too small to fill the GPU:
@@ -437,12 +472,14 @@ struct SplitPlan {
 // uses past_len = T - S (the longest tiles a call with this T can have).
 // Only selection-mask (DSA) calls split: there kv_offset = 0 and T >= P + S,
 // so T - S bounds past_len and the bound plan covers every actual call.
-// Window (SWA) tiles are short by construction and never split.
+// Window (SWA) tiles are short by construction and never split, nor are
+// calls with more than kMaxSplitTiles query tiles (their grid is large).
 SplitPlan make_split_plan(int B, int S, int T, int P, int H, int kv_offset, int window) {
   SplitPlan pl;
   pl.nqt = (S + kBQ - 1) / kBQ;
   pl.M = 0x7FFFFFFF;  // no split
-  if (window <= 0 && kv_offset == 0 && (int64_t)B * H * pl.nqt < 1024) {
+  if (window <= 0 && kv_offset == 0 && (int64_t)B * H * pl.nqt < 1024 &&
+      pl.nqt <= kMaxSplitTiles) {
     int64_t total_bound = 0;
     for (int t = 0; t < pl.nqt; ++t) total_bound += tile_blocks(t, S, T - S, T, 0, 0);
     total_bound *= (int64_t)B * H;
@@ -450,10 +487,12 @@ SplitPlan make_split_plan(int B, int S, int T, int P, int H, int kv_offset, int 
     pl.M = (int)std::max<int64_t>(16, m);
   }
   pl.items = 0;
-  for (int t = 0; t < pl.nqt; ++t) {
-    const int nb = tile_blocks(t, S, P, T, kv_offset, window);
+  for (int o = 0; o < pl.nqt; ++o) {
+    if (o <= kMaxSplitTiles) pl.tab.start[o] = pl.items;
+    const int nb = tile_blocks(pl.nqt - 1 - o, S, P, T, kv_offset, window);
     pl.items += nb > pl.M ? (nb + pl.M - 1) / pl.M : 1;
   }
+  if (pl.nqt <= kMaxSplitTiles) pl.tab.start[pl.nqt] = pl.items;
   return pl;
 }
 
@@ -468,15 +507,15 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (window > 0)
     hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, bm, gate,
                        out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
-                       pl.nqt, pl.M);
+                       pl.nqt, pl.M, pl.tab);
   else
     hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, bm, gate,
                        out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
-                       pl.nqt, pl.M);
+                       pl.nqt, pl.M, pl.tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.items == pl.nqt) return e;
-  hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt, H, B), dim3(256), 0, st, part, gate,
-                     out, S, P, Tbuf, H, pl.items, pl.nqt, pl.M, scale_log2, gate_dim);
+  hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt * (kBQ / kMergeRows), H, B), dim3(256),
+                     0, st, part, gate, out, S, H, pl.items, pl.nqt, scale_log2, gate_dim, pl.tab);
   return hipGetLastError();
 }
 
