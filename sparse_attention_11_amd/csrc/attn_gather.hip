@@ -244,15 +244,41 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   float g1 = 1.0f;
   if (gate_dim == 1)
     g1 = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
-  for (int d = lane; d < DV; d += 64) {
-    float acc = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) acc = fmaf(pbase[sp * sstride + d], wsh[wave][sp], acc);
+  // lane owns dv columns lane + 64 c (DV <= 256); splits are read 8 at a
+  // time with every load of a group in flight before the sums
+  constexpr int kC = 4, kU = 8;
+  float acc[kC] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int sp = 0;
+  for (; sp + kU <= nsplit; sp += kU) {
+    float x[kU][kC];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        const int d = lane + 64 * c;
+        x[u][c] = d < DV ? pbase[(sp + u) * sstride + d] : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int c = 0; c < kC; ++c) acc[c] = fmaf(x[u][c], wsh[wave][sp + u], acc[c]);
+  }
+  for (; sp < nsplit; ++sp)
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      const int d = lane + 64 * c;
+      if (d < DV) acc[c] = fmaf(pbase[sp * sstride + d], wsh[wave][sp], acc[c]);
+    }
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int d = lane + 64 * c;
+    if (d >= DV) break;
     float gg = g1;
     if (gate_dim > 1) {
       const int64_t gi = rh * DV + d;
       gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[gi]) : ((const float*)gate)[gi]);
     }
-    const float r = acc * inv * gg;
+    const float r = acc[c] * inv * gg;
     if (DT)
       ((uint16_t*)out)[rh * DV + d] = f32_to_bf16(r);
     else
@@ -267,7 +293,9 @@ struct Plan {
 Plan make_plan(int64_t rows, int H, int nent) {
   const int64_t hgroups = (H + 31) / 32;
   const int64_t base = rows * hgroups;
-  int nsplit = (int)std::max<int64_t>(1, (2048 + base - 1) / base);
+  // about 512 workgroups: enough to keep HBM busy, while fewer splits mean
+  // less partial-state traffic through the merge
+  int nsplit = (int)std::max<int64_t>(1, (512 + base - 1) / base);
   const int max_split = std::max(1, (nent + 15) / 16);  // at least 16 entries per split
   nsplit = std::min(std::min(nsplit, max_split), kMaxSplit);
   int per = (nent + nsplit - 1) / nsplit;

@@ -279,60 +279,70 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       load_bits(jb + kBN);
     }
 
-    // two 32-key halves in sequence: S^T, masked online softmax, O^T += V^T P^T
+    // S^T for both 32-key halves, one masked online-softmax update over the
+    // 64 keys, then O^T += V^T P^T for both halves
+    f32x16_t st[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      f32x16_t st = zero16();
+      st[i] = zero16();
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) {
         const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Ks[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
-        st = mfma32x32x16(a, bq[ks], st);
+        st[i] = mfma32x32x16(a, bq[ks], st[i]);
       }
-      // mask, then the running max on raw logits (scale > 0 keeps the order)
-      float mx = -INFINITY;
+    }
+    // mask, then the running max on raw logits (scale > 0 keeps the order)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       const uint32_t wbits = (MASK == 0) ? (bits[i] >> (4 * lh)) : 0u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x;
         if (MASK == 0) {
-          x = keep_or_neg_inf(st[e], wbits, 8 * (e >> 2) + (e & 3));
+          x = keep_or_neg_inf(st[i][e], wbits, 8 * (e >> 2) + (e & 3));
         } else {
           const int jj = jb + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
           const int t = kv_offset + jj;
-          x = ((jj < Tbuf) && (t <= p) && (t > p - window)) ? st[e] : -INFINITY;
+          x = ((jj < Tbuf) && (t <= p) && (t > p - window)) ? st[i][e] : -INFINITY;
         }
-        st[e] = x;
-        mx = fmaxf(mx, x);
+        st[i][e] = x;
+        mx = max_f32(mx, x);
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      // The reference max m only moves when the block max exceeds it by more
-      // than kLazyLog2 in log2 units, so p = 2^(c(x - m)) stays below
-      // 2^kLazyLog2 and O, l are rescaled rarely. Any m gives the same O / l.
-      const bool bump = mx > m + lazy_thr;
-      const bool resc = bump && (m != -INFINITY);  // m = -inf: O and l are still 0
-      const float mnew = bump ? mx : m;
-      const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
-      const float alpha = resc ? exp2_hw((m - mnew) * scale_log2) : 1.0f;
-      m = mnew;
-      uint32_t pk[2][4];  // [16-key half][packed pair]
-      float psum = 0.0f;
+    }
+    mx = max_other_half(mx);
+    // The reference max m only moves when the block max exceeds it by more
+    // than kLazyLog2 in log2 units, so p = 2^(c(x - m)) stays below
+    // 2^kLazyLog2 and O, l are rescaled rarely. Any m gives the same O / l.
+    const bool bump = mx > m + lazy_thr;
+    const bool resc = bump && (m != -INFINITY);  // m = -inf: O and l are still 0
+    const float mnew = bump ? mx : m;
+    const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
+    const float alpha = resc ? exp2_hw((m - mnew) * scale_log2) : 1.0f;
+    m = mnew;
+    uint32_t pk[2][2][4];  // [32-key half][16-key chunk][packed pair]
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = exp2_hw(fmaf(st[e], scale_log2, nms));
-        const float p1 = exp2_hw(fmaf(st[e + 1], scale_log2, nms));
+        const float p0 = exp2_hw(fmaf(st[i][e], scale_log2, nms));
+        const float p1 = exp2_hw(fmaf(st[i][e + 1], scale_log2, nms));
         psum += p0 + p1;
-        pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+        pk[i][e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
       }
-      l = l * alpha + psum;
-      if (__any(resc)) {
+    l = l * alpha + psum;
+    if (__any(resc)) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      }
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8_t pb = as_bf16x8(u32x4_t{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+        const bf16x8_t pb = as_bf16x8(u32x4_t{pk[i][c][0], pk[i][c][1], pk[i][c][2], pk[i][c][3]});
         const int kcol = 32 * i + 16 * c + 8 * lh;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
@@ -341,7 +351,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           o[d] = mfma32x32x16(va, pb, o[d]);
         }
       }
-    }
   }
 
   // ---- normalise, gate, store

@@ -101,5 +101,17 @@ __device__ __forceinline__ uint32_t orderable_key(float f) {
 }
 #define DSA_NEG_INF_KEY 0x007FFFFFu  // orderable_key(-inf)
 
+// max of two floats as one v_max_f32 (no NaN-quieting of the inputs first)
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// max(x, x of lane l ^ 32): one cross-half lane swap, no LDS round trip
+__device__ __forceinline__ float max_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Lane-swap helpers (wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }

@@ -132,6 +132,9 @@ def test_topk_on_oracle_scores_tiny_and_mla():
     (100, 60, 1, 0), (100, 60, 17, 1), (256, 0, 64, 2), (5000, 4000, 2048, 1),
     (5000, 4500, 512, 2), (2048, 2000, 2048, 0), (33000, 32900, 2048, 1), (40000, 39990, 300, 2),
     (8192, 8100, 8, 1),
+    # one-wave-per-row path (T <= 4096, k <= 512)
+    (4096, 4000, 512, 1), (4096, 3990, 256, 2), (3000, 2900, 300, 1), (1000, 976, 512, 0),
+    (4096, 4072, 129, 0),
 ])
 def test_topk_synthetic_rows(T, P, k, mode):
     S = T - P
@@ -141,8 +144,8 @@ def test_topk_synthetic_rows(T, P, k, mode):
     np.testing.assert_array_equal(got, oracle.topk(sc, k))
 
 
-def test_topk_constant_and_all_masked_tail():
-    T, k = 3000, 2048
+@pytest.mark.parametrize("T,k", [(3000, 2048), (2000, 500), (4096, 512)])
+def test_topk_constant_and_all_masked_tail(T, k):
     sc = np.zeros((2, T), np.float32)
     sc[1, 5:] = -np.inf
     sc[0, ::2] = -0.0
