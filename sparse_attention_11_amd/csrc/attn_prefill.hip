@@ -281,16 +281,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
     // S^T for both 32-key halves, one masked online-softmax update over the
     // 64 keys, then O^T += V^T P^T for both halves
-    f32x16_t st[2];
+    // (the two halves' accumulation chains are interleaved, so consecutive
+    // MFMAs never depend on each other)
+    f32x16_t st[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      st[i] = zero16();
+    for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) {
+      for (int i = 0; i < 2; ++i) {
         const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Ks[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
         st[i] = mfma32x32x16(a, bq[ks], st[i]);
       }
-    }
     // mask, then the running max on raw logits (scale > 0 keeps the order)
     float mx = -INFINITY;
 #pragma unroll
@@ -320,6 +320,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
     const float alpha = resc ? exp2_hw((m - mnew) * scale_log2) : 1.0f;
     m = mnew;
+    // weights rounded to bf16 once; the row sum is taken over the same
+    // rounded weights that P.V multiplies (one bf16 dot2 per pair)
     uint32_t pk[2][2][4];  // [32-key half][16-key chunk][packed pair]
     float psum = 0.0f;
 #pragma unroll
@@ -328,8 +330,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       for (int e = 0; e < 16; e += 2) {
         const float p0 = exp2_hw(fmaf(st[i][e], scale_log2, nms));
         const float p1 = exp2_hw(fmaf(st[i][e + 1], scale_log2, nms));
-        psum += p0 + p1;
-        pk[i][e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(pp, psum);
+        pk[i][e >> 3][(e & 7) >> 1] = pp;
       }
     l = l * alpha + psum;
     if (__any(resc)) {

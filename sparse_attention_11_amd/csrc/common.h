@@ -101,6 +101,12 @@ __device__ __forceinline__ uint32_t orderable_key(float f) {
 }
 #define DSA_NEG_INF_KEY 0x007FFFFFu  // orderable_key(-inf)
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2 with ones)
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
+}
+
 // max of two floats as one v_max_f32 (no NaN-quieting of the inputs first)
 __device__ __forceinline__ float max_f32(float a, float b) {
   float r;
@@ -111,6 +117,36 @@ __device__ __forceinline__ float max_f32(float a, float b) {
 __device__ __forceinline__ float max_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Value of lane l ^ m (m = 1, 2, 4, 8, 16 or 32) without an LDS round trip:
+// DPP quad permutes for 1 and 2, row shifts for 4, a row rotate for 8, and
+// the cross-row / cross-half permlane swaps for 16 and 32. m must fold to a
+// constant at the call site.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m, int lane) {
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);
+      const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);
+      return (lane & 4) ? dn : up;
+    }
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? r[0] : r[1];
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? r[0] : r[1];
+    }
+  }
+}
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int m, int lane) {
+  const uint32_t lo = lane_xor_u32((uint32_t)v, m, lane);
+  const uint32_t hi = lane_xor_u32((uint32_t)(v >> 32), m, lane);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Lane-swap helpers (wave64).

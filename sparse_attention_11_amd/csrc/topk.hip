@@ -380,7 +380,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     const int i = tid * E + e;
     a[e] = (i < kk) ? sel[i] : 0ull;
   }
+#pragma unroll
   for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride < E) {
 #pragma unroll
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int i = tid * E + e;
-          const uint64_t other = shfl_xor_u64(a[e], lm);
+          const uint64_t other = lane_xor_u64(a[e], lm, lane);
           const bool desc = (i & size) == 0;
           const bool low = (i & stride) == 0;  // lower index of its pair
           const bool keep_max = (low == desc);
