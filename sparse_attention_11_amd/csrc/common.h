@@ -143,6 +143,23 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m, int lane) {
     }
   }
 }
+// Inclusive prefix sum over the 64 lanes without LDS: DPP row shifts by 1,
+// 2, 4, 8 inside each row of 16, then the row-15 and row-31 broadcasts
+// carry row totals into the rows above.
+__device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+// Sum over the 64 lanes, returned in every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_incl_u32(x), 63);
+}
+
 __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int m, int lane) {
   const uint32_t lo = lane_xor_u32((uint32_t)v, m, lane);
   const uint32_t hi = lane_xor_u32((uint32_t)(v >> 32), m, lane);

@@ -50,12 +50,6 @@ __device__ __forceinline__ uint64_t score_key(float sc, int t) {
   return ((uint64_t)orderable_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // digit layout: pass 0..2 on the high word, 3..5 on the low word
 __device__ __forceinline__ int digit_shift(int pass) {
   const int lo = (pass >= 3) ? 0 : 32;
@@ -65,8 +59,7 @@ __device__ __forceinline__ int digit_shift(int pass) {
 __device__ __forceinline__ uint32_t digit_mask(int pass) { return (pass % 3 == 2) ? 0x3FFu : 0x7FFu; }
 
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  v = wave_sum_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
@@ -91,12 +84,9 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
     bins[q] = hist[8 * tid + q];
     local += bins[q];
   }
-  uint32_t x = local;  // inclusive suffix sum within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += y;
-  }
+  // inclusive suffix sum within the wave = wave total - exclusive prefix
+  const uint32_t pre = wave_scan_incl_u32(local);
+  const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + local;
   if (lane == 0) red[wave] = x;
   __syncthreads();
   uint32_t above_waves = 0;
@@ -230,12 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
           v[q] = i < EPT * kWaves ? s_col[i] : 0u;
           loc += v[q];
         }
-        uint32_t x = loc;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(x, off, 64);
-          if (lane >= off) x += y;
-        }
+        const uint32_t x = wave_scan_incl_u32(loc);
         uint32_t run = x - loc;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -265,12 +250,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
       takebits |= (uint64_t)take << j;
       ntake += take;
     }
-    uint32_t x = ntake;  // inclusive prefix over the block
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_scan_incl_u32(ntake);  // inclusive prefix over the wave
     if (lane == 63) s_red[wave] = x;
     __syncthreads();
     uint32_t base = x - ntake;
@@ -334,12 +314,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
           takebits |= (uint64_t)take << j;
           ntake += take;
         }
-        uint32_t x = ntake;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(x, off, 64);
-          if (lane >= off) x += y;
-        }
+        const uint32_t x = wave_scan_incl_u32(ntake);
         if (lane == 63) s_red[wave] = x;
         __syncthreads();
         uint32_t base = x - ntake;
