@@ -156,22 +156,23 @@ __global__ __launch_bounds__(256) void gather_kernel(
 #pragma unroll
         for (int e = 0; e < EP; ++e) dot = fmaf(qf[i][e], kf[e], dot);
       }
-      dot += shfl_xor_f(dot, 1);
-      dot += shfl_xor_f(dot, 2);
-      dot += shfl_xor_f(dot, 4);
+      // sum over the 8 lanes of this head (DPP lane exchanges, no LDS)
+      dot += __uint_as_float(lane_xor_u32(__float_as_uint(dot), 1, lane));
+      dot += __uint_as_float(lane_xor_u32(__float_as_uint(dot), 2, lane));
+      dot += __uint_as_float(lane_xor_u32(__float_as_uint(dot), 4, lane));
       x[g] = ok[g] ? dot : -INFINITY;
     }
     float mx = m;
 #pragma unroll
     for (int g = 0; g < kG; ++g) mx = fmaxf(mx, x[g]);
     const float muse = (mx == -INFINITY) ? 0.0f : mx;
-    const float alpha = exp2f(m - muse);
+    const float alpha = exp2_hw(m - muse);
     m = mx;
     float pg[kG];
     float ps = 0.0f;
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      pg[g] = exp2f(x[g] - muse);  // 0 for a skipped slot (x = -inf)
+      pg[g] = exp2_hw(x[g] - muse);  // 0 for a skipped slot (x = -inf)
       ps += pg[g];
     }
     l = l * alpha + ps;
