@@ -119,6 +119,12 @@ __device__ __forceinline__ float max_other_half(float x) {
   return max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// x + (x of lane l ^ 32): one cross-half lane swap, no LDS round trip
+__device__ __forceinline__ float sum_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Value of lane l ^ m (m = 1, 2, 4, 8, 16 or 32) without an LDS round trip:
 // DPP quad permutes for 1 and 2, row shifts for 4, a row rotate for 8, and
 // the cross-row / cross-half permlane swaps for 16 and 32. m must fold to a

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
 // A wave streams kRowsKeys keys in blocks of 32; the query operand is loaded
 // once per wave and the next block's keys are loaded during the current
 // block's MFMAs.
-constexpr int kRowsKeys = 256;  // keys per wave
+constexpr int kRowsKeys = 512;  // keys per wave (measured best: fewer per-wave query loads, enough waves)
 template <int DI, int NHB, int MODE>
 __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
@@ -328,12 +328,12 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           float x = acc[e];
-          if (MODE == 0) x = fmaxf(x, 0.0f);
+          if (MODE == 0) x = relu_bits(x);
           part = fmaf(wv[hb][e], x, part);
         }
       }
-      part += shfl_xor_f(part, 32);
-      if (MODE == 2) part = fmaxf(part, 0.0f);
+      part = sum_other_half(part);
+      if (MODE == 2) part = relu_bits(part);
     }
     if (lh == 0 && t < T) orow[t] = (t <= p) ? part : -INFINITY;
     if (more) {

@@ -39,8 +39,6 @@
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 2048;
 constexpr int kBins = 2048;
 constexpr int kSegLen = 16384;  // segment length of the first stage (long rows)
@@ -58,6 +56,7 @@ __device__ __forceinline__ int digit_shift(int pass) {
 }
 __device__ __forceinline__ uint32_t digit_mask(int pass) { return (pass % 3 == 2) ? 0x3FFu : 0x7FFu; }
 
+template <int NW>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
   v = wave_sum_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -66,22 +65,24 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
   __syncthreads();
   uint32_t s = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[w];
+  for (int w = 0; w < NW; ++w) s += red[w];
   return s;
 }
 
 // After a histogram pass: find the digit holding the krem-th largest key.
-// Thread t owns bins 8t..8t+7; a block suffix scan over threads (high digits
-// first) locates the bin. Writes the digit, the count still needed inside
-// it, and whether that bin is taken whole.
+// Thread t owns bins BPT t .. BPT t + BPT - 1; a block suffix scan over
+// threads (high digits first) locates the bin. Writes the digit, the count
+// still needed inside it, and whether that bin is taken whole.
+template <int NT>
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, int krem, int tid,
                                            int lane, int wave, int* s_krem, int* s_done,
                                            int* s_digit) {
-  uint32_t bins[8];
+  constexpr int BPT = kBins / NT, NW = NT / 64;
+  uint32_t bins[BPT];
   uint32_t local = 0;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    bins[q] = hist[8 * tid + q];
+  for (int q = 0; q < BPT; ++q) {
+    bins[q] = hist[BPT * tid + q];
     local += bins[q];
   }
   // inclusive suffix sum within the wave = wave total - exclusive prefix
@@ -91,19 +92,19 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
   __syncthreads();
   uint32_t above_waves = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w)
+  for (int w = 0; w < NW; ++w)
     if (w > wave) above_waves += red[w];
-  const uint32_t suf = x + above_waves;   // keys in bins >= 8*tid
-  const uint32_t suf_next = suf - local;  // keys in bins >= 8*tid + 8
+  const uint32_t suf = x + above_waves;   // keys in bins >= BPT*tid
+  const uint32_t suf_next = suf - local;  // keys in bins >= BPT*tid + BPT
   if (suf >= (uint32_t)krem && suf_next < (uint32_t)krem) {
     uint32_t cum = suf_next;
-    int q = 7;
+    int q = BPT - 1;
     for (; q > 0; --q) {
       if (cum + bins[q] >= (uint32_t)krem) break;
       cum += bins[q];
     }
     const int kr = krem - (int)cum;
-    *s_digit = 8 * tid + q;
+    *s_digit = BPT * tid + q;
     *s_krem = kr;
     *s_done = (bins[q] == (uint32_t)kr) ? 1 : 0;
   }
@@ -114,17 +115,19 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
 // SRC 0: T fp32 scores; SRC 1: T 64-bit candidate keys (0 = empty).
 // DST 0: sorted indices to out_idx[row, 0..k); DST 1: unsorted keys of this
 //        segment to out_keys[(row*nseg + seg)*k ...], padded with 0.
-// EPT > 0 keeps the elements in registers (range <= 256*EPT); EPT == 0 streams.
-// E: sort elements per thread (the sort covers max(k, 256) = 256*E keys).
-template <int SRC, int DST, int EPT, int E>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__ src,
+// NT threads per workgroup (256, or 1024 when a stage has few workgroups).
+// EPT > 0 keeps the elements in registers (range <= NT*EPT); EPT == 0 streams.
+// E: sort elements per thread (the sort covers max(k, NT) = NT*E keys).
+template <int NT, int SRC, int DST, int EPT, int E>
+__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
                                                         int32_t* __restrict__ out_idx,
                                                         uint64_t* __restrict__ out_keys, int T,
                                                         int k, int seg_len, int nseg) {
+  constexpr int NW = NT / 64;
   __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
-  __shared__ uint64_t sel[kMaxK > 256 * E ? kMaxK : 256 * E];
-  __shared__ uint32_t s_red[kWaves];
-  __shared__ uint32_t s_col[(EPT > 0 ? EPT : 1) * kWaves];
+  __shared__ uint64_t sel[kMaxK > NT * E ? kMaxK : NT * E];
+  __shared__ uint32_t s_red[NW];
+  __shared__ uint32_t s_col[(EPT > 0 ? EPT : 1) * NW];
   __shared__ int s_krem, s_done, s_digit;
   __shared__ uint32_t s_cnt;
 
@@ -145,14 +148,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   KT kreg[EPT > 0 ? EPT : 1];
   auto reg_key = [&](int j) -> uint64_t {
     if (SRC == 1) return (uint64_t)kreg[j];
-    const int t = t0 + tid + j * kThreads;
+    const int t = t0 + tid + j * NT;
     return kreg[j] ? (((uint64_t)kreg[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t)) : 0ull;
   };
   uint32_t valid = 0;
   if (EPT > 0 && SRC == 0) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const int e = tid + j * kThreads;
+      const int e = tid + j * NT;
       const float sc = e < n ? srow[t0 + e] : -INFINITY;
       const uint32_t hi = (sc == -INFINITY) ? 0u : orderable_key(sc);
       kreg[j] = (KT)hi;
@@ -161,15 +164,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   } else if (EPT > 0) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const int e = tid + j * kThreads;
+      const int e = tid + j * NT;
       const uint64_t key = e < n ? load_key(e) : 0ull;
       kreg[j] = (KT)key;
       valid += key != 0ull;
     }
   } else {
-    for (int e = tid; e < n; e += kThreads) valid += load_key(e) != 0ull;
+    for (int e = tid; e < n; e += NT) valid += load_key(e) != 0ull;
   }
-  const int nvalid = (int)block_sum(valid, s_red);
+  const int nvalid = (int)block_sum<NW>(valid, s_red);
   const int kk = min(k, nvalid);
 
   // Register path on score input: the selection is decided on the 32-bit
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     for (int pass = 0; pass < 3 && !done; ++pass) {
       const int shift = (pass == 0) ? 21 : (pass == 1 ? 10 : 0);
       const uint32_t dmask = (pass == 2) ? 0x3FFu : 0x7FFu;
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
         atomicAdd(&hist[m ? ((hi >> shift) & dmask) : (uint32_t)(kBins + lane)], 1u);
       }
       __syncthreads();
-      pick_digit(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+      pick_digit<NT>(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
       __syncthreads();
       prefix |= (uint32_t)s_digit << shift;
       mask |= dmask << shift;
@@ -207,17 +210,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
         const uint64_t b = __ballot((uint32_t)kreg[j] == prefix);
-        if (lane == 0) s_col[j * kWaves + wave] = (uint32_t)__popcll(b);
+        if (lane == 0) s_col[j * NW + wave] = (uint32_t)__popcll(b);
       }
       __syncthreads();
       if (wave == 0) {  // exclusive prefix over the EPT*4 column counts
-        constexpr int PER = EPT > 0 ? (EPT * kWaves + 63) / 64 : 1;
+        constexpr int PER = EPT > 0 ? (EPT * NW + 63) / 64 : 1;
         uint32_t v[PER];
         uint32_t loc = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const int i = lane * PER + q;
-          v[q] = i < EPT * kWaves ? s_col[i] : 0u;
+          v[q] = i < EPT * NW ? s_col[i] : 0u;
           loc += v[q];
         }
         const uint32_t x = wave_scan_incl_u32(loc);
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const int i = lane * PER + q;
-          if (i < EPT * kWaves) s_col[i] = run;
+          if (i < EPT * NW) s_col[i] = run;
           run += v[q];
         }
       }
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
       } else {
         const bool tie = hi == prefix;
         const uint64_t b = __ballot(tie);
-        const uint32_t rank = s_col[j * kWaves + wave] + (uint32_t)__popcll(b & lt_mask);
+        const uint32_t rank = s_col[j * NW + wave] + (uint32_t)__popcll(b & lt_mask);
         take = hi > prefix || (tie && rank < (uint32_t)krem);
       }
       takebits |= (uint64_t)take << j;
@@ -255,12 +258,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
     __syncthreads();
     uint32_t base = x - ntake;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < NW; ++w)
       if (w < wave) base += s_red[w];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       if ((takebits >> j) & 1ull) {
-        const uint32_t t = (uint32_t)(t0 + tid + j * kThreads);
+        const uint32_t t = (uint32_t)(t0 + tid + j * NT);
         if (base < (uint32_t)kMaxK) sel[base] = ((uint64_t)kreg[j] << 32) | (0xFFFFFFFFu - t);
         ++base;
       }
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
       for (int pass = 0; pass < 6; ++pass) {
         const int shift = digit_shift(pass);
         const uint32_t dmask = digit_mask(pass);
-        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0;
         __syncthreads();
         if (EPT > 0) {
 #pragma unroll
@@ -284,14 +287,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
               atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
           }
         } else {
-          for (int e = tid; e < n; e += kThreads) {
+          for (int e = tid; e < n; e += NT) {
             const uint64_t key = load_key(e);
             if (key != 0ull && (key & mask) == prefix)
               atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
           }
         }
         __syncthreads();
-        pick_digit(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+        pick_digit<NT>(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
         __syncthreads();
         prefix |= (uint64_t)s_digit << shift;
         mask |= (uint64_t)dmask << shift;
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
         __syncthreads();
         uint32_t base = x - ntake;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
+        for (int w = 0; w < NW; ++w)
           if (w < wave) base += s_red[w];
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
           }
         }
       } else {
-        for (int e = tid; e < n; e += kThreads) {
+        for (int e = tid; e < n; e += NT) {
           const uint64_t key = load_key(e);
           if (key != 0ull && key >= thr) {
             const uint32_t pos = atomicAdd(&s_cnt, 1u);
@@ -343,12 +346,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
 
   if (DST == 1) {  // first stage of a long row: unsorted candidates
     uint64_t* o = out_keys + ((int64_t)row * nseg + seg) * k;
-    for (int i = tid; i < k; i += kThreads) o[i] = (i < kk) ? sel[i] : 0ull;
+    for (int i = tid; i < k; i += NT) o[i] = (i < kk) ? sel[i] : 0ull;
     return;
   }
 
   // ---- bitonic sort (descending) of N = 256*E keys, padded with 0
-  constexpr int N = 256 * E;
+  constexpr int N = NT * E;
   uint64_t a[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -409,22 +412,35 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const void* __restrict__
   }
 }
 
-template <int SRC, int DST, int EPT>
+template <int NT, int SRC, int DST, int EPT>
 hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T, int k,
                     int seg_len, int nseg, hipStream_t st) {
-  const dim3 g((unsigned)blocks), b(kThreads);
-  if (DST == 1 || k <= 256)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
-  else if (k <= 512)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
-  else if (k <= 1024)
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  const dim3 g((unsigned)blocks), b(NT);
+  // sort width NT*E >= max(k, NT)
+  if (DST == 1 || k <= NT)
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else if (k <= 2 * NT)
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else if (NT == 256 && k <= 1024)
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, (NT == 256 ? 4 : 2)>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
   else
-    hipLaunchKernelGGL((topk_kernel<SRC, DST, EPT, 8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, (NT == 256 ? 8 : 2)>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
   return hipGetLastError();
 }
 
-constexpr int kCand = kThreads * 64;  // candidate keys one register-resident workgroup takes
+// A stage with few workgroups (few rows: decode, one long sequence) uses
+// 1024-thread workgroups so that each row gets four times the lanes; a
+// stage whose elements per workgroup are at most `range` keeps them in
+// registers (range / NT each).
+template <int SRC, int DST, int RANGE>
+hipError_t launch_stage(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T,
+                        int k, int seg_len, int nseg, hipStream_t st) {
+  if (blocks < 256)
+    return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
+  return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
+}
+
+constexpr int kCand = 16384;  // candidate keys one register-resident workgroup takes
 
 // number of candidate-reduction passes and their group counts for a row of T scores
 int stage_groups(int T, int k, int* groups, int max_levels) {
@@ -456,8 +472,8 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
                        void* workspace, hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
   if (T <= kSegLen) {  // one register-resident workgroup per row
-    if (T <= kThreads * 16) return launch_e<0, 0, 16>(scores, indices, nullptr, rows, T, topk, T, 1, st);
-    return launch_e<0, 0, 64>(scores, indices, nullptr, rows, T, topk, T, 1, st);
+    if (T <= 4096) return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st);
+    return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st);
   }
   int groups[8];
   const int lv = stage_groups(T, topk, groups, 8);
@@ -465,14 +481,14 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
   uint64_t* bufb = bufa + rows * groups[0] * (int64_t)topk;
   if (rows * groups[0] > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   // stage 1: k candidate keys per 16384-score segment
-  hipError_t e = launch_e<0, 1, kSegLen / kThreads>(scores, nullptr, bufa, rows * groups[0], T,
-                                                    topk, kSegLen, groups[0], st);
+  hipError_t e = launch_stage<0, 1, kSegLen>(scores, nullptr, bufa, rows * groups[0], T, topk,
+                                             kSegLen, groups[0], st);
   if (e != hipSuccess) return e;
   // candidate reductions: groups of kCand candidates -> k each
   int C = groups[0] * topk;
   uint64_t *in = bufa, *outb = bufb;
   for (int l = 1; l < lv; ++l) {
-    e = launch_e<1, 1, 64>(in, nullptr, outb, rows * groups[l], C, topk, kCand, groups[l], st);
+    e = launch_stage<1, 1, kCand>(in, nullptr, outb, rows * groups[l], C, topk, kCand, groups[l], st);
     if (e != hipSuccess) return e;
     C = groups[l] * topk;
     uint64_t* tmp = in;
@@ -480,7 +496,7 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
     outb = tmp;
   }
   // final selection and sort among at most kCand candidates per row
-  return launch_e<1, 0, 64>(in, indices, nullptr, rows, C, topk, C, 1, st);
+  return launch_stage<1, 0, kCand>(in, indices, nullptr, rows, C, topk, C, 1, st);
 }
 
 }  // namespace dsa

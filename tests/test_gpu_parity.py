@@ -144,6 +144,16 @@ def test_topk_synthetic_rows(T, P, k, mode):
     np.testing.assert_array_equal(got, oracle.topk(sc, k))
 
 
+# Enough rows that every stage runs 256-thread workgroups (few-row calls use
+# 1024-thread ones): a mid-length single-stage row and a two-stage row.
+@pytest.mark.parametrize("rows,T,k,mode", [(300, 6000, 1024, 1), (96, 33000, 2048, 0)])
+def test_topk_many_rows(rows, T, k, mode):
+    P = T - rows
+    sc = datagen.scores_host(0, rows, rows, T, P, seed=rows + T, mode=mode)
+    got = _run_topk(sc[None], k)[0]
+    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+
+
 @pytest.mark.parametrize("T,k", [(3000, 2048), (2000, 500), (4096, 512)])
 def test_topk_constant_and_all_masked_tail(T, k):
     sc = np.zeros((2, T), np.float32)
