@@ -126,17 +126,16 @@ __device__ __forceinline__ float sum_other_half(float x) {
 }
 
 // Value of lane l ^ m (m = 1, 2, 4, 8, 16 or 32) without an LDS round trip:
-// DPP quad permutes for 1 and 2, row shifts for 4, a row rotate for 8, and
+// DPP quad permutes for 1 and 2, two mirrors for 4, a row rotate for 8, and
 // the cross-row / cross-half permlane swaps for 16 and 32. m must fold to a
 // constant at the call site.
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m, int lane) {
   switch (m) {
     case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
     case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-    case 4: {
-      const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);
-      const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);
-      return (lane & 4) ? dn : up;
+    case 4: {  // i ^ 7 inside each half row, then i ^ 3 inside each quad
+      const int r = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+      return (uint32_t)__builtin_amdgcn_mov_dpp(r, 0x1B, 0xF, 0xF, false);     // quad_perm 3,2,1,0
     }
     case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
     case 16: {

@@ -350,7 +350,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
     return;
   }
 
-  // ---- bitonic sort (descending) of N = 256*E keys, padded with 0
+  // ---- bitonic sort (descending) of N = NT*E keys, padded with 0. Keys are
+  // unique apart from the 0 padding, so one compare decides each exchange:
+  // a slot keeps its own key iff (own > partner) equals "this slot keeps the
+  // larger key"; both conditions are lane masks and meet in one mask XOR.
   constexpr int N = NT * E;
   uint64_t a[E];
 #pragma unroll
@@ -368,37 +371,28 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
           const int pe = e ^ stride;
           if (pe > e) {
             const int i = tid * E + e;
-            const bool desc = (i & size) == 0;
+            const bool desc = (i & size) == 0;  // larger key to the lower slot
             const uint64_t lo = a[e], hi = a[pe];
-            const bool sw = desc ? (lo < hi) : (lo > hi);
+            const bool sw = (hi > lo) == desc;
             a[e] = sw ? hi : lo;
             a[pe] = sw ? lo : hi;
           }
         }
-      } else if (stride < 64 * E) {
-        const int lm = stride / E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          const uint64_t other = lane_xor_u64(a[e], lm, lane);
-          const bool desc = (i & size) == 0;
-          const bool low = (i & stride) == 0;  // lower index of its pair
-          const bool keep_max = (low == desc);
-          a[e] = keep_max ? (a[e] > other ? a[e] : other) : (a[e] < other ? a[e] : other);
-        }
       } else {
-        __syncthreads();
+        if (stride >= 64 * E) {
+          __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) sel[tid * E + e] = a[e];
-        __syncthreads();
+          for (int e = 0; e < E; ++e) sel[tid * E + e] = a[e];
+          __syncthreads();
+        }
+        // the slot's role depends on tid bits only (stride, size >= E)
+        const int i0 = tid * E;
+        const bool keep_max = ((i0 & stride) == 0) == ((i0 & size) == 0);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          const uint64_t other = sel[i ^ stride];
-          const bool desc = (i & size) == 0;
-          const bool low = (i & stride) == 0;
-          const bool keep_max = (low == desc);
-          a[e] = keep_max ? (a[e] > other ? a[e] : other) : (a[e] < other ? a[e] : other);
+          const uint64_t other =
+              stride < 64 * E ? lane_xor_u64(a[e], stride / E, lane) : sel[(tid * E + e) ^ stride];
+          a[e] = ((a[e] > other) == keep_max) ? a[e] : other;
         }
       }
     }
