@@ -291,8 +291,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Ks[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
         st[i] = mfma32x32x16(a, bq[ks], st[i]);
       }
-    // mask, then the running max on raw logits (scale > 0 keeps the order)
-    float mx = -INFINITY;
+    // mask, then the running max on raw logits (scale > 0 keeps the order),
+    // as a tree of three-input maxima (16 ops, 4 deep)
+    float mx3[11];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t wbits = (MASK == 0) ? (bits[i] >> (4 * lh)) : 0u;
@@ -307,9 +308,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           x = ((jj < Tbuf) && (t <= p) && (t > p - window)) ? st[i][e] : -INFINITY;
         }
         st[i][e] = x;
-        mx = max_f32(mx, x);
       }
     }
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {  // 30 of the 32 logits
+      const int e0 = 3 * r;
+      mx3[r] = max3_f32(st[e0 >> 4][e0 & 15], st[(e0 + 1) >> 4][(e0 + 1) & 15],
+                        st[(e0 + 2) >> 4][(e0 + 2) & 15]);
+    }
+    mx3[10] = max_f32(st[1][14], st[1][15]);
+    float mx = max3_f32(max3_f32(mx3[0], mx3[1], mx3[2]), max3_f32(mx3[3], mx3[4], mx3[5]),
+                        max3_f32(mx3[6], mx3[7], mx3[8]));
+    mx = max3_f32(mx, mx3[9], mx3[10]);
     mx = max_other_half(mx);
     // The reference max m only moves when the block max exceeds it by more
     // than kLazyLog2 in log2 units, so p = 2^(c(x - m)) stays below

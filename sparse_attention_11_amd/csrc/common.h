@@ -113,6 +113,12 @@ __device__ __forceinline__ float max_f32(float a, float b) {
   asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+// max of three floats as one v_max3_f32
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 // max(x, x of lane l ^ 32): one cross-half lane swap, no LDS round trip
 __device__ __forceinline__ float max_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
