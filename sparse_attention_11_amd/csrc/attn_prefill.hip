@@ -19,9 +19,9 @@
 // lane owns one query column: the softmax max/sum stay in registers except
 // for one swap with the other half-wave. The 32x32 accumulator layout then
 // holds keys {8g + 4*half + r}; the P.V product uses exactly that key order
-// as its contraction index, and V is staged in LDS transposed with the same
-// permutation (bits 2 and 3 of the key offset swapped within each 16 keys),
-// so P never leaves registers. Q^T stays in registers for the whole key loop.
+// as its contraction index, so P never leaves registers: V stays row-major in
+// LDS and its operand is read with gfx950's transposing LDS load, four keys
+// per read, in that key order. Q^T stays in registers for the whole key loop.
 #include <algorithm>
 
 #include "common.h"
@@ -72,13 +72,14 @@ __global__ __launch_bounds__(256) void bitmap_global_kernel(const int32_t* __res
   }
 }
 
-// Column of key position `pos` in row `row` of the transposed V tile: the
-// 16-byte chunk index (8 keys) is XORed with bits 4..6 of the row. The 16
-// rows 8 apart that one store instruction writes then fall into distinct
-// LDS banks, while the 16 consecutive rows one operand read covers share the
-// same swizzle and stay conflict-free as well.
-__device__ __forceinline__ int vt_col(int row, int pos) {
-  return ((((pos >> 3) ^ (row >> 4)) & 7) << 3) | (pos & 7);
+// Swizzle of the row-major V tile (rows of DV bf16 = VCH 16-byte chunks):
+// chunk c of key row r is stored at chunk c ^ vt_xor(r). A transposing read
+// covers four consecutive rows x 64 bytes per half-wave; the XOR moves those
+// four row pieces into four different 16-bank groups (rows of 256 bytes all
+// start at bank 0, rows of 128 bytes at bank 0 or 32).
+template <int VCH>
+__device__ __forceinline__ int vt_xor(int row) {
+  return VCH >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 // Buffer-row range [jlo, jhi] (64-aligned start) of the keys a 128-query tile
@@ -150,7 +151,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int KSQ = DQK / 16;
   constexpr int NDB = DV / 32;
   constexpr int KPAD = DQK + 8;           // bf16 elements per K row in LDS
-  constexpr int VPAD = kBN + 8;           // bf16 elements per V^T row in LDS
   constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
   constexpr int KLD = kBN * KCH / 256;    // K chunks per thread per block
   constexpr int VCH = DV / 8;             // 8-dv groups per V row
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int VLD = (VUN + 255) / 256;  // units per thread
   static_assert((kBN * KCH) % 256 == 0, "K block must split evenly over 256 threads");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * VPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * DV];
 
   int qt, split, nsplit;
   if (!item_tile(blockIdx.x, nqt, M, tab, &qt, &split, &nsplit)) return;
@@ -219,32 +219,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       for (int e = 0; e < 4; ++e) vpre[e] = buffer_load16(vr, vbo + e * vrowb);
     }
   };
-  // ---- registers -> LDS: K row-major, V transposed with bits 2/3 of the key
-  // offset swapped inside each 16-key chunk (the order the P^T operand uses)
+  // ---- registers -> LDS: K row-major (padded rows), V row-major (swizzled)
   auto store_block = [&]() {
 #pragma unroll
     for (int n = 0; n < N1; ++n) *(u32x4_t*)(&Ks[(krow1 + n * R1) * KPAD + 8 * kc1]) = kpre[n];
 #pragma unroll
     for (int n = 0; n < N2; ++n) *(u32x4_t*)(&Ks[(krow2 + n * R2) * KPAD + 8 * kc2]) = kpre[N1 + n];
     if (tid < VUN) {
-      const int o16 = (4 * vkg) & 15;
-      const int pos = ((4 * vkg) & ~15) + (((o16 >> 2) & 1) << 3) + (((o16 >> 3) & 1) << 2);
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const uint32_t a0 = vpre[0][mm], a1 = vpre[1][mm];
-        const uint32_t a2 = vpre[2][mm], a3 = vpre[3][mm];
-        // even dv of the four keys, then odd dv
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int r0 = 8 * vdg + 2 * mm, r1 = r0 + 1;
-        *(uint2*)(&Vt[r0 * VPAD + vt_col(r0, pos)]) = lo;
-        *(uint2*)(&Vt[r1 * VPAD + vt_col(r1, pos)]) = hi;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * vkg + e;
+        *(u32x4_t*)(&Vs[r * DV + 8 * (vdg ^ vt_xor<VCH>(r))]) = vpre[e];
       }
     }
   };
+  // Byte offset in Vs of this lane's transposing read for dv block d and the
+  // first 16-key chunk: in each 16-lane group (g = lane / 16), lane 4j + q
+  // addresses key row 4 * (lane / 32) + j, bytes 64 d + 32 (g & 1) + 8 q, and
+  // lane i of the group receives dv 32 d + lane % 32 of those four rows; the
+  // read 8 rows further gives the other four keys of the operand.
+  uint32_t vrd[NDB];
+  {
+    const int g16 = lane >> 4, jr = (lane >> 2) & 3, qr = lane & 3;
+    const int r = 4 * lh + jr;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int chunk = 4 * d + 2 * (g16 & 1) + (qr >> 1);
+      vrd[d] = (uint32_t)(r * DV * 2 + 16 * (chunk ^ vt_xor<VCH>(r)) + 8 * (qr & 1));
+    }
+  }
 
   float m = -INFINITY, l = 0.0f;
   const float lazy_thr = kLazyLog2 / scale_log2;  // raw-logit units
@@ -356,11 +359,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8_t pb = as_bf16x8(u32x4_t{pk[i][c][0], pk[i][c][1], pk[i][c][2], pk[i][c][3]});
-        const int kcol = 32 * i + 16 * c + 8 * lh;
+        const uint32_t crow = (uint32_t)(16 * (2 * i + c) * DV * 2);  // first row of the chunk
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
-          const int vr = 32 * d + ln;
-          const bf16x8_t va = as_bf16x8(*(const u32x4_t*)(&Vt[vr * VPAD + vt_col(vr, kcol)]));
+          const bf16x8_t va = lds_read_tr_pair(Vs, vrd[d] + crow, 8 * DV * 2);
           o[d] = mfma32x32x16(va, pb, o[d]);
         }
       }

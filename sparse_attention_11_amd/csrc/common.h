@@ -113,6 +113,23 @@ __device__ __forceinline__ float max_f32(float a, float b) {
   asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+// Transposing LDS read pair (gfx950 ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane 4j + q supplies a byte address a and lane i receives element
+// i % 4 at a of lane 4j + i / 4 as its element j. Two reads `second` bytes
+// apart fill an 8-element MFMA operand (first read -> elements 0..3).
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t lds_read_tr_pair(const uint16_t* lds, uint32_t byte_off,
+                                                     uint32_t second) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const __attribute__((address_space(3))) char* base =
+      (const __attribute__((address_space(3))) char*)lds;
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + byte_off));
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + byte_off + second));
+  const i16x4_t lo = a, hi = b;
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 // max of three floats as one v_max3_f32
 __device__ __forceinline__ float max3_f32(float a, float b, float c) {
   float r;
