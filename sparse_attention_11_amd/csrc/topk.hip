@@ -118,14 +118,19 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
 // NT threads per workgroup (256, or 1024 when a stage has few workgroups).
 // EPT > 0 keeps the elements in registers (range <= NT*EPT); EPT == 0 streams.
 // E: sort elements per thread (the sort covers max(k, NT) = NT*E keys).
+// Stages with at most 16 keys per thread are held to 64 registers so that
+// 2048 threads (8 waves per SIMD) fit a CU; the 64-key stages need more.
 template <int NT, int SRC, int DST, int EPT, int E>
-__global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
+__global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(const void* __restrict__ src,
                                                         int32_t* __restrict__ out_idx,
                                                         uint64_t* __restrict__ out_keys, int T,
                                                         int k, int seg_len, int nseg) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
-  __shared__ uint64_t sel[kMaxK > NT * E ? kMaxK : NT * E];
+  // selected keys: k of them for a candidate stage, at most NT*E >= k for a
+  // sorting stage (sized to that, so more workgroups fit a CU's LDS)
+  constexpr int kSel = DST == 1 ? kMaxK : NT * E;
+  __shared__ uint64_t sel[kSel];
   __shared__ uint32_t s_red[NW];
   __shared__ uint32_t s_col[(EPT > 0 ? EPT : 1) * NW];
   __shared__ int s_krem, s_done, s_digit;
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
     for (int j = 0; j < EPT; ++j) {
       if ((takebits >> j) & 1ull) {
         const uint32_t t = (uint32_t)(t0 + tid + j * NT);
-        if (base < (uint32_t)kMaxK) sel[base] = ((uint64_t)kreg[j] << 32) | (0xFFFFFFFFu - t);
+        if (base < (uint32_t)kSel) sel[base] = ((uint64_t)kreg[j] << 32) | (0xFFFFFFFFu - t);
         ++base;
       }
     }
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
           if ((takebits >> j) & 1ull) {
-            if (base < (uint32_t)kMaxK) sel[base] = reg_key(j);
+            if (base < (uint32_t)kSel) sel[base] = reg_key(j);
             ++base;
           }
         }
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const void* __restrict__ src,
           const uint64_t key = load_key(e);
           if (key != 0ull && key >= thr) {
             const uint32_t pos = atomicAdd(&s_cnt, 1u);
-            if (pos < (uint32_t)kMaxK) sel[pos] = key;
+            if (pos < (uint32_t)kSel) sel[pos] = key;
           }
         }
       }
