@@ -74,6 +74,12 @@ def _load():
         lib.oracle_swa_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                         i32, i32, i32, dbl, i32, vp]
         lib.oracle_swa_attn.restype = None
+        lib.oracle_sparse_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                               i32, i32, i32, i32, i32, i32, dbl, i32, vp]
+        lib.oracle_sparse_attn_pas.restype = None
+        lib.oracle_swa_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, i32, dbl, i32, vp]
+        lib.oracle_swa_attn_pas.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         _lib = lib
@@ -134,11 +140,23 @@ def _gate_dim(gate, Dv, gate_dim):
     return gate_dim
 
 
+def _sinks(sink_k, sink_v, H, Dqk, Dv):
+    """Sink rows [n_sink,H,Dqk] / [n_sink,H,Dv] (or None for none) -> (sk, sv, n)."""
+    if sink_k is None:
+        assert sink_v is None
+        return None, None, 0
+    sink_k, sink_v = _c(sink_k), _c(sink_v)
+    n = sink_k.shape[0]
+    assert sink_k.shape == (n, H, Dqk) and sink_v.shape == (n, H, Dv)
+    return sink_k, sink_v, n
+
+
 def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: int,
                 qk_rope_dim: int, sm_scale: float | None = None,
-                gate_dim: int | None = None) -> np.ndarray:
+                gate_dim: int | None = None, sink_k=None, sink_v=None) -> np.ndarray:
     """q [B,S,H,Dqk], caches [B,T,H,D], indices [B,S,k] int32, gate [B,S,H] (one logit
-    per head) or [B,S,H,Dv] (one per element) or None -> out [B,S,H,Dv] float64."""
+    per head) or [B,S,H,Dv] (one per element) or None, optional attention sinks
+    sink_k [n,H,Dqk] / sink_v [n,H,Dv] -> out [B,S,H,Dv] float64."""
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     indices = _c(np.asarray(indices, dtype=np.int32))
     B, S, H, Dqk = q.shape
@@ -152,17 +170,20 @@ def sparse_attn(q, k_cache, v_cache, indices, gate, past_len: int, qk_nope_dim: 
     if sm_scale is None:
         sm_scale = Dqk ** -0.5
     out = np.empty((B, S, H, Dv), np.float64)
-    _load().oracle_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate),
-                               _dtype_of(q, k_cache, v_cache, gate), B, S, T, past_len, H, Dqk,
-                               Dv, topk_, float(sm_scale), gate_dim, _ptr(out))
+    sk, sv, ns = _sinks(sink_k, sink_v, H, Dqk, Dv)
+    _load().oracle_sparse_attn_pas(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sk), _ptr(sv), ns,
+                                   _ptr(indices), _ptr(gate),
+                                   _dtype_of(q, k_cache, v_cache, gate, sk, sv), B, S, T,
+                                   past_len, H, Dqk, Dv, topk_, float(sm_scale), gate_dim,
+                                   _ptr(out))
     return out
 
 
 def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
              qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
-             gate_dim: int | None = None) -> np.ndarray:
-    """q [B,S,H,Dqk], buffers [B,T_buf,H,D] (row j = position kv_offset + j)
-    -> out [B,S,H,Dv] float64."""
+             gate_dim: int | None = None, sink_k=None, sink_v=None) -> np.ndarray:
+    """q [B,S,H,Dqk], buffers [B,T_buf,H,D] (row j = position kv_offset + j), optional
+    attention sinks as in sparse_attn -> out [B,S,H,Dv] float64."""
     q, k_buf, v_buf = _c(q), _c(k_buf), _c(v_buf)
     B, S, H, Dqk = q.shape
     assert Dqk == qk_nope_dim + qk_rope_dim
@@ -174,7 +195,9 @@ def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
     if sm_scale is None:
         sm_scale = Dqk ** -0.5
     out = np.empty((B, S, H, Dv), np.float64)
-    _load().oracle_swa_attn(_ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate),
-                            _dtype_of(q, k_buf, v_buf, gate), B, S, T_buf, past_len, kv_offset,
-                            H, Dqk, Dv, window, float(sm_scale), gate_dim, _ptr(out))
+    sk, sv, ns = _sinks(sink_k, sink_v, H, Dqk, Dv)
+    _load().oracle_swa_attn_pas(_ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(sk), _ptr(sv), ns,
+                                _ptr(gate), _dtype_of(q, k_buf, v_buf, gate, sk, sv), B, S,
+                                T_buf, past_len, kv_offset, H, Dqk, Dv, window, float(sm_scale),
+                                gate_dim, _ptr(out))
     return out

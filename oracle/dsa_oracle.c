@@ -20,6 +20,10 @@
  *   oracle_swa_attn      -- sliding-window attention, window W keys
  *                           [Spark-X2.5 page, "why the gate" (sliding_window
  *                           512); openPangu-2.0 page §3.2]
+ *   *_pas variants       -- the same two with parametric attention sinks:
+ *                           n_sink learned K/V rows every query attends to
+ *                           besides its selected or windowed keys
+ *                           [openPangu-2.0 page §3.4 (PAS)]
  * Decode is the same functions with S = 1 and past_len = T - 1.
  *
  * Arithmetic is IEEE double throughout; inputs are read in their storage type
@@ -41,6 +45,10 @@
  *  - SWA window: the W keys p-W+1 .. p.
  *  - Gate: sigmoid(x) = 1 / (1 + exp(-x)), one scalar per (token, head)
  *    (gate_dim 1) or one per output element (gate_dim = v_dim).
+ *  - Sinks (PAS): given per head as expanded K/V rows sink_k [n_sink,H,Dqk],
+ *    sink_v [n_sink,H,Dv], shared by the whole batch; they carry no position,
+ *    so no causal mask applies to them; the softmax runs over the sinks and
+ *    the selected (or windowed) keys together.
  */
 #include <math.h>
 #include <stdint.h>
@@ -167,19 +175,32 @@ void oracle_topk(const float *scores, int64_t R, int64_t T, int k,
 static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /*
- * Softmax attention of one (b, s, h) query over the keys marked in sel[0..T),
- * followed by the gate. Shared by the DSA and SWA functions below (both are
- * the same masked softmax, they differ only in which keys are marked).
+ * Softmax attention of one (b, s, h) query over the keys marked in sel[0..T)
+ * and the n_sink sink rows, followed by the gate. Shared by the DSA and SWA
+ * functions below (both are the same masked softmax, they differ only in
+ * which keys are marked).
  *   qrow [Dqk] at q + qoff; key t row at kc + ((b*T + t)*H + h)*Dqk, likewise
- *   vc with Dv. o [Dv] receives the result.
+ *   vc with Dv; sink r at sk + (r*H + h)*Dqk and sv + (r*H + h)*Dv.
+ *   logit has room for T + n_sink values. o [Dv] receives the result.
  */
 static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
-                               const void *vc, int dtype, int64_t b, int64_t T,
+                               const void *vc, const void *sk, const void *sv,
+                               int n_sink, int dtype, int64_t b, int64_t T,
                                int H, int h, int Dqk, int Dv, double sm_scale,
                                const unsigned char *sel, double *logit,
                                double *o) {
   double mx = -INFINITY;
   int64_t nsel = 0;
+  double *slog = logit + T; /* sink logits */
+  for (int r = 0; r < n_sink; ++r) {
+    double dot = 0.0;
+    for (int d = 0; d < Dqk; ++d)
+      dot += rd(q, dtype, qoff + d) *
+             rd(sk, dtype, ((int64_t)r * H + h) * (int64_t)Dqk + d);
+    slog[r] = sm_scale * dot;
+    if (slog[r] > mx) mx = slog[r];
+    ++nsel;
+  }
   for (int64_t t = 0; t < T; ++t) {
     if (!sel[t]) continue;
     double dot = 0.0;
@@ -191,8 +212,14 @@ static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
     ++nsel;
   }
   for (int d = 0; d < Dv; ++d) o[d] = 0.0;
-  if (nsel == 0) return; /* no visible selected key: output 0 */
+  if (nsel == 0) return; /* no visible selected key and no sink: output 0 */
   double den = 0.0;
+  for (int r = 0; r < n_sink; ++r) {
+    double e = exp(slog[r] - mx);
+    den += e;
+    for (int d = 0; d < Dv; ++d)
+      o[d] += e * rd(sv, dtype, ((int64_t)r * H + h) * (int64_t)Dv + d);
+  }
   for (int64_t t = 0; t < T; ++t) {
     if (!sel[t]) continue;
     double e = exp(logit[t] - mx);
@@ -227,16 +254,18 @@ static void apply_gate(const void *gate, int dtype, int gate_dim, int64_t bs,
  *   indices [B,S,topk] int32, gate [B,S,H] or [B,S,H,Dv] or NULL
  *   out [B,S,H,Dv] double
  */
-void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
-                        const int32_t *indices, const void *gate, int dtype,
-                        int B, int S, int T, int past_len, int H, int Dqk,
-                        int Dv, int topk, double sm_scale, int gate_dim,
-                        double *out) {
+void oracle_sparse_attn_pas(const void *q, const void *k_cache,
+                            const void *v_cache, const void *sink_k,
+                            const void *sink_v, int n_sink,
+                            const int32_t *indices, const void *gate,
+                            int dtype, int B, int S, int T, int past_len,
+                            int H, int Dqk, int Dv, int topk, double sm_scale,
+                            int gate_dim, double *out) {
   int64_t n = (int64_t)B * S * H;
 #pragma omp parallel
   {
     unsigned char *sel = (unsigned char *)malloc((size_t)T);
-    double *logit = (double *)malloc(sizeof(double) * (size_t)T);
+    double *logit = (double *)malloc(sizeof(double) * ((size_t)T + n_sink));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t e = 0; e < n; ++e) {
       int h = (int)(e % H);
@@ -251,13 +280,23 @@ void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
         if (t >= 0 && t <= p && t < T) sel[t] = 1;
       }
       double *o = out + e * Dv;
-      masked_softmax_row(q, e * Dqk, k_cache, v_cache, dtype, b, T, H, h, Dqk,
-                         Dv, sm_scale, sel, logit, o);
+      masked_softmax_row(q, e * Dqk, k_cache, v_cache, sink_k, sink_v, n_sink,
+                         dtype, b, T, H, h, Dqk, Dv, sm_scale, sel, logit, o);
       apply_gate(gate, dtype, gate_dim, bs, H, h, Dv, o);
     }
     free(logit);
     free(sel);
   }
+}
+
+void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *indices, const void *gate, int dtype,
+                        int B, int S, int T, int past_len, int H, int Dqk,
+                        int Dv, int topk, double sm_scale, int gate_dim,
+                        double *out) {
+  oracle_sparse_attn_pas(q, k_cache, v_cache, NULL, NULL, 0, indices, gate,
+                         dtype, B, S, T, past_len, H, Dqk, Dv, topk, sm_scale,
+                         gate_dim, out);
 }
 
 /*
@@ -268,15 +307,18 @@ void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
  *   q [B,S,H,Dqk], k_buf [B,T_buf,H,Dqk], v_buf [B,T_buf,H,Dv], gate as above
  *   out [B,S,H,Dv] double
  */
-void oracle_swa_attn(const void *q, const void *k_buf, const void *v_buf,
-                     const void *gate, int dtype, int B, int S, int T_buf,
-                     int past_len, int kv_offset, int H, int Dqk, int Dv,
-                     int window, double sm_scale, int gate_dim, double *out) {
+void oracle_swa_attn_pas(const void *q, const void *k_buf, const void *v_buf,
+                         const void *sink_k, const void *sink_v, int n_sink,
+                         const void *gate, int dtype, int B, int S, int T_buf,
+                         int past_len, int kv_offset, int H, int Dqk, int Dv,
+                         int window, double sm_scale, int gate_dim,
+                         double *out) {
   int64_t n = (int64_t)B * S * H;
 #pragma omp parallel
   {
     unsigned char *sel = (unsigned char *)malloc((size_t)T_buf);
-    double *logit = (double *)malloc(sizeof(double) * (size_t)T_buf);
+    double *logit =
+        (double *)malloc(sizeof(double) * ((size_t)T_buf + n_sink));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t e = 0; e < n; ++e) {
       int h = (int)(e % H);
@@ -291,11 +333,21 @@ void oracle_swa_attn(const void *q, const void *k_buf, const void *v_buf,
         sel[j] = (t >= lo && t <= p) ? 1 : 0;
       }
       double *o = out + e * Dv;
-      masked_softmax_row(q, e * Dqk, k_buf, v_buf, dtype, b, T_buf, H, h, Dqk,
-                         Dv, sm_scale, sel, logit, o);
+      masked_softmax_row(q, e * Dqk, k_buf, v_buf, sink_k, sink_v, n_sink,
+                         dtype, b, T_buf, H, h, Dqk, Dv, sm_scale, sel, logit,
+                         o);
       apply_gate(gate, dtype, gate_dim, bs, H, h, Dv, o);
     }
     free(logit);
     free(sel);
   }
+}
+
+void oracle_swa_attn(const void *q, const void *k_buf, const void *v_buf,
+                     const void *gate, int dtype, int B, int S, int T_buf,
+                     int past_len, int kv_offset, int H, int Dqk, int Dv,
+                     int window, double sm_scale, int gate_dim, double *out) {
+  oracle_swa_attn_pas(q, k_buf, v_buf, NULL, NULL, 0, gate, dtype, B, S, T_buf,
+                      past_len, kv_offset, H, Dqk, Dv, window, sm_scale,
+                      gate_dim, out);
 }

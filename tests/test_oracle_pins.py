@@ -358,3 +358,79 @@ def test_swa_equals_sparse_attn_with_window_indices():
     a = oracle.swa_attn(q, kc, vc, g, 0, 0, W, 4, 4)
     b = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------- attention sinks (PAS)
+def _with_sinks_prepended(kc, vc, sk, sv):
+    """Caches with the sink rows placed in front of every sequence."""
+    B = kc.shape[0]
+    ks = np.broadcast_to(sk[None], (B,) + sk.shape)
+    vs = np.broadcast_to(sv[None], (B,) + sv.shape)
+    return np.concatenate([ks, kc], axis=1), np.concatenate([vs, vc], axis=1)
+
+
+@pytest.mark.parametrize("n_sink", [1, 3])
+def test_sinks_match_sdpa_with_sink_columns(n_sink):
+    # softmax over sinks and selected keys = SDPA over [sinks; cache] with a
+    # mask that always admits the sink columns
+    B, S, P, H, nope, rope, Dv, k = 2, 7, 3, 3, 6, 2, 5, 4
+    T = P + S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, nope + rope, Dv)
+    sk, sv = f32(n_sink, H, nope + rope), f32(n_sink, H, Dv)
+    rng = np.random.default_rng(7)
+    idx = np.full((B, S, k), -1, np.int32)
+    mask = np.zeros((B, S, n_sink + T), bool)
+    mask[:, :, :n_sink] = True
+    for b in range(B):
+        for s in range(S):
+            pick = rng.permutation(P + s + 1)[: min(k, P + s + 1)]
+            idx[b, s, : len(pick)] = pick
+            mask[b, s, n_sink + pick] = True
+    got = oracle.sparse_attn(q, kc, vc, idx, g, P, nope, rope, gate_dim=1, sink_k=sk, sink_v=sv)
+    k2, v2 = _with_sinks_prepended(kc, vc, sk, sv)
+    ref = sdpa_masked(q, k2, v2, mask, (nope + rope) ** -0.5) * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sinks_only_when_nothing_is_selected():
+    # an empty selection leaves the sinks: one sink gives its V row times the gate
+    B, S, H, Dqk, Dv = 1, 4, 2, 8, 6
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    sk, sv = f32(1, H, Dqk), f32(1, H, Dv)
+    idx = np.full((B, S, 3), -1, np.int32)
+    got = oracle.sparse_attn(q, kc, vc, idx, g, 0, 4, 4, sink_k=sk, sink_v=sv)
+    ref = sv[0].astype(np.float64)[None, None] * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, np.broadcast_to(ref, got.shape), rtol=1e-14)
+
+
+def test_sinks_weight_limits():
+    # a sink aligned with q at a huge scale takes all the weight; one pointing
+    # away takes none (output equals the sink-free result)
+    B, S, H, Dqk, Dv = 1, 5, 2, 8, 4
+    q, kc, vc, g = _attn_inputs(B, S, S, H, Dqk, Dv)
+    q[:] = np.abs(q[:1, :1])  # the same positive query everywhere
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (B, S, S)).copy()
+    sv = f32(1, H, Dv)
+    base = oracle.sparse_attn(q, kc, vc, idx, None, 0, 4, 4)
+    away = oracle.sparse_attn(q, kc, vc, idx, None, 0, 4, 4,
+                              sink_k=-1e4 * np.abs(q[0, :1]), sink_v=sv)
+    np.testing.assert_allclose(away, base, rtol=1e-12, atol=1e-14)
+    toward = oracle.sparse_attn(q, kc, vc, idx, None, 0, 4, 4,
+                                sink_k=1e4 * np.abs(q[0, :1]), sink_v=sv)
+    np.testing.assert_allclose(toward, np.broadcast_to(sv[0].astype(np.float64), toward.shape),
+                               rtol=1e-12)
+
+
+def test_swa_sinks_match_sdpa_band_plus_sinks():
+    B, S, P, H, Dqk, Dv, W, n_sink = 1, 6, 4, 2, 8, 3, 3, 2
+    T = P + S
+    q, kc, vc, g = _attn_inputs(B, S, T, H, Dqk, Dv)
+    sk, sv = f32(n_sink, H, Dqk), f32(n_sink, H, Dv)
+    p = P + np.arange(S)[:, None]
+    t = np.arange(T)[None, :]
+    band = (t <= p) & (t > p - W)
+    mask = np.concatenate([np.ones((S, n_sink), bool), band], axis=1)[None]
+    got = oracle.swa_attn(q, kc, vc, g, P, 0, W, 4, 4, gate_dim=1, sink_k=sk, sink_v=sv)
+    k2, v2 = _with_sinks_prepended(kc, vc, sk, sv)
+    ref = sdpa_masked(q, k2, v2, mask, Dqk ** -0.5) * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
