@@ -13,7 +13,8 @@
  *  [DSV2]    DeepSeek-V2 attention constructor parameters: items 4-6
  *            (qk_nope_head_dim, qk_rope_head_dim, v_head_dim).
  *  [PANGU]   openPangu-2.0 technical-report walkthrough: §3.2 (DSA-SWA-SWA,
- *            window 512), §3.3 (lightning indexer, fixed top-K), §3.5 Table 1.
+ *            window 512), §3.3 (lightning indexer, fixed top-K), §3.4 (PAS
+ *            attention sinks), §3.5 Table 1.
  *
  * Conventions shared by every entry point
  *  - Dtypes: DSA_F32 or DSA_BF16 applies to every floating input and to the
@@ -69,6 +70,7 @@ extern "C" {
 /* limits */
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_HEAD_DIM 256
+#define DSA_MAX_SINKS 256
 
 /*
  * Lightning-indexer scores with causal mask ([AXK2] §1: per-head dot products
@@ -173,6 +175,46 @@ int swa_attn(const void* q, const void* k_buf, const void* v_buf, const void* ga
              int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
              int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Parametric attention sinks ([PANGU] §3.4: every layer learns 128 key-value
+ * pairs that absorb redundant attention; at inference they are a fixed set of
+ * virtual KV entries, in DSA and SWA layers alike, at negligible cost).
+ * The *_pas entry points are the three attention calls above with n_sink
+ * extra rows that every query attends to besides its selected (or windowed)
+ * keys: the softmax runs over the sinks and those keys together. Sinks carry
+ * no position (no causal mask applies to them) and are shared by every
+ * sequence of the batch:
+ *   sink_k [n_sink,H,Dqk], sink_v [n_sink,H,Dv]   same dtype and head layout
+ *                                                 as the caches
+ *   0 <= n_sink <= DSA_MAX_SINKS; with n_sink = 0 the pointers may be NULL
+ *   and each call equals its plain counterpart.
+ * All other arguments, the workspace rule and the errors are those of the
+ * plain entry point (with the *_pas_workspace_size functions). An empty
+ * selection with n_sink > 0 attends to the sinks alone.
+ */
+size_t dsa_sparse_attn_prefill_pas_workspace_size(int B, int S, int T, int H, int qk_dim,
+                                                  int v_dim, int topk, int n_sink, int dtype);
+int dsa_sparse_attn_prefill_pas(const void* q, const void* k_cache, const void* v_cache,
+                                const void* sink_k, const void* sink_v, int n_sink,
+                                const int32_t* indices, const void* gate, void* out, int B, int S,
+                                int T, int past_len, int H, int qk_nope_dim, int qk_rope_dim,
+                                int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t dsa_sparse_attn_decode_pas_workspace_size(int B, int H, int v_dim, int topk, int n_sink);
+int dsa_sparse_attn_decode_pas(const void* q, const void* k_cache, const void* v_cache,
+                               const void* sink_k, const void* sink_v, int n_sink,
+                               const int32_t* indices, const void* gate, void* out, int B, int T,
+                               int H, int qk_nope_dim, int qk_rope_dim, int v_dim, int topk,
+                               float sm_scale, int gate_dim, int dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t swa_attn_pas_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                                   int n_sink, int dtype);
+int swa_attn_pas(const void* q, const void* k_buf, const void* v_buf, const void* sink_k,
+                 const void* sink_v, int n_sink, const void* gate, void* out, int B, int S,
+                 int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim, int qk_rope_dim,
+                 int v_dim, int window, float sm_scale, int gate_dim, int dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
 
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);

@@ -31,7 +31,11 @@ _EXPORTS = [
     "dsa_sparse_attn_prefill_workspace_size", "dsa_sparse_attn_prefill",
     "dsa_sparse_attn_decode_workspace_size", "dsa_sparse_attn_decode",
     "swa_attn_workspace_size", "swa_attn", "dsa_status_string", "dsa_last_error",
+    "dsa_sparse_attn_prefill_pas_workspace_size", "dsa_sparse_attn_prefill_pas",
+    "dsa_sparse_attn_decode_pas_workspace_size", "dsa_sparse_attn_decode_pas",
+    "swa_attn_pas_workspace_size", "swa_attn_pas",
 ]
+MAX_SINKS = 256
 
 
 class DsaError(RuntimeError):
@@ -69,8 +73,23 @@ def lib():
         L.swa_attn_workspace_size.restype = sz
         L.swa_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                i32, f32, i32, i32, vp, sz, vp]
+        L.dsa_sparse_attn_prefill_pas_workspace_size.argtypes = [i32] * 9
+        L.dsa_sparse_attn_prefill_pas_workspace_size.restype = sz
+        L.dsa_sparse_attn_prefill_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32,
+                                                  i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                  i32, vp, sz, vp]
+        L.dsa_sparse_attn_decode_pas_workspace_size.argtypes = [i32] * 5
+        L.dsa_sparse_attn_decode_pas_workspace_size.restype = sz
+        L.dsa_sparse_attn_decode_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32,
+                                                 i32, i32, i32, i32, i32, f32, i32, i32, vp, sz,
+                                                 vp]
+        L.swa_attn_pas_workspace_size.argtypes = [i32] * 8
+        L.swa_attn_pas_workspace_size.restype = sz
+        L.swa_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
         for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
-                   "dsa_sparse_attn_decode", "swa_attn"):
+                   "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
+                   "dsa_sparse_attn_decode_pas", "swa_attn_pas"):
             getattr(L, fn).restype = i32
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -221,6 +240,88 @@ def swa_attn(q, k_buf, v_buf, gate, out, past_len: int, kv_offset: int, window: 
         _ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate), _ptr(out), B, S, T_buf, past_len,
         kv_offset, H, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale, _gate_dim(gate, Dv), dt,
         _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def _n_sink(sink_k, sink_v, H, Dqk, Dv) -> int:
+    """Sink rows [n,H,Dqk] / [n,H,Dv] on the GPU, same dtype as q."""
+    n = sink_k.shape[0]
+    if tuple(sink_k.shape) != (n, H, Dqk) or tuple(sink_v.shape) != (n, H, Dv):
+        raise ValueError(f"sink_k {tuple(sink_k.shape)} / sink_v {tuple(sink_v.shape)} do not "
+                         f"match [n,{H},{Dqk}] / [n,{H},{Dv}]")
+    return n
+
+
+def dsa_sparse_attn_prefill_pas_workspace_size(B, S, T, H, qk_dim, v_dim, topk, n_sink,
+                                               dtype) -> int:
+    return int(lib().dsa_sparse_attn_prefill_pas_workspace_size(B, S, T, H, qk_dim, v_dim, topk,
+                                                                n_sink, dtype))
+
+
+def dsa_sparse_attn_prefill_pas(q, k_cache, v_cache, sink_k, sink_v, indices, gate, out,
+                                past_len: int, qk_nope_dim: int, qk_rope_dim: int,
+                                sm_scale: float | None = None, workspace=None, stream=None):
+    B, S, H, Dqk = q.shape
+    T, Dv = k_cache.shape[1], v_cache.shape[3]
+    topk = indices.shape[-1]
+    ns = _n_sink(sink_k, sink_v, H, Dqk, Dv)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    dt = _dtype(q)
+    if workspace is None:
+        workspace = _workspace(
+            dsa_sparse_attn_prefill_pas_workspace_size(B, S, T, H, Dqk, Dv, topk, ns, dt), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_attn_prefill_pas", lib().dsa_sparse_attn_prefill_pas(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sink_k), _ptr(sink_v), ns, _ptr(indices),
+        _ptr(gate), _ptr(out), B, S, T, past_len, H, qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale,
+        _gate_dim(gate, Dv), dt, _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def dsa_sparse_attn_decode_pas_workspace_size(B, H, v_dim, topk, n_sink) -> int:
+    return int(lib().dsa_sparse_attn_decode_pas_workspace_size(B, H, v_dim, topk, n_sink))
+
+
+def dsa_sparse_attn_decode_pas(q, k_cache, v_cache, sink_k, sink_v, indices, gate, out,
+                               qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+                               workspace=None, stream=None):
+    B, _, H, Dqk = q.shape
+    T, Dv = k_cache.shape[1], v_cache.shape[3]
+    topk = indices.shape[-1]
+    ns = _n_sink(sink_k, sink_v, H, Dqk, Dv)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    if workspace is None:
+        workspace = _workspace(dsa_sparse_attn_decode_pas_workspace_size(B, H, Dv, topk, ns), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_attn_decode_pas", lib().dsa_sparse_attn_decode_pas(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sink_k), _ptr(sink_v), ns, _ptr(indices),
+        _ptr(gate), _ptr(out), B, T, H, qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale,
+        _gate_dim(gate, Dv), _dtype(q), _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def swa_attn_pas_workspace_size(B, S, H, qk_dim, v_dim, window, n_sink, dtype) -> int:
+    return int(lib().swa_attn_pas_workspace_size(B, S, H, qk_dim, v_dim, window, n_sink, dtype))
+
+
+def swa_attn_pas(q, k_buf, v_buf, sink_k, sink_v, gate, out, past_len: int, kv_offset: int,
+                 window: int, qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+                 workspace=None, stream=None):
+    B, S, H, Dqk = q.shape
+    T_buf, Dv = k_buf.shape[1], v_buf.shape[3]
+    ns = _n_sink(sink_k, sink_v, H, Dqk, Dv)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    dt = _dtype(q)
+    if workspace is None:
+        workspace = _workspace(swa_attn_pas_workspace_size(B, S, H, Dqk, Dv, window, ns, dt), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("swa_attn_pas", lib().swa_attn_pas(
+        _ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(sink_k), _ptr(sink_v), ns, _ptr(gate), _ptr(out),
+        B, S, T_buf, past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale,
+        _gate_dim(gate, Dv), dt, _ptr(workspace), nbytes, _stream(stream)))
     return out
 
 

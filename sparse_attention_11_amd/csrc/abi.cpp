@@ -66,15 +66,130 @@ int check_ws(const char* fn, void* ws, size_t have, size_t need) {
   return DSA_OK;
 }
 
-size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, int dtype) {
+// (the gather path lists the n_sink sinks as extra entries; the MFMA path
+// runs them as extra key blocks and needs no more workspace)
+size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, int dtype,
+                  int n_sink) {
   if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim))
     return dsa::prefill_mfma_workspace_bytes(B, S, T, H, v_dim);
-  return dsa::gather_workspace_bytes(B * S, H, v_dim, topk);
+  return dsa::gather_workspace_bytes(B * S, H, v_dim, topk + n_sink);
 }
 
-size_t swa_ws(int B, int S, int H, int qk_dim, int v_dim, int window, int dtype) {
+size_t swa_ws(int B, int S, int H, int qk_dim, int v_dim, int window, int dtype, int n_sink) {
   if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return 0;
-  return dsa::gather_workspace_bytes(B * S, H, v_dim, window);
+  return dsa::gather_workspace_bytes(B * S, H, v_dim, window + n_sink);
+}
+
+int check_sinks(const char* fn, const void* sink_k, const void* sink_v, int n_sink) {
+  if (n_sink < 0 || n_sink > DSA_MAX_SINKS)
+    return fail(DSA_ERR_INVALID_ARG, "%s: n_sink must be in [0, %d] (got %d)", fn, DSA_MAX_SINKS,
+                n_sink);
+  if (n_sink > 0 && (!sink_k || !sink_v))
+    return fail(DSA_ERR_INVALID_ARG, "%s: sink_k / sink_v is NULL with n_sink %d", fn, n_sink);
+  return DSA_OK;
+}
+
+int prefill_impl(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                 const void* sink_k, const void* sink_v, int n_sink, const int32_t* indices,
+                 const void* gate, void* out, int B, int S, int T, int past_len, int H,
+                 int qk_nope_dim, int qk_rope_dim, int v_dim, int topk, float sm_scale,
+                 int gate_dim, int dtype, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  g_err.clear();
+  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, S, T, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if ((st = check_sinks(fn, sink_k, sink_v, n_sink))) return st;
+  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
+  if (past_len < 0 || (long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: need 0 <= past_len and past_len + S <= T", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  const int dqk = qk_nope_dim + qk_rope_dim;
+  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
+  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
+  st = check_ws(fn, workspace, workspace_bytes,
+                prefill_ws(B, S, T, H, dqk, v_dim, topk, dtype, n_sink));
+  if (st) return st;
+  hipError_t e;
+  if (mfma)
+    e = dsa::launch_prefill_mfma(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate, out,
+                                 B, S, T, past_len, 0, H, dqk, v_dim, topk, 0, sm_scale, gate_dim,
+                                 workspace, stream);
+  else
+    e = dsa::launch_gather(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate, out, B, S,
+                           T, past_len, 0, H, dqk, v_dim, topk, 0, sm_scale, gate_dim, dtype,
+                           workspace, stream);
+  return hip_status(e, fn);
+}
+
+int decode_impl(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                const void* sink_k, const void* sink_v, int n_sink, const int32_t* indices,
+                const void* gate, void* out, int B, int T, int H, int qk_nope_dim,
+                int qk_rope_dim, int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, 1, T, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if ((st = check_sinks(fn, sink_k, sink_v, n_sink))) return st;
+  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  st = check_ws(fn, workspace, workspace_bytes,
+                dsa::gather_workspace_bytes(B, H, v_dim, topk + n_sink));
+  if (st) return st;
+  return hip_status(dsa::launch_gather(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate,
+                                       out, B, 1, T, T - 1, 0, H, qk_nope_dim + qk_rope_dim, v_dim,
+                                       topk, 0, sm_scale, gate_dim, dtype, workspace, stream),
+                    fn);
+}
+
+int swa_impl(const char* fn, const void* q, const void* k_buf, const void* v_buf,
+             const void* sink_k, const void* sink_v, int n_sink, const void* gate, void* out,
+             int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
+             int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  int st = check_attn(fn, q, k_buf, v_buf, gate, out, B, S, T_buf, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if ((st = check_sinks(fn, sink_k, sink_v, n_sink))) return st;
+  if (window < 1) return fail(DSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
+  if (past_len < 0 || kv_offset < 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: past_len and kv_offset must be >= 0", fn);
+  const long long lim = std::max(0LL, (long long)past_len - window + 1);
+  if (kv_offset > lim)
+    return fail(DSA_ERR_INVALID_ARG,
+                "%s: kv_offset %d > max(0, past_len - window + 1) = %lld (window not in buffer)",
+                fn, kv_offset, lim);
+  if ((long long)T_buf != (long long)past_len + S - kv_offset)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T_buf (%d) must equal past_len + S - kv_offset (%lld)",
+                fn, T_buf, (long long)past_len + S - kv_offset);
+  const int dqk = qk_nope_dim + qk_rope_dim;
+  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
+  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
+  st = check_ws(fn, workspace, workspace_bytes,
+                swa_ws(B, S, H, dqk, v_dim, window, dtype, n_sink));
+  if (st) return st;
+  hipError_t e;
+  if (mfma)
+    e = dsa::launch_prefill_mfma(q, k_buf, v_buf, sink_k, sink_v, n_sink, nullptr, gate, out, B,
+                                 S, T_buf, past_len, kv_offset, H, dqk, v_dim, 0, window,
+                                 sm_scale, gate_dim, nullptr, stream);
+  else
+    e = dsa::launch_gather(q, k_buf, v_buf, sink_k, sink_v, n_sink, nullptr, gate, out, B, S,
+                           T_buf, past_len, kv_offset, H, dqk, v_dim, 0, window, sm_scale,
+                           gate_dim, dtype, workspace, stream);
+  return hip_status(e, fn);
 }
 
 }  // namespace
@@ -142,8 +257,14 @@ int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int top
 
 size_t dsa_sparse_attn_prefill_workspace_size(int B, int S, int T, int H, int qk_dim, int v_dim,
                                               int topk, int dtype) {
-  if (B < 1 || S < 1 || T < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || topk < 1) return 0;
-  return prefill_ws(B, S, T, H, qk_dim, v_dim, topk, dtype);
+  return dsa_sparse_attn_prefill_pas_workspace_size(B, S, T, H, qk_dim, v_dim, topk, 0, dtype);
+}
+
+size_t dsa_sparse_attn_prefill_pas_workspace_size(int B, int S, int T, int H, int qk_dim,
+                                                  int v_dim, int topk, int n_sink, int dtype) {
+  if (B < 1 || S < 1 || T < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || topk < 1 || n_sink < 0)
+    return 0;
+  return prefill_ws(B, S, T, H, qk_dim, v_dim, topk, dtype, n_sink);
 }
 
 int dsa_sparse_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
@@ -151,39 +272,29 @@ int dsa_sparse_attn_prefill(const void* q, const void* k_cache, const void* v_ca
                             int T, int past_len, int H, int qk_nope_dim, int qk_rope_dim,
                             int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "dsa_sparse_attn_prefill";
-  g_err.clear();
-  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, S, T, H, qk_nope_dim, qk_rope_dim,
-                      v_dim, sm_scale, gate_dim, dtype);
-  if (st) return st;
-  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
-  if (past_len < 0 || (long long)past_len + S > T)
-    return fail(DSA_ERR_INVALID_ARG, "%s: need 0 <= past_len and past_len + S <= T", fn);
-  if (topk < 1 || topk > T)
-    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
-  if (topk > DSA_MAX_TOPK)
-    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
-  const int dqk = qk_nope_dim + qk_rope_dim;
-  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
-  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
-  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
-    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
-  st = check_ws(fn, workspace, workspace_bytes,
-                prefill_ws(B, S, T, H, dqk, v_dim, topk, dtype));
-  if (st) return st;
-  hipError_t e;
-  if (mfma)
-    e = dsa::launch_prefill_mfma(q, k_cache, v_cache, indices, gate, out, B, S, T, past_len, 0, H,
-                                 dqk, v_dim, topk, 0, sm_scale, gate_dim, workspace, stream);
-  else
-    e = dsa::launch_gather(q, k_cache, v_cache, indices, gate, out, B, S, T, past_len, 0, H, dqk,
-                           v_dim, topk, 0, sm_scale, gate_dim, dtype, workspace, stream);
-  return hip_status(e, fn);
+  return prefill_impl("dsa_sparse_attn_prefill", q, k_cache, v_cache, nullptr, nullptr, 0, indices,
+                      gate, out, B, S, T, past_len, H, qk_nope_dim, qk_rope_dim, v_dim, topk,
+                      sm_scale, gate_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_prefill_pas(const void* q, const void* k_cache, const void* v_cache,
+                                const void* sink_k, const void* sink_v, int n_sink,
+                                const int32_t* indices, const void* gate, void* out, int B, int S,
+                                int T, int past_len, int H, int qk_nope_dim, int qk_rope_dim,
+                                int v_dim, int topk, float sm_scale, int gate_dim, int dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl("dsa_sparse_attn_prefill_pas", q, k_cache, v_cache, sink_k, sink_v, n_sink,
+                      indices, gate, out, B, S, T, past_len, H, qk_nope_dim, qk_rope_dim, v_dim,
+                      topk, sm_scale, gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t dsa_sparse_attn_decode_workspace_size(int B, int H, int v_dim, int topk) {
-  if (B < 1 || H < 1 || v_dim < 1 || topk < 1) return 0;
-  return dsa::gather_workspace_bytes(B, H, v_dim, topk);
+  return dsa_sparse_attn_decode_pas_workspace_size(B, H, v_dim, topk, 0);
+}
+
+size_t dsa_sparse_attn_decode_pas_workspace_size(int B, int H, int v_dim, int topk, int n_sink) {
+  if (B < 1 || H < 1 || v_dim < 1 || topk < 1 || n_sink < 0) return 0;
+  return dsa::gather_workspace_bytes(B, H, v_dim, topk + n_sink);
 }
 
 int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -191,66 +302,50 @@ int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            int H, int qk_nope_dim, int qk_rope_dim, int v_dim, int topk,
                            float sm_scale, int gate_dim, int dtype, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "dsa_sparse_attn_decode";
-  g_err.clear();
-  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, 1, T, H, qk_nope_dim, qk_rope_dim,
-                      v_dim, sm_scale, gate_dim, dtype);
-  if (st) return st;
-  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
-  if (topk < 1 || topk > T)
-    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
-  if (topk > DSA_MAX_TOPK)
-    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
-  st = check_ws(fn, workspace, workspace_bytes, dsa::gather_workspace_bytes(B, H, v_dim, topk));
-  if (st) return st;
-  return hip_status(dsa::launch_gather(q, k_cache, v_cache, indices, gate, out, B, 1, T, T - 1, 0,
-                                       H, qk_nope_dim + qk_rope_dim, v_dim, topk, 0, sm_scale,
-                                       gate_dim, dtype, workspace, stream),
-                    fn);
+  return decode_impl("dsa_sparse_attn_decode", q, k_cache, v_cache, nullptr, nullptr, 0, indices,
+                     gate, out, B, T, H, qk_nope_dim, qk_rope_dim, v_dim, topk, sm_scale,
+                     gate_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_decode_pas(const void* q, const void* k_cache, const void* v_cache,
+                               const void* sink_k, const void* sink_v, int n_sink,
+                               const int32_t* indices, const void* gate, void* out, int B, int T,
+                               int H, int qk_nope_dim, int qk_rope_dim, int v_dim, int topk,
+                               float sm_scale, int gate_dim, int dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl("dsa_sparse_attn_decode_pas", q, k_cache, v_cache, sink_k, sink_v, n_sink,
+                     indices, gate, out, B, T, H, qk_nope_dim, qk_rope_dim, v_dim, topk, sm_scale,
+                     gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t swa_attn_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
                                int dtype) {
-  if (B < 1 || S < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || window < 1) return 0;
-  return swa_ws(B, S, H, qk_dim, v_dim, window, dtype);
+  return swa_attn_pas_workspace_size(B, S, H, qk_dim, v_dim, window, 0, dtype);
+}
+
+size_t swa_attn_pas_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                                   int n_sink, int dtype) {
+  if (B < 1 || S < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || window < 1 || n_sink < 0) return 0;
+  return swa_ws(B, S, H, qk_dim, v_dim, window, dtype, n_sink);
 }
 
 int swa_attn(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,
              int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
              int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "swa_attn";
-  g_err.clear();
-  int st = check_attn(fn, q, k_buf, v_buf, gate, out, B, S, T_buf, H, qk_nope_dim, qk_rope_dim,
-                      v_dim, sm_scale, gate_dim, dtype);
-  if (st) return st;
-  if (window < 1) return fail(DSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
-  if (past_len < 0 || kv_offset < 0)
-    return fail(DSA_ERR_INVALID_ARG, "%s: past_len and kv_offset must be >= 0", fn);
-  const long long lim = std::max(0LL, (long long)past_len - window + 1);
-  if (kv_offset > lim)
-    return fail(DSA_ERR_INVALID_ARG,
-                "%s: kv_offset %d > max(0, past_len - window + 1) = %lld (window not in buffer)",
-                fn, kv_offset, lim);
-  if ((long long)T_buf != (long long)past_len + S - kv_offset)
-    return fail(DSA_ERR_INVALID_ARG, "%s: T_buf (%d) must equal past_len + S - kv_offset (%lld)",
-                fn, T_buf, (long long)past_len + S - kv_offset);
-  const int dqk = qk_nope_dim + qk_rope_dim;
-  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
-  if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
-  if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
-    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
-  st = check_ws(fn, workspace, workspace_bytes, swa_ws(B, S, H, dqk, v_dim, window, dtype));
-  if (st) return st;
-  hipError_t e;
-  if (mfma)
-    e = dsa::launch_prefill_mfma(q, k_buf, v_buf, nullptr, gate, out, B, S, T_buf, past_len,
-                                 kv_offset, H, dqk, v_dim, 0, window, sm_scale, gate_dim, nullptr,
-                                 stream);
-  else
-    e = dsa::launch_gather(q, k_buf, v_buf, nullptr, gate, out, B, S, T_buf, past_len, kv_offset,
-                           H, dqk, v_dim, 0, window, sm_scale, gate_dim, dtype, workspace, stream);
-  return hip_status(e, fn);
+  return swa_impl("swa_attn", q, k_buf, v_buf, nullptr, nullptr, 0, gate, out, B, S, T_buf,
+                  past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
+                  gate_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+int swa_attn_pas(const void* q, const void* k_buf, const void* v_buf, const void* sink_k,
+                 const void* sink_v, int n_sink, const void* gate, void* out, int B, int S,
+                 int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim, int qk_rope_dim,
+                 int v_dim, int window, float sm_scale, int gate_dim, int dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return swa_impl("swa_attn_pas", q, k_buf, v_buf, sink_k, sink_v, n_sink, gate, out, B, S, T_buf,
+                  past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
+                  gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

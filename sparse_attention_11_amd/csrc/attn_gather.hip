@@ -17,7 +17,9 @@
 // per step.
 //
 // The same kernels serve the fp32 path and sliding-window attention (the
-// window is an implicit list p, p-1, ..., p-W+1).
+// window is an implicit list p, p-1, ..., p-W+1). Attention sinks
+// (openPangu-2.0 page §3.4, PAS) are n_sink extra entries in front of the
+// list: entry r < n_sink is sink row r, visible to every query.
 #include <algorithm>
 
 #include "common.h"
@@ -57,6 +59,7 @@ struct Elem<1> {  // bf16
 template <int DT, int WIN, int KC, int VC>
 __global__ __launch_bounds__(256) void gather_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
+    const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
     const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
     int kv_offset, int H, int DQK, int DV, int nent, int per_split, int nsplit, int window,
     float scale_log2) {
@@ -77,6 +80,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
   const char* qb = (const char*)qv;
   const char* kb = (const char*)kv;
   const char* vb = (const char*)vv;
+  const char* skb = (const char*)skv;
+  const char* svb = (const char*)svv;
 
   float qf[KC][EP];
 #pragma unroll
@@ -99,14 +104,17 @@ __global__ __launch_bounds__(256) void gather_kernel(
 #pragma unroll
     for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
 
+  // entries 0 .. n_sink-1 are the sinks, n_sink .. nent-1 the list
   const int e0 = split * per_split;
   const int e1 = min(nent, e0 + per_split);
-  const int32_t* irow = idx + row * (int64_t)nent;
+  const int nlist = nent - n_sink;
+  const int32_t* irow = idx + row * (int64_t)nlist;
   const int64_t kvrow0 = (int64_t)b * Tbuf;
 
-  auto pos_of = [&](int ent) -> int {
-    if (WIN) return p - ent;
-    return (ent < e1) ? irow[ent] : -1;
+  auto pos_of = [&](int ent) -> int {  // (sink entries: unused)
+    const int le = ent - n_sink;
+    if (WIN) return p - le;
+    return (ent < e1 && le >= 0) ? irow[le] : -1;
   };
   int tn[kG];  // positions of the next group (index loads run one group ahead)
 #pragma unroll
@@ -115,21 +123,28 @@ __global__ __launch_bounds__(256) void gather_kernel(
   for (int base = e0; base < e1; base += kG) {
     int jrow[kG];
     bool ok[kG];
+    bool snk[kG];  // wave-uniform: entries are the same for every lane
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
       const int ent = base + g;
       const int t = tn[g];
       const int j = t - kv_offset;
+      snk[g] = ent < n_sink;
       ok[g] = (ent < e1) && t >= 0 && t <= p && j >= 0 && j < Tbuf;
-      if (WIN) ok[g] = ok[g] && ent < window;
-      jrow[g] = ok[g] ? j : 0;
+      if (WIN) ok[g] = ok[g] && ent - n_sink < window;
+      if (snk[g]) ok[g] = ent < e1;
+      jrow[g] = snk[g] ? ent : (ok[g] ? j : 0);
     }
     // all K and V chunks of the group in flight at once
     u32x4_t kr[kG][KC], vr[kG][VC];
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      const char* krow = kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
-      const char* vrow = vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
+      const char* krow =
+          snk[g] ? skb + (((int64_t)jrow[g] * H + hh) * (int64_t)DQK) * esz
+                 : kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
+      const char* vrow =
+          snk[g] ? svb + (((int64_t)jrow[g] * H + hh) * (int64_t)DV) * esz
+                 : vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const int c = sub + 8 * i;
@@ -312,22 +327,23 @@ size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries) {
   return (size_t)rows * pl.nsplit * H * (size_t)(Dv + 2) * sizeof(float);
 }
 
-hipError_t launch_gather(const void* q, const void* k, const void* v, const int32_t* indices,
+hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
+                         const void* sink_v, int n_sink, const int32_t* indices,
                          const void* gate, void* out, int B, int S, int T, int past_len,
                          int kv_offset, int H, int Dqk, int Dv, int topk, int window,
                          float sm_scale, int gate_dim, int dtype, void* workspace,
                          hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
-  const int nent = window > 0 ? window : topk;
+  const int nent = n_sink + (window > 0 ? window : topk);
   const Plan pl = make_plan(rows, H, nent);
   float* part = (float*)workspace;
   const dim3 grid((unsigned)(rows * pl.nsplit), (H + 31) / 32);
   if (rows * pl.nsplit > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float sl2 = sm_scale * DSA_LOG2E;
 #define DSA_GATHER(DT, WIN, KC, VC)                                                            \
-  hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC>), grid, dim3(256), 0, st, q, k, v, indices,  \
-                     part, S, T, past_len, kv_offset, H, Dqk, Dv, nent, pl.per_split, pl.nsplit,  \
-                     window, sl2)
+  hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC>), grid, dim3(256), 0, st, q, k, v, sink_k,  \
+                     sink_v, n_sink, indices, part, S, T, past_len, kv_offset, H, Dqk, Dv, nent, \
+                     pl.per_split, pl.nsplit, window, sl2)
 #define DSA_GATHER_VC(DT, WIN, KC)            \
   switch (vc) {                               \
     case 1: DSA_GATHER(DT, WIN, KC, 1); break; \

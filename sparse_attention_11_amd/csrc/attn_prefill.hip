@@ -144,7 +144,8 @@ __device__ __forceinline__ bool item_tile(int item, int nqt, int M, const SplitT
 template <int DQK, int DV, int MASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ sk,
+    const uint16_t* __restrict__ sv, int n_sink, const uint32_t* __restrict__ bm,
     const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ part,
     int S, int Tbuf, int P, int kv_offset, int H, int W32, int window, float scale_log2,
     int gate_dim, int nqt, int M, const SplitTable tab) {
@@ -186,6 +187,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int jlo = (int)((int64_t)tjlo + (int64_t)split * M * kBN);
   const int jhi = (int)std::min<int64_t>(tjhi, (int64_t)jlo + (int64_t)M * kBN - 1);
   const int64_t kvrow0 = (int64_t)b * Tbuf;
+  // Blocks of this item: first the attention-sink rows (split 0 only, every
+  // query sees all of them, no position), then the cache rows jlo .. jhi.
+  // Block bi < nsb holds sink rows 64 bi .. 64 bi + 63.
+  const int nsb = (split == 0) ? (n_sink + kBN - 1) / kBN : 0;
+  const int nblk = nsb + (jlo <= jhi ? (jhi - jlo) / kBN + 1 : 0);
 
   // ---- register prefetch of one key block. A K row of KCH 16-byte chunks is
   // covered by one or two power-of-two parts (24 = 16 + 8), so that a thread
@@ -206,10 +212,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const uint32_t vbo = 4 * vkg * vrowb + 16u * vdg;
   u32x4_t kpre[KLD];
   u32x4_t vpre[4];
-  auto load_block = [&](int jb) {
-    const int64_t rows = (int64_t)Tbuf - jb;  // rows of the buffer from jb on
-    const auto kr = make_rsrc(k + ((kvrow0 + jb) * H + h) * DQK, rows * rowb - (int64_t)h * DQK * 2);
-    const auto vr = make_rsrc(v + ((kvrow0 + jb) * H + h) * DV, rows * vrowb - (int64_t)h * DV * 2);
+  auto load_block = [&](int bi) {
+    // rows of the buffer (cache or sinks) from the block's first row on
+    const uint16_t *kp, *vp;
+    int64_t rows;
+    if (bi < nsb) {
+      kp = sk + ((int64_t)bi * kBN * H + h) * DQK;
+      vp = sv + ((int64_t)bi * kBN * H + h) * DV;
+      rows = n_sink - bi * kBN;
+    } else {
+      const int jb = jlo + (bi - nsb) * kBN;
+      kp = k + ((kvrow0 + jb) * H + h) * DQK;
+      vp = v + ((kvrow0 + jb) * H + h) * DV;
+      rows = (int64_t)Tbuf - jb;
+    }
+    const auto kr = make_rsrc(kp, rows * rowb - (int64_t)h * DQK * 2);
+    const auto vr = make_rsrc(vp, rows * vrowb - (int64_t)h * DV * 2);
 #pragma unroll
     for (int n = 0; n < N1; ++n) kpre[n] = buffer_load16(kr, kbo1 + n * R1 * rowb);
 #pragma unroll
@@ -256,30 +274,37 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   for (int d = 0; d < NDB; ++d) o[d] = zero16();
   const uint32_t* bmrow = bm + qrow * (int64_t)W32;
 
-  // selection-bitmap words of a block, loaded one block ahead like K and V
+  // selection-bitmap words of a block, loaded one block ahead like K and V;
+  // a sink block's words mark its rows below n_sink
   uint32_t nbits[2] = {0u, 0u};
-  auto load_bits = [&](int jb) {
-    if (MASK == 0) {
-      const int w0 = jb >> 5;
+  auto load_bits = [&](int bi) {
+    if (bi < nsb) {
+      const int nv = min(kBN, n_sink - bi * kBN);  // >= 1
+      nbits[0] = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+      nbits[1] = nv >= 64 ? 0xFFFFFFFFu : (nv > 32 ? (1u << (nv - 32)) - 1u : 0u);
+    } else if (MASK == 0) {
+      const int w0 = (jlo + (bi - nsb) * kBN) >> 5;
       nbits[0] = (w0 < W32) ? bmrow[w0] : 0u;
       nbits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
     }
   };
 
-  if (jlo <= jhi) {
-    load_block(jlo);
-    load_bits(jlo);
+  if (nblk > 0) {
+    load_block(0);
+    load_bits(0);
   }
-  for (int jb = jlo; jb <= jhi; jb += kBN) {
+  for (int bi = 0; bi < nblk; ++bi) {
     __syncthreads();  // every wave is done reading the previous block
     store_block();
     __syncthreads();
     const uint32_t bits[2] = {nbits[0], nbits[1]};
+    const bool sinkb = bi < nsb;
+    const int jb = jlo + (bi - nsb) * kBN;  // first cache row (cache blocks)
 
     // the next block's loads overlap this block's MFMA and softmax work
-    if (jb + kBN <= jhi) {
-      load_block(jb + kBN);
-      load_bits(jb + kBN);
+    if (bi + 1 < nblk) {
+      load_block(bi + 1);
+      load_bits(bi + 1);
     }
 
     // S^T for both 32-key halves, one masked online-softmax update over the
@@ -299,11 +324,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     float mx3[11];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t wbits = (MASK == 0) ? (bits[i] >> (4 * lh)) : 0u;
+      const uint32_t wbits = bits[i] >> (4 * lh);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x;
-        if (MASK == 0) {
+        if (MASK == 0 || sinkb) {
           x = keep_or_neg_inf(st[i][e], wbits, 8 * (e >> 2) + (e & 3));
         } else {
           const int jj = jb + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
@@ -522,6 +547,7 @@ SplitPlan make_split_plan(int B, int S, int T, int P, int H, int kv_offset, int 
 
 template <int DQK, int DV>
 hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* sk, const uint16_t* sv, int n_sink,
                        const uint32_t* bm, const uint16_t* gate, uint16_t* out, int B, int S,
                        int Tbuf, int P, int kv_offset, int H, int W32, int window,
                        float scale_log2, int gate_dim, float* part, hipStream_t st) {
@@ -529,11 +555,13 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (pl.items != pl.nqt && part == nullptr) return hipErrorInvalidValue;  // no partial buffer
   const dim3 grid(pl.items, H, B);
   if (window > 0)
-    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, bm, gate,
+    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, sk, sv, n_sink, bm,
+                       gate,
                        out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
                        pl.nqt, pl.M, pl.tab);
   else
-    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, bm, gate,
+    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, sk, sv, n_sink, bm,
+                       gate,
                        out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
                        pl.nqt, pl.M, pl.tab);
   hipError_t e = hipGetLastError();
@@ -565,7 +593,8 @@ size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv) {
   return bmb + (size_t)B * H * pl.items * kBQ * (Dv + 4) * sizeof(float);
 }
 
-hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* sink_k,
+                               const void* sink_v, int n_sink, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
                                int kv_offset, int H, int Dqk, int Dv, int topk, int window,
                                float sm_scale, int gate_dim, void* workspace, hipStream_t st) {
@@ -597,7 +626,8 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   uint16_t* oo = (uint16_t*)out;
 #define DSA_PREFILL_CASE(A, C)                                                                    \
   if (Dqk == A && Dv == C)                                                                        \
-    return launch_dims<A, C>(qq, kk, vv, bm, gg, oo, B, S, T, past_len, kv_offset, H, W32, window, \
+    return launch_dims<A, C>(qq, kk, vv, (const uint16_t*)sink_k, (const uint16_t*)sink_v, n_sink, \
+                             bm, gg, oo, B, S, T, past_len, kv_offset, H, W32, window,         \
                              sl2, gate_dim, part, st);
   DSA_PREFILL_CASE(64, 64)
   DSA_PREFILL_CASE(128, 64)

@@ -21,16 +21,21 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
 // (attn_prefill.hip). Requires bf16, Dqk % 16 == 0, Dv % 32 == 0.
 size_t bitmap_bytes(int B, int S, int T);
 size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv);
-hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* indices,
+// sink_k [n_sink,H,Dqk] / sink_v [n_sink,H,Dv]: attention sinks every query
+// attends to (n_sink may be 0, then the pointers are unused).
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* sink_k,
+                               const void* sink_v, int n_sink, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
                                int kv_offset, int H, int Dqk, int Dv, int topk, int window,
                                float sm_scale, int gate_dim, void* workspace, hipStream_t stream);
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv);
 
 // Split-K row-gather attention + merge (attn_gather.hip); any dtype, any S.
-// window > 0 selects the implicit window list, else `indices` is used.
+// window > 0 selects the implicit window list, else `indices` is used; the
+// n_sink sink rows are entries in front of that list.
 size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries);
-hipError_t launch_gather(const void* q, const void* k, const void* v, const int32_t* indices,
+hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
+                         const void* sink_v, int n_sink, const int32_t* indices,
                          const void* gate, void* out, int B, int S, int T, int past_len,
                          int kv_offset, int H, int Dqk, int Dv, int topk, int window,
                          float sm_scale, int gate_dim, int dtype, void* workspace,

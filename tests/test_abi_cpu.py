@@ -145,3 +145,56 @@ def decode(**kw):
 ])
 def test_decode_validation(kw, code):
     assert decode(**kw) == code
+
+
+# ---------------------------------------------------- attention sinks (PAS)
+def prefill_pas(**kw):
+    a = dict(q=P, k=P, v=P, sk=P, sv=P, ns=128, i=P, g=P, o=P, B=1, S=32, T=64, past=0, H=2,
+             nope=64, rope=64, v_dim=128, topk=16, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_sparse_attn_prefill_pas(
+        a["q"], a["k"], a["v"], a["sk"], a["sv"], a["ns"], a["i"], a["g"], a["o"], a["B"],
+        a["S"], a["T"], a["past"], a["H"], a["nope"], a["rope"], a["v_dim"], a["topk"], a["sc"],
+        a["gd"], a["dt"], a["ws"], a["nb"], None)
+
+
+def decode_pas(**kw):
+    a = dict(q=P, k=P, v=P, sk=P, sv=P, ns=128, i=P, g=P, o=P, B=2, T=100, H=2, nope=64, rope=64,
+             v_dim=128, topk=16, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_sparse_attn_decode_pas(
+        a["q"], a["k"], a["v"], a["sk"], a["sv"], a["ns"], a["i"], a["g"], a["o"], a["B"], a["T"],
+        a["H"], a["nope"], a["rope"], a["v_dim"], a["topk"], a["sc"], a["gd"], a["dt"], a["ws"],
+        a["nb"], None)
+
+
+def swa_pas(**kw):
+    a = dict(q=P, k=P, v=P, sk=P, sv=P, ns=128, g=P, o=P, B=1, S=10, Tb=10, past=0, off=0, H=2,
+             nope=64, rope=64, v_dim=128, W=4, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().swa_attn_pas(
+        a["q"], a["k"], a["v"], a["sk"], a["sv"], a["ns"], a["g"], a["o"], a["B"], a["S"], a["Tb"],
+        a["past"], a["off"], a["H"], a["nope"], a["rope"], a["v_dim"], a["W"], a["sc"], a["gd"],
+        a["dt"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("fn", [prefill_pas, decode_pas, swa_pas])
+@pytest.mark.parametrize("kw,code", [
+    (dict(sk=None), 1), (dict(sv=None), 1), (dict(ns=-1), 1), (dict(ns=257), 1),
+    (dict(ns=0, sk=None, sv=None, q=None), 1),  # no sinks: NULL sink pointers are fine
+])
+def test_sink_validation(fn, kw, code):
+    assert fn(**kw) == code
+
+
+def test_sink_workspace_sizes():
+    L = dsa.lib()
+    # MFMA path: sinks are extra key blocks and need no workspace of their own
+    assert (L.dsa_sparse_attn_prefill_pas_workspace_size(1, 4096, 4096, 20, 128, 128, 512, 128, 1)
+            == L.dsa_sparse_attn_prefill_workspace_size(1, 4096, 4096, 20, 128, 128, 512, 1))
+    assert L.swa_attn_pas_workspace_size(1, 4096, 32, 192, 128, 512, 128, 1) == 0
+    # gather path: sinks are extra entries (more splits may need more partial states)
+    assert (L.dsa_sparse_attn_decode_pas_workspace_size(8, 128, 128, 2048, 0)
+            == L.dsa_sparse_attn_decode_workspace_size(8, 128, 128, 2048))
+    assert (L.dsa_sparse_attn_decode_pas_workspace_size(1, 4, 128, 16, 128)
+            > L.dsa_sparse_attn_decode_workspace_size(1, 4, 128, 16))

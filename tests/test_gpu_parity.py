@@ -347,3 +347,88 @@ def test_chain_mla_s4k_end_to_end():
     got = from_dev(out)
     rows = np.nonzero(same)[0]
     _cmp_attn(got[0, rows], ref[0, rows], 2e-2, "chain mla-s4k")
+
+
+# ------------------------------------------------ attention sinks (PAS)
+def _sinks(H, nope, rope, Dv, n, seed, dt="bf16"):
+    Dqk = nope + rope
+    g = lambda shape, tid, sc: datagen.normal_host(shape, dt, seed, tid, sc)
+    return g((n, H, Dqk), 11, Dqk ** -0.25), g((n, H, Dv), 12, 1.0)
+
+
+# (B, S, P, H, nope, rope, Dv, topk, n_sink): sink counts that fill, half-fill and
+# overrun a 64-key block; the MFMA path (bf16, S >= 16) and the gather path
+PAS_PREFILL_CASES = [
+    (1, 200, 50, 3, 128, 64, 128, 64, 128), (2, 130, 100, 2, 64, 64, 128, 200, 1),
+    (1, 77, 300, 4, 32, 32, 64, 33, 100), (1, 300, 1800, 1, 128, 64, 128, 2048, 256),
+    (2, 8, 500, 5, 128, 64, 128, 128, 65), (1, 40, 30, 3, 32, 16, 32, 20, 7),
+]
+
+
+@pytest.mark.parametrize("B,S,P,H,nope,rope,Dv,k,n_sink", PAS_PREFILL_CASES)
+def test_prefill_with_sinks(B, S, P, H, nope, rope, Dv, k, n_sink):
+    dt = "f32" if (B, S) == (1, 40) else "bf16"
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=S + n_sink, dt=dt)
+    sk, sv = _sinks(H, nope, rope, Dv, n_sink, seed=n_sink, dt=dt)
+    idx = datagen.indices_host(0, B * S, S, P, k, seed=S + k).reshape(B, S, k)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.dsa_sparse_attn_prefill_pas(to_dev(hi["q"]), to_dev(hi["k"]), to_dev(hi["v"]), to_dev(sk),
+                                    to_dev(sv), to_dev(idx), to_dev(hi["gate"]), out, P, nope, rope)
+    _sync()
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], P, nope, rope,
+                             sink_k=sk, sink_v=sv)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2,
+              f"prefill+sinks {B, S, P, H, nope, rope, Dv, k, n_sink}")
+
+
+def test_prefill_sinks_only_when_selection_is_empty():
+    B, S, P, H, nope, rope, Dv, n_sink = 1, 130, 0, 2, 64, 64, 128, 70
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=5)
+    sk, sv = _sinks(H, nope, rope, Dv, n_sink, seed=6)
+    idx = np.full((B, S, 8), -1, np.int32)
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_prefill_pas(to_dev(hi["q"]), to_dev(hi["k"]), to_dev(hi["v"]), to_dev(sk),
+                                    to_dev(sv), to_dev(idx), to_dev(hi["gate"]), out, P, nope, rope)
+    _sync()
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], P, nope, rope,
+                             sink_k=sk, sink_v=sv)
+    _cmp_attn(from_dev(out), ref, 2e-2, "sinks only")
+
+
+@pytest.mark.parametrize("B,T,H,nope,rope,Dv,k,n_sink,dt", [
+    (3, 3000, 16, 128, 64, 128, 256, 128, "bf16"), (1, 5000, 8, 128, 64, 128, 2048, 200, "bf16"),
+    (2, 300, 4, 32, 16, 32, 64, 3, "f32"),
+])
+def test_decode_with_sinks(B, T, H, nope, rope, Dv, k, n_sink, dt):
+    P = T - 1
+    hi = _attn_case(B, 1, P, H, nope, rope, Dv, seed=T + n_sink, dt=dt)
+    sk, sv = _sinks(H, nope, rope, Dv, n_sink, seed=k, dt=dt)
+    idx = np.stack([datagen.indices_host(0, 1, 1, P, k, seed=T + b) for b in range(B)])
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, 1, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.dsa_sparse_attn_decode_pas(to_dev(hi["q"]), to_dev(hi["k"]), to_dev(hi["v"]), to_dev(sk),
+                                   to_dev(sv), to_dev(idx), to_dev(hi["gate"]), out, nope, rope)
+    _sync()
+    ref = oracle.sparse_attn(hi["q"], hi["k"], hi["v"], idx, hi["gate"], P, nope, rope,
+                             sink_k=sk, sink_v=sv)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"decode+sinks {B, T, k, n_sink}")
+
+
+@pytest.mark.parametrize("B,S,P,W,H,nope,rope,Dv,n_sink,dt", [
+    (1, 300, 700, 128, 2, 128, 64, 128, 128, "bf16"), (2, 200, 0, 64, 3, 64, 64, 128, 30, "bf16"),
+    (1, 1, 900, 512, 4, 128, 64, 128, 128, "bf16"), (1, 50, 20, 16, 2, 32, 16, 32, 5, "f32"),
+])
+def test_swa_with_sinks(B, S, P, W, H, nope, rope, Dv, n_sink, dt):
+    kv_off = max(0, P - W + 1)
+    full = _attn_case(B, S, P, H, nope, rope, Dv, seed=W + n_sink, dt=dt)
+    sk, sv = _sinks(H, nope, rope, Dv, n_sink, seed=W, dt=dt)
+    kb, vb = full["k"][:, kv_off:].copy(), full["v"][:, kv_off:].copy()
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.swa_attn_pas(to_dev(full["q"]), to_dev(kb), to_dev(vb), to_dev(sk), to_dev(sv),
+                     to_dev(full["gate"]), out, P, kv_off, W, nope, rope)
+    _sync()
+    ref = oracle.swa_attn(full["q"], kb, vb, full["gate"], P, kv_off, W, nope, rope,
+                          sink_k=sk, sink_v=sv)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"swa+sinks {B, S, P, W, n_sink}")
