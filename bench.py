@@ -7,6 +7,7 @@ inputs already resident in HBM:
   hybrid-512k        DSA chunk (indexer, top-k, attention) + 2 SWA chunk
                      layers, then one decode token through the DSA layer and
                      both SWA layers
+  *-pas              the same with 128 attention sinks per layer
 Every stage is a C-ABI call of libdsa.so; stage times come from HIP events
 recorded on the same stream the library launches on.
 
@@ -39,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla-s4k")
-    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k",
+    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -74,10 +75,14 @@ class Layer:
         self.scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
         self.idx = torch.empty(B, S, k, dtype=torch.int32, device=dev)
         self.out = E(B, S, H, Dv)
+        ns = wl.n_sink
+        if ns:  # attention sinks (one set per layer)
+            self.sk = gen(E(ns, H, Dqk), datagen.TID_SINK_K, wl.scale_k)
+            self.sv = gen(E(ns, H, Dv), datagen.TID_SINK_V, wl.scale_v)
         if S > 1:
-            nb = dsa.dsa_sparse_attn_prefill_workspace_size(B, S, T, H, Dqk, Dv, k, wl.dtype)
+            nb = dsa.dsa_sparse_attn_prefill_pas_workspace_size(B, S, T, H, Dqk, Dv, k, ns, wl.dtype)
         else:
-            nb = dsa.dsa_sparse_attn_decode_workspace_size(B, H, Dv, k)
+            nb = dsa.dsa_sparse_attn_decode_pas_workspace_size(B, H, Dv, k, ns)
         self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         self.tk_ws = torch.empty(max(dsa.dsa_topk_workspace_size(B, S, T, k), 1), dtype=torch.uint8,
                                  device=dev)
@@ -92,7 +97,7 @@ class Layer:
             self.sd = torch.empty(B, 1, T + 1, dtype=torch.float32, device=dev)
             self.idd = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
             self.od = E(B, 1, H, Dv)
-            self.wsd = torch.empty(dsa.dsa_sparse_attn_decode_workspace_size(B, H, Dv, k),
+            self.wsd = torch.empty(dsa.dsa_sparse_attn_decode_pas_workspace_size(B, H, Dv, k, ns),
                                    dtype=torch.uint8, device=dev)
             self.tk_wsd = torch.empty(max(dsa.dsa_topk_workspace_size(B, 1, T + 1, k), 1),
                                       dtype=torch.uint8, device=dev)
@@ -114,12 +119,38 @@ class Layer:
                     "o": E(B, S, H, Dv), "od": E(B, 1, H, Dv),
                     "off": off, "Tb": Tb, "offd": offd, "Tbd": Tbd,
                 }
-                nbw = dsa.swa_attn_workspace_size(B, S, H, Dqk, Dv, W, wl.dtype)
+                if ns:
+                    lay["sk"] = gen(E(ns, H, Dqk), tid(datagen.TID_SINK_K), wl.scale_k)
+                    lay["sv"] = gen(E(ns, H, Dv), tid(datagen.TID_SINK_V), wl.scale_v)
+                nbw = dsa.swa_attn_pas_workspace_size(B, S, H, Dqk, Dv, W, ns, wl.dtype)
                 lay["ws"] = torch.empty(max(nbw, 1), dtype=torch.uint8, device=dev)
-                lay["wsd"] = torch.empty(dsa.swa_attn_workspace_size(B, 1, H, Dqk, Dv, W, wl.dtype),
-                                         dtype=torch.uint8, device=dev)
+                lay["wsd"] = torch.empty(
+                    max(dsa.swa_attn_pas_workspace_size(B, 1, H, Dqk, Dv, W, ns, wl.dtype), 1),
+                    dtype=torch.uint8, device=dev)
                 self.swa.append(lay)
         torch.cuda.synchronize()
+
+    # attention calls with or without the layer's sinks
+    def _prefill(self, q, k, v, idx, g, o, P, ws):
+        if self.wl.n_sink:
+            return self.dsa.dsa_sparse_attn_prefill_pas(q, k, v, self.sk, self.sv, idx, g, o, P,
+                                                        self.wl.nope, self.wl.rope, workspace=ws)
+        return self.dsa.dsa_sparse_attn_prefill(q, k, v, idx, g, o, P, self.wl.nope, self.wl.rope,
+                                                workspace=ws)
+
+    def _decode(self, q, k, v, idx, g, o, ws):
+        if self.wl.n_sink:
+            return self.dsa.dsa_sparse_attn_decode_pas(q, k, v, self.sk, self.sv, idx, g, o,
+                                                       self.wl.nope, self.wl.rope, workspace=ws)
+        return self.dsa.dsa_sparse_attn_decode(q, k, v, idx, g, o, self.wl.nope, self.wl.rope,
+                                               workspace=ws)
+
+    def _swa(self, L, q, k, v, g, o, P, off, ws):
+        wl = self.wl
+        if wl.n_sink:
+            return self.dsa.swa_attn_pas(q, k, v, L["sk"], L["sv"], g, o, P, off, wl.window,
+                                         wl.nope, wl.rope, workspace=ws)
+        return self.dsa.swa_attn(q, k, v, g, o, P, off, wl.window, wl.nope, wl.rope, workspace=ws)
 
     # each stage: (name, callable)
     def stages(self):
@@ -132,29 +163,28 @@ class Layer:
         kc = self.k if self.T_alloc == wl.T else self.k[:, : wl.T]
         vc = self.v if self.T_alloc == wl.T else self.v[:, : wl.T]
         if S > 1:
-            st.append(("K3 sparse_attn_prefill", lambda: dsa.dsa_sparse_attn_prefill(
-                self.q, kc, vc, self.idx, self.gate, self.out, P, wl.nope, wl.rope, workspace=self.ws)))
+            st.append(("K3 sparse_attn_prefill", lambda: self._prefill(
+                self.q, kc, vc, self.idx, self.gate, self.out, P, self.ws)))
         else:
-            st.append(("K4 sparse_attn_decode", lambda: dsa.dsa_sparse_attn_decode(
-                self.q, kc, vc, self.idx, self.gate, self.out, wl.nope, wl.rope, workspace=self.ws)))
+            st.append(("K4 sparse_attn_decode", lambda: self._decode(
+                self.q, kc, vc, self.idx, self.gate, self.out, self.ws)))
         for j, L in enumerate(self.swa):
-            st.append((f"K5 swa_attn chunk L{j + 1}", lambda L=L: dsa.swa_attn(
-                L["q"], L["k"][:, : L["Tb"]], L["v"][:, : L["Tb"]], L["g"], L["o"], P, L["off"],
-                wl.window, wl.nope, wl.rope, workspace=L["ws"])))
+            st.append((f"K5 swa_attn chunk L{j + 1}", lambda L=L: self._swa(
+                L, L["q"], L["k"][:, : L["Tb"]], L["v"][:, : L["Tb"]], L["g"], L["o"], P, L["off"],
+                L["ws"])))
         if wl.decode_after:
             Td = wl.T + 1
             st += [
                 ("D K1 index_scores", lambda: dsa.dsa_index_scores(self.qd_idx, self.k_idx, self.wd, self.sd, Td - 1)),
                 ("D K2 topk", lambda: dsa.dsa_topk(self.sd, self.idd, self.tk_wsd)),
-                ("D K4 sparse_attn_decode", lambda: dsa.dsa_sparse_attn_decode(
-                    self.qd, self.k, self.v, self.idd, self.gd, self.od, wl.nope, wl.rope,
-                    workspace=self.wsd)),
+                ("D K4 sparse_attn_decode", lambda: self._decode(
+                    self.qd, self.k, self.v, self.idd, self.gd, self.od, self.wsd)),
             ]
             for j, L in enumerate(self.swa):
-                st.append((f"D K5 swa_attn L{j + 1}", lambda L=L: dsa.swa_attn(
-                    L["qd"], L["k"][:, L["offd"] - L["off"]:L["offd"] - L["off"] + L["Tbd"]],
+                st.append((f"D K5 swa_attn L{j + 1}", lambda L=L: self._swa(
+                    L, L["qd"], L["k"][:, L["offd"] - L["off"]:L["offd"] - L["off"] + L["Tbd"]],
                     L["v"][:, L["offd"] - L["off"]:L["offd"] - L["off"] + L["Tbd"]], L["gd"],
-                    L["od"], Td - 1, L["offd"], wl.window, wl.nope, wl.rope, workspace=L["wsd"])))
+                    L["od"], Td - 1, L["offd"], L["wsd"])))
         return st
 
 
@@ -209,24 +239,25 @@ def work(wl):
     pos = P + np.arange(S, dtype=np.float64)
     vis = float(B * np.sum(pos + 1))                 # visible (s, t) pairs
     sel = float(B * np.sum(np.minimum(k, pos + 1)))  # selected pairs
+    sink = float(B * S * wl.n_sink)                  # (query, sink) pairs
     out = {
         "K1": {"flops": 2.0 * wl.HI * wl.DI * vis,
                "bytes": esz * (B * S * wl.HI * wl.DI + B * T * wl.DI + B * S * wl.HI) + 4.0 * B * S * T},
         "K2": {"bytes": 4.0 * B * S * T + 4.0 * B * S * k},
-        "attn": {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * sel,
-                 "dense_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * vis,
+        "attn": {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * (sel + sink),
+                 "dense_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * (vis + sink),
                  "bytes_once": esz * (B * T * wl.H * (wl.Dqk + wl.v) + B * S * wl.H * (wl.Dqk + 2 * wl.v)),
-                 "bytes_gather": esz * sel * wl.H * (wl.Dqk + wl.v)},
+                 "bytes_gather": esz * (sel + sink) * wl.H * (wl.Dqk + wl.v)},
     }
     if wl.decode_after:
         Td = T + 1
         out["D"] = {"K1_bytes": esz * (B * Td * wl.DI) + 4.0 * B * Td,
-                    "K4_bytes": esz * B * k * wl.H * (wl.Dqk + wl.v),
-                    "K4_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * B * k}
+                    "K4_bytes": esz * B * (k + wl.n_sink) * wl.H * (wl.Dqk + wl.v),
+                    "K4_flops": 2.0 * wl.H * (wl.Dqk + wl.v) * B * (k + wl.n_sink)}
     if wl.n_swa:
         W = wl.window
         win = float(B * np.sum(np.minimum(W, pos + 1)))
-        out["K5"] = {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * win}
+        out["K5"] = {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * (win + sink)}
     return out
 
 

@@ -29,6 +29,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=
 
 # tensor ids of the stream keys
 TID_Q, TID_K, TID_V, TID_QIDX, TID_KIDX, TID_W, TID_GATE, TID_INDICES, TID_SCORES = range(1, 10)
+TID_SINK_K, TID_SINK_V = 10, 11  # attention-sink rows [n_sink, H, D]
 SWA_TID_STRIDE = 16  # SWA layer j (1, 2) uses id + 16*j
 
 

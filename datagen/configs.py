@@ -19,6 +19,9 @@ N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
                 v 128), indexer 32 x 128, top-k 2048; two SWA layers, window
                 512; a 4096-token chunk (past_len 524288) then one decode
                 token (position 528384); index weights / sqrt(32).
+  mla-s4k-pas, hybrid-512k-pas
+                the same with 128 attention sinks per layer (sink K/V drawn
+                like the cache's K/V, tensor ids 10 and 11).
 
 Element (b, t, h, d) of a cache is element ((b*T_alloc + t)*H + h)*D + d of
 its stream, so a window buffer starting at absolute position kv_offset is the
@@ -27,6 +30,7 @@ stream from kv_offset*H*D on (B = 1).
 from __future__ import annotations
 
 import math
+import dataclasses
 from dataclasses import dataclass
 
 F32, BF16 = 0, 1
@@ -50,6 +54,7 @@ class Workload:
     window: int = 512
     n_swa: int = 0            # SWA layers in the stack (hybrid: 2)
     decode_after: bool = False  # hybrid: one decode token after the chunk
+    n_sink: int = 0            # attention sinks per layer (PAS), shared by the batch
     scale_q: float = 1.0
     scale_k: float = 1.0
     scale_v: float = 1.0
@@ -87,5 +92,12 @@ WORKLOADS = {
                             rope=64, v=128, HI=32, DI=128, topk=2048, seed=4, n_swa=2,
                             decode_after=True, scale_w=1 / math.sqrt(32)),
 }
+# The same layers with 128 parametric attention sinks per layer (openPangu-2.0
+# page §3.4: 128 learnable KV pairs in every DSA and SWA layer).
+WORKLOADS["mla-s4k-pas"] = dataclasses.replace(WORKLOADS["mla-s4k"], name="mla-s4k-pas",
+                                               n_sink=128)
+WORKLOADS["hybrid-512k-pas"] = dataclasses.replace(WORKLOADS["hybrid-512k"],
+                                                   name="hybrid-512k-pas", n_sink=128)
 
-ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k"]
+ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k", "mla-s4k-pas",
+         "hybrid-512k-pas"]

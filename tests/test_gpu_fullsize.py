@@ -52,8 +52,9 @@ def compact_cache(wl, positions, b, T_alloc, H, D, tid, scale):
 
 
 def check_attn_rows(wl, out, idx, rows, b, T_alloc, qtid=datagen.TID_Q, gtid=datagen.TID_GATE,
-                    S_stream=None, ktid=datagen.TID_K, vtid=datagen.TID_V):
-    """Compare out[b, s] for s in rows against the oracle on compact caches."""
+                    S_stream=None, ktid=datagen.TID_K, vtid=datagen.TID_V, sinks=(None, None)):
+    """Compare out[b, s] for s in rows against the oracle on compact caches
+    (plus the layer's attention sinks, if any)."""
     S_stream = wl.S if S_stream is None else S_stream
     H, Dqk, Dv = wl.H, wl.Dqk, wl.v
     for s in rows:
@@ -65,7 +66,8 @@ def check_attn_rows(wl, out, idx, rows, b, T_alloc, qtid=datagen.TID_Q, gtid=dat
         g = host_row(wl, gtid, wl.scale_gate, r, H).reshape(1, 1, H)
         n = len(sel)
         ci = np.arange(n, dtype=np.int32).reshape(1, 1, n)
-        ref = oracle.sparse_attn(q, kc, vc, ci, g, n - 1, wl.nope, wl.rope)[0, 0]
+        ref = oracle.sparse_attn(q, kc, vc, ci, g, n - 1, wl.nope, wl.rope,
+                                 sink_k=sinks[0], sink_v=sinks[1])[0, 0]
         assert_rows_close(out[s].reshape(H, Dv), ref, 2e-2, what=f"{wl.name} attn row {s}")
 
 
@@ -126,6 +128,30 @@ def test_dsa_s32k_prefill_sampled_rows():
     del q, k, v, g, idx, out
     _free()
     check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, T)
+
+
+# ------------------------------------------------- mla-s4k with sinks
+def test_mla_s4k_pas_prefill_sampled_rows():
+    wl = WORKLOADS["mla-s4k-pas"]
+    S, T, H, ns = wl.S, wl.T, wl.H, wl.n_sink
+    q = dev_normal((1, S, H, wl.Dqk), wl, datagen.TID_Q, wl.scale_q)
+    k = dev_normal((1, T, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)
+    v = dev_normal((1, T, H, wl.v), wl, datagen.TID_V, wl.scale_v)
+    g = dev_normal((1, S, H), wl, datagen.TID_GATE, wl.scale_gate)
+    sk = dev_normal((ns, H, wl.Dqk), wl, datagen.TID_SINK_K, wl.scale_k)
+    sv = dev_normal((ns, H, wl.v), wl, datagen.TID_SINK_V, wl.scale_v)
+    idx = torch.empty(1, S, wl.topk, dtype=torch.int32, device=DEV)
+    datagen.indices_device(idx.view(S, wl.topk), 0, S, 0, seed=wl.seed)
+    out = torch.empty(1, S, H, wl.v, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_sparse_attn_prefill_pas(q, k, v, sk, sv, idx, g, out, 0, wl.nope, wl.rope)
+    rows = sample_rows(S, wl.topk, n=8, seed=5)
+    got = from_dev(out[0, rows])
+    idx_h = datagen.indices_host(0, S, S, 0, wl.topk, seed=wl.seed)
+    del q, k, v, g, idx, out, sk, sv
+    _free()
+    skh = datagen.normal_host((ns, H, wl.Dqk), "bf16", wl.seed, datagen.TID_SINK_K, wl.scale_k)
+    svh = datagen.normal_host((ns, H, wl.v), "bf16", wl.seed, datagen.TID_SINK_V, wl.scale_v)
+    check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, T, sinks=(skh, svh))
 
 
 # ----------------------------------------------------------- decode-b8
