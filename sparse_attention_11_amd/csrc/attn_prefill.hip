@@ -134,14 +134,16 @@ __device__ __forceinline__ bool item_tile(int item, int nqt, int M, const SplitT
 }
 
 // ------------------------------------------------------------ flash kernel
-// MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA).
+// MASK 0: selection bitmap (DSA); MASK 1: window [p-W+1, p] (SWA). SINK:
+// whether attention-sink blocks come first (a separate instantiation, so the
+// sink-free loop carries no sink checks).
 //
 // One workgroup = one head x 128 queries, wave w owning queries 32w..32w+31.
 // Register budget is held to 256 per wave so two workgroups share a CU: one
 // computes while the other waits on its barrier or loads. Inside a
 // workgroup the next 64-key block is loaded into registers while the current
 // block is computed (software pipelining) and written to LDS after a barrier.
-template <int DQK, int DV, int MASK>
+template <int DQK, int DV, int MASK, bool SINK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ sk,
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // Blocks of this item: first the attention-sink rows (split 0 only, every
   // query sees all of them, no position), then the cache rows jlo .. jhi.
   // Block bi < nsb holds sink rows 64 bi .. 64 bi + 63.
-  const int nsb = (split == 0) ? (n_sink + kBN - 1) / kBN : 0;
+  const int nsb = (SINK && split == 0) ? (n_sink + kBN - 1) / kBN : 0;
   const int nblk = nsb + (jlo <= jhi ? (jhi - jlo) / kBN + 1 : 0);
 
   // ---- register prefetch of one key block. A K row of KCH 16-byte chunks is
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     // rows of the buffer (cache or sinks) from the block's first row on
     const uint16_t *kp, *vp;
     int64_t rows;
-    if (bi < nsb) {
+    if (SINK && bi < nsb) {
       kp = sk + ((int64_t)bi * kBN * H + h) * DQK;
       vp = sv + ((int64_t)bi * kBN * H + h) * DV;
       rows = n_sink - bi * kBN;
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // a sink block's words mark its rows below n_sink
   uint32_t nbits[2] = {0u, 0u};
   auto load_bits = [&](int bi) {
-    if (bi < nsb) {
+    if (SINK && bi < nsb) {
       const int nv = min(kBN, n_sink - bi * kBN);  // >= 1
       nbits[0] = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
       nbits[1] = nv >= 64 ? 0xFFFFFFFFu : (nv > 32 ? (1u << (nv - 32)) - 1u : 0u);
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     store_block();
     __syncthreads();
     const uint32_t bits[2] = {nbits[0], nbits[1]};
-    const bool sinkb = bi < nsb;
+    const bool sinkb = SINK && bi < nsb;
     const int jb = jlo + (bi - nsb) * kBN;  // first cache row (cache blocks)
 
     // the next block's loads overlap this block's MFMA and softmax work
@@ -554,16 +556,22 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const SplitPlan pl = make_split_plan(B, S, Tbuf, P, H, kv_offset, window);
   if (pl.items != pl.nqt && part == nullptr) return hipErrorInvalidValue;  // no partial buffer
   const dim3 grid(pl.items, H, B);
-  if (window > 0)
-    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 1>), grid, dim3(256), 0, st, q, k, v, sk, sv, n_sink, bm,
-                       gate,
-                       out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
-                       pl.nqt, pl.M, pl.tab);
-  else
-    hipLaunchKernelGGL((prefill_kernel<DQK, DV, 0>), grid, dim3(256), 0, st, q, k, v, sk, sv, n_sink, bm,
-                       gate,
-                       out, part, S, Tbuf, P, kv_offset, H, W32, window, scale_log2, gate_dim,
-                       pl.nqt, pl.M, pl.tab);
+#define DSA_FLASH_LAUNCH(MK, SK)                                                                 \
+  hipLaunchKernelGGL((prefill_kernel<DQK, DV, MK, SK>), grid, dim3(256), 0, st, q, k, v, sk, sv,   \
+                     n_sink, bm, gate, out, part, S, Tbuf, P, kv_offset, H, W32, window,          \
+                     scale_log2, gate_dim, pl.nqt, pl.M, pl.tab)
+  if (window > 0) {
+    if (n_sink > 0)
+      DSA_FLASH_LAUNCH(1, true);
+    else
+      DSA_FLASH_LAUNCH(1, false);
+  } else {
+    if (n_sink > 0)
+      DSA_FLASH_LAUNCH(0, true);
+    else
+      DSA_FLASH_LAUNCH(0, false);
+  }
+#undef DSA_FLASH_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.items == pl.nqt) return e;
   hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt * (kBQ / kMergeRows), H, B), dim3(256),
