@@ -167,15 +167,24 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
       load_weights(st + 1);
     }
     if (active) {
+      // B operands of one (head, query group) of the stage; the next pair's
+      // are read from LDS while the current pair is multiplied
+      auto read_ops = [&](int gq, bf16x8_t* dst) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          dst[ks] = as_bf16x8(*(const u32x4_t*)(
+              &qs[buf][(((gq / kQG) * KS + ks) * kQG + gq % kQG) * 1024 + 16 * lane]));
+      };
+      bf16x8_t bqn[KS];
+      read_ops(0, bqn);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int qg = 0; qg < kQG; ++qg) {
           bf16x8_t bq[KS];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            bq[ks] = as_bf16x8(
-                *(const u32x4_t*)(&qs[buf][((g * KS + ks) * kQG + qg) * 1024 + 16 * lane]));
+          for (int ks = 0; ks < KS; ++ks) bq[ks] = bqn[ks];
+          if (g * kQG + qg + 1 < G * kQG) read_ops(g * kQG + qg + 1, bqn);
           f32x4_t acc[8];
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) acc[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -433,12 +442,12 @@ hipError_t dispatch_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* w
   // Light per-score work (few index heads x small dim): two 16-query groups
   // per workgroup share each wave's key registers. Measured: 24 -> 22 us at
   // 4 heads x 64 (4096 x 4096); 3% slower at 64 heads x 128, where the
-  // products dominate.
-  if (HI * DI <= 512) {
+  // products dominate. (At dim 128 two groups' operands exceed the register
+  // budget, so that dim always runs one group.)
+  if (HI * DI <= 512 && DI <= 64) {
     switch (DI) {
       case 32: return launch_tiles<32, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-      case 64: return launch_tiles<64, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-      default: return launch_tiles<128, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
+      default: return launch_tiles<64, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
     }
   }
   switch (DI) {

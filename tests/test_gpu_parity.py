@@ -85,7 +85,9 @@ INDEX_CASES = [
     # several 512-key tiles, head counts that leave a partial last LDS stage
     (1, 600, 0, 9, 64, 0), (1, 1000, 500, 13, 128, 2), (2, 333, 1200, 17, 32, 1),
     # heads x dim <= 512: 32-query tiles (two query groups share the key registers)
-    (1, 700, 100, 4, 64, 0), (2, 150, 600, 4, 128, 2), (1, 1100, 0, 8, 64, 1),
+    (1, 700, 100, 4, 64, 0), (2, 150, 600, 8, 32, 2), (1, 1100, 0, 8, 64, 1),
+    # few heads at dim 128 (one query group)
+    (2, 150, 600, 4, 128, 2),
 ]
 
 
