@@ -20,6 +20,8 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                 limits.
   swa_attn      pinned: window >= context equals dense causal SDPA, window 1
                 closed form, buffer-offset equivalence.
+  swa_attn_gqa  pinned: torch SDPA with grouped KV heads (enable_gqa) under the
+                band mask; equals swa_attn on explicitly repeated KV heads.
 Parity unpinned by the pages (fixed by convention, tested in every mode):
 ReLU placement (per head by default), the two scale constants, and the
 inclusive window boundary.
@@ -80,6 +82,9 @@ def _load():
         lib.oracle_swa_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, i32, dbl, i32, vp]
         lib.oracle_swa_attn_pas.restype = None
+        lib.oracle_swa_attn_gqa.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, dbl, i32, vp]
+        lib.oracle_swa_attn_gqa.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         _lib = lib
@@ -200,4 +205,28 @@ def swa_attn(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
                                 _ptr(gate), _dtype_of(q, k_buf, v_buf, gate, sk, sv), B, S,
                                 T_buf, past_len, kv_offset, H, Dqk, Dv, window, float(sm_scale),
                                 gate_dim, _ptr(out))
+    return out
+
+
+def swa_attn_gqa(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: int,
+                 qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+                 gate_dim: int | None = None) -> np.ndarray:
+    """swa_attn with grouped KV heads: q [B,S,H,Dqk], buffers [B,T_buf,H_kv,D] with H_kv
+    dividing H; query head h reads KV head h // (H // H_kv) -> out [B,S,H,Dv] float64."""
+    q, k_buf, v_buf = _c(q), _c(k_buf), _c(v_buf)
+    B, S, H, Dqk = q.shape
+    assert Dqk == qk_nope_dim + qk_rope_dim
+    T_buf, H_kv = k_buf.shape[1], k_buf.shape[2]
+    assert H % H_kv == 0 and v_buf.shape[2] == H_kv
+    Dv = v_buf.shape[3]
+    gate_dim = _gate_dim(gate, Dv, gate_dim)
+    if gate is not None:
+        gate = _c(gate)
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    out = np.empty((B, S, H, Dv), np.float64)
+    _load().oracle_swa_attn_gqa(_ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate),
+                                _dtype_of(q, k_buf, v_buf, gate), B, S, T_buf, past_len,
+                                kv_offset, H, H_kv, Dqk, Dv, window, float(sm_scale), gate_dim,
+                                _ptr(out))
     return out

@@ -24,6 +24,10 @@
  *                           n_sink learned K/V rows every query attends to
  *                           besides its selected or windowed keys
  *                           [openPangu-2.0 page §3.4 (PAS)]
+ *   oracle_swa_attn_gqa  -- sliding-window attention whose K/V buffers hold
+ *                           fewer heads than q (grouped KV heads)
+ *                           [Spark-X2.5 page, "why the gate": 8 query heads,
+ *                           2 KV heads, head_dim 256]
  * Decode is the same functions with S = 1 and past_len = T - 1.
  *
  * Arithmetic is IEEE double throughout; inputs are read in their storage type
@@ -49,6 +53,8 @@
  *    sink_v [n_sink,H,Dv], shared by the whole batch; they carry no position,
  *    so no causal mask applies to them; the softmax runs over the sinks and
  *    the selected (or windowed) keys together.
+ *  - Grouped KV heads: query head h reads KV head h / (H / H_kv), i.e.
+ *    consecutive query heads share a KV head.
  */
 #include <math.h>
 #include <stdint.h>
@@ -176,17 +182,19 @@ static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /*
  * Softmax attention of one (b, s, h) query over the keys marked in sel[0..T)
- * and the n_sink sink rows, followed by the gate. Shared by the DSA and SWA
- * functions below (both are the same masked softmax, they differ only in
- * which keys are marked).
- *   qrow [Dqk] at q + qoff; key t row at kc + ((b*T + t)*H + h)*Dqk, likewise
- *   vc with Dv; sink r at sk + (r*H + h)*Dqk and sv + (r*H + h)*Dv.
+ * and the n_sink sink rows (the gate is applied by the caller). Shared by the
+ * DSA and SWA functions below (both are the same masked softmax, they differ
+ * only in which keys are marked). The caches hold Hc heads per row and this
+ * query reads cache head hc.
+ *   qrow [Dqk] at q + qoff; key t row at kc + ((b*T + t)*Hc + hc)*Dqk,
+ *   likewise vc with Dv; sink r at sk + (r*Hc + hc)*Dqk and
+ *   sv + (r*Hc + hc)*Dv.
  *   logit has room for T + n_sink values. o [Dv] receives the result.
  */
 static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
                                const void *vc, const void *sk, const void *sv,
                                int n_sink, int dtype, int64_t b, int64_t T,
-                               int H, int h, int Dqk, int Dv, double sm_scale,
+                               int Hc, int hc, int Dqk, int Dv, double sm_scale,
                                const unsigned char *sel, double *logit,
                                double *o) {
   double mx = -INFINITY;
@@ -196,7 +204,7 @@ static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
     double dot = 0.0;
     for (int d = 0; d < Dqk; ++d)
       dot += rd(q, dtype, qoff + d) *
-             rd(sk, dtype, ((int64_t)r * H + h) * (int64_t)Dqk + d);
+             rd(sk, dtype, ((int64_t)r * Hc + hc) * (int64_t)Dqk + d);
     slog[r] = sm_scale * dot;
     if (slog[r] > mx) mx = slog[r];
     ++nsel;
@@ -206,7 +214,7 @@ static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
     double dot = 0.0;
     for (int d = 0; d < Dqk; ++d)
       dot += rd(q, dtype, qoff + d) *
-             rd(kc, dtype, ((b * T + t) * H + h) * (int64_t)Dqk + d);
+             rd(kc, dtype, ((b * T + t) * Hc + hc) * (int64_t)Dqk + d);
     logit[t] = sm_scale * dot;
     if (logit[t] > mx) mx = logit[t];
     ++nsel;
@@ -218,14 +226,14 @@ static void masked_softmax_row(const void *q, int64_t qoff, const void *kc,
     double e = exp(slog[r] - mx);
     den += e;
     for (int d = 0; d < Dv; ++d)
-      o[d] += e * rd(sv, dtype, ((int64_t)r * H + h) * (int64_t)Dv + d);
+      o[d] += e * rd(sv, dtype, ((int64_t)r * Hc + hc) * (int64_t)Dv + d);
   }
   for (int64_t t = 0; t < T; ++t) {
     if (!sel[t]) continue;
     double e = exp(logit[t] - mx);
     den += e;
     for (int d = 0; d < Dv; ++d)
-      o[d] += e * rd(vc, dtype, ((b * T + t) * H + h) * (int64_t)Dv + d);
+      o[d] += e * rd(vc, dtype, ((b * T + t) * Hc + hc) * (int64_t)Dv + d);
   }
   for (int d = 0; d < Dv; ++d) o[d] /= den;
 }
@@ -307,13 +315,14 @@ void oracle_sparse_attn(const void *q, const void *k_cache, const void *v_cache,
  *   q [B,S,H,Dqk], k_buf [B,T_buf,H,Dqk], v_buf [B,T_buf,H,Dv], gate as above
  *   out [B,S,H,Dv] double
  */
-void oracle_swa_attn_pas(const void *q, const void *k_buf, const void *v_buf,
-                         const void *sink_k, const void *sink_v, int n_sink,
-                         const void *gate, int dtype, int B, int S, int T_buf,
-                         int past_len, int kv_offset, int H, int Dqk, int Dv,
-                         int window, double sm_scale, int gate_dim,
-                         double *out) {
+static void swa_attn(const void *q, const void *k_buf, const void *v_buf,
+                     const void *sink_k, const void *sink_v, int n_sink,
+                     const void *gate, int dtype, int B, int S, int T_buf,
+                     int past_len, int kv_offset, int H, int H_kv, int Dqk,
+                     int Dv, int window, double sm_scale, int gate_dim,
+                     double *out) {
   int64_t n = (int64_t)B * S * H;
+  int group = H / H_kv; /* query heads per KV head */
 #pragma omp parallel
   {
     unsigned char *sel = (unsigned char *)malloc((size_t)T_buf);
@@ -334,8 +343,8 @@ void oracle_swa_attn_pas(const void *q, const void *k_buf, const void *v_buf,
       }
       double *o = out + e * Dv;
       masked_softmax_row(q, e * Dqk, k_buf, v_buf, sink_k, sink_v, n_sink,
-                         dtype, b, T_buf, H, h, Dqk, Dv, sm_scale, sel, logit,
-                         o);
+                         dtype, b, T_buf, H_kv, h / group, Dqk, Dv, sm_scale,
+                         sel, logit, o);
       apply_gate(gate, dtype, gate_dim, bs, H, h, Dv, o);
     }
     free(logit);
@@ -343,11 +352,36 @@ void oracle_swa_attn_pas(const void *q, const void *k_buf, const void *v_buf,
   }
 }
 
+void oracle_swa_attn_pas(const void *q, const void *k_buf, const void *v_buf,
+                         const void *sink_k, const void *sink_v, int n_sink,
+                         const void *gate, int dtype, int B, int S, int T_buf,
+                         int past_len, int kv_offset, int H, int Dqk, int Dv,
+                         int window, double sm_scale, int gate_dim,
+                         double *out) {
+  swa_attn(q, k_buf, v_buf, sink_k, sink_v, n_sink, gate, dtype, B, S, T_buf,
+           past_len, kv_offset, H, H, Dqk, Dv, window, sm_scale, gate_dim, out);
+}
+
 void oracle_swa_attn(const void *q, const void *k_buf, const void *v_buf,
                      const void *gate, int dtype, int B, int S, int T_buf,
                      int past_len, int kv_offset, int H, int Dqk, int Dv,
                      int window, double sm_scale, int gate_dim, double *out) {
-  oracle_swa_attn_pas(q, k_buf, v_buf, NULL, NULL, 0, gate, dtype, B, S, T_buf,
-                      past_len, kv_offset, H, Dqk, Dv, window, sm_scale,
-                      gate_dim, out);
+  swa_attn(q, k_buf, v_buf, NULL, NULL, 0, gate, dtype, B, S, T_buf, past_len,
+           kv_offset, H, H, Dqk, Dv, window, sm_scale, gate_dim, out);
+}
+
+/*
+ * Sliding-window attention with grouped KV heads [Spark-X2.5 page, "why the
+ * gate": num_attention_heads 8, num_key_value_heads 2]. The buffers hold H_kv
+ * heads (H_kv divides H): k_buf [B,T_buf,H_kv,Dqk], v_buf [B,T_buf,H_kv,Dv];
+ * query head h reads KV head h / (H / H_kv). Everything else as
+ * oracle_swa_attn.
+ */
+void oracle_swa_attn_gqa(const void *q, const void *k_buf, const void *v_buf,
+                         const void *gate, int dtype, int B, int S, int T_buf,
+                         int past_len, int kv_offset, int H, int H_kv, int Dqk,
+                         int Dv, int window, double sm_scale, int gate_dim,
+                         double *out) {
+  swa_attn(q, k_buf, v_buf, NULL, NULL, 0, gate, dtype, B, S, T_buf, past_len,
+           kv_offset, H, H_kv, Dqk, Dv, window, sm_scale, gate_dim, out);
 }

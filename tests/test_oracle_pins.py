@@ -434,3 +434,45 @@ def test_swa_sinks_match_sdpa_band_plus_sinks():
     k2, v2 = _with_sinks_prepended(kc, vc, sk, sv)
     ref = sdpa_masked(q, k2, v2, mask, Dqk ** -0.5) * sigmoid64(g)[..., None]
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------- SWA with grouped KV heads
+def _band(S, T_buf, past_len, kv_offset, W):
+    p = past_len + np.arange(S)[:, None]
+    t = kv_offset + np.arange(T_buf)[None, :]
+    return (t <= p) & (t > p - W)
+
+
+@pytest.mark.parametrize("H,H_kv,P,off,W", [(8, 2, 0, 0, 4), (8, 2, 9, 3, 5), (6, 3, 4, 0, 100),
+                                           (4, 1, 7, 2, 3)])
+def test_swa_gqa_matches_sdpa_with_grouped_heads(H, H_kv, P, off, W):
+    # torch SDPA's grouped-query mode repeats each KV head over H / H_kv
+    # consecutive query heads; the band mask is the window
+    B, S, Dqk, Dv = 2, 7, 12, 10
+    T_buf = P + S - off
+    q, g = f32(B, S, H, Dqk), f32(B, S, H)
+    kb, vb = f32(B, T_buf, H_kv, Dqk), f32(B, T_buf, H_kv, Dv)
+    got = oracle.swa_attn_gqa(q, kb, vb, g, P, off, W, 8, 4)
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(kb.astype(np.float64)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(vb.astype(np.float64)).permute(0, 2, 1, 3).contiguous()
+    m = torch.from_numpy(_band(S, T_buf, P, off, W))[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m,
+                                                           scale=Dqk ** -0.5, enable_gqa=True)
+    ref = ref.permute(0, 2, 1, 3).numpy() * sigmoid64(g)[..., None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_swa_gqa_equals_swa_on_repeated_kv_heads():
+    # expanding each KV head to its H / H_kv query heads gives plain SWA
+    B, S, H, H_kv, Dqk, Dv, P, W = 1, 9, 8, 2, 16, 8, 5, 6
+    T = P + S
+    q, g = f32(B, S, H, Dqk), f32(B, S, H, Dv)
+    kb, vb = f32(B, T, H_kv, Dqk), f32(B, T, H_kv, Dv)
+    got = oracle.swa_attn_gqa(q, kb, vb, g, P, 0, W, 16, 0)
+    ref = oracle.swa_attn(q, np.repeat(kb, H // H_kv, axis=2), np.repeat(vb, H // H_kv, axis=2),
+                          g, P, 0, W, 16, 0)
+    np.testing.assert_array_equal(got, ref)
+    same = oracle.swa_attn_gqa(q, np.repeat(kb, H // H_kv, axis=2),
+                               np.repeat(vb, H // H_kv, axis=2), g, P, 0, W, 16, 0)
+    np.testing.assert_array_equal(same, ref)
