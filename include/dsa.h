@@ -216,6 +216,26 @@ int swa_attn_pas(const void* q, const void* k_buf, const void* v_buf, const void
                  int v_dim, int window, float sm_scale, int gate_dim, int dtype, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Sliding-window attention with grouped KV heads ([SPARK] "为什么要加这一层门控":
+ * 8 query heads share 2 KV heads, head_dim 256, sliding_window 512, one
+ * sigmoid gate per head). swa_attn with caches that hold H_kv heads:
+ *   k_buf [B,T_buf,H_kv,Dqk], v_buf [B,T_buf,H_kv,Dv]; q, gate, out as in
+ *   swa_attn with H query heads.
+ * Query head h reads cache head h / (H / H_kv): consecutive query heads form
+ * the groups. 1 <= H_kv <= H and H_kv must divide H (else
+ * DSA_ERR_INVALID_ARG); H_kv = H is swa_attn. All other arguments, the
+ * workspace rule and the errors are those of swa_attn (workspace from
+ * swa_attn_gqa_workspace_size, which takes the query head count).
+ */
+size_t swa_attn_gqa_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                                   int dtype);
+int swa_attn_gqa(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,
+                 int B, int S, int T_buf, int past_len, int kv_offset, int H, int H_kv,
+                 int qk_nope_dim, int qk_rope_dim, int v_dim, int window, float sm_scale,
+                 int gate_dim, int dtype, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */

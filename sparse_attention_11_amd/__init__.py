@@ -34,6 +34,7 @@ _EXPORTS = [
     "dsa_sparse_attn_prefill_pas_workspace_size", "dsa_sparse_attn_prefill_pas",
     "dsa_sparse_attn_decode_pas_workspace_size", "dsa_sparse_attn_decode_pas",
     "swa_attn_pas_workspace_size", "swa_attn_pas",
+    "swa_attn_gqa_workspace_size", "swa_attn_gqa",
 ]
 MAX_SINKS = 256
 
@@ -87,9 +88,13 @@ def lib():
         L.swa_attn_pas_workspace_size.restype = sz
         L.swa_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+        L.swa_attn_gqa_workspace_size.argtypes = [i32] * 7
+        L.swa_attn_gqa_workspace_size.restype = sz
+        L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, f32, i32, i32, vp, sz, vp]
         for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
-                   "dsa_sparse_attn_decode_pas", "swa_attn_pas"):
+                   "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa"):
             getattr(L, fn).restype = i32
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -322,6 +327,29 @@ def swa_attn_pas(q, k_buf, v_buf, sink_k, sink_v, gate, out, past_len: int, kv_o
         _ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(sink_k), _ptr(sink_v), ns, _ptr(gate), _ptr(out),
         B, S, T_buf, past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale,
         _gate_dim(gate, Dv), dt, _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def swa_attn_gqa_workspace_size(B, S, H, qk_dim, v_dim, window, dtype) -> int:
+    return int(lib().swa_attn_gqa_workspace_size(B, S, H, qk_dim, v_dim, window, dtype))
+
+
+def swa_attn_gqa(q, k_buf, v_buf, gate, out, past_len: int, kv_offset: int, window: int,
+                 qk_nope_dim: int, qk_rope_dim: int, sm_scale: float | None = None,
+                 workspace=None, stream=None):
+    """swa_attn with grouped KV heads: k_buf [B,T_buf,H_kv,Dqk], v_buf [B,T_buf,H_kv,Dv]."""
+    B, S, H, Dqk = q.shape
+    T_buf, H_kv, Dv = k_buf.shape[1], k_buf.shape[2], v_buf.shape[3]
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    dt = _dtype(q)
+    if workspace is None:
+        workspace = _workspace(swa_attn_gqa_workspace_size(B, S, H, Dqk, Dv, window, dt), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("swa_attn_gqa", lib().swa_attn_gqa(
+        _ptr(q), _ptr(k_buf), _ptr(v_buf), _ptr(gate), _ptr(out), B, S, T_buf, past_len,
+        kv_offset, H, H_kv, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale, _gate_dim(gate, Dv),
+        dt, _ptr(workspace), nbytes, _stream(stream)))
     return out
 
 

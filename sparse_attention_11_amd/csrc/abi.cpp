@@ -118,11 +118,11 @@ int prefill_impl(const char* fn, const void* q, const void* k_cache, const void*
   hipError_t e;
   if (mfma)
     e = dsa::launch_prefill_mfma(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate, out,
-                                 B, S, T, past_len, 0, H, dqk, v_dim, topk, 0, sm_scale, gate_dim,
-                                 workspace, stream);
+                                 B, S, T, past_len, 0, H, H, dqk, v_dim, topk, 0, sm_scale,
+                                 gate_dim, workspace, stream);
   else
     e = dsa::launch_gather(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate, out, B, S,
-                           T, past_len, 0, H, dqk, v_dim, topk, 0, sm_scale, gate_dim, dtype,
+                           T, past_len, 0, H, H, dqk, v_dim, topk, 0, sm_scale, gate_dim, dtype,
                            workspace, stream);
   return hip_status(e, fn);
 }
@@ -146,20 +146,24 @@ int decode_impl(const char* fn, const void* q, const void* k_cache, const void* 
                 dsa::gather_workspace_bytes(B, H, v_dim, topk + n_sink));
   if (st) return st;
   return hip_status(dsa::launch_gather(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate,
-                                       out, B, 1, T, T - 1, 0, H, qk_nope_dim + qk_rope_dim, v_dim,
+                                       out, B, 1, T, T - 1, 0, H, H, qk_nope_dim + qk_rope_dim, v_dim,
                                        topk, 0, sm_scale, gate_dim, dtype, workspace, stream),
                     fn);
 }
 
 int swa_impl(const char* fn, const void* q, const void* k_buf, const void* v_buf,
              const void* sink_k, const void* sink_v, int n_sink, const void* gate, void* out,
-             int B, int S, int T_buf, int past_len, int kv_offset, int H, int qk_nope_dim,
-             int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+             int B, int S, int T_buf, int past_len, int kv_offset, int H, int H_kv,
+             int qk_nope_dim, int qk_rope_dim, int v_dim, int window, float sm_scale,
+             int gate_dim, int dtype, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
   g_err.clear();
   int st = check_attn(fn, q, k_buf, v_buf, gate, out, B, S, T_buf, H, qk_nope_dim, qk_rope_dim,
                       v_dim, sm_scale, gate_dim, dtype);
   if (st) return st;
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: kv heads must divide the query heads (H %d, H_kv %d)",
+                fn, H, H_kv);
   if ((st = check_sinks(fn, sink_k, sink_v, n_sink))) return st;
   if (window < 1) return fail(DSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
   if (past_len < 0 || kv_offset < 0)
@@ -183,11 +187,11 @@ int swa_impl(const char* fn, const void* q, const void* k_buf, const void* v_buf
   hipError_t e;
   if (mfma)
     e = dsa::launch_prefill_mfma(q, k_buf, v_buf, sink_k, sink_v, n_sink, nullptr, gate, out, B,
-                                 S, T_buf, past_len, kv_offset, H, dqk, v_dim, 0, window,
+                                 S, T_buf, past_len, kv_offset, H, H_kv, dqk, v_dim, 0, window,
                                  sm_scale, gate_dim, nullptr, stream);
   else
     e = dsa::launch_gather(q, k_buf, v_buf, sink_k, sink_v, n_sink, nullptr, gate, out, B, S,
-                           T_buf, past_len, kv_offset, H, dqk, v_dim, 0, window, sm_scale,
+                           T_buf, past_len, kv_offset, H, H_kv, dqk, v_dim, 0, window, sm_scale,
                            gate_dim, dtype, workspace, stream);
   return hip_status(e, fn);
 }
@@ -334,7 +338,7 @@ int swa_attn(const void* q, const void* k_buf, const void* v_buf, const void* ga
              int qk_rope_dim, int v_dim, int window, float sm_scale, int gate_dim, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return swa_impl("swa_attn", q, k_buf, v_buf, nullptr, nullptr, 0, gate, out, B, S, T_buf,
-                  past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
+                  past_len, kv_offset, H, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
                   gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -344,7 +348,22 @@ int swa_attn_pas(const void* q, const void* k_buf, const void* v_buf, const void
                  int v_dim, int window, float sm_scale, int gate_dim, int dtype, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
   return swa_impl("swa_attn_pas", q, k_buf, v_buf, sink_k, sink_v, n_sink, gate, out, B, S, T_buf,
-                  past_len, kv_offset, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
+                  past_len, kv_offset, H, H, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
+                  gate_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t swa_attn_gqa_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
+                                   int dtype) {
+  return swa_ws(B, S, H, qk_dim, v_dim, window, dtype, 0);
+}
+
+int swa_attn_gqa(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,
+                 int B, int S, int T_buf, int past_len, int kv_offset, int H, int H_kv,
+                 int qk_nope_dim, int qk_rope_dim, int v_dim, int window, float sm_scale,
+                 int gate_dim, int dtype, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return swa_impl("swa_attn_gqa", q, k_buf, v_buf, nullptr, nullptr, 0, gate, out, B, S, T_buf,
+                  past_len, kv_offset, H, H_kv, qk_nope_dim, qk_rope_dim, v_dim, window, sm_scale,
                   gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 

@@ -61,8 +61,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
     const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
     const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
-    int kv_offset, int H, int DQK, int DV, int nent, int per_split, int nsplit, int window,
-    float scale_log2) {
+    int kv_offset, int H, int HKV, int DQK, int DV, int nent, int per_split, int nsplit,
+    int window, float scale_log2) {
   using E = Elem<DT>;
   constexpr int EP = E::kPer16;
   constexpr int esz = DT ? 2 : 4;
@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
   const int h = 32 * blockIdx.y + 8 * wave + (lane >> 3);
   const bool hvalid = h < H;
   const int hh = hvalid ? h : H - 1;
+  const int hk = hh / (H / HKV);  // cache head: query heads come in groups of H / HKV
   const int nck = DQK / EP, ncv = DV / EP;
 
   const char* qb = (const char*)qv;
@@ -140,11 +141,11 @@ __global__ __launch_bounds__(256) void gather_kernel(
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
       const char* krow =
-          snk[g] ? skb + (((int64_t)jrow[g] * H + hh) * (int64_t)DQK) * esz
-                 : kb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DQK) * esz;
+          snk[g] ? skb + (((int64_t)jrow[g] * HKV + hk) * (int64_t)DQK) * esz
+                 : kb + (((kvrow0 + jrow[g]) * HKV + hk) * (int64_t)DQK) * esz;
       const char* vrow =
-          snk[g] ? svb + (((int64_t)jrow[g] * H + hh) * (int64_t)DV) * esz
-                 : vb + (((kvrow0 + jrow[g]) * H + hh) * (int64_t)DV) * esz;
+          snk[g] ? svb + (((int64_t)jrow[g] * HKV + hk) * (int64_t)DV) * esz
+                 : vb + (((kvrow0 + jrow[g]) * HKV + hk) * (int64_t)DV) * esz;
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const int c = sub + 8 * i;
@@ -330,8 +331,8 @@ size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries) {
 hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
                          const void* sink_v, int n_sink, const int32_t* indices,
                          const void* gate, void* out, int B, int S, int T, int past_len,
-                         int kv_offset, int H, int Dqk, int Dv, int topk, int window,
-                         float sm_scale, int gate_dim, int dtype, void* workspace,
+                         int kv_offset, int H, int Hkv, int Dqk, int Dv, int topk,
+                         int window, float sm_scale, int gate_dim, int dtype, void* workspace,
                          hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
   const int nent = n_sink + (window > 0 ? window : topk);
@@ -342,8 +343,8 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
   const float sl2 = sm_scale * DSA_LOG2E;
 #define DSA_GATHER(DT, WIN, KC, VC)                                                            \
   hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC>), grid, dim3(256), 0, st, q, k, v, sink_k,  \
-                     sink_v, n_sink, indices, part, S, T, past_len, kv_offset, H, Dqk, Dv, nent, \
-                     pl.per_split, pl.nsplit, window, sl2)
+                     sink_v, n_sink, indices, part, S, T, past_len, kv_offset, H, Hkv, Dqk, Dv,  \
+                     nent, pl.per_split, pl.nsplit, window, sl2)
 #define DSA_GATHER_VC(DT, WIN, KC)            \
   switch (vc) {                               \
     case 1: DSA_GATHER(DT, WIN, KC, 1); break; \

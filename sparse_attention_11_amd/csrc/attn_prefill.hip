@@ -144,12 +144,12 @@ __device__ __forceinline__ bool item_tile(int item, int nqt, int M, const SplitT
 // workgroup the next 64-key block is loaded into registers while the current
 // block is computed (software pipelining) and written to LDS after a barrier.
 template <int DQK, int DV, int MASK, bool SINK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+__global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ sk,
     const uint16_t* __restrict__ sv, int n_sink, const uint32_t* __restrict__ bm,
     const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, float* __restrict__ part,
-    int S, int Tbuf, int P, int kv_offset, int H, int W32, int window, float scale_log2,
+    int S, int Tbuf, int P, int kv_offset, int H, int HKV, int W32, int window, float scale_log2,
     int gate_dim, int nqt, int M, const SplitTable tab) {
   constexpr int KSQ = DQK / 16;
   constexpr int NDB = DV / 32;
@@ -166,6 +166,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   int qt, split, nsplit;
   if (!item_tile(blockIdx.x, nqt, M, tab, &qt, &split, &nsplit)) return;
   const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (H / HKV);  // cache head: query heads come in groups of H / HKV
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
   const int q0 = qt * kBQ;
@@ -204,40 +205,50 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int KP2 = KCH - KP1;               // part 2 (0 or 8)
   constexpr int R1 = 256 / KP1, N1 = kBN / R1;  // rows per load, loads
   constexpr int R2 = KP2 ? 256 / KP2 : 1, N2 = KP2 ? kBN / R2 : 0;
-  static_assert(N1 + N2 == KLD && VLD == 1, "load split");
+  static_assert(N1 + N2 == KLD && (VLD == 1 || VUN == 256 * VLD), "load split");
   const int krow1 = tid / KP1, kc1 = tid % KP1;
   const int krow2 = KP2 ? tid / KP2 : 0, kc2 = KP2 ? KP1 + tid % KP2 : 0;
-  const uint32_t rowb = (uint32_t)H * DQK * 2u;  // bytes between key rows
+  const uint32_t rowb = (uint32_t)HKV * DQK * 2u;  // bytes between key rows
   const uint32_t kbo1 = krow1 * rowb + 16u * kc1, kbo2 = krow2 * rowb + 16u * kc2;
-  const int vkg = tid / VCH, vdg = tid - vkg * VCH;
-  const uint32_t vrowb = (uint32_t)H * DV * 2u;
-  const uint32_t vbo = 4 * vkg * vrowb + 16u * vdg;
+  // V unit n (4 key rows x 8 dv) of a block: thread tid takes n = tid + 256 u
+  int vkg[VLD], vdg[VLD];
+  const uint32_t vrowb = (uint32_t)HKV * DV * 2u;
+  uint32_t vbo[VLD];
+#pragma unroll
+  for (int u = 0; u < VLD; ++u) {
+    const int un = tid + 256 * u;
+    vkg[u] = un / VCH;
+    vdg[u] = un - vkg[u] * VCH;
+    vbo[u] = 4 * vkg[u] * vrowb + 16u * vdg[u];
+  }
   u32x4_t kpre[KLD];
-  u32x4_t vpre[4];
+  u32x4_t vpre[VLD][4];
   auto load_block = [&](int bi) {
     // rows of the buffer (cache or sinks) from the block's first row on
     const uint16_t *kp, *vp;
     int64_t rows;
     if (SINK && bi < nsb) {
-      kp = sk + ((int64_t)bi * kBN * H + h) * DQK;
-      vp = sv + ((int64_t)bi * kBN * H + h) * DV;
+      kp = sk + ((int64_t)bi * kBN * HKV + hk) * DQK;
+      vp = sv + ((int64_t)bi * kBN * HKV + hk) * DV;
       rows = n_sink - bi * kBN;
     } else {
       const int jb = jlo + (bi - nsb) * kBN;
-      kp = k + ((kvrow0 + jb) * H + h) * DQK;
-      vp = v + ((kvrow0 + jb) * H + h) * DV;
+      kp = k + ((kvrow0 + jb) * HKV + hk) * DQK;
+      vp = v + ((kvrow0 + jb) * HKV + hk) * DV;
       rows = (int64_t)Tbuf - jb;
     }
-    const auto kr = make_rsrc(kp, rows * rowb - (int64_t)h * DQK * 2);
-    const auto vr = make_rsrc(vp, rows * vrowb - (int64_t)h * DV * 2);
+    const auto kr = make_rsrc(kp, rows * rowb - (int64_t)hk * DQK * 2);
+    const auto vr = make_rsrc(vp, rows * vrowb - (int64_t)hk * DV * 2);
 #pragma unroll
     for (int n = 0; n < N1; ++n) kpre[n] = buffer_load16(kr, kbo1 + n * R1 * rowb);
 #pragma unroll
     for (int n = 0; n < N2; ++n) kpre[N1 + n] = buffer_load16(kr, kbo2 + n * R2 * rowb);
-    if (tid < VUN) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vpre[e] = buffer_load16(vr, vbo + e * vrowb);
-    }
+    for (int u = 0; u < VLD; ++u)
+      if (tid + 256 * u < VUN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vpre[u][e] = buffer_load16(vr, vbo[u] + e * vrowb);
+      }
   };
   // ---- registers -> LDS: K row-major (padded rows), V row-major (swizzled)
   auto store_block = [&]() {
@@ -245,13 +256,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     for (int n = 0; n < N1; ++n) *(u32x4_t*)(&Ks[(krow1 + n * R1) * KPAD + 8 * kc1]) = kpre[n];
 #pragma unroll
     for (int n = 0; n < N2; ++n) *(u32x4_t*)(&Ks[(krow2 + n * R2) * KPAD + 8 * kc2]) = kpre[N1 + n];
-    if (tid < VUN) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * vkg + e;
-        *(u32x4_t*)(&Vs[r * DV + 8 * (vdg ^ vt_xor<VCH>(r))]) = vpre[e];
+    for (int u = 0; u < VLD; ++u)
+      if (tid + 256 * u < VUN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * vkg[u] + e;
+          *(u32x4_t*)(&Vs[r * DV + 8 * (vdg[u] ^ vt_xor<VCH>(r))]) = vpre[u][e];
+        }
       }
-    }
   };
   // Byte offset in Vs of this lane's transposing read for dv block d and the
   // first 16-key chunk: in each 16-lane group (g = lane / 16), lane 4j + q
@@ -442,7 +455,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 // of one (tile, head, b), 32 threads per row and 4 output dims per thread,
 // and issues every split's loads before combining them (up to kMergeUnroll
 // splits in flight; longer lists run in chunks).
-constexpr int kMergeRows = 8;
+// query rows per merge workgroup: DV / 4 threads per row
+template <int DV>
+constexpr int merge_rows() { return 256 / (DV / 4) < 8 ? 256 / (DV / 4) : 8; }
 constexpr int kMergeUnroll = 8;
 template <int DV>
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part,
@@ -452,7 +467,8 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
                                                            float scale_log2, int gate_dim,
                                                            const SplitTable tab) {
   constexpr int TPR = DV / 4;  // threads per query row
-  static_assert(TPR * kMergeRows <= 256, "row group must fit the workgroup");
+  constexpr int kMergeRows = merge_rows<DV>();
+  static_assert(TPR * kMergeRows <= 256 && kBQ % kMergeRows == 0, "row group must fit the workgroup");
   const int qt = blockIdx.x / (kBQ / kMergeRows);
   const int rg = blockIdx.x % (kBQ / kMergeRows);
   const int h = blockIdx.y, b = blockIdx.z;
@@ -551,14 +567,14 @@ template <int DQK, int DV>
 hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* sk, const uint16_t* sv, int n_sink,
                        const uint32_t* bm, const uint16_t* gate, uint16_t* out, int B, int S,
-                       int Tbuf, int P, int kv_offset, int H, int W32, int window,
+                       int Tbuf, int P, int kv_offset, int H, int Hkv, int W32, int window,
                        float scale_log2, int gate_dim, float* part, hipStream_t st) {
   const SplitPlan pl = make_split_plan(B, S, Tbuf, P, H, kv_offset, window);
   if (pl.items != pl.nqt && part == nullptr) return hipErrorInvalidValue;  // no partial buffer
   const dim3 grid(pl.items, H, B);
 #define DSA_FLASH_LAUNCH(MK, SK)                                                                 \
   hipLaunchKernelGGL((prefill_kernel<DQK, DV, MK, SK>), grid, dim3(256), 0, st, q, k, v, sk, sv,   \
-                     n_sink, bm, gate, out, part, S, Tbuf, P, kv_offset, H, W32, window,          \
+                     n_sink, bm, gate, out, part, S, Tbuf, P, kv_offset, H, Hkv, W32, window,     \
                      scale_log2, gate_dim, pl.nqt, pl.M, pl.tab)
   if (window > 0) {
     if (n_sink > 0)
@@ -574,7 +590,7 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #undef DSA_FLASH_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.items == pl.nqt) return e;
-  hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt * (kBQ / kMergeRows), H, B), dim3(256),
+  hipLaunchKernelGGL((merge_splits_kernel<DV>), dim3(pl.nqt * (kBQ / merge_rows<DV>()), H, B), dim3(256),
                      0, st, part, gate, out, S, H, pl.items, pl.nqt, scale_log2, gate_dim, pl.tab);
   return hipGetLastError();
 }
@@ -586,7 +602,7 @@ constexpr int kBitmapLdsMaxWords = 12288;  // 48 KiB of LDS
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv) {
   if (dtype != 1 || S < 16) return false;
   return (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128) ||
-         (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64);
+         (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64) || (Dqk == 256 && Dv == 256);
 }
 
 size_t bitmap_bytes(int B, int S, int T) {
@@ -604,7 +620,7 @@ size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv) {
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* sink_k,
                                const void* sink_v, int n_sink, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
-                               int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                               int kv_offset, int H, int Hkv, int Dqk, int Dv, int topk, int window,
                                float sm_scale, int gate_dim, void* workspace, hipStream_t st) {
   const int W32 = (T + 31) / 32;
   uint32_t* bm = (uint32_t*)workspace;
@@ -635,13 +651,14 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
 #define DSA_PREFILL_CASE(A, C)                                                                    \
   if (Dqk == A && Dv == C)                                                                        \
     return launch_dims<A, C>(qq, kk, vv, (const uint16_t*)sink_k, (const uint16_t*)sink_v, n_sink, \
-                             bm, gg, oo, B, S, T, past_len, kv_offset, H, W32, window,         \
+                             bm, gg, oo, B, S, T, past_len, kv_offset, H, Hkv, W32, window,    \
                              sl2, gate_dim, part, st);
   DSA_PREFILL_CASE(64, 64)
   DSA_PREFILL_CASE(128, 64)
   DSA_PREFILL_CASE(128, 128)
   DSA_PREFILL_CASE(192, 128)
   DSA_PREFILL_CASE(256, 128)
+  DSA_PREFILL_CASE(256, 256)
 #undef DSA_PREFILL_CASE
   return hipErrorInvalidValue;
 }

@@ -18,26 +18,29 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
                        void* workspace, hipStream_t stream);
 
 // Selection bitmap + MFMA flash attention with a bitmap or window mask
-// (attn_prefill.hip). Requires bf16, Dqk % 16 == 0, Dv % 32 == 0.
+// (attn_prefill.hip). Requires bf16 and a (Dqk, Dv) pair that
+// prefill_mfma_supported accepts. The caches hold Hkv heads; query head h
+// reads cache head h / (H / Hkv) (Hkv divides H; Hkv = H for expanded K/V).
 size_t bitmap_bytes(int B, int S, int T);
 size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv);
-// sink_k [n_sink,H,Dqk] / sink_v [n_sink,H,Dv]: attention sinks every query
+// sink_k [n_sink,Hkv,Dqk] / sink_v [n_sink,Hkv,Dv]: attention sinks every query
 // attends to (n_sink may be 0, then the pointers are unused).
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* sink_k,
                                const void* sink_v, int n_sink, const int32_t* indices,
                                const void* gate, void* out, int B, int S, int T, int past_len,
-                               int kv_offset, int H, int Dqk, int Dv, int topk, int window,
-                               float sm_scale, int gate_dim, void* workspace, hipStream_t stream);
+                               int kv_offset, int H, int Hkv, int Dqk, int Dv, int topk,
+                               int window, float sm_scale, int gate_dim, void* workspace,
+                               hipStream_t stream);
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv);
 
 // Split-K row-gather attention + merge (attn_gather.hip); any dtype, any S.
 // window > 0 selects the implicit window list, else `indices` is used; the
-// n_sink sink rows are entries in front of that list.
+// n_sink sink rows are entries in front of that list. Cache heads as above.
 size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries);
 hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
                          const void* sink_v, int n_sink, const int32_t* indices,
                          const void* gate, void* out, int B, int S, int T, int past_len,
-                         int kv_offset, int H, int Dqk, int Dv, int topk, int window,
+                         int kv_offset, int H, int Hkv, int Dqk, int Dv, int topk, int window,
                          float sm_scale, int gate_dim, int dtype, void* workspace,
                          hipStream_t stream);
 

@@ -198,3 +198,32 @@ def test_sink_workspace_sizes():
             == L.dsa_sparse_attn_decode_workspace_size(8, 128, 128, 2048))
     assert (L.dsa_sparse_attn_decode_pas_workspace_size(1, 4, 128, 16, 128)
             > L.dsa_sparse_attn_decode_workspace_size(1, 4, 128, 16))
+
+
+def swa_gqa(**kw):
+    a = dict(q=P, k=P, v=P, g=P, o=P, B=1, S=10, Tb=10, past=0, off=0, H=8, Hkv=2, nope=128,
+             rope=128, v_dim=256, W=4, sc=0.1, gd=1, dt=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().swa_attn_gqa(a["q"], a["k"], a["v"], a["g"], a["o"], a["B"], a["S"], a["Tb"],
+                                  a["past"], a["off"], a["H"], a["Hkv"], a["nope"], a["rope"],
+                                  a["v_dim"], a["W"], a["sc"], a["gd"], a["dt"], a["ws"], a["nb"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=0), 1), (dict(Hkv=3), 1), (dict(Hkv=16), 1), (dict(H=6, Hkv=4), 1),
+    (dict(W=0), 1), (dict(Tb=11), 1), (dict(k=None), 1), (dict(nope=8, rope=0), 2),
+    (dict(S=1, Tb=10, past=9), 3),  # gather path (decode) without a workspace
+])
+def test_swa_gqa_validation(kw, code):
+    assert swa_gqa(**kw) == code
+    assert dsa.dsa_last_error().startswith("swa_attn_gqa")
+
+
+def test_swa_gqa_workspace_sizes():
+    L = dsa.lib()
+    # same partial states as plain SWA: they are kept per query head
+    for args in [(1, 4096, 8, 256, 256, 512, 1), (1, 1, 8, 256, 256, 512, 1),
+                 (2, 5, 4, 48, 32, 16, 0)]:
+        assert L.swa_attn_gqa_workspace_size(*args) == L.swa_attn_workspace_size(*args)
+    assert L.swa_attn_gqa_workspace_size(1, 4096, 8, 256, 256, 512, 1) == 0

@@ -223,6 +223,8 @@ PREFILL_CASES = [
     (1, 200, 50, 3, 128, 64, 128, 64), (2, 130, 100, 2, 64, 64, 128, 200), (1, 77, 300, 4, 32, 32, 64, 33),
     (1, 64, 0, 2, 128, 128, 128, 64), (1, 96, 10, 2, 64, 64, 64, 16), (2, 8, 500, 5, 128, 64, 128, 128),
     (1, 1, 40, 3, 64, 64, 128, 41), (1, 300, 1800, 1, 128, 64, 128, 2048),
+    # head dims 256 / 256 (one workgroup per CU, long tiles split and merged)
+    (1, 150, 100, 2, 128, 128, 256, 64),
 ]
 
 
@@ -315,6 +317,34 @@ def test_swa_cases(B, S, P, W, H, nope, rope, Dv, dt, offset):
     _sync()
     ref = oracle.swa_attn(full["q"], kb, vb, full["gate"], P, kv_off, W, nope, rope)
     _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"swa {B, S, P, W}")
+
+
+# ------------------------------------------------- SWA, grouped KV heads
+@pytest.mark.parametrize("B,S,P,W,H,H_kv,nope,rope,Dv,dt,offset", [
+    (1, 300, 700, 512, 8, 2, 128, 128, 256, "bf16", True),   # Spark heads, MFMA path
+    (2, 200, 0, 64, 8, 2, 128, 64, 128, "bf16", False),
+    (1, 130, 5, 512, 6, 3, 64, 64, 64, "bf16", False),
+    (2, 100, 50, 32, 8, 8, 128, 128, 256, "bf16", True),     # H_kv = H at dims 256
+    (1, 1, 900, 512, 8, 2, 128, 128, 256, "bf16", True),     # decode (gather path)
+    (2, 5, 60, 16, 4, 1, 32, 16, 32, "f32", True),
+    (1, 20, 10, 8, 8, 2, 128, 128, 256, "f32", False),
+])
+def test_swa_gqa_cases(B, S, P, W, H, H_kv, nope, rope, Dv, dt, offset):
+    kv_off = max(0, P - W + 1) if offset else 0
+    T = P + S
+    Dqk = nope + rope
+    g = lambda shape, tid, sc: datagen.normal_host(shape, dt, W + S + H_kv, tid, sc)
+    q, gate = g((B, S, H, Dqk), 1, Dqk ** -0.25), g((B, S, H), 7, 1.0)
+    kb = g((B, T, H_kv, Dqk), 2, Dqk ** -0.25)[:, kv_off:].copy()
+    vb = g((B, T, H_kv, Dv), 3, 1.0)[:, kv_off:].copy()
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((B, S, H, Dv), float("nan"), dtype=tdt, device=DEV)
+    dsa.swa_attn_gqa(to_dev(q), to_dev(kb), to_dev(vb), to_dev(gate), out, P, kv_off, W, nope,
+                     rope)
+    _sync()
+    ref = oracle.swa_attn_gqa(q, kb, vb, gate, P, kv_off, W, nope, rope)
+    _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2,
+              f"swa gqa {B, S, P, W, H, H_kv, Dv, dt}")
 
 
 # ------------------------------------------------------------ full chain
