@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla-s4k")
-    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas",
+    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -188,6 +188,55 @@ class Layer:
         return st
 
 
+class SwaLayer:
+    """One sliding-window layer with grouped KV heads: a chunk of S tokens
+    after past_len cached ones, then one decode token. The K/V buffers hold
+    the window suffix only (row r = absolute position off + r)."""
+
+    def __init__(self, wl, torch, dsa, datagen):
+        self.wl, self.dsa = wl, dsa
+        dev = torch.device("cuda")
+        B, S, P, W = wl.B, wl.S, wl.past_len, wl.window
+        H, Hkv, Dqk, Dv = wl.H, wl.H_kv or wl.H, wl.Dqk, wl.v
+        E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=dev)
+        gen = lambda t, tid, sc, start=0: datagen.normal_device(t, wl.seed, tid, sc, start)
+        self.off = max(0, P - W + 1)
+        self.Tb = P + S - self.off
+        self.offd = max(0, P + S - W + 1)
+        self.Tbd = P + S + 1 - self.offd
+        self.k = gen(E(B, self.Tb + 1, Hkv, Dqk), datagen.TID_K, wl.scale_k, self.off * Hkv * Dqk)
+        self.v = gen(E(B, self.Tb + 1, Hkv, Dv), datagen.TID_V, wl.scale_v, self.off * Hkv * Dv)
+        self.q = gen(E(B, S + 1, H, Dqk), datagen.TID_Q, wl.scale_q)
+        self.g = gen(E(B, S + 1, H), datagen.TID_GATE, wl.scale_gate)
+        self.qc, self.gc = self.q[:, :S], self.g[:, :S]
+        self.qd, self.gd = self.q[:, S:].contiguous(), self.g[:, S:].contiguous()
+        self.kc, self.vc = self.k[:, : self.Tb], self.v[:, : self.Tb]
+        d0 = self.offd - self.off
+        self.kd = self.k[:, d0:d0 + self.Tbd].contiguous()
+        self.vd = self.v[:, d0:d0 + self.Tbd].contiguous()
+        self.o, self.od = E(B, S, H, Dv), E(B, 1, H, Dv)
+        ws = lambda s_: torch.empty(max(dsa.swa_attn_gqa_workspace_size(B, s_, H, Dqk, Dv, W, 1), 1),
+                                    dtype=torch.uint8, device=dev)
+        self.ws, self.wsd = ws(S), ws(1)
+        torch.cuda.synchronize()
+
+    def stages(self):
+        wl, dsa = self.wl, self.dsa
+        P, S, W = wl.past_len, wl.S, wl.window
+        return [
+            ("K5 swa_attn chunk", lambda: dsa.swa_attn_gqa(
+                self.qc, self.kc, self.vc, self.gc, self.o, P, self.off, W, wl.nope, wl.rope,
+                workspace=self.ws)),
+            ("D K5 swa_attn", lambda: dsa.swa_attn_gqa(
+                self.qd, self.kd, self.vd, self.gd, self.od, P + S, self.offd, W, wl.nope,
+                wl.rope, workspace=self.wsd)),
+        ]
+
+
+def make_layer(wl, torch, dsa, datagen):
+    return (SwaLayer if wl.swa_only else Layer)(wl, torch, dsa, datagen)
+
+
 def contiguous_view(t):
     return t if t.is_contiguous() else t.contiguous()
 
@@ -257,7 +306,11 @@ def work(wl):
     if wl.n_swa:
         W = wl.window
         win = float(B * np.sum(np.minimum(W, pos + 1)))
-        out["K5"] = {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * (win + sink)}
+        hkv = wl.H_kv or wl.H
+        out["K5"] = {"flops": 2.0 * wl.H * (wl.Dqk + wl.v) * (win + sink),
+                     # decode token: its window's K/V rows once, plus q and out
+                     "decode_bytes": esz * B * (min(W, T + 1) * hkv * (wl.Dqk + wl.v)
+                                                + wl.H * (wl.Dqk + wl.v))}
     return out
 
 
@@ -266,6 +319,13 @@ def summarize(wl, per_stage, total_ms):
     g = lambda name: per_stage[name]["mean_us"] * 1e-6
     r = {"workload": wl.name, "ms_per_step": total_ms,
          "stages_us": {k: round(v["mean_us"], 2) for k, v in per_stage.items()}}
+    if wl.swa_only:  # one grouped-KV SWA layer: chunk and decode token
+        t5, t5d = g("K5 swa_attn chunk"), g("D K5 swa_attn")
+        r["prefill_tokens_per_s"] = wl.B * wl.S / t5
+        r["K5_mfma_frac"] = w["K5"]["flops"] / t5 / PEAK_BF16
+        r["decode_us_per_step"] = t5d * 1e6
+        r["D_K5_hbm_frac"] = w["K5"]["decode_bytes"] / t5d / PEAK_HBM
+        return r
     t1, t2 = g("K1 index_scores"), g("K2 topk")
     r["K1_mfma_frac"] = w["K1"]["flops"] / t1 / PEAK_BF16
     r["K1_tflops"] = w["K1"]["flops"] / t1 / 1e12
@@ -378,7 +438,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = WORKLOADS[args.workload]
-    layer = Layer(wl, torch, dsa, datagen)
+    layer = make_layer(wl, torch, dsa, datagen)
     per_stage, total_ms, wall = time_layer(layer, args.steps, args.warmup, torch)
     main_r = summarize(wl, per_stage, total_ms)
     del layer
@@ -388,7 +448,7 @@ def main():
     for name in [s for s in args.also.split(",") if s]:
         if name == wl.name:
             continue
-        lay = Layer(WORKLOADS[name], torch, dsa, datagen)
+        lay = make_layer(WORKLOADS[name], torch, dsa, datagen)
         ps, tm, _ = time_layer(lay, args.also_steps, 2, torch)
         also[name] = summarize(WORKLOADS[name], ps, tm)
         del lay
@@ -396,8 +456,15 @@ def main():
         print(f"# {name}: {tm:.3f} ms/step", file=sys.stderr, flush=True)
 
     w = work(wl)
-    t3 = per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6 if wl.S > 1 else None
-    if t3 is not None:
+    t3 = per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6 if wl.S > 1 and not wl.swa_only else None
+    if wl.swa_only:
+        t5 = per_stage["K5 swa_attn chunk"]["mean_us"] * 1e-6
+        ach = w["K5"]["flops"] / t5 / 1e12
+        roof = {"kernel": "K5 swa_attn_gqa chunk (MFMA flash, window mask)", "bound": "mfma",
+                "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
+                "algorithmic_flops_per_launch": w["K5"]["flops"], "mean_launch_us": t5 * 1e6}
+    elif t3 is not None:
         ach = w["attn"]["flops"] / t3 / 1e12
         roof = {"kernel": "K3 sparse_attn_prefill (bitmap + MFMA flash)", "bound": "mfma",
                 "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
@@ -413,7 +480,7 @@ def main():
                 "traffic": None, "mean_launch_us": t4 * 1e6}
     roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not wl.swa_only:
         cpu = cpu_baseline(wl, args.cpu_seconds)
     line = {
         "metric": METRIC,

@@ -1,4 +1,4 @@
-"""The five workloads, as shapes plus the distribution of every input tensor.
+"""The workloads, as shapes plus the distribution of every input tensor.
 
 Every tensor is drawn from the seeded generator in this package: a normal
 N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
@@ -22,6 +22,11 @@ N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
   mla-s4k-pas, hybrid-512k-pas
                 the same with 128 attention sinks per layer (sink K/V drawn
                 like the cache's K/V, tensor ids 10 and 11).
+  spark-swa     one sliding-window layer with grouped KV heads (Spark-X2.5
+                page: 8 query heads over 2 KV heads, head_dim 256, window 512,
+                one gate logit per head): a 4096-token chunk after 131072
+                cached tokens, then one decode token; the K/V buffers hold
+                the window suffix only. N(0,1) inputs.
 
 Element (b, t, h, d) of a cache is element ((b*T_alloc + t)*H + h)*D + d of
 its stream, so a window buffer starting at absolute position kv_offset is the
@@ -55,6 +60,8 @@ class Workload:
     n_swa: int = 0            # SWA layers in the stack (hybrid: 2)
     decode_after: bool = False  # hybrid: one decode token after the chunk
     n_sink: int = 0            # attention sinks per layer (PAS), shared by the batch
+    H_kv: int = 0              # KV heads of grouped-KV SWA layers (0: H)
+    swa_only: bool = False     # one SWA layer and no DSA stages
     scale_q: float = 1.0
     scale_k: float = 1.0
     scale_v: float = 1.0
@@ -99,5 +106,9 @@ WORKLOADS["mla-s4k-pas"] = dataclasses.replace(WORKLOADS["mla-s4k"], name="mla-s
 WORKLOADS["hybrid-512k-pas"] = dataclasses.replace(WORKLOADS["hybrid-512k"],
                                                    name="hybrid-512k-pas", n_sink=128)
 
+WORKLOADS["spark-swa"] = Workload("spark-swa", BF16, B=1, S=4096, past_len=131072, H=8, nope=128,
+                                  rope=128, v=256, HI=0, DI=0, topk=0, seed=5, n_swa=1,
+                                  decode_after=True, H_kv=2, swa_only=True)
+
 ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k", "mla-s4k-pas",
-         "hybrid-512k-pas"]
+         "hybrid-512k-pas", "spark-swa"]

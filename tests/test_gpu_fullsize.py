@@ -291,3 +291,40 @@ def test_hybrid_512k_swa_layers():
             gh = host_row(wl, tid(datagen.TID_GATE), wl.scale_gate, s, H).reshape(1, 1, H)
             ref = oracle.swa_attn(qh, kc, vc, gh, p, p - W + 1, W, wl.nope, wl.rope)[0, 0]
             assert_rows_close(o.reshape(H, wl.v), ref, 2e-2, what=f"swa layer {j} row {s}")
+
+
+# ----------------------------------------------------------- spark-swa
+def test_spark_swa_chunk_and_decode():
+    """One grouped-KV SWA layer (8 query heads over 2 KV heads, dims 256):
+    the 4096-token chunk through the MFMA path and the decode token through
+    the gather path, sampled rows against the oracle on the window rows."""
+    wl = WORKLOADS["spark-swa"]
+    S, P, H, Hkv, W = wl.S, wl.past_len, wl.H, wl.H_kv, wl.window
+    Dqk, Dv = wl.Dqk, wl.v
+    off = P - W + 1
+    Tb = P + S - off
+    kb = dev_normal((1, Tb + 1, Hkv, Dqk), wl, datagen.TID_K, wl.scale_k, off * Hkv * Dqk)
+    vb = dev_normal((1, Tb + 1, Hkv, Dv), wl, datagen.TID_V, wl.scale_v, off * Hkv * Dv)
+    q = dev_normal((1, S + 1, H, Dqk), wl, datagen.TID_Q, wl.scale_q)
+    g = dev_normal((1, S + 1, H), wl, datagen.TID_GATE, wl.scale_gate)
+    out = torch.empty(1, S, H, Dv, dtype=torch.bfloat16, device=DEV)
+    dsa.swa_attn_gqa(q[:, :S], kb[:, :Tb], vb[:, :Tb], g[:, :S], out, P, off, W, wl.nope, wl.rope)
+    offd = P + S - W + 1
+    od = torch.empty(1, 1, H, Dv, dtype=torch.bfloat16, device=DEV)
+    dsa.swa_attn_gqa(q[:, S:].contiguous(), kb[:, offd - off:].contiguous(),
+                     vb[:, offd - off:].contiguous(), g[:, S:].contiguous(), od, P + S, offd, W,
+                     wl.nope, wl.rope)
+    rows = [0, 1, 511, 2047, S - 1]
+    got = from_dev(out[0, rows])
+    got_d = from_dev(od[0, 0])
+    del kb, vb, q, g, out, od
+    _free()
+    for s, o in list(zip(rows, got)) + [(S, got_d)]:
+        p = P + s
+        pos = list(range(p - W + 1, p + 1))
+        kc = compact_cache(wl, pos, 0, 0, Hkv, Dqk, datagen.TID_K, wl.scale_k)
+        vc = compact_cache(wl, pos, 0, 0, Hkv, Dv, datagen.TID_V, wl.scale_v)
+        qh = host_row(wl, datagen.TID_Q, wl.scale_q, s, H * Dqk).reshape(1, 1, H, Dqk)
+        gh = host_row(wl, datagen.TID_GATE, wl.scale_gate, s, H).reshape(1, 1, H)
+        ref = oracle.swa_attn_gqa(qh, kc, vc, gh, p, p - W + 1, W, wl.nope, wl.rope)[0, 0]
+        assert_rows_close(o.reshape(H, Dv), ref, 2e-2, what=f"spark-swa row {s}")
