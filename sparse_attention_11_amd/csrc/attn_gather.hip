@@ -210,8 +210,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 
   if (!hvalid) return;
-  // partial state: [row][split][h][DV + 2] = o[0..DV), m, l
-  float* pr = part + ((row * nsplit + split) * H + h) * (int64_t)(DV + 2);
+  // partial state: [row][split][h][DV + 4] = o[0..DV), m, l (16-byte rows)
+  float* pr = part + ((row * nsplit + split) * H + h) * (int64_t)(DV + 4);
 #pragma unroll
   for (int i = 0; i < VC; ++i) {
     const int c = sub + 8 * i;
@@ -226,76 +226,97 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 }
 
-// One wave per (row, head): split weights w_s = 2^(m_s - M) are computed once
-// into LDS, then every lane accumulates its dv columns over the splits.
+// One workgroup per (row, head). Thread i < nsplit reads split i's (m, l) and
+// forms its weight w_i = 2^(m_i - M) (M = the largest m); the output columns
+// are then summed over the splits by 256 / (DV / 4) groups of threads, each
+// taking every G-th split with eight splits' loads in flight, and the groups
+// are added through LDS. Every split is read once and the whole workgroup
+// waits on only a few memory round trips.
 template <int DT>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
                                                     const void* __restrict__ gate,
-                                                    void* __restrict__ out, int64_t nrh, int H,
-                                                    int DV, int nsplit, int gate_dim) {
-  __shared__ float wsh[4][kMaxSplit];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;  // row * H + h
-  if (rh >= nrh) return;
+                                                    void* __restrict__ out, int H, int DV,
+                                                    int nsplit, int gate_dim) {
+  __shared__ float wsh[kMaxSplit];
+  __shared__ float red[2][4];
+  __shared__ float4 accsh[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rh = blockIdx.x;  // row * H + h
   const int64_t row = rh / H;
   const int h = (int)(rh % H);
-  const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 2);
-  const int64_t sstride = (int64_t)H * (DV + 2);
-  float M = -INFINITY;
-  for (int sp = lane; sp < nsplit; sp += 64) M = fmaxf(M, pbase[sp * sstride + DV]);
+  const int64_t sstride = (int64_t)H * (DV + 4);
+  const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 4);
+  float mt = -INFINITY, lt = 0.0f;
+  if (tid < nsplit) {
+    mt = pbase[tid * sstride + DV];
+    lt = pbase[tid * sstride + DV + 1];
+  }
+  float M = mt;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   const float Muse = (M == -INFINITY) ? 0.0f : M;
-  float L = 0.0f;
-  for (int sp = lane; sp < nsplit; sp += 64) {
-    const float* ps = pbase + sp * sstride;
-    const float w = exp2f(ps[DV] - Muse);
-    wsh[wave][sp] = w;
-    L += w * ps[DV + 1];
-  }
+  const float wt = (tid < nsplit && mt != -INFINITY) ? exp2f(mt - Muse) : 0.0f;
+  if (tid < nsplit) wsh[tid] = wt;
+  float L = wt * lt;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  if (lane == 0) red[1][wave] = L;
+  // columns: group j of G sums splits j, j + G, ...; thread (j, cg) owns
+  // output columns 4 cg .. 4 cg + 3
+  const int ncg = DV / 4, G = 256 / ncg;
+  const int cg = tid % ncg, j = tid / ncg;
+  __syncthreads();
+  L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (j < G) {
+    const float* pc = pbase + 4 * cg;
+    constexpr int kU = 8;
+    for (int s0 = j; s0 < nsplit; s0 += G * kU) {
+      float4 x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int sp = s0 + G * u;
+        x[u] = sp < nsplit ? *(const float4*)(pc + sp * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int sp = s0 + G * u;
+        const float ww = sp < nsplit ? wsh[sp] : 0.0f;
+        acc.x = fmaf(x[u].x, ww, acc.x);
+        acc.y = fmaf(x[u].y, ww, acc.y);
+        acc.z = fmaf(x[u].z, ww, acc.z);
+        acc.w = fmaf(x[u].w, ww, acc.w);
+      }
+    }
+  }
+  accsh[tid] = acc;
+  __syncthreads();
+  if (tid >= ncg) return;
+  float4 t = accsh[tid];
+  for (int jj = 1; jj < G; ++jj) {
+    const float4 y = accsh[jj * ncg + tid];
+    t.x += y.x;
+    t.y += y.y;
+    t.z += y.z;
+    t.w += y.w;
+  }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float g1 = 1.0f;
   if (gate_dim == 1)
     g1 = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
-  // lane owns dv columns lane + 64 c (DV <= 256); splits are read 8 at a
-  // time with every load of a group in flight before the sums
-  constexpr int kC = 4, kU = 8;
-  float acc[kC] = {0.0f, 0.0f, 0.0f, 0.0f};
-  int sp = 0;
-  for (; sp + kU <= nsplit; sp += kU) {
-    float x[kU][kC];
+  const float tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int c = 0; c < kC; ++c) {
-        const int d = lane + 64 * c;
-        x[u][c] = d < DV ? pbase[(sp + u) * sstride + d] : 0.0f;
-      }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int c = 0; c < kC; ++c) acc[c] = fmaf(x[u][c], wsh[wave][sp + u], acc[c]);
-  }
-  for (; sp < nsplit; ++sp)
-#pragma unroll
-    for (int c = 0; c < kC; ++c) {
-      const int d = lane + 64 * c;
-      if (d < DV) acc[c] = fmaf(pbase[sp * sstride + d], wsh[wave][sp], acc[c]);
-    }
-#pragma unroll
-  for (int c = 0; c < kC; ++c) {
-    const int d = lane + 64 * c;
-    if (d >= DV) break;
+  for (int c = 0; c < 4; ++c) {
+    const int d = 4 * tid + c;
     float gg = g1;
     if (gate_dim > 1) {
       const int64_t gi = rh * DV + d;
       gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[gi]) : ((const float*)gate)[gi]);
     }
-    const float r = acc[c] * inv * gg;
+    const float r = tv[c] * inv * gg;
     if (DT)
       ((uint16_t*)out)[rh * DV + d] = f32_to_bf16(r);
     else
@@ -313,7 +334,9 @@ Plan make_plan(int64_t rows, int H, int nent) {
   // about 512 workgroups: enough to keep HBM busy, while fewer splits mean
   // less partial-state traffic through the merge
   int nsplit = (int)std::max<int64_t>(1, (512 + base - 1) / base);
-  const int max_split = std::max(1, (nent + 15) / 16);  // at least 16 entries per split
+  // at least one group of kG entries per split (measured on a 512-key window
+  // decode: 16 entries per split 15.7 us, 8 12.1, 4 11.4)
+  const int max_split = std::max(1, (nent + kG - 1) / kG);
   nsplit = std::min(std::min(nsplit, max_split), kMaxSplit);
   int per = (nent + nsplit - 1) / nsplit;
   per = (per + kG - 1) / kG * kG;
@@ -325,7 +348,7 @@ Plan make_plan(int64_t rows, int H, int nent) {
 
 size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries) {
   const Plan pl = make_plan(rows, H, nentries);
-  return (size_t)rows * pl.nsplit * H * (size_t)(Dv + 2) * sizeof(float);
+  return (size_t)rows * pl.nsplit * H * (size_t)(Dv + 4) * sizeof(float);
 }
 
 hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
@@ -387,13 +410,13 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nrh = rows * H;
-  const unsigned mg = (unsigned)((nrh + 3) / 4);
+  if (nrh > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<1>, dim3(mg), dim3(256), 0, st, part, gate, out, nrh, H, Dv,
-                       pl.nsplit, gate_dim);
+    hipLaunchKernelGGL(merge_kernel<1>, dim3((unsigned)nrh), dim3(256), 0, st, part, gate, out, H,
+                       Dv, pl.nsplit, gate_dim);
   else
-    hipLaunchKernelGGL(merge_kernel<0>, dim3(mg), dim3(256), 0, st, part, gate, out, nrh, H, Dv,
-                       pl.nsplit, gate_dim);
+    hipLaunchKernelGGL(merge_kernel<0>, dim3((unsigned)nrh), dim3(256), 0, st, part, gate, out, H,
+                       Dv, pl.nsplit, gate_dim);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@
 //                    paired (j, last-j) so every pair costs the same, pairs
 //                    dealt to XCDs round-robin.
 //  idx_rows_kernel   few-query calls (decode): the index heads become the
-//                    MFMA M axis; a wave streams 256 keys of k in blocks of 32.
+//                    MFMA M axis; a wave streams 128 or 512 keys of k in blocks
+//                    of 32.
 //  idx_f32_kernel    fp32 inputs: plain fp32 loops (parity-size workloads).
 #include "common.h"
 #include "kernels.h"
@@ -265,24 +266,28 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
 }
 
 // Few queries per call: MFMA M = index heads (NHB blocks of 32), N = 32 keys.
-// A wave streams kRowsKeys keys in blocks of 32; the query operand is loaded
+// A wave streams KPW keys in blocks of 32; the query operand is loaded
 // once per wave and the next block's keys are loaded during the current
 // block's MFMAs.
-constexpr int kRowsKeys = 512;  // keys per wave (measured best: fewer per-wave query loads, enough waves)
-template <int DI, int NHB, int MODE>
+// KPW keys per wave: 512 where that still gives 2048 waves (fewer per-wave
+// query loads), else 128 so that more waves stream the keys. Measured on
+// one 528385-key row (32 heads): 512 keys 35.9 us, 256 32.0, 128 29.7; on
+// 8 rows of 131072 (64 heads): 512 48.8 us, 256 54.2, 128 64.9.
+constexpr int kRowsWaves = 2048;
+template <int DI, int NHB, int MODE, int KPW>
 __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ w,
                                                        float* __restrict__ scores, int S, int T,
                                                        int P, int HI, float scale) {
   constexpr int KS = DI / 16;
-  constexpr int NB = kRowsKeys / 32;
+  constexpr int NB = KPW / 32;
   const int64_t row = blockIdx.y;
   const int b = (int)(row / S), s = (int)(row % S);
   const int p = P + s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 31, lh = lane >> 5;
-  const int tbase = (blockIdx.x * 4 + wave) * kRowsKeys;
+  const int tbase = (blockIdx.x * 4 + wave) * KPW;
   float* orow = scores + row * T;
   if (tbase >= T) return;
 
@@ -409,8 +414,16 @@ hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w,
 template <int DI, int NHB, int MODE>
 hipError_t launch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
                        int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
-  hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE>), dim3((T + 4 * kRowsKeys - 1) / (4 * kRowsKeys), B * S),
-                     dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale);
+  const int64_t rows = (int64_t)B * S;
+  auto waves = [&](int kpw) { return rows * ((T + kpw - 1) / kpw); };
+#define DSA_ROWS_LAUNCH(KPW)                                                                     \
+  hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE, KPW>), dim3((T + 4 * KPW - 1) / (4 * KPW), \
+                     (unsigned)rows), dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale)
+  if (waves(512) >= kRowsWaves)
+    DSA_ROWS_LAUNCH(512);
+  else
+    DSA_ROWS_LAUNCH(128);
+#undef DSA_ROWS_LAUNCH
   return hipGetLastError();
 }
 
