@@ -22,6 +22,13 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                 closed form, buffer-offset equivalence.
   swa_attn_gqa  pinned: torch SDPA with grouped KV heads (enable_gqa) under the
                 band mask; equals swa_attn on explicitly repeated KV heads.
+  index_quant_fp8
+                pinned: closed forms (a unit vector rotates to all ones),
+                torch's float8_e4m3fn conversion of the same scaled values,
+                scipy's Hadamard matrix within FP8 rounding, the scale rule.
+  index_scores_fp8
+                pinned: index_scores on the dequantised rows with scale / D;
+                Hadamard invariance of index_scores (H q . H k = D q . k).
 Parity unpinned by the pages (fixed by convention, tested in every mode):
 ReLU placement (per head by default), the two scale constants, and the
 inclusive window boundary.
@@ -85,6 +92,13 @@ def _load():
         lib.oracle_swa_attn_gqa.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             i32, i32, i32, i32, dbl, i32, vp]
         lib.oracle_swa_attn_gqa.restype = None
+        lib.oracle_e4m3_codes.argtypes = [vp, i64, vp]
+        lib.oracle_e4m3_codes.restype = None
+        lib.oracle_index_quant_fp8.argtypes = [vp, i64, i32, vp, vp]
+        lib.oracle_index_quant_fp8.restype = None
+        lib.oracle_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                i32, i32, dbl, i32, vp]
+        lib.oracle_index_scores_fp8.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         _lib = lib
@@ -229,4 +243,46 @@ def swa_attn_gqa(q, k_buf, v_buf, gate, past_len: int, kv_offset: int, window: i
                                 _dtype_of(q, k_buf, v_buf, gate), B, S, T_buf, past_len,
                                 kv_offset, H, H_kv, Dqk, Dv, window, float(sm_scale), gate_dim,
                                 _ptr(out))
+    return out
+
+
+def e4m3_codes(v) -> np.ndarray:
+    """float32 values with |v| <= 448 -> FP8 E4M3 codes (round to nearest, ties to even)."""
+    v = _c(np.asarray(v, np.float32))
+    assert np.all(np.abs(v) <= 448)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_codes(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def index_quant_fp8(x):
+    """x [..., D] uint16 bf16 bits (D a power of two) -> (codes [..., D] uint8 FP8 E4M3,
+    scales [...] float32): Hadamard-rotated rows, value = code * scale."""
+    x = _c(x)
+    assert x.dtype == np.uint16
+    D = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1]))
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    _load().oracle_index_quant_fp8(_ptr(x), rows, D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, past_len: int,
+                     scale: float | None = None, relu_mode: int = RELU_PER_HEAD) -> np.ndarray:
+    """q_codes [B,S,HI,DI] / q_scales [B,S,HI], k_codes [B,T,DI] / k_scales [B,T] (from
+    index_quant_fp8), w [B,S,HI] -> scores [B,S,T] float64."""
+    q_codes, k_codes, w = _c(q_codes), _c(k_codes), _c(w)
+    q_scales = _c(np.asarray(q_scales, np.float32))
+    k_scales = _c(np.asarray(k_scales, np.float32))
+    B, S, HI, DI = q_codes.shape
+    T = k_codes.shape[1]
+    assert k_codes.shape == (B, T, DI) and w.shape == (B, S, HI)
+    assert q_scales.shape == (B, S, HI) and k_scales.shape == (B, T)
+    if scale is None:
+        scale = DI ** -0.5
+    out = np.empty((B, S, T), np.float64)
+    _load().oracle_index_scores_fp8(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales),
+                                    _ptr(w), _dtype_of(w), B, S, T, past_len, HI, DI,
+                                    float(scale), relu_mode, _ptr(out))
     return out

@@ -24,6 +24,14 @@
  *                           n_sink learned K/V rows every query attends to
  *                           besides its selected or windowed keys
  *                           [openPangu-2.0 page §3.4 (PAS)]
+ *   oracle_index_quant_fp8, oracle_index_scores_fp8
+ *                        -- the indexer on FP8 operands: each q and k row is
+ *                           rotated by a Hadamard matrix and stored as FP8
+ *                           codes with one scale per row; scores are formed
+ *                           from those codes [A.X-K2 page, implementation
+ *                           notes: the reference indexer rotates with a
+ *                           Hadamard transform and scores in FP8; the
+ *                           rotation cancels since H q . H k = D q . k]
  *   oracle_swa_attn_gqa  -- sliding-window attention whose K/V buffers hold
  *                           fewer heads than q (grouped KV heads)
  *                           [Spark-X2.5 page, "why the gate": 8 query heads,
@@ -55,6 +63,13 @@
  *    the selected (or windowed) keys together.
  *  - Grouped KV heads: query head h reads KV head h / (H / H_kv), i.e.
  *    consecutive query heads share a KV head.
+ *  - FP8 indexer (the page names the steps, not their details): the rotation
+ *    is the Sylvester-ordered Walsh-Hadamard matrix with entries +-1 (no
+ *    normalisation; scores divide by D instead), computed by the fast
+ *    transform in fp32, stride 1 first. A row's scale is the power of two
+ *    2^e with the smallest e such that max|y| * 2^-e <= 448, and each code is
+ *    the OCP FP8 E4M3 value of y * 2^-e rounded to nearest, ties to even
+ *    (largest finite 448, subnormal step 2^-9). An all-zero row has scale 1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -123,6 +138,129 @@ void oracle_index_scores(const void *q_idx, const void *k_idx, const void *w,
                rd(k_idx, dtype, (b * T + t) * DI + d);
       double u = scale * dot;
       double wh = rd(w, dtype, bs * HI + h);
+      if (relu_mode == ORACLE_RELU_PER_HEAD)
+        total += wh * (u > 0.0 ? u : 0.0);
+      else
+        total += wh * u;
+    }
+    if (relu_mode == ORACLE_RELU_POST_SUM && !(total > 0.0)) total = 0.0;
+    out[e] = total;
+  }
+}
+
+/*
+ * FP8 E4M3 (OCP "e4m3fn": bias 7, 3 mantissa bits, no infinities, largest
+ * finite 448) of a float with |v| <= 448, rounded to nearest, ties to even.
+ * Written from the format's definition: subnormals are multiples of 2^-9
+ * below 2^-6; a normal value 2^E (1 + m/8) has code (E + 7) << 3 | m.
+ */
+static uint8_t e4m3_rne(float v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs((double)v);
+  if (a < 0x1p-6) { /* subnormal range (a result of 8 is the smallest normal) */
+    double q = rint(a * 512.0);
+    return (uint8_t)(sign | (uint8_t)q);
+  }
+  int E = ilogb(a);
+  double m = rint((ldexp(a, -E) - 1.0) * 8.0);
+  if (m >= 8.0) {
+    m = 0.0;
+    E += 1;
+  }
+  return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | (int)m));
+}
+
+/* FP8 E4M3 codes of n floats with |v| <= 448 (exposes e4m3_rne to the pins). */
+void oracle_e4m3_codes(const float *v, int64_t n, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_rne(v[i]);
+}
+
+/* The value of an FP8 E4M3 code. */
+static double e4m3_value(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+/*
+ * Rotate and quantise rows of bf16 values to FP8 [A.X-K2 page, implementation
+ * notes: Hadamard rotation, then FP8 quantisation, of the indexer's q and k].
+ *   x [rows, dim] bf16 bits (dim a power of two, <= 4096)
+ *   codes [rows, dim] FP8 E4M3, scales [rows]: row value = code * scale.
+ */
+void oracle_index_quant_fp8(const uint16_t *x, int64_t rows, int dim,
+                            uint8_t *codes, float *scales) {
+#pragma omp parallel
+  {
+    float *y = (float *)malloc(sizeof(float) * (size_t)dim);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int i = 0; i < dim; ++i) {
+        uint32_t bits = (uint32_t)x[r * dim + i] << 16;
+        memcpy(&y[i], &bits, sizeof(float));
+      }
+      /* fast Walsh-Hadamard transform in fp32: butterflies (a, b) ->
+       * (a + b, a - b) on pairs (i, i + h), h = 1, 2, 4, ... */
+      for (int h = 1; h < dim; h <<= 1)
+        for (int i = 0; i < dim; i += 2 * h)
+          for (int j = i; j < i + h; ++j) {
+            float a = y[j], b = y[j + h];
+            y[j] = a + b;
+            y[j + h] = a - b;
+          }
+      float amax = 0.0f;
+      for (int i = 0; i < dim; ++i)
+        if (fabsf(y[i]) > amax) amax = fabsf(y[i]);
+      if (amax == 0.0f) {
+        scales[r] = 1.0f;
+        for (int i = 0; i < dim; ++i) codes[r * dim + i] = 0;
+        continue;
+      }
+      /* smallest e with amax * 2^-e <= 448 */
+      int E = ilogbf(amax);
+      int e = (ldexpf(amax, -(E - 8)) <= 448.0f) ? E - 8 : E - 7;
+      scales[r] = ldexpf(1.0f, e);
+      for (int i = 0; i < dim; ++i)
+        codes[r * dim + i] = e4m3_rne(ldexpf(y[i], -e));
+    }
+    free(y);
+  }
+}
+
+/*
+ * Indexer scores from FP8 operands: the formula of oracle_index_scores on the
+ * dequantised rotated rows, divided by dim (the rotation scales every dot
+ * product by dim):
+ *   score[b,s,t] = sum_h w[b,s,h] * relu(scale / DI * (qh . kt))
+ *   qh = q_codes[b,s,h,:] * q_scales[b,s,h], kt = k_codes[b,t,:] * k_scales[b,t]
+ * with the causal mask and relu_mode of oracle_index_scores.
+ */
+void oracle_index_scores_fp8(const uint8_t *q_codes, const float *q_scales,
+                             const uint8_t *k_codes, const float *k_scales,
+                             const void *w, int w_dtype, int B, int S, int T,
+                             int past_len, int HI, int DI, double scale,
+                             int relu_mode, double *out) {
+  int64_t n = (int64_t)B * S * T;
+#pragma omp parallel for schedule(dynamic, 256)
+  for (int64_t e = 0; e < n; ++e) {
+    int64_t t = e % T;
+    int64_t bs = e / T;
+    int64_t s = bs % S;
+    int64_t b = bs / S;
+    int64_t p = (int64_t)past_len + s;
+    if (t > p) {
+      out[e] = -INFINITY;
+      continue;
+    }
+    double total = 0.0;
+    for (int h = 0; h < HI; ++h) {
+      const uint8_t *qc = q_codes + (bs * HI + h) * DI;
+      const uint8_t *kc = k_codes + (b * T + t) * DI;
+      double dot = 0.0;
+      for (int d = 0; d < DI; ++d) dot += e4m3_value(qc[d]) * e4m3_value(kc[d]);
+      double u = scale / DI * dot * (double)q_scales[bs * HI + h] *
+                 (double)k_scales[b * T + t];
+      double wh = rd(w, w_dtype, bs * HI + h);
       if (relu_mode == ORACLE_RELU_PER_HEAD)
         total += wh * (u > 0.0 ? u : 0.0);
       else

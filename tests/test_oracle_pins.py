@@ -476,3 +476,160 @@ def test_swa_gqa_equals_swa_on_repeated_kv_heads():
     same = oracle.swa_attn_gqa(q, np.repeat(kb, H // H_kv, axis=2),
                                np.repeat(vb, H // H_kv, axis=2), g, P, 0, W, 16, 0)
     np.testing.assert_array_equal(same, ref)
+
+
+# ------------------------------------------------------------ FP8 indexer
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_value(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def _torch_e4m3(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_table():
+    """Value of every finite E4M3 code (from the format's definition)."""
+    c = np.arange(256)
+    e, m = (c >> 3) & 15, c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where(c & 0x80, -v, v)
+    finite = (c & 0x7F) != 0x7F
+    return c[finite], v[finite]
+
+
+def test_e4m3_rounding_matches_torch_and_brute_force():
+    codes, vals = _e4m3_table()
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[1:] + pos[:-1]) / 2  # every tie between neighbours
+    rng = np.random.default_rng(5)
+    rand = rng.uniform(-448, 448, 20000) * 2.0 ** rng.integers(-14, 1, 20000)
+    v = np.concatenate([pos, -pos, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rand, [0.0, -0.0, 448.0, -448.0, 2 ** -10, 2 ** -9 * 1.5]]).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    got = oracle.e4m3_codes(v)
+    np.testing.assert_array_equal(got, _torch_e4m3(v))
+    # brute force: the nearest finite value, ties to the even code
+    best = np.empty(len(v), np.int64)
+    for i, x in enumerate(v.astype(np.float64)):
+        d = np.abs(vals - x)
+        cand = codes[d == d.min()]
+        cand = cand[(cand & 0x80) == (0x80 if np.signbit(x) else 0)] if len(cand) > 1 else cand
+        even = cand[(cand & 1) == 0]
+        best[i] = even[0] if len(even) else cand[0]
+    mag = lambda c: c & 0x7F
+    np.testing.assert_array_equal(mag(got), mag(best))
+
+
+@pytest.mark.parametrize("D", [8, 32, 128])
+def test_fp8_quant_unit_vectors_closed_form(D):
+    # H e_j is column j of the Hadamard matrix: entries (-1)^popcount(i & j), so
+    # every rotated value is +-1: scale 2^-8, codes +-256 (0x78 / 0xF8)
+    x = np.zeros((D, D), np.uint16)
+    x[np.arange(D), np.arange(D)] = 0x3F80  # bf16 1.0
+    codes, scales = oracle.index_quant_fp8(x)
+    i = np.arange(D)
+    parity = np.array([[bin(a & b).count("1") & 1 for a in i] for b in i])
+    np.testing.assert_array_equal(codes, np.where(parity == 1, 0xF8, 0x78))
+    np.testing.assert_array_equal(scales, np.full(D, 2.0 ** -8, np.float32))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fp8_quant_equals_torch_e4m3_of_exact_rotation(D):
+    # mantissas in [1, 2) times 2^0..2^3: every butterfly sum is exact in fp32, so
+    # the rotation equals scipy's Hadamard product; the codes must be torch's
+    # float8_e4m3fn of the rows scaled by 2^-e, e the smallest with max|y| 2^-e <= 448
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(D)
+    R = 64
+    x = (rng.choice([-1, 1], (R, D)) * (1 + rng.integers(0, 128, (R, D)) / 128.0)
+         * 2.0 ** rng.integers(0, 4, (R, D))).astype(np.float32)
+    xb = _bf16_bits(x)
+    y = _bf16_value(xb).astype(np.float64) @ hadamard(D).T.astype(np.float64)
+    codes, scales = oracle.index_quant_fp8(xb)
+    amax = np.abs(y).max(axis=1)
+    e = np.log2(scales.astype(np.float64))
+    assert np.all(e == np.round(e))
+    assert np.all((amax / scales > 224) & (amax / scales <= 448))
+    np.testing.assert_array_equal(codes, _torch_e4m3((y / scales[:, None]).astype(np.float32)))
+
+
+def test_fp8_quant_random_rows_within_rounding():
+    from scipy.linalg import hadamard
+    D = 128
+    rng = np.random.default_rng(11)
+    xb = _bf16_bits(rng.standard_normal((200, D)).astype(np.float32))
+    xb[7] = 0  # an all-zero row: scale 1, codes 0
+    codes, scales = oracle.index_quant_fp8(xb)
+    assert scales[7] == 1.0 and not codes[7].any()
+    y = _bf16_value(xb).astype(np.float64) @ hadamard(D).T
+    _, vals = _e4m3_table()
+    table = np.zeros(256)
+    table[_e4m3_table()[0]] = vals
+    deq = table[codes] * scales[:, None]
+    # E4M3 keeps 3 mantissa bits: half a unit in the last place is 1/16 relative;
+    # below 2^-6 the step is 2^-9 (times the row scale)
+    err = np.abs(deq - y)
+    assert np.all(err <= np.abs(y) / 16 + 2.0 ** -10 * scales[:, None] + 1e-12)
+
+
+def test_fp8_scores_equal_index_scores_of_dequantised_rows():
+    # the FP8 scorer is index_scores on the dequantised rotated rows with scale / D
+    B, S, T, HI, D, P = 1, 6, 9, 3, 32, 3
+    rng = np.random.default_rng(3)
+    q = _bf16_bits(rng.standard_normal((B, S, HI, D)))
+    k = _bf16_bits(rng.standard_normal((B, T, D)))
+    w = _bf16_bits(rng.standard_normal((B, S, HI)))
+    qc, qs = oracle.index_quant_fp8(q)
+    kc, ks = oracle.index_quant_fp8(k)
+    codes, vals = _e4m3_table()
+    table = np.zeros(256)
+    table[codes] = vals
+    qd = (table[qc] * qs[..., None]).astype(np.float32)  # exact in fp32
+    kd = (table[kc] * ks[..., None]).astype(np.float32)
+    for mode in (0, 1, 2):
+        got = oracle.index_scores_fp8(qc, qs, kc, ks, w, P, relu_mode=mode)
+        ref = oracle.index_scores(qd, kd, _bf16_value(w), P, scale=D ** -0.5 / D, relu_mode=mode)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_index_scores_invariant_under_hadamard_rotation():
+    # rotating q and k by the same Hadamard matrix multiplies every dot product by D
+    # (the page's reason for scoring the rotated rows); small integers keep H q exact
+    from scipy.linalg import hadamard
+    B, S, T, HI, D, P = 1, 5, 8, 2, 16, 3
+    rng = np.random.default_rng(9)
+    q = rng.integers(-4, 5, (B, S, HI, D)).astype(np.float32)
+    k = rng.integers(-4, 5, (B, T, D)).astype(np.float32)
+    w = rng.standard_normal((B, S, HI)).astype(np.float32)
+    Hm = hadamard(D).astype(np.float32)
+    ref = oracle.index_scores(q, k, w, P, scale=0.25)
+    got = oracle.index_scores(q @ Hm.T, k @ Hm.T, w, P, scale=0.25 / D)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_scores_track_bf16_scores():
+    # FP8 rounding moves scores by a few percent of their rms on average (measured
+    # here: mean 3%, max 16%), and the top 64 of 512 keys keep most of their
+    # members (measured 96%): properties of the approximation, not parity bounds
+    B, S, T, HI, D = 1, 4, 512, 8, 128
+    rng = np.random.default_rng(21)
+    q = _bf16_bits(rng.standard_normal((B, S, HI, D)) / np.sqrt(D))
+    k = _bf16_bits(rng.standard_normal((B, T, D)))
+    w = _bf16_bits(rng.standard_normal((B, S, HI)) / np.sqrt(HI))
+    P = T - S
+    ref = oracle.index_scores(q, k, w, P)
+    qc, qs = oracle.index_quant_fp8(q)
+    kc, ks = oracle.index_quant_fp8(k)
+    got = oracle.index_scores_fp8(qc, qs, kc, ks, w, P)
+    fin = np.isfinite(ref)
+    rms = np.sqrt(np.mean(ref[fin] ** 2))
+    err = np.abs(got[fin] - ref[fin])
+    assert np.mean(err) < 0.06 * rms and np.max(err) < 0.3 * rms
+    a = oracle.topk(ref.astype(np.float32), 64)
+    b = oracle.topk(got.astype(np.float32), 64)
+    recall = np.mean([len(set(a[0, s]) & set(b[0, s])) / 64 for s in range(S)])
+    assert recall > 0.85
