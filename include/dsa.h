@@ -93,6 +93,38 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float*
                      int relu_mode, int dtype, hipStream_t stream);
 
 /*
+ * The indexer on FP8 operands ([AXK2] implementation notes: the reference
+ * indexer rotates q and k with a Hadamard transform and scores FP8-quantised
+ * copies; the rotation cancels in the dot products, so the scores
+ * approximate dsa_index_scores). Two calls:
+ *
+ * dsa_index_quant_fp8 rotates each row of x [rows, dim] (bf16) by the
+ * Sylvester-ordered Walsh-Hadamard matrix with +-1 entries (fast transform in
+ * fp32, stride 1 first), picks the row scale 2^e with the smallest e such
+ * that max|y| * 2^-e <= 448 (1 for an all-zero row), and stores
+ *   codes [rows, dim]  OCP FP8 E4M3 (e4m3fn) of y * 2^-e, round to nearest even
+ *   scales [rows]      fp32 2^e: a row's value is code * scale
+ * Use it on q_idx (rows = B*S*n_idx_heads) every call and on the new rows of
+ * the indexer key cache (rows = B*T, or just the appended ones) when they are
+ * written. dim in {32, 64, 128}; dtype must be DSA_BF16 (DSA_F32 is
+ * DSA_ERR_UNSUPPORTED).
+ *
+ * dsa_index_scores_fp8 computes, with the causal mask of dsa_index_scores,
+ *   score[b,s,t] = sum_h w[b,s,h] * relu(scale / idx_dim * (qh . kt))
+ *   qh = q_codes[b,s,h,:] * q_scales[b,s,h],  kt = k_codes[b,t,:] * k_scales[b,t]
+ * (the 1 / idx_dim undoes the unnormalised rotation). q_codes
+ * [B,S,n_idx_heads,idx_dim], q_scales [B,S,n_idx_heads], k_codes [B,T,idx_dim],
+ * k_scales [B,T], w [B,S,n_idx_heads] (dtype), scores [B,S,T] fp32 written in
+ * full. Supported: idx_dim 128, dtype DSA_BF16; every relu_mode.
+ */
+int dsa_index_quant_fp8(const void* x, uint8_t* codes, float* scales, long long rows, int dim,
+                        int dtype, hipStream_t stream);
+int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                         const float* k_scales, const void* w, float* scores, int B, int S, int T,
+                         int past_len, int n_idx_heads, int idx_dim, float scale, int relu_mode,
+                         int dtype, hipStream_t stream);
+
+/*
  * Per-query top-k of the score rows ([AXK2] §1: the indexer returns the top
  * index_topk positions as int32 [B,S,topk]; AXK2Config: index_topk, clamped
  * to the number of keys by the caller).

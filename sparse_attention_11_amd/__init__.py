@@ -35,6 +35,7 @@ _EXPORTS = [
     "dsa_sparse_attn_decode_pas_workspace_size", "dsa_sparse_attn_decode_pas",
     "swa_attn_pas_workspace_size", "swa_attn_pas",
     "swa_attn_gqa_workspace_size", "swa_attn_gqa",
+    "dsa_index_quant_fp8", "dsa_index_scores_fp8",
 ]
 MAX_SINKS = 256
 
@@ -88,13 +89,17 @@ def lib():
         L.swa_attn_pas_workspace_size.restype = sz
         L.swa_attn_pas.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+        L.dsa_index_quant_fp8.argtypes = [vp, vp, vp, ctypes.c_longlong, i32, i32, vp]
+        L.dsa_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           f32, i32, i32, vp]
         L.swa_attn_gqa_workspace_size.argtypes = [i32] * 7
         L.swa_attn_gqa_workspace_size.restype = sz
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, i32, i32, vp, sz, vp]
         for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
-                   "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa"):
+                   "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
+                   "dsa_index_quant_fp8", "dsa_index_scores_fp8"):
             getattr(L, fn).restype = i32
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -351,6 +356,33 @@ def swa_attn_gqa(q, k_buf, v_buf, gate, out, past_len: int, kv_offset: int, wind
         kv_offset, H, H_kv, qk_nope_dim, qk_rope_dim, Dv, window, sm_scale, _gate_dim(gate, Dv),
         dt, _ptr(workspace), nbytes, _stream(stream)))
     return out
+
+
+def dsa_index_quant_fp8(x, codes, scales, stream=None):
+    """x [..., D] bf16 -> codes [..., D] uint8 (FP8 E4M3 of the Hadamard-rotated rows),
+    scales [...] float32 (one power of two per row)."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if tuple(codes.shape) != tuple(x.shape) or tuple(scales.shape) != tuple(x.shape[:-1]):
+        raise ValueError("codes must match x and scales x.shape[:-1]")
+    _check("dsa_index_quant_fp8", lib().dsa_index_quant_fp8(
+        _ptr(x), _ptr(codes), _ptr(scales), rows, D, _dtype(x), _stream(stream)))
+    return codes, scales
+
+
+def dsa_index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, scores, past_len: int,
+                         scale: float | None = None, relu_mode: int = RELU_PER_HEAD,
+                         stream=None):
+    """q_codes [B,S,HI,D] / q_scales [B,S,HI], k_codes [B,T,D] / k_scales [B,T] (from
+    dsa_index_quant_fp8), w [B,S,HI] bf16 -> scores [B,S,T] float32."""
+    B, S, HI, D = q_codes.shape
+    T = k_codes.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    _check("dsa_index_scores_fp8", lib().dsa_index_scores_fp8(
+        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(w), _ptr(scores),
+        B, S, T, past_len, HI, D, scale, relu_mode, _dtype(w), _stream(stream)))
+    return scores
 
 
 def dsa_status_string(status: int) -> str:

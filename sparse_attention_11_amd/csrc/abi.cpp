@@ -239,6 +239,47 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float*
                     fn);
 }
 
+int dsa_index_quant_fp8(const void* x, uint8_t* codes, float* scales, long long rows, int dim,
+                        int dtype, hipStream_t stream) {
+  const char* fn = "dsa_index_quant_fp8";
+  g_err.clear();
+  if (!x || !codes || !scales) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (rows < 1 || dim < 1) return fail(DSA_ERR_INVALID_ARG, "%s: rows and dim must be >= 1", fn);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 input only", fn);
+  if (dim != 32 && dim != 64 && dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: dim must be 32, 64 or 128 (got %d)", fn, dim);
+  return hip_status(dsa::launch_quant_fp8(x, codes, scales, rows, dim, stream), fn);
+}
+
+int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                         const float* k_scales, const void* w, float* scores, int B, int S, int T,
+                         int past_len, int n_idx_heads, int idx_dim, float scale, int relu_mode,
+                         int dtype, hipStream_t stream) {
+  const char* fn = "dsa_index_scores_fp8";
+  g_err.clear();
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !w || !scores)
+    return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || S < 1 || T < 1 || n_idx_heads < 1 || idx_dim < 1 || past_len < 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1 and past_len >= 0", fn);
+  if ((long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T (%d) < past_len + S (%d + %d)", fn, T, past_len, S);
+  if (!finite_pos(scale)) return fail(DSA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (relu_mode < DSA_RELU_PER_HEAD || relu_mode > DSA_RELU_POST_SUM)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad relu_mode %d", fn, relu_mode);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 weights only", fn);
+  if (idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: idx_dim must be 128 (got %d)", fn, idx_dim);
+  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  return hip_status(dsa::launch_index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, scores,
+                                                 B, S, T, past_len, n_idx_heads, idx_dim, scale,
+                                                 relu_mode, stream),
+                    fn);
+}
+
 size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
   if (B < 1 || S < 1 || T < 1 || topk < 1) return 0;
   return dsa::topk_workspace_bytes(B, S, T, topk);

@@ -25,6 +25,7 @@
 //                    of 32.
 //  idx_f32_kernel    fp32 inputs: plain fp32 loops (parity-size workloads).
 #include "common.h"
+#include "idx_tiles.h"
 #include "kernels.h"
 
 namespace dsa {
@@ -32,14 +33,8 @@ namespace {
 
 constexpr int kWaveK = 128;            // keys per wave (8 MFMA M blocks of 16)
 constexpr int kTileK = 4 * kWaveK;     // keys per workgroup
+static_assert(kTileK == kIdxTileK, "tile schedule");
 constexpr int kStageBytes = 16384;     // query operands staged in LDS per step
-
-// Key tiles a query tile of tq queries needs (the causal triangle).
-__host__ __device__ __forceinline__ int tiles_for_qtile(int qt, int tq, int S, int P, int nkt) {
-  int last_q = min((qt + 1) * tq, S) - 1;
-  int c = (P + last_q) / kTileK + 1;
-  return c < nkt ? c : nkt;
-}
 
 // One workgroup = 16 QG queries x 512 keys; wave w keeps keys 128w..128w+127
 // of the tile in registers as 16x16x32 MFMA A operands for the whole kernel,
@@ -67,30 +62,9 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kStageBytes];
 
   const int b = blockIdx.y;
-  // block -> (query tile, key tile); tiles paired (j, nqt-1-j), pairs dealt
-  // round-robin to the 8 XCDs
-  const int pid = blockIdx.x;
-  const int xcd = pid & 7;
-  const int n = pid >> 3;
-  const int slot = n / maxlen;
-  int u = n - slot * maxlen;
-  const int j = slot * 8 + xcd;
-  if (j >= npairs) return;
-  const int qa = j, qb = nqt - 1 - j;
-  const int ca = tiles_for_qtile(qa, kTileQ, S, P, nkt);
-  const int cb = qb == qa ? 0 : tiles_for_qtile(qb, kTileQ, S, P, nkt);
-  const int v = u;  // index of this workgroup among the pair's ca + cb
-  int qt, kt;
-  if (u < ca) {
-    qt = qa;
-    kt = u;
-  } else {
-    if (qb == qa) return;
-    u -= ca;
-    if (u >= cb) return;
-    qt = qb;
-    kt = u;
-  }
+  IdxTile tile;
+  if (!idx_tile_of(blockIdx.x, kTileQ, S, P, nqt, nkt, npairs, maxlen, &tile)) return;
+  const int qt = tile.qt, kt = tile.kt;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -209,35 +183,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
 
   // lane (lq, lg) holds keys kw0 + 16 kb + 4 lg + e of query q0 + 16 qg + lq
   const bool vec = (T & 3) == 0;
-  // Key tiles above the diagonal get -inf. The pair's (nkt - ca) + (nkt - cb)
-  // such (query tile, key tile) units are dealt round-robin to its ca + cb
-  // workgroups, whose counts nearly match, so the fill rides along with the
-  // products instead of a separate pass over HBM.
-  {
-    const int na = nkt - ca, nunits = na + (qb == qa ? 0 : nkt - cb);
-    for (int un = v; un < nunits; un += ca + cb) {
-      const int fq = un < na ? qa : qb;
-      const int fk = un < na ? ca + un : cb + (un - na);
-      const int tid = threadIdx.x;
-#pragma unroll
-      for (int rr = 0; rr < kTileQ; rr += 16) {
-        const int fs = fq * kTileQ + rr + tid / 16;
-        if (fs >= S) continue;
-        float* frow = scores + ((int64_t)b * S + fs) * T;
-#pragma unroll
-        for (int i = 0; i < kTileK / 64; ++i) {
-          const int t0 = fk * kTileK + 4 * (tid % 16 + 16 * i);
-          if (vec && t0 + 3 < T) {
-            *(float4*)(frow + t0) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (t0 + e < T) frow[t0 + e] = -INFINITY;
-          }
-        }
-      }
-    }
-  }
+  idx_fill_upper<kTileQ>(scores, tile, b, S, T, nkt, vec);
 #pragma unroll
   for (int qg = 0; qg < kQG; ++qg) {
     const int s = q0 + 16 * qg + lq;
@@ -393,21 +339,10 @@ __global__ __launch_bounds__(256) void idx_f32_kernel(const float* __restrict__ 
 template <int DI, int QG, int MODE>
 hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
                         int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
-  constexpr int kTileQ = 16 * QG;
-  const int nqt = (S + kTileQ - 1) / kTileQ;
-  const int nkt = (T + kTileK - 1) / kTileK;
-  const int npairs = (nqt + 1) / 2;
-  int maxlen = 1;
-  for (int j = 0; j < npairs; ++j) {
-    int len = tiles_for_qtile(j, kTileQ, S, P, nkt);
-    if (nqt - 1 - j != j) len += tiles_for_qtile(nqt - 1 - j, kTileQ, S, P, nkt);
-    if (len > maxlen) maxlen = len;
-  }
-  const int64_t slots = (npairs + 7) / 8;
-  const int64_t gx = 8 * slots * (int64_t)maxlen;
-  if (gx > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((idx_tile_kernel<DI, QG, MODE>), dim3((unsigned)gx, B), dim3(256), 0, st, q, k,
-                     w, scores, S, T, P, HI, scale, nqt, nkt, npairs, maxlen);
+  const IdxGrid g = idx_grid(S, T, P, 16 * QG);
+  if (g.gx > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((idx_tile_kernel<DI, QG, MODE>), dim3((unsigned)g.gx, B), dim3(256), 0, st, q,
+                     k, w, scores, S, T, P, HI, scale, g.nqt, g.nkt, g.npairs, g.maxlen);
   return hipGetLastError();
 }
 

@@ -12,6 +12,16 @@ hipError_t launch_index_scores(const void* q_idx, const void* k_idx, const void*
                                int B, int S, int T, int past_len, int HI, int DI, float scale,
                                int relu_mode, int dtype, hipStream_t stream);
 
+// FP8 indexer (index_fp8.hip): Hadamard rotation + E4M3 codes with one
+// power-of-two scale per row (dim 32, 64 or 128, bf16 input); scores from
+// the codes (idx_dim 128, bf16 weights).
+hipError_t launch_quant_fp8(const void* x, uint8_t* codes, float* scales, int64_t rows, int dim,
+                            hipStream_t stream);
+hipError_t launch_index_scores_fp8(const uint8_t* q_codes, const float* q_scales,
+                                   const uint8_t* k_codes, const float* k_scales, const void* w,
+                                   float* scores, int B, int S, int T, int P, int HI, int DI,
+                                   float scale, int relu_mode, hipStream_t stream);
+
 // Per-row top-k (topk.hip).
 size_t topk_workspace_bytes(int B, int S, int T, int topk);
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,

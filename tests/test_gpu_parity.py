@@ -464,3 +464,84 @@ def test_swa_with_sinks(B, S, P, W, H, nope, rope, Dv, n_sink, dt):
     ref = oracle.swa_attn(full["q"], kb, vb, full["gate"], P, kv_off, W, nope, rope,
                           sink_k=sk, sink_v=sv)
     _cmp_attn(from_dev(out), ref, RTOL[F32] if dt == "f32" else 2e-2, f"swa+sinks {B, S, P, W, n_sink}")
+
+
+# ------------------------------------------------------------ FP8 indexer
+def _fp8_rows(R, D, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((R, D)) * 2.0 ** rng.integers(-20, 20, (R, 1))).astype(np.float32)
+    if R >= 4:
+        x[0] = 0.0                   # all-zero row: scale 1, codes 0
+        x[1] = 0.0
+        x[1, 3] = -3.0               # one spike: every rotated value is +-3
+        x[2] = 1e-30                 # tiny rows stay normal in fp32 after the rotation
+        x[3, : D // 2] = 448.0       # large values
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("R,D", [(1, 32), (37, 32), (300, 64), (1000, 128), (4097, 128)])
+def test_quant_fp8_bit_exact(R, D):
+    xh = _fp8_rows(R, D, seed=R + D)
+    codes = torch.empty(R, D, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(R, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_quant_fp8(to_dev(xh), codes, scales)
+    _sync()
+    rc, rs = oracle.index_quant_fp8(xh)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+FP8_CASES = [  # (B, S, P, HI, mode): idx_dim 128
+    (1, 200, 0, 64, 0), (2, 130, 73, 5, 0), (1, 257, 600, 9, 1), (1, 1000, 500, 13, 2),
+    (2, 1, 999, 64, 0), (1, 3, 40, 130, 0), (1, 600, 0, 17, 0),
+]
+
+
+@pytest.mark.parametrize("B,S,P,HI,mode", FP8_CASES)
+def test_index_scores_fp8_cases(B, S, P, HI, mode):
+    T, D = P + S, 128
+    seed = 300 + S + HI
+    g = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", seed, tid, sc)
+    q, k, w = g((B, S, HI, D), 4, D ** -0.5), g((B, T, D), 5, 1.0), g((B, S, HI), 6, HI ** -0.5)
+    qc = torch.empty(B, S, HI, D, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(B, S, HI, dtype=torch.float32, device=DEV)
+    kc = torch.empty(B, T, D, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(B, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_quant_fp8(to_dev(q), qc, qs)
+    dsa.dsa_index_quant_fp8(to_dev(k), kc, ks)
+    sc = torch.full((B, S, T), float("nan"), dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores_fp8(qc, qs, kc, ks, to_dev(w), sc, P, relu_mode=mode)
+    _sync()
+    rqc, rqs = oracle.index_quant_fp8(q)
+    rkc, rks = oracle.index_quant_fp8(k)
+    np.testing.assert_array_equal(qc.cpu().numpy(), rqc)
+    np.testing.assert_array_equal(kc.cpu().numpy(), rkc)
+    np.testing.assert_array_equal(ks.cpu().numpy(), rks)
+    ref = oracle.index_scores_fp8(rqc, rqs, rkc, rks, w, P, relu_mode=mode)
+    # same codes on both sides; the FP8 MFMA sums its products with a few bits
+    # less than fp32 (measured about 1e-4 of the sum of |products|)
+    assert_rows_close(sc.cpu().numpy(), ref, 1e-3, what=f"fp8 scores {B, S, P, HI, mode}")
+
+
+def test_index_fp8_top_k_recall_against_bf16():
+    # the approximation keeps most of the exact indexer's top-k (a property of
+    # FP8 scoring, measured here; not a parity bound)
+    B, S, P, HI, D, K = 1, 64, 2000, 16, 128, 256
+    T = P + S
+    g = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", 77, tid, sc)
+    q, k, w = g((B, S, HI, D), 4, D ** -0.5), g((B, T, D), 5, 1.0), g((B, S, HI), 6, HI ** -0.5)
+    qc = torch.empty(B, S, HI, D, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(B, S, HI, dtype=torch.float32, device=DEV)
+    kc = torch.empty(B, T, D, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(B, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_quant_fp8(to_dev(q), qc, qs)
+    dsa.dsa_index_quant_fp8(to_dev(k), kc, ks)
+    sc = torch.empty(B, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores_fp8(qc, qs, kc, ks, to_dev(w), sc, P)
+    idx = torch.empty(B, S, K, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(sc, idx)
+    _sync()
+    exact = oracle.topk(oracle.index_scores(q, k, w, P).astype(np.float32), K)
+    got = idx.cpu().numpy()
+    recall = np.mean([len(set(got[0, s]) & set(exact[0, s])) / K for s in range(S)])
+    assert recall > 0.85, recall
