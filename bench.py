@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA layer prefill tokens/s + decode µs/step; % MFMA / HBM roofline"
 PEAK_BF16 = 2.5e15
+PEAK_FP8 = 5.0e15
 PEAK_HBM = 8.0e12
 
 
@@ -73,6 +74,11 @@ class Layer:
         self.w = gen(E(B, S, HI), datagen.TID_W, wl.scale_w)
         self.gate = gen(E(B, S, H), datagen.TID_GATE, wl.scale_gate)
         self.scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+        if wl.idx_fp8:  # FP8 codes and row scales of q_idx and k_idx
+            u8 = lambda *shape: torch.empty(*shape, dtype=torch.uint8, device=dev)
+            f32 = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
+            self.qc, self.qs = u8(B, S, HI, DI), f32(B, S, HI)
+            self.kc, self.ks = u8(B, self.T_alloc, DI), f32(B, self.T_alloc)
         self.idx = torch.empty(B, S, k, dtype=torch.int32, device=dev)
         self.out = E(B, S, H, Dv)
         ns = wl.n_sink
@@ -156,10 +162,21 @@ class Layer:
     def stages(self):
         wl, dsa = self.wl, self.dsa
         P, S = wl.past_len, wl.S
-        st = [
-            ("K1 index_scores", lambda: dsa.dsa_index_scores(self.q_idx, self.k_idx[:, : wl.T] if wl.B == 1 else self.k_idx, self.w, self.scores, P)),
-            ("K2 topk", lambda: dsa.dsa_topk(self.scores, self.idx, self.tk_ws)),
-        ]
+        if wl.idx_fp8:
+            # the step quantises q_idx and the k_idx rows this chunk appended
+            # (all of them in a prefill from position 0)
+            kn = lambda t: t[:, P: wl.T]
+            st = [
+                ("K1q quant_fp8 q_idx", lambda: dsa.dsa_index_quant_fp8(self.q_idx, self.qc, self.qs)),
+                ("K1k quant_fp8 k_idx", lambda: dsa.dsa_index_quant_fp8(
+                    kn(self.k_idx), kn(self.kc), kn(self.ks))),
+                ("K1 index_scores", lambda: dsa.dsa_index_scores_fp8(
+                    self.qc, self.qs, self.kc[:, : wl.T], self.ks[:, : wl.T], self.w, self.scores, P)),
+            ]
+        else:
+            st = [("K1 index_scores", lambda: dsa.dsa_index_scores(
+                self.q_idx, self.k_idx[:, : wl.T] if wl.B == 1 else self.k_idx, self.w, self.scores, P))]
+        st.append(("K2 topk", lambda: dsa.dsa_topk(self.scores, self.idx, self.tk_ws)))
         kc = self.k if self.T_alloc == wl.T else self.k[:, : wl.T]
         vc = self.v if self.T_alloc == wl.T else self.v[:, : wl.T]
         if S > 1:
@@ -327,7 +344,10 @@ def summarize(wl, per_stage, total_ms):
         r["D_K5_hbm_frac"] = w["K5"]["decode_bytes"] / t5d / PEAK_HBM
         return r
     t1, t2 = g("K1 index_scores"), g("K2 topk")
-    r["K1_mfma_frac"] = w["K1"]["flops"] / t1 / PEAK_BF16
+    r["K1_mfma_frac"] = w["K1"]["flops"] / t1 / (PEAK_FP8 if wl.idx_fp8 else PEAK_BF16)
+    if wl.idx_fp8:
+        r["K1_peak"] = "fp8 5.0 PFLOP/s"
+        r["K1_with_quant_us"] = (t1 + g("K1q quant_fp8 q_idx") + g("K1k quant_fp8 k_idx")) * 1e6
     r["K1_tflops"] = w["K1"]["flops"] / t1 / 1e12
     r["K2_hbm_frac"] = w["K2"]["bytes"] / t2 / PEAK_HBM
     if wl.S > 1:

@@ -22,6 +22,8 @@ N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
   mla-s4k-pas, hybrid-512k-pas
                 the same with 128 attention sinks per layer (sink K/V drawn
                 like the cache's K/V, tensor ids 10 and 11).
+  dsa-s32k-fp8  dsa-s32k with the FP8 indexer: q_idx and k_idx are rotated and
+                quantised to E4M3 codes every step, then scored from the codes.
   spark-swa     one sliding-window layer with grouped KV heads (Spark-X2.5
                 page: 8 query heads over 2 KV heads, head_dim 256, window 512,
                 one gate logit per head): a 4096-token chunk after 131072
@@ -62,6 +64,7 @@ class Workload:
     n_sink: int = 0            # attention sinks per layer (PAS), shared by the batch
     H_kv: int = 0              # KV heads of grouped-KV SWA layers (0: H)
     swa_only: bool = False     # one SWA layer and no DSA stages
+    idx_fp8: bool = False      # indexer on FP8 codes (Hadamard rotation + E4M3)
     scale_q: float = 1.0
     scale_k: float = 1.0
     scale_v: float = 1.0
@@ -106,9 +109,13 @@ WORKLOADS["mla-s4k-pas"] = dataclasses.replace(WORKLOADS["mla-s4k"], name="mla-s
 WORKLOADS["hybrid-512k-pas"] = dataclasses.replace(WORKLOADS["hybrid-512k"],
                                                    name="hybrid-512k-pas", n_sink=128)
 
+# The dsa-s32k layer with the FP8 indexer (A.X-K2 page implementation notes):
+# q_idx and the chunk's k_idx rows are rotated and quantised every step.
+WORKLOADS["dsa-s32k-fp8"] = dataclasses.replace(WORKLOADS["dsa-s32k"], name="dsa-s32k-fp8",
+                                                idx_fp8=True)
 WORKLOADS["spark-swa"] = Workload("spark-swa", BF16, B=1, S=4096, past_len=131072, H=8, nope=128,
                                   rope=128, v=256, HI=0, DI=0, topk=0, seed=5, n_swa=1,
                                   decode_after=True, H_kv=2, swa_only=True)
 
 ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k", "mla-s4k-pas",
-         "hybrid-512k-pas", "spark-swa"]
+         "hybrid-512k-pas", "spark-swa", "dsa-s32k-fp8"]

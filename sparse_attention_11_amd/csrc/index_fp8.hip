@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
                                                         float* __restrict__ scales,
                                                         int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
+  static_assert(LPR >= 1 && LPR <= 16, "a row lies inside one 16-lane DPP row");
   const int lane = threadIdx.x & 63;
   const int lr = lane % LPR;
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
@@ -77,12 +78,13 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
         y[j + h] = a - b;
       }
   // strides 8, 16, ... across lanes: the lane with the lower index holds a
+  // (DPP lane exchanges: LPR <= 16 keeps a row inside one DPP row)
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) {
     const bool upper = (lr & m) != 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float o = __shfl_xor(y[j], m, 64);
+      const float o = __uint_as_float(lane_xor_u32(__float_as_uint(y[j]), m, lane));
       y[j] = upper ? o - y[j] : y[j] + o;
     }
   }
@@ -90,7 +92,8 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 #pragma unroll
   for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(y[j]));
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  for (int m = 1; m < LPR; m <<= 1)
+    amax = fmaxf(amax, __uint_as_float(lane_xor_u32(__float_as_uint(amax), m, lane)));
   int e = 0;
   if (amax > 0.0f) {
     int E;

@@ -92,6 +92,42 @@ def test_dsa_s32k_indexer_sampled_rows():
         assert_rows_close(got[i], ref, 2e-2, what=f"dsa-s32k scores row {s}")
 
 
+def test_dsa_s32k_fp8_indexer_sampled_rows():
+    """FP8 indexer at full size: every k_idx code and the sampled rows' q codes
+    bit-exact, sampled score rows against the oracle's FP8 scores."""
+    wl = WORKLOADS["dsa-s32k-fp8"]
+    S, T, HI, DI = wl.S, wl.T, wl.HI, wl.DI
+    q_idx = dev_normal((1, S, HI, DI), wl, datagen.TID_QIDX, wl.scale_qidx)
+    k_idx = dev_normal((1, T, DI), wl, datagen.TID_KIDX, wl.scale_kidx)
+    w = dev_normal((1, S, HI), wl, datagen.TID_W, wl.scale_w)
+    qc = torch.empty(1, S, HI, DI, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(1, S, HI, dtype=torch.float32, device=DEV)
+    kc = torch.empty(1, T, DI, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(1, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_quant_fp8(q_idx, qc, qs)
+    dsa.dsa_index_quant_fp8(k_idx, kc, ks)
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores_fp8(qc, qs, kc, ks, w, sc, 0)
+    rows = sample_rows(S, wl.topk, n=10, seed=2)
+    got = sc[0, rows].cpu().numpy()
+    got_qc, got_qs = qc[0, rows].cpu().numpy(), qs[0, rows].cpu().numpy()
+    got_kc, got_ks = kc.cpu().numpy(), ks.cpu().numpy()
+    del sc, q_idx, k_idx, w, qc, qs, kc, ks
+    _free()
+    kh = datagen.normal_host((1, T, DI), "bf16", wl.seed, datagen.TID_KIDX, wl.scale_kidx)
+    rkc, rks = oracle.index_quant_fp8(kh)
+    np.testing.assert_array_equal(got_kc, rkc)
+    np.testing.assert_array_equal(got_ks, rks)
+    for i, s in enumerate(rows):
+        qh = host_row(wl, datagen.TID_QIDX, wl.scale_qidx, s, HI * DI).reshape(1, 1, HI, DI)
+        wh = host_row(wl, datagen.TID_W, wl.scale_w, s, HI).reshape(1, 1, HI)
+        rqc, rqs = oracle.index_quant_fp8(qh)
+        np.testing.assert_array_equal(got_qc[i], rqc[0, 0])
+        np.testing.assert_array_equal(got_qs[i], rqs[0, 0])
+        ref = oracle.index_scores_fp8(rqc, rqs, rkc, rks, wh, s)[0, 0]
+        assert_rows_close(got[i], ref, 1e-3, what=f"dsa-s32k fp8 scores row {s}")
+
+
 def _topk_full(wl, S, T, P, k, mode, rows, seed_off=0):
     sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
     datagen.scores_device(sc.view(S, T), 0, S, P, wl.seed + seed_off, mode=mode)
