@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla-s4k")
-    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa",
+    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
