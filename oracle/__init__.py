@@ -29,6 +29,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   index_scores_fp8
                 pinned: index_scores on the dequantised rows with scale / D;
                 Hadamard invariance of index_scores (H q . H k = D q . k).
+  indexer_prologue
+                pinned: torch's linear and layer_norm, RoPE closed forms
+                (position 0 is the identity, pair norms are kept, rotating by
+                a and then by -a restores the input, the angle-sum identity).
 Parity unpinned by the pages (fixed by convention, tested in every mode):
 ReLU placement (per head by default), the two scale constants, and the
 inclusive window boundary.
@@ -94,6 +98,8 @@ def _load():
         lib.oracle_swa_attn_gqa.restype = None
         lib.oracle_e4m3_codes.argtypes = [vp, i64, vp]
         lib.oracle_e4m3_codes.restype = None
+        lib.oracle_indexer_prologue.argtypes = [vp] * 9 + [i32] * 9 + [dbl, vp, vp, vp]
+        lib.oracle_indexer_prologue.restype = None
         lib.oracle_index_quant_fp8.argtypes = [vp, i64, i32, vp, vp]
         lib.oracle_index_quant_fp8.restype = None
         lib.oracle_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -286,3 +292,30 @@ def index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, past_len: int,
                                     _ptr(w), _dtype_of(w), B, S, T, past_len, HI, DI,
                                     float(scale), relu_mode, _ptr(out))
     return out
+
+
+def indexer_prologue(q_lora, hidden, wq_b, wk, k_norm_w, k_norm_b, weights_proj, rope_cos,
+                     rope_sin, past_len: int, n_idx_heads: int, eps: float = 1e-6):
+    """q_lora [B,S,Q], hidden [B,S,Hd], weights [out, in], k_norm [D], rope tables fp32
+    [T, R/2] or None -> (q_idx [B,S,HI,D], k [B,S,D], w [B,S,HI]) float64."""
+    q_lora, hidden, wq_b, wk = _c(q_lora), _c(hidden), _c(wq_b), _c(wk)
+    k_norm_w, k_norm_b, weights_proj = _c(k_norm_w), _c(k_norm_b), _c(weights_proj)
+    B, S, Q = q_lora.shape
+    Hd = hidden.shape[2]
+    HI = n_idx_heads
+    D = wk.shape[0]
+    assert wq_b.shape == (HI * D, Q) and wk.shape == (D, Hd) and weights_proj.shape == (HI, Hd)
+    R = 0
+    if rope_cos is not None:
+        rope_cos = _c(np.asarray(rope_cos, np.float32))
+        rope_sin = _c(np.asarray(rope_sin, np.float32))
+        R = 2 * rope_cos.shape[1]
+    oq = np.empty((B, S, HI, D), np.float64)
+    ok = np.empty((B, S, D), np.float64)
+    ow = np.empty((B, S, HI), np.float64)
+    _load().oracle_indexer_prologue(
+        _ptr(q_lora), _ptr(hidden), _ptr(wq_b), _ptr(wk), _ptr(k_norm_w), _ptr(k_norm_b),
+        _ptr(weights_proj), _ptr(rope_cos), _ptr(rope_sin),
+        _dtype_of(q_lora, hidden, wq_b, wk, k_norm_w, k_norm_b, weights_proj), B, S, past_len,
+        Q, Hd, HI, D, R, float(eps), _ptr(oq), _ptr(ok), _ptr(ow))
+    return oq, ok, ow

@@ -32,6 +32,12 @@
  *                           notes: the reference indexer rotates with a
  *                           Hadamard transform and scores in FP8; the
  *                           rotation cancels since H q . H k = D q . k]
+ *   oracle_indexer_prologue
+ *                        -- the indexer's projections: q_idx from the query
+ *                           LoRA bottleneck (wq_b), the key from the hidden
+ *                           state (wk) through a LayerNorm, per-head weights
+ *                           (weights_proj), half-split RoPE on q and k
+ *                           [A.X-K2 page, SGA bullets and "two RoPE layouts"]
  *   oracle_swa_attn_gqa  -- sliding-window attention whose K/V buffers hold
  *                           fewer heads than q (grouped KV heads)
  *                           [Spark-X2.5 page, "why the gate": 8 query heads,
@@ -63,6 +69,12 @@
  *    the selected (or windowed) keys together.
  *  - Grouped KV heads: query head h reads KV head h / (H / H_kv), i.e.
  *    consecutive query heads share a KV head.
+ *  - Indexer prologue: weights in the nn.Linear layout [out, in]; LayerNorm
+ *    with the mean and the biased variance over idx_dim plus eps, then the
+ *    affine weight and bias; RoPE on the last rope_dim dims of each index head
+ *    and of the key: pair (j, j + rope_dim/2) of that slice rotates by the
+ *    caller's (cos, sin) of position p and frequency j. The pages' bf16
+ *    modules round each projection to bf16; the oracle keeps fp64 throughout.
  *  - FP8 indexer (the page names the steps, not their details): the rotation
  *    is the Sylvester-ordered Walsh-Hadamard matrix with entries +-1 (no
  *    normalisation; scores divide by D instead), computed by the fast
@@ -268,6 +280,78 @@ void oracle_index_scores_fp8(const uint8_t *q_codes, const float *q_scales,
     }
     if (relu_mode == ORACLE_RELU_POST_SUM && !(total > 0.0)) total = 0.0;
     out[e] = total;
+  }
+}
+
+/*
+ * The indexer's projections for S tokens at positions past_len + s [A.X-K2
+ * page, SGA bullets: wq_b on the query LoRA bottleneck, wk + k_norm
+ * (LayerNorm) on the key, weights_proj for the head weights; "two RoPE
+ * layouts": the indexer's RoPE is half-split].
+ *   q_lora [B,S,Q], hidden [B,S,Hd]; wq_b [HI*D, Q], wk [D, Hd],
+ *   weights_proj [HI, Hd], k_norm_w / k_norm_b [D]   (dtype)
+ *   rope_cos / rope_sin [T, R/2] fp32 (unused when R = 0)
+ *   out_q [B,S,HI,D], out_k [B,S,D], out_w [B,S,HI]   double
+ */
+static void rope_half_split(double *x, int R, const float *cs, const float *sn) {
+  int half = R / 2;
+  for (int j = 0; j < half; ++j) {
+    double a = x[j], b = x[j + half], c = cs[j], s = sn[j];
+    x[j] = a * c - b * s;
+    x[j + half] = b * c + a * s;
+  }
+}
+
+void oracle_indexer_prologue(const void *q_lora, const void *hidden,
+                             const void *wq_b, const void *wk,
+                             const void *k_norm_w, const void *k_norm_b,
+                             const void *weights_proj, const float *rope_cos,
+                             const float *rope_sin, int dtype, int B, int S,
+                             int past_len, int Q, int Hd, int HI, int D, int R,
+                             double eps, double *out_q, double *out_k,
+                             double *out_w) {
+  int64_t n = (int64_t)B * S;
+  int half = R / 2;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bs = 0; bs < n; ++bs) {
+    int64_t p = past_len + bs % S;
+    const float *cs = R > 0 ? rope_cos + p * half : NULL;
+    const float *sn = R > 0 ? rope_sin + p * half : NULL;
+    /* q_idx: wq_b applied to the query bottleneck, then RoPE per head */
+    for (int o = 0; o < HI * D; ++o) {
+      double acc = 0.0;
+      for (int i = 0; i < Q; ++i)
+        acc += rd(q_lora, dtype, bs * Q + i) * rd(wq_b, dtype, (int64_t)o * Q + i);
+      out_q[bs * HI * D + o] = acc;
+    }
+    if (R > 0)
+      for (int h = 0; h < HI; ++h)
+        rope_half_split(out_q + (bs * HI + h) * D + (D - R), R, cs, sn);
+    /* key: wk, LayerNorm, RoPE */
+    double *k = out_k + bs * D;
+    for (int o = 0; o < D; ++o) {
+      double acc = 0.0;
+      for (int i = 0; i < Hd; ++i)
+        acc += rd(hidden, dtype, bs * Hd + i) * rd(wk, dtype, (int64_t)o * Hd + i);
+      k[o] = acc;
+    }
+    double mean = 0.0, var = 0.0;
+    for (int o = 0; o < D; ++o) mean += k[o];
+    mean /= D;
+    for (int o = 0; o < D; ++o) var += (k[o] - mean) * (k[o] - mean);
+    var /= D;
+    for (int o = 0; o < D; ++o)
+      k[o] = (k[o] - mean) / sqrt(var + eps) * rd(k_norm_w, dtype, o) +
+             rd(k_norm_b, dtype, o);
+    if (R > 0) rope_half_split(k + (D - R), R, cs, sn);
+    /* head weights */
+    for (int o = 0; o < HI; ++o) {
+      double acc = 0.0;
+      for (int i = 0; i < Hd; ++i)
+        acc += rd(hidden, dtype, bs * Hd + i) *
+               rd(weights_proj, dtype, (int64_t)o * Hd + i);
+      out_w[bs * HI + o] = acc;
+    }
   }
 }
 

@@ -633,3 +633,84 @@ def test_fp8_scores_track_bf16_scores():
     b = oracle.topk(got.astype(np.float32), 64)
     recall = np.mean([len(set(a[0, s]) & set(b[0, s])) / 64 for s in range(S)])
     assert recall > 0.85
+
+
+# ------------------------------------------------------ indexer prologue
+def _prologue_inputs(B, S, Q, Hd, HI, D, seed):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    d = dict(q_lora=f(B, S, Q), hidden=f(B, S, Hd), wq_b=f(HI * D, Q) / np.sqrt(Q),
+             wk=f(D, Hd) / np.sqrt(Hd), k_norm_w=1 + 0.1 * f(D), k_norm_b=0.1 * f(D),
+             weights_proj=f(HI, Hd) / np.sqrt(Hd))
+    return {n: v.astype(np.float32) for n, v in d.items()}
+
+
+def _tables(T, half, seed):
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(-np.pi, np.pi, (T, half))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def test_prologue_without_rope_matches_torch_linear_and_layer_norm():
+    B, S, Q, Hd, HI, D, eps = 2, 5, 32, 48, 3, 16, 1e-5
+    x = _prologue_inputs(B, S, Q, Hd, HI, D, 1)
+    q, k, w = oracle.indexer_prologue(x["q_lora"], x["hidden"], x["wq_b"], x["wk"], x["k_norm_w"],
+                                      x["k_norm_b"], x["weights_proj"], None, None, 0, HI, eps)
+    t = {n: torch.from_numpy(v.astype(np.float64)) for n, v in x.items()}
+    F = torch.nn.functional
+    rq = F.linear(t["q_lora"], t["wq_b"]).reshape(B, S, HI, D)
+    rk = F.layer_norm(F.linear(t["hidden"], t["wk"]), (D,), t["k_norm_w"], t["k_norm_b"], eps)
+    rw = F.linear(t["hidden"], t["weights_proj"])
+    np.testing.assert_allclose(q, rq.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(k, rk.numpy(), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(w, rw.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_prologue_rope_identity_norms_and_slice():
+    B, S, Q, Hd, HI, D, R, P = 1, 4, 32, 32, 2, 16, 8, 5
+    x = _prologue_inputs(B, S, Q, Hd, HI, D, 2)
+    args = (x["q_lora"], x["hidden"], x["wq_b"], x["wk"], x["k_norm_w"], x["k_norm_b"],
+            x["weights_proj"])
+    q0, k0, w0 = oracle.indexer_prologue(*args, None, None, P, HI)
+    ones, zeros = np.ones((P + S, R // 2), np.float32), np.zeros((P + S, R // 2), np.float32)
+    qi, ki, wi = oracle.indexer_prologue(*args, ones, zeros, P, HI)  # angle 0: identity
+    np.testing.assert_array_equal(qi, q0)
+    np.testing.assert_array_equal(ki, k0)
+    c, s = _tables(P + S, R // 2, 3)
+    q1, k1, w1 = oracle.indexer_prologue(*args, c, s, P, HI)
+    np.testing.assert_array_equal(w1, w0)
+    # only the last R dims move, and every (j, j + R/2) pair keeps its norm
+    np.testing.assert_array_equal(q1[..., : D - R], q0[..., : D - R])
+    np.testing.assert_array_equal(k1[..., : D - R], k0[..., : D - R])
+    for a, b in ((q1, q0), (k1, k0)):
+        h = R // 2
+        n1 = a[..., D - R: D - h] ** 2 + a[..., D - h:] ** 2
+        n0 = b[..., D - R: D - h] ** 2 + b[..., D - h:] ** 2
+        np.testing.assert_allclose(n1, n0, rtol=1e-6)  # fp32 tables: cos^2 + sin^2 = 1 to 1e-7
+    # token s uses table row P + s: rows outside P .. P + S - 1 do not matter
+    c2, s2 = c.copy(), s.copy()
+    c2[:P], s2[:P] = 0.3, 0.9
+    q2, _, _ = oracle.indexer_prologue(*args, c2, s2, P, HI)
+    np.testing.assert_array_equal(q2, q1)
+
+
+def test_prologue_rope_rotation_group():
+    # with wq_b = identity, q_idx is the rotated q_lora itself: rotating by a and
+    # then by -a restores it, and a then b equals a + b (pair and sign convention)
+    B, S, HI, D, R = 1, 3, 2, 16, 16
+    Q = HI * D
+    rng = np.random.default_rng(4)
+    xq = rng.standard_normal((B, S, Q)).astype(np.float32)
+    hid = rng.standard_normal((B, S, 32)).astype(np.float32)
+    eye = np.eye(Q, dtype=np.float32)
+    rest = (np.ones((D, 32), np.float32), np.ones(D, np.float32), np.zeros(D, np.float32),
+            np.ones((HI, 32), np.float32))
+    a = rng.uniform(-3, 3, (S, R // 2))
+    b = rng.uniform(-3, 3, (S, R // 2))
+    rot = lambda x, ang: oracle.indexer_prologue(
+        x.astype(np.float32), hid, eye, rest[0], rest[1], rest[2], rest[3],
+        np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32), 0, HI)[0]
+    ya = rot(xq, a).reshape(B, S, Q)
+    np.testing.assert_allclose(rot(ya, -a).reshape(B, S, Q), xq, rtol=1e-6, atol=1e-6)
+    ab = rot(rot(xq, a).reshape(B, S, Q), b)
+    np.testing.assert_allclose(ab, rot(xq, a + b), rtol=1e-5, atol=1e-5)
