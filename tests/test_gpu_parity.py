@@ -545,3 +545,43 @@ def test_index_fp8_top_k_recall_against_bf16():
     got = idx.cpu().numpy()
     recall = np.mean([len(set(got[0, s]) & set(exact[0, s])) / K for s in range(S)])
     assert recall > 0.85, recall
+
+
+# ------------------------------------------------------ indexer prologue
+def _prologue_case(B, S, Q, Hd, HI, D, seed):
+    g = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", seed, tid, sc)
+    return dict(q_lora=g((B, S, Q), 20, 1.0), hidden=g((B, S, Hd), 21, 1.0),
+                wq_b=g((HI * D, Q), 22, Q ** -0.5), wk=g((D, Hd), 23, Hd ** -0.5),
+                k_norm_w=g((D,), 24, 1.0), k_norm_b=g((D,), 25, 0.1),
+                weights_proj=g((HI, Hd), 26, Hd ** -0.5))
+
+
+PROLOGUE_CASES = [  # (B, S, P, Q, Hd, HI, D, R)
+    (1, 200, 0, 64, 96, 4, 64, 32), (2, 130, 70, 96, 160, 5, 128, 64), (1, 1, 999, 32, 64, 3, 128, 0),
+    (1, 300, 17, 128, 256, 64, 128, 64), (3, 7, 5, 64, 32, 2, 64, 64),
+]
+
+
+@pytest.mark.parametrize("B,S,P,Q,Hd,HI,D,R", PROLOGUE_CASES)
+def test_indexer_prologue_cases(B, S, P, Q, Hd, HI, D, R):
+    T = P + S + 3  # rows past the call's must stay untouched
+    x = _prologue_case(B, S, Q, Hd, HI, D, seed=S + HI)
+    rng = np.random.default_rng(S)
+    ang = rng.uniform(-np.pi, np.pi, (T, R // 2))
+    cos, sin = (np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)) if R else (None, None)
+    qd = torch.full((B, S, HI, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kd = torch.full((B, T, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    wd = torch.full((B, S, HI), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_indexer_prologue(*[to_dev(x[n]) for n in ("q_lora", "hidden", "wq_b", "wk", "k_norm_w",
+                                                      "k_norm_b", "weights_proj")],
+                             None if cos is None else to_dev(cos), None if sin is None else to_dev(sin),
+                             qd, kd, wd, P, ln_eps=1e-6)
+    _sync()
+    rq, rk, rw = oracle.indexer_prologue(x["q_lora"], x["hidden"], x["wq_b"], x["wk"], x["k_norm_w"],
+                                         x["k_norm_b"], x["weights_proj"], cos, sin, P, HI, 1e-6)
+    what = f"prologue {B, S, P, Q, Hd, HI, D, R}"
+    assert_rows_close(from_dev(qd), rq, 2e-2, what=what + " q_idx")
+    got_k = from_dev(kd)
+    assert_rows_close(got_k[:, P:P + S], rk, 2e-2, what=what + " k")
+    assert np.all(got_k[:, :P] == 7.0) and np.all(got_k[:, P + S:] == 7.0), "rows outside the call changed"
+    assert_rows_close(from_dev(wd), rw, 2e-2, what=what + " w")
