@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla-s4k")
-    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8",
+    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8,prologue-s32k",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -250,7 +250,36 @@ class SwaLayer:
         ]
 
 
+class PrologueLayer:
+    """The indexer's projections for S tokens (one stage)."""
+
+    def __init__(self, wl, torch, dsa, datagen):
+        self.wl, self.dsa = wl, dsa
+        dev = torch.device("cuda")
+        B, S, P, HI, D, Q, Hd, R = wl.B, wl.S, wl.past_len, wl.HI, wl.DI, wl.q_lora, wl.hidden, wl.rope_idx
+        E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=dev)
+        gen = lambda t, tid, sc: datagen.normal_device(t, wl.seed, tid, sc)
+        self.q_lora, self.hidden = gen(E(B, S, Q), 20, 1.0), gen(E(B, S, Hd), 21, 1.0)
+        self.wq_b, self.wk = gen(E(HI * D, Q), 22, Q ** -0.5), gen(E(D, Hd), 23, Hd ** -0.5)
+        self.knw, self.knb = gen(E(D), 24, 1.0), gen(E(D), 25, 0.1)
+        self.wp = gen(E(HI, Hd), 26, Hd ** -0.5)
+        pos = torch.arange(P + S, device=dev, dtype=torch.float64)[:, None]
+        freq = 10000.0 ** (-2.0 * torch.arange(R // 2, device=dev, dtype=torch.float64) / R)
+        self.cos, self.sin = torch.cos(pos * freq).float(), torch.sin(pos * freq).float()
+        self.q_idx, self.k_cache, self.w = E(B, S, HI, D), E(B, P + S, D), E(B, S, HI)
+        self.ws = torch.empty(dsa.dsa_indexer_prologue_workspace_size(B, S, D), dtype=torch.uint8,
+                              device=dev)
+        torch.cuda.synchronize()
+
+    def stages(self):
+        return [("K0 indexer_prologue", lambda: self.dsa.dsa_indexer_prologue(
+            self.q_lora, self.hidden, self.wq_b, self.wk, self.knw, self.knb, self.wp, self.cos,
+            self.sin, self.q_idx, self.k_cache, self.w, self.wl.past_len, workspace=self.ws))]
+
+
 def make_layer(wl, torch, dsa, datagen):
+    if wl.prologue_only:
+        return PrologueLayer(wl, torch, dsa, datagen)
     return (SwaLayer if wl.swa_only else Layer)(wl, torch, dsa, datagen)
 
 
@@ -336,6 +365,14 @@ def summarize(wl, per_stage, total_ms):
     g = lambda name: per_stage[name]["mean_us"] * 1e-6
     r = {"workload": wl.name, "ms_per_step": total_ms,
          "stages_us": {k: round(v["mean_us"], 2) for k, v in per_stage.items()}}
+    if wl.prologue_only:  # the indexer's projections: three GEMMs + LayerNorm / RoPE
+        t0 = g("K0 indexer_prologue")
+        M = wl.B * wl.S
+        fl = 2.0 * M * (wl.q_lora * wl.HI * wl.DI + wl.hidden * wl.DI + wl.hidden * wl.HI)
+        r["prefill_tokens_per_s"] = M / t0
+        r["K0_mfma_frac"] = fl / t0 / PEAK_BF16
+        r["K0_tflops"] = fl / t0 / 1e12
+        return r
     if wl.swa_only:  # one grouped-KV SWA layer: chunk and decode token
         t5, t5d = g("K5 swa_attn chunk"), g("D K5 swa_attn")
         r["prefill_tokens_per_s"] = wl.B * wl.S / t5
@@ -476,8 +513,17 @@ def main():
         print(f"# {name}: {tm:.3f} ms/step", file=sys.stderr, flush=True)
 
     w = work(wl)
-    t3 = per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6 if wl.S > 1 and not wl.swa_only else None
-    if wl.swa_only:
+    t3 = (per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6
+          if wl.S > 1 and not wl.swa_only and not wl.prologue_only else None)
+    if wl.prologue_only:
+        t0 = per_stage["K0 indexer_prologue"]["mean_us"] * 1e-6
+        M = wl.B * wl.S
+        fl = 2.0 * M * (wl.q_lora * wl.HI * wl.DI + wl.hidden * wl.DI + wl.hidden * wl.HI)
+        roof = {"kernel": "K0 indexer_prologue (bf16 GEMMs + LayerNorm / RoPE)", "bound": "mfma",
+                "achieved": fl / t0 / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": fl / t0 / PEAK_BF16, "traffic": None, "algorithmic_flops_per_launch": fl,
+                "mean_launch_us": t0 * 1e6}
+    elif wl.swa_only:
         t5 = per_stage["K5 swa_attn chunk"]["mean_us"] * 1e-6
         ach = w["K5"]["flops"] / t5 / 1e12
         roof = {"kernel": "K5 swa_attn_gqa chunk (MFMA flash, window mask)", "bound": "mfma",
@@ -500,7 +546,7 @@ def main():
                 "traffic": None, "mean_launch_us": t4 * 1e6}
     roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
     cpu = None
-    if not args.no_cpu and not wl.swa_only:
+    if not args.no_cpu and not wl.swa_only and not wl.prologue_only:
         cpu = cpu_baseline(wl, args.cpu_seconds)
     line = {
         "metric": METRIC,

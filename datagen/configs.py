@@ -24,6 +24,11 @@ N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
                 like the cache's K/V, tensor ids 10 and 11).
   dsa-s32k-fp8  dsa-s32k with the FP8 indexer: q_idx and k_idx are rotated and
                 quantised to E4M3 codes every step, then scored from the codes.
+  prologue-s32k the indexer's projections (wq_b from a 1536-wide query
+                bottleneck, wk + LayerNorm and weights_proj from a 7168-wide
+                hidden state, RoPE on 64 dims) for 32768 tokens; inputs N(0,1),
+                weights N(0,1) / sqrt(fan-in), LayerNorm weight N(0,1) and
+                bias N(0,1) / 10, RoPE angles p * 10000^(-2j/64).
   spark-swa     one sliding-window layer with grouped KV heads (Spark-X2.5
                 page: 8 query heads over 2 KV heads, head_dim 256, window 512,
                 one gate logit per head): a 4096-token chunk after 131072
@@ -65,6 +70,10 @@ class Workload:
     H_kv: int = 0              # KV heads of grouped-KV SWA layers (0: H)
     swa_only: bool = False     # one SWA layer and no DSA stages
     idx_fp8: bool = False      # indexer on FP8 codes (Hadamard rotation + E4M3)
+    prologue_only: bool = False  # the indexer's projections alone
+    q_lora: int = 0            # query LoRA rank (prologue input width)
+    hidden: int = 0            # hidden size (prologue input width)
+    rope_idx: int = 0          # rotary dims of each index head and key
     scale_q: float = 1.0
     scale_k: float = 1.0
     scale_v: float = 1.0
@@ -113,9 +122,15 @@ WORKLOADS["hybrid-512k-pas"] = dataclasses.replace(WORKLOADS["hybrid-512k"],
 # q_idx and the chunk's k_idx rows are rotated and quantised every step.
 WORKLOADS["dsa-s32k-fp8"] = dataclasses.replace(WORKLOADS["dsa-s32k"], name="dsa-s32k-fp8",
                                                 idx_fp8=True)
+# The indexer's projections for the dsa-s32k tokens: wq_b on a 1536-wide query
+# bottleneck, wk + LayerNorm and weights_proj on a 7168-wide hidden state
+# (DeepSeek-V3-sized synthetic shapes), half-split RoPE on 64 of the 128 dims.
+WORKLOADS["prologue-s32k"] = Workload("prologue-s32k", BF16, B=1, S=32768, past_len=0, H=0, nope=0,
+                                      rope=0, v=0, HI=64, DI=128, topk=0, seed=6,
+                                      prologue_only=True, q_lora=1536, hidden=7168, rope_idx=64)
 WORKLOADS["spark-swa"] = Workload("spark-swa", BF16, B=1, S=4096, past_len=131072, H=8, nope=128,
                                   rope=128, v=256, HI=0, DI=0, topk=0, seed=5, n_swa=1,
                                   decode_after=True, H_kv=2, swa_only=True)
 
 ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k", "mla-s4k-pas",
-         "hybrid-512k-pas", "spark-swa", "dsa-s32k-fp8"]
+         "hybrid-512k-pas", "spark-swa", "dsa-s32k-fp8", "prologue-s32k"]

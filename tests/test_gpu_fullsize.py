@@ -17,7 +17,7 @@ import datagen
 import oracle
 import sparse_attention_11_amd as dsa
 from datagen.configs import WORKLOADS
-from tests._helpers import assert_rows_close, from_dev
+from tests._helpers import assert_rows_close, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -364,3 +364,38 @@ def test_spark_swa_chunk_and_decode():
         gh = host_row(wl, datagen.TID_GATE, wl.scale_gate, s, H).reshape(1, 1, H)
         ref = oracle.swa_attn_gqa(qh, kc, vc, gh, p, p - W + 1, W, wl.nope, wl.rope)[0, 0]
         assert_rows_close(o.reshape(H, Dv), ref, 2e-2, what=f"spark-swa row {s}")
+
+
+# -------------------------------------------------------- prologue-s32k
+def test_prologue_s32k_sampled_rows():
+    """The indexer's projections at full size (three GEMMs + LayerNorm / RoPE in
+    the benchmark's launch configuration), sampled tokens against the oracle."""
+    wl = WORKLOADS["prologue-s32k"]
+    S, HI, D, Q, Hd, R = wl.S, wl.HI, wl.DI, wl.q_lora, wl.hidden, wl.rope_idx
+    E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=DEV)
+    gen = lambda t, tid, sc: datagen.normal_device(t, wl.seed, tid, sc)
+    q_lora, hidden = gen(E(1, S, Q), 20, 1.0), gen(E(1, S, Hd), 21, 1.0)
+    host = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", wl.seed, tid, sc)
+    wts = dict(wq_b=host((HI * D, Q), 22, Q ** -0.5), wk=host((D, Hd), 23, Hd ** -0.5),
+               k_norm_w=host((D,), 24, 1.0), k_norm_b=host((D,), 25, 0.1),
+               weights_proj=host((HI, Hd), 26, Hd ** -0.5))
+    pos = np.arange(S, dtype=np.float64)[:, None]
+    ang = pos * 10000.0 ** (-2.0 * np.arange(R // 2) / R)
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    q_idx, k_cache, w = E(1, S, HI, D), E(1, S, D), E(1, S, HI)
+    dsa.dsa_indexer_prologue(q_lora, hidden, *[to_dev(wts[n]) for n in (
+        "wq_b", "wk", "k_norm_w", "k_norm_b", "weights_proj")], to_dev(cos), to_dev(sin),
+        q_idx, k_cache, w, 0)
+    rows = sample_rows(S, 2048, n=8, seed=3)
+    got_q, got_k, got_w = from_dev(q_idx[0, rows]), from_dev(k_cache[0, rows]), from_dev(w[0, rows])
+    del q_lora, hidden, q_idx, k_cache, w
+    _free()
+    for i, s in enumerate(rows):
+        ql = host_row(wl, 20, 1.0, s, Q).reshape(1, 1, Q)
+        hd = host_row(wl, 21, 1.0, s, Hd).reshape(1, 1, Hd)
+        # one-token call at position s: the tables' row s
+        rq, rk, rw = oracle.indexer_prologue(ql, hd, wts["wq_b"], wts["wk"], wts["k_norm_w"],
+                                             wts["k_norm_b"], wts["weights_proj"], cos, sin, s, HI)
+        assert_rows_close(got_q[i], rq[0, 0], 2e-2, what=f"prologue q_idx row {s}")
+        assert_rows_close(got_k[i], rk[0, 0], 2e-2, what=f"prologue k row {s}")
+        assert_rows_close(got_w[i], rw[0, 0], 2e-2, what=f"prologue w row {s}")
