@@ -268,6 +268,43 @@ int swa_attn_gqa(const void* q, const void* k_buf, const void* v_buf, const void
                  int gate_dim, int dtype, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/*
+ * The indexer's projections, in front of dsa_index_scores ([AXK2] §1 SGA: the
+ * indexer's own light projections, wq_b on the query LoRA bottleneck, wk
+ * followed by a LayerNorm (k_norm) on the key, per-head weights from
+ * weights_proj, and its own key cache appended to by update_indexer; [AXK2]
+ * "two RoPE layouts": the indexer's rotary embedding is non-interleaved,
+ * half-split). For the S tokens of a call (positions past_len + s):
+ *   q_idx[b,s,h,:] = RoPE_p((q_lora[b,s,:] . wq_b^T)[h * idx_dim ...])
+ *   k_idx_cache[b, past_len + s, :] = RoPE_p(LayerNorm(hidden[b,s,:] . wk^T))
+ *   w[b,s,:] = hidden[b,s,:] . weights_proj^T
+ * Weights use the nn.Linear layout [out_features, in_features]:
+ *   wq_b [n_idx_heads * idx_dim, q_lora_rank], wk [idx_dim, hidden_dim],
+ *   weights_proj [n_idx_heads, hidden_dim], k_norm_weight / k_norm_bias
+ *   [idx_dim] (LayerNorm with mean and biased variance over idx_dim, ln_eps).
+ * RoPE acts on the last rope_dim dims of each index head and of the key
+ * (rope_dim even, 0 = none): with half = rope_dim / 2 and j < half, the pair
+ * (x_j, x_{j+half}) of that slice becomes (x_j c - x_{j+half} s,
+ * x_{j+half} c + x_j s), c = rope_cos[p * half + j], s = rope_sin[p * half + j]
+ * (fp32 tables [T, half]: the caller's frequency schedule).
+ * q_lora [B,S,q_lora_rank], hidden [B,S,hidden_dim], q_idx [B,S,n_idx_heads,
+ * idx_dim], k_idx_cache [B,T,idx_dim] (rows past_len .. past_len + S - 1 are
+ * written), w [B,S,n_idx_heads]; all bf16 (dtype DSA_BF16; DSA_F32 is
+ * DSA_ERR_UNSUPPORTED). Each projection's output is rounded to bf16, as the
+ * page's bf16 modules do; LayerNorm and RoPE compute in fp32.
+ * Supported: idx_dim 64 or 128; q_lora_rank and hidden_dim multiples of 32.
+ * workspace: at least dsa_indexer_prologue_workspace_size(B, S, idx_dim)
+ * bytes (the key projection before its LayerNorm).
+ */
+size_t dsa_indexer_prologue_workspace_size(int B, int S, int idx_dim);
+int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_b, const void* wk,
+                         const void* k_norm_weight, const void* k_norm_bias,
+                         const void* weights_proj, const float* rope_cos, const float* rope_sin,
+                         void* q_idx, void* k_idx_cache, void* w, int B, int S, int T,
+                         int past_len, int q_lora_rank, int hidden_dim, int n_idx_heads,
+                         int idx_dim, int rope_dim, float ln_eps, int dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */

@@ -36,6 +36,7 @@ _EXPORTS = [
     "swa_attn_pas_workspace_size", "swa_attn_pas",
     "swa_attn_gqa_workspace_size", "swa_attn_gqa",
     "dsa_index_quant_fp8", "dsa_index_scores_fp8",
+    "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
 ]
 MAX_SINKS = 256
 
@@ -92,6 +93,9 @@ def lib():
         L.dsa_index_quant_fp8.argtypes = [vp, vp, vp, ctypes.c_longlong, i32, i32, vp]
         L.dsa_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                            f32, i32, i32, vp]
+        L.dsa_indexer_prologue_workspace_size.argtypes = [i32] * 3
+        L.dsa_indexer_prologue_workspace_size.restype = sz
+        L.dsa_indexer_prologue.argtypes = [vp] * 12 + [i32] * 9 + [f32, i32, vp, sz, vp]
         L.swa_attn_gqa_workspace_size.argtypes = [i32] * 7
         L.swa_attn_gqa_workspace_size.restype = sz
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
@@ -99,7 +103,7 @@ def lib():
         for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
                    "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
-                   "dsa_index_quant_fp8", "dsa_index_scores_fp8"):
+                   "dsa_index_quant_fp8", "dsa_index_scores_fp8", "dsa_indexer_prologue"):
             getattr(L, fn).restype = i32
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -383,6 +387,32 @@ def dsa_index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, scores, past_l
         _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(w), _ptr(scores),
         B, S, T, past_len, HI, D, scale, relu_mode, _dtype(w), _stream(stream)))
     return scores
+
+
+def dsa_indexer_prologue_workspace_size(B, S, idx_dim) -> int:
+    return int(lib().dsa_indexer_prologue_workspace_size(B, S, idx_dim))
+
+
+def dsa_indexer_prologue(q_lora, hidden, wq_b, wk, k_norm_weight, k_norm_bias, weights_proj,
+                         rope_cos, rope_sin, q_idx, k_idx_cache, w, past_len: int,
+                         ln_eps: float = 1e-6, workspace=None, stream=None):
+    """Indexer projections: q_lora [B,S,Q], hidden [B,S,Hd] -> q_idx [B,S,HI,D] (RoPE'd),
+    k_idx_cache rows past_len.. (LayerNorm + RoPE), w [B,S,HI]; weights [out, in];
+    rope_cos / rope_sin fp32 [T, rope_dim / 2] (None for no RoPE)."""
+    B, S, Q = q_lora.shape
+    Hd = hidden.shape[2]
+    HI, D = q_idx.shape[2], q_idx.shape[3]
+    T = k_idx_cache.shape[1]
+    R = 0 if rope_cos is None else 2 * rope_cos.shape[1]
+    if workspace is None:
+        workspace = _workspace(dsa_indexer_prologue_workspace_size(B, S, D), q_lora)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_indexer_prologue", lib().dsa_indexer_prologue(
+        _ptr(q_lora), _ptr(hidden), _ptr(wq_b), _ptr(wk), _ptr(k_norm_weight), _ptr(k_norm_bias),
+        _ptr(weights_proj), _ptr(rope_cos), _ptr(rope_sin), _ptr(q_idx), _ptr(k_idx_cache),
+        _ptr(w), B, S, T, past_len, Q, Hd, HI, D, R, ln_eps, _dtype(q_lora), _ptr(workspace),
+        nbytes, _stream(stream)))
+    return q_idx, k_idx_cache, w
 
 
 def dsa_status_string(status: int) -> str:

@@ -280,6 +280,55 @@ int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const ui
                     fn);
 }
 
+size_t dsa_indexer_prologue_workspace_size(int B, int S, int idx_dim) {
+  if (B < 1 || S < 1 || idx_dim < 1) return 0;
+  return (size_t)B * S * idx_dim * 2;  // the key projection before its LayerNorm (bf16)
+}
+
+int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_b, const void* wk,
+                         const void* k_norm_weight, const void* k_norm_bias,
+                         const void* weights_proj, const float* rope_cos, const float* rope_sin,
+                         void* q_idx, void* k_idx_cache, void* w, int B, int S, int T,
+                         int past_len, int q_lora_rank, int hidden_dim, int n_idx_heads,
+                         int idx_dim, int rope_dim, float ln_eps, int dtype, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_indexer_prologue";
+  g_err.clear();
+  if (!q_lora || !hidden || !wq_b || !wk || !k_norm_weight || !k_norm_bias || !weights_proj ||
+      !q_idx || !k_idx_cache || !w)
+    return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (rope_dim > 0 && (!rope_cos || !rope_sin))
+    return fail(DSA_ERR_INVALID_ARG, "%s: rope tables are NULL with rope_dim %d", fn, rope_dim);
+  if (B < 1 || S < 1 || T < 1 || past_len < 0 || q_lora_rank < 1 || hidden_dim < 1 ||
+      n_idx_heads < 1 || idx_dim < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1 and past_len >= 0", fn);
+  if ((long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T (%d) < past_len + S (%d + %d)", fn, T, past_len, S);
+  if (rope_dim < 0 || rope_dim > idx_dim || rope_dim % 2 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "%s: rope_dim must be even and in [0, idx_dim]", fn);
+  if (!(ln_eps > 0.0f) || !std::isfinite(ln_eps))
+    return fail(DSA_ERR_INVALID_ARG, "%s: ln_eps must be finite and > 0", fn);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (idx_dim != 64 && idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: idx_dim must be 64 or 128 (got %d)", fn, idx_dim);
+  if (q_lora_rank % 32 != 0 || hidden_dim % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: q_lora_rank and hidden_dim must be multiples of 32",
+                fn);
+  if ((long long)B * S > 0x7FFFFFFF / 128 || (long long)n_idx_heads * idx_dim > 0x7FFFFFFF / 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  int st = check_ws(fn, workspace, workspace_bytes,
+                    dsa_indexer_prologue_workspace_size(B, S, idx_dim));
+  if (st) return st;
+  return hip_status(dsa::launch_indexer_prologue(q_lora, hidden, wq_b, wk, k_norm_weight,
+                                                 k_norm_bias, weights_proj, rope_cos, rope_sin,
+                                                 q_idx, k_idx_cache, w, B, S, T, past_len,
+                                                 q_lora_rank, hidden_dim, n_idx_heads, idx_dim,
+                                                 rope_dim, ln_eps, workspace, stream),
+                    fn);
+}
+
 size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
   if (B < 1 || S < 1 || T < 1 || topk < 1) return 0;
   return dsa::topk_workspace_bytes(B, S, T, topk);

@@ -22,6 +22,18 @@ hipError_t launch_index_scores_fp8(const uint8_t* q_codes, const float* q_scales
                                    float* scores, int B, int S, int T, int P, int HI, int DI,
                                    float scale, int relu_mode, hipStream_t stream);
 
+// Indexer prologue (prologue.hip): bf16 GEMM with nn.Linear weights
+// (C = A W^T, K % 32 == 0), then RoPE / LayerNorm + RoPE + cache append.
+hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int ldc,
+                            hipStream_t stream);
+hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_b,
+                                   const void* wk, const void* k_norm_weight,
+                                   const void* k_norm_bias, const void* weights_proj,
+                                   const float* rope_cos, const float* rope_sin, void* q_idx,
+                                   void* k_idx_cache, void* w, int B, int S, int T, int past_len,
+                                   int q_lora_rank, int hidden_dim, int HI, int DI, int R,
+                                   float eps, void* workspace, hipStream_t stream);
+
 // Per-row top-k (topk.hip).
 size_t topk_workspace_bytes(int B, int S, int T, int topk);
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,

@@ -1,0 +1,249 @@
+// prologue.hip -- the indexer's projections in front of the lightning indexer
+// (gfx950).
+//
+// A.X-K2 page, SGA ("Sparse Gated Attention") bullets: the indexer has its own
+// light projections, wq_b on the query LoRA bottleneck and wk followed by a
+// LayerNorm (k_norm) on the key, and per-head weights from weights_proj; its
+// key cache is appended to by update_indexer. "Two RoPE layouts": the
+// indexer uses the non-interleaved (half-split) rotary layout.
+//
+// Kernels
+//  gemm_bf16_kernel   C[M,N] = A[M,K] W[N,K]^T (nn.Linear weights), bf16 in,
+//                     fp32 accumulate, bf16 out. 128 x 128 tiles, 4 waves of
+//                     64 x 64, v_mfma_f32_32x32x16_bf16 with both operands
+//                     read K-contiguous from LDS (K steps of 64,
+//                     double-buffered, the next step loaded into registers
+//                     under the current MFMAs); the MFMA forms C^T so that a
+//                     lane stores four consecutive columns at once.
+//  rope_q_kernel      half-split RoPE on the last rope_dim dims of every
+//                     index head, in place.
+//  ln_rope_k_kernel   LayerNorm over idx_dim (fp32 statistics), then the
+//                     same RoPE, written into the key cache rows
+//                     past_len .. past_len + S - 1.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kGBM = 128, kGBN = 128, kGBK = 64;
+constexpr int kGPad = kGBK + 8;  // bf16 per LDS row (144 bytes: conflict-free 16-byte reads)
+constexpr int kGLd = kGBM * kGBK / 8 / 256;  // 16-byte chunks per thread per operand tile
+
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ W,
+                                                           uint16_t* __restrict__ C, int M, int N,
+                                                           int K, int ldc) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGBM * kGPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGBN * kGPad];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
+
+  // global -> register staging: 1024 16-byte chunks per operand tile, 4 per thread
+  u32x4_t ra[kGLd], rw[kGLd];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kGLd; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = 8 * (c & 7);
+      const int m = m0 + r, n = n0 + r;
+      const bool kin = k0 + kc < K;  // K % 32 == 0: a chunk is all in or all out
+      ra[i] = (m < M && kin) ? load16(A + (int64_t)m * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+      rw[i] = (n < N && kin) ? load16(W + (int64_t)n * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kGLd; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = 8 * (c & 7);
+      *(u32x4_t*)(&As[buf][r * kGPad + kc]) = ra[i];
+      *(u32x4_t*)(&Ws[buf][r * kGPad + kc]) = rw[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+  const int nk = (K + kGBK - 1) / kGBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tile((kt + 1) * kGBK);
+#pragma unroll
+    for (int s = 0; s < kGBK / 16; ++s) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + (lane & 31);
+        a[i] = as_bf16x8(*(const u32x4_t*)(&As[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + 32 * j + (lane & 31);
+        b[j] = as_bf16x8(*(const u32x4_t*)(&Ws[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
+    }
+    if (kt + 1 < nk) {
+      store_tile(buf ^ 1);  // the other buffer was last read before the previous barrier
+      __syncthreads();
+    }
+  }
+  // the MFMA computes C^T: lane l holds C[m][n] for m = 32 i + l % 32 and
+  // n = 32 j + 8 g + 4 (l / 32) + r (e = 4 g + r) of the wave's tile, so each
+  // group of four is one 8-byte store of consecutive columns
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+      if (m >= M) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 64 + 32 * j + 8 * g + 4 * (lane >> 5);
+        uint16_t* cp = C + (int64_t)m * ldc + n;
+        if (n + 3 < N && ((ldc | n) & 3) == 0) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *(uint2*)cp = pk;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) cp[r] = f32_to_bf16(acc[i][j][4 * g + r]);
+        }
+      }
+    }
+}
+
+// Half-split RoPE of one (x1, x2) pair: (x1 cos - x2 sin, x2 cos + x1 sin).
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s) {
+  const float a = x1, b = x2;
+  x1 = a * c - b * s;
+  x2 = b * c + a * s;
+}
+
+// q [M, HI, D] in place: one thread per (row, head, pair j < R / 2); the pair
+// is (D - R + j, D - R + j + R / 2). Row m is token s = m % S at p = P + s.
+__global__ __launch_bounds__(256) void rope_q_kernel(uint16_t* __restrict__ q,
+                                                     const float* __restrict__ cosb,
+                                                     const float* __restrict__ sinb, int64_t M,
+                                                     int S, int P, int HI, int D, int R) {
+  const int half = R / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * HI * half) return;
+  const int j = (int)(i % half);
+  const int64_t mh = i / half;
+  const int64_t m = mh / HI;
+  const int p = P + (int)(m % S);
+  uint16_t* row = q + mh * D + (D - R);
+  float x1 = bf16_to_f32(row[j]), x2 = bf16_to_f32(row[j + half]);
+  rope_pair(x1, x2, cosb[(int64_t)p * half + j], sinb[(int64_t)p * half + j]);
+  row[j] = f32_to_bf16(x1);
+  row[j + half] = f32_to_bf16(x2);
+}
+
+// One wave per key row (D = 64 .. 256 values, D / 64 per lane): LayerNorm
+// with fp32 mean and biased variance, affine gamma / beta, then the RoPE of
+// the last R dims, stored to cache row b * T + P + s.
+__global__ __launch_bounds__(256) void ln_rope_k_kernel(const uint16_t* __restrict__ kraw,
+                                                        const uint16_t* __restrict__ gamma,
+                                                        const uint16_t* __restrict__ beta,
+                                                        const float* __restrict__ cosb,
+                                                        const float* __restrict__ sinb,
+                                                        uint16_t* __restrict__ kcache, int64_t M,
+                                                        int S, int T, int P, int D, int R,
+                                                        float eps) {
+  __shared__ float rowbuf[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m = (int64_t)blockIdx.x * 4 + wave;
+  if (m >= M) return;  // whole waves only: no workgroup barrier below
+  const int per = D / 64;
+  float x[4];
+  float sum = 0.0f;
+  for (int c = 0; c < per; ++c) {
+    x[c] = bf16_to_f32(kraw[m * D + lane + 64 * c]);
+    sum += x[c];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  const float mean = sum / (float)D;
+  float var = 0.0f;
+  for (int c = 0; c < per; ++c) {
+    const float d = x[c] - mean;
+    var += d * d;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) var += __shfl_xor(var, off, 64);
+  const float inv = 1.0f / sqrtf(var / (float)D + eps);
+  for (int c = 0; c < per; ++c) {
+    const int d = lane + 64 * c;
+    rowbuf[wave][d] = (x[c] - mean) * inv * bf16_to_f32(gamma[d]) + bf16_to_f32(beta[d]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int b = (int)(m / S), s = (int)(m % S), p = P + s;
+  const int half = R / 2, r0 = D - R;
+  uint16_t* out = kcache + ((int64_t)b * T + p) * D;
+  for (int c = 0; c < per; ++c) {
+    const int d = lane + 64 * c;
+    float v = rowbuf[wave][d];
+    if (d >= r0) {  // the rotary slice: pair (r0 + j, r0 + j + half)
+      const int j = (d - r0) % half;
+      const float cs = cosb[(int64_t)p * half + j], sn = sinb[(int64_t)p * half + j];
+      const float x1 = rowbuf[wave][r0 + j], x2 = rowbuf[wave][r0 + j + half];
+      v = (d - r0 < half) ? x1 * cs - x2 * sn : x2 * cs + x1 * sn;
+    }
+    out[d] = f32_to_bf16(v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int ldc,
+                            hipStream_t st) {
+  if (K % 32 != 0) return hipErrorInvalidValue;
+  const dim3 grid((N + kGBN - 1) / kGBN, (M + kGBM - 1) / kGBM);
+  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, (const uint16_t*)A,
+                     (const uint16_t*)W, (uint16_t*)C, M, N, K, ldc);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_b,
+                                   const void* wk, const void* k_norm_weight,
+                                   const void* k_norm_bias, const void* weights_proj,
+                                   const float* rope_cos, const float* rope_sin, void* q_idx,
+                                   void* k_idx_cache, void* w, int B, int S, int T, int past_len,
+                                   int q_lora_rank, int hidden_dim, int HI, int DI, int R,
+                                   float eps, void* workspace, hipStream_t st) {
+  const int M = B * S;
+  hipError_t e = launch_gemm_bf16(q_lora, wq_b, q_idx, M, HI * DI, q_lora_rank, HI * DI, st);
+  if (e != hipSuccess) return e;
+  e = launch_gemm_bf16(hidden, wk, workspace, M, DI, hidden_dim, DI, st);
+  if (e != hipSuccess) return e;
+  e = launch_gemm_bf16(hidden, weights_proj, w, M, HI, hidden_dim, HI, st);
+  if (e != hipSuccess) return e;
+  if (R > 0) {
+    const int64_t n = (int64_t)M * HI * (R / 2);
+    hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (uint16_t*)q_idx, rope_cos, rope_sin, (int64_t)M, S, past_len, HI, DI, R);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(ln_rope_k_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st,
+                     (const uint16_t*)workspace, (const uint16_t*)k_norm_weight,
+                     (const uint16_t*)k_norm_bias, rope_cos, rope_sin, (uint16_t*)k_idx_cache,
+                     (int64_t)M, S, T, past_len, DI, R, eps);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
