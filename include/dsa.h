@@ -290,8 +290,10 @@ int swa_attn_gqa(const void* q, const void* k_buf, const void* v_buf, const void
  * q_lora [B,S,q_lora_rank], hidden [B,S,hidden_dim], q_idx [B,S,n_idx_heads,
  * idx_dim], k_idx_cache [B,T,idx_dim] (rows past_len .. past_len + S - 1 are
  * written), w [B,S,n_idx_heads]; all bf16 (dtype DSA_BF16; DSA_F32 is
- * DSA_ERR_UNSUPPORTED). Each projection's output is rounded to bf16, as the
- * page's bf16 modules do; LayerNorm and RoPE compute in fp32.
+ * DSA_ERR_UNSUPPORTED). The key projection is rounded to bf16 before its
+ * LayerNorm, as the page's bf16 modules do; LayerNorm and RoPE compute in
+ * fp32. q_idx is rounded once, after its RoPE, when rope_dim is 32 or 64 (the
+ * GEMM applies it), else rounded and then rotated.
  * Supported: idx_dim 64 or 128; q_lora_rank and hidden_dim multiples of 32.
  * workspace: at least dsa_indexer_prologue_workspace_size(B, S, idx_dim)
  * bytes (the key projection before its LayerNorm).

@@ -29,16 +29,55 @@ namespace {
 constexpr int kGBM = 128, kGBN = 128, kGBK = 64;
 constexpr int kGPad = kGBK + 8;  // bf16 per LDS row (144 bytes: conflict-free 16-byte reads)
 constexpr int kGLd = kGBM * kGBK / 8 / 256;  // 16-byte chunks per thread per operand tile
+constexpr int kGroupedTiles = 8;  // column tiles up to which a row tile stays on one XCD
 
+// Two weight / output pairs share one pass over A (the key and head-weight
+// projections both read the hidden state): column tiles 0 .. nt1-1 belong to
+// (W1, C1), the rest to (W2, C2). With few column tiles (skinny outputs, A
+// the big operand) tile ids are dealt so that the column tiles of one row
+// tile run back to back on the same XCD (the A tile is then an L2 hit for
+// all but the first); with many, column tiles vary fastest over all XCDs, so
+// each XCD's L2 holds only its share of W for the row tiles in flight.
+struct GemmOut {
+  const uint16_t* W;
+  uint16_t* C;
+  int N, ldc;
+};
+// Optional RoPE epilogue (q_idx): heads of D dims, rotary slice = the last R
+// dims of each head (R 32 or 64), row m at position P + m % S.
+struct GemmRope {
+  const float* cosb;
+  const float* sinb;
+  int D, R, S, P;
+};
+
+// RHALF: half the rotary width (16 or 32) for the RoPE epilogue, 0 for none;
+// a compile-time constant so that every rotary pair's registers are fixed.
+template <int RHALF>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                           const uint16_t* __restrict__ W,
-                                                           uint16_t* __restrict__ C, int M, int N,
-                                                           int K, int ldc) {
+                                                           GemmOut o1, GemmOut o2, int M, int K,
+                                                           int ntiles_n, int nt1, GemmRope rp) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGBM * kGPad];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGBN * kGPad];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
+  const int pid = blockIdx.x;
+  int mt, nt;
+  if (ntiles_n <= kGroupedTiles) {  // the row tile's column tiles together on one XCD
+    const int xcd = pid & 7, q = pid >> 3;
+    mt = (q / ntiles_n) * 8 + xcd;
+    nt = q % ntiles_n;
+  } else {
+    mt = pid / ntiles_n;
+    nt = pid % ntiles_n;
+  }
+  const int m0 = mt * kGBM;
+  if (m0 >= M) return;
+  const bool second = nt >= nt1;
+  const uint16_t* __restrict__ W = second ? o2.W : o1.W;
+  uint16_t* __restrict__ C = second ? o2.C : o1.C;
+  const int N = second ? o2.N : o1.N, ldc = second ? o2.ldc : o1.ldc;
+  const int n0 = (second ? nt - nt1 : nt) * kGBN;
 
   // global -> register staging: 1024 16-byte chunks per operand tile, 4 per thread
   u32x4_t ra[kGLd], rw[kGLd];
@@ -100,6 +139,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   // the MFMA computes C^T: lane l holds C[m][n] for m = 32 i + l % 32 and
   // n = 32 j + 8 g + 4 (l / 32) + r (e = 4 g + r) of the wave's tile, so each
   // group of four is one 8-byte store of consecutive columns
+  if (RHALF > 0) {
+    // A wave's 64 columns lie inside one head (D = 64 or 128, 64-aligned), so
+    // a rotary pair (d, d + R/2) sits in one lane: R/2 = 32 is the next 32-
+    // column block j, R/2 = 16 the group g + 2 of the same block.
+    constexpr int half = RHALF;
+    const int hd0 = (n0 + wn * 64) % rp.D;  // head dim of the wave's first column
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+      const int p = rp.P + (m < M ? m : M - 1) % rp.S;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = hd0 + 32 * j + 8 * g + 4 * (lane >> 5) + r;
+            const int jj = d - (rp.D - rp.R);  // index in the rotary slice
+            if (jj < 0 || jj >= half) continue;
+            // partner at d + half: (j + 1, g) for half 32, (j, g + 2) for 16
+            constexpr int dj = half == 32 ? 1 : 0, dg = half == 32 ? 0 : 2;
+            const int j2 = j + dj, g2 = g + dg;
+            if (j2 > 1 || g2 > 3) continue;  // folds at compile time (unrolled loops)
+            const float cs = rp.cosb[(int64_t)p * half + jj], sn = rp.sinb[(int64_t)p * half + jj];
+            const float x1 = acc[i][j][4 * g + r], x2 = acc[i][j2][4 * g2 + r];
+            acc[i][j][4 * g + r] = x1 * cs - x2 * sn;
+            acc[i][j2][4 * g2 + r] = x2 * cs + x1 * sn;
+          }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -209,13 +278,32 @@ __global__ __launch_bounds__(256) void ln_rope_k_kernel(const uint16_t* __restri
 
 }  // namespace
 
+namespace {
+hipError_t gemm_launch(const void* A, GemmOut o1, GemmOut o2, int M, int K, const GemmRope* rp,
+                       hipStream_t st) {
+  if (K % 32 != 0) return hipErrorInvalidValue;
+  const int nt1 = (o1.N + kGBN - 1) / kGBN, nt2 = o2.N > 0 ? (o2.N + kGBN - 1) / kGBN : 0;
+  const int ntn = nt1 + nt2;
+  const int64_t mtiles = (M + kGBM - 1) / kGBM;
+  const int64_t g = (ntn <= kGroupedTiles ? (mtiles + 7) / 8 * 8 : mtiles) * ntn;
+  if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (rp && rp->R == 64)
+    hipLaunchKernelGGL((gemm_bf16_kernel<32>), dim3((unsigned)g), dim3(256), 0, st,
+                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, *rp);
+  else if (rp && rp->R == 32)
+    hipLaunchKernelGGL((gemm_bf16_kernel<16>), dim3((unsigned)g), dim3(256), 0, st,
+                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, *rp);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<0>), dim3((unsigned)g), dim3(256), 0, st,
+                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, GemmRope{});
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int ldc,
                             hipStream_t st) {
-  if (K % 32 != 0) return hipErrorInvalidValue;
-  const dim3 grid((N + kGBN - 1) / kGBN, (M + kGBM - 1) / kGBM);
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, (const uint16_t*)A,
-                     (const uint16_t*)W, (uint16_t*)C, M, N, K, ldc);
-  return hipGetLastError();
+  return gemm_launch(A, GemmOut{(const uint16_t*)W, (uint16_t*)C, N, ldc},
+                     GemmOut{nullptr, nullptr, 0, 0}, M, K, nullptr, st);
 }
 
 hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_b,
@@ -226,13 +314,21 @@ hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const
                                    int q_lora_rank, int hidden_dim, int HI, int DI, int R,
                                    float eps, void* workspace, hipStream_t st) {
   const int M = B * S;
-  hipError_t e = launch_gemm_bf16(q_lora, wq_b, q_idx, M, HI * DI, q_lora_rank, HI * DI, st);
+  // q_idx = q_lora wq_b^T, with the RoPE in the epilogue where a rotary pair
+  // sits in one lane (idx_dim 64 or 128, rope_dim 32 or 64)
+  const bool fused = (DI == 64 || DI == 128) && (R == 32 || R == 64);
+  const GemmRope rp{rope_cos, rope_sin, DI, R, S, past_len};
+  hipError_t e = gemm_launch(q_lora, GemmOut{(const uint16_t*)wq_b, (uint16_t*)q_idx, HI * DI,
+                                             HI * DI},
+                             GemmOut{nullptr, nullptr, 0, 0}, M, q_lora_rank, fused ? &rp : nullptr,
+                             st);
   if (e != hipSuccess) return e;
-  e = launch_gemm_bf16(hidden, wk, workspace, M, DI, hidden_dim, DI, st);
+  // the key and head-weight projections in one pass over the hidden state
+  e = gemm_launch(hidden, GemmOut{(const uint16_t*)wk, (uint16_t*)workspace, DI, DI},
+                  GemmOut{(const uint16_t*)weights_proj, (uint16_t*)w, HI, HI}, M, hidden_dim,
+                  nullptr, st);
   if (e != hipSuccess) return e;
-  e = launch_gemm_bf16(hidden, weights_proj, w, M, HI, hidden_dim, HI, st);
-  if (e != hipSuccess) return e;
-  if (R > 0) {
+  if (R > 0 && !fused) {
     const int64_t n = (int64_t)M * HI * (R / 2);
     hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        (uint16_t*)q_idx, rope_cos, rope_sin, (int64_t)M, S, past_len, HI, DI, R);

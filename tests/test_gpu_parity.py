@@ -559,6 +559,8 @@ def _prologue_case(B, S, Q, Hd, HI, D, seed):
 PROLOGUE_CASES = [  # (B, S, P, Q, Hd, HI, D, R)
     (1, 200, 0, 64, 96, 4, 64, 32), (2, 130, 70, 96, 160, 5, 128, 64), (1, 1, 999, 32, 64, 3, 128, 0),
     (1, 300, 17, 128, 256, 64, 128, 64), (3, 7, 5, 64, 32, 2, 64, 64),
+    # rope_dim 128 and 16: the separate RoPE pass instead of the GEMM epilogue
+    (1, 50, 3, 64, 64, 3, 128, 128), (1, 40, 0, 32, 64, 2, 64, 16),
 ]
 
 
