@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
                                                           float* __restrict__ scores, int S,
                                                           int T, int P, int HI, float scale,
                                                           int nqt, int nkt, int npairs,
-                                                          int maxlen) {
+                                                          int maxlen, int two) {
   constexpr int kQG = QG;
   constexpr int kTileQ = 16 * QG;                      // queries per workgroup (MFMA N axis)
   constexpr int KS = DI / 32;                          // 32-dim steps per head
@@ -62,20 +62,23 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) uint8_t qs[2][kStageBytes];
 
   const int b = blockIdx.y;
-  IdxTile tile;
-  if (!idx_tile_of(blockIdx.x, kTileQ, S, P, nqt, nkt, npairs, maxlen, &tile)) return;
-  const int qt = tile.qt, kt = tile.kt;
+  IdxTile2 tile;
+  if (!idx_tile2_of(blockIdx.x, kTileQ, S, P, nqt, nkt, npairs, maxlen, two != 0, &tile)) return;
+  const int kt = tile.kt;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int lq = lane & 15, lg = lane >> 4;
-  const int q0 = qt * kTileQ;
   const int kw0 = kt * kTileK + wave * kWaveK;  // first key of this wave
+  // the query tile being multiplied: q1, then q2 with the same key registers
+  int qt = tile.q1;
+  int q0 = qt * kTileQ;
   int64_t row[kQG];  // this lane's query row of each group (clamped to S-1)
 #pragma unroll
   for (int qg = 0; qg < kQG; ++qg) row[qg] = (int64_t)b * S + min(q0 + 16 * qg + lq, S - 1);
   // waves whose keys all lie above the tile's last query skip the products
-  const bool active = kw0 <= P + min(q0 + kTileQ, S) - 1;
+  // (q1's causal range covers q2's, so q1 decides the key loads)
+  bool active = kw0 <= P + min(q0 + kTileQ, S) - 1;
 
   bf16x8_t a[8][KS];
 #pragma unroll
@@ -118,7 +121,17 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
       for (int g = 0; g < G; ++g) wn[qg][g] = w[row[qg] * HI + min(st * G + g, HI - 1)];
   };
 
+  const bool vec = (T & 3) == 0;
   f32x4_t sc[kQG][8];
+  for (int tl = 0; tl < (tile.q2 >= 0 ? 2 : 1); ++tl) {
+  if (tl == 1) {  // the pair's earlier query tile with the same key registers
+    qt = tile.q2;
+    q0 = qt * kTileQ;
+#pragma unroll
+    for (int qg = 0; qg < kQG; ++qg) row[qg] = (int64_t)b * S + min(q0 + 16 * qg + lq, S - 1);
+    active = kw0 <= P + min(q0 + kTileQ, S) - 1;
+    __syncthreads();  // every wave is done with the previous tile's last stage buffer
+  }
 #pragma unroll
   for (int qg = 0; qg < kQG; ++qg)
 #pragma unroll
@@ -182,8 +195,6 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
   }
 
   // lane (lq, lg) holds keys kw0 + 16 kb + 4 lg + e of query q0 + 16 qg + lq
-  const bool vec = (T & 3) == 0;
-  idx_fill_upper<kTileQ>(scores, tile, b, S, T, nkt, vec);
 #pragma unroll
   for (int qg = 0; qg < kQG; ++qg) {
     const int s = q0 + 16 * qg + lq;
@@ -209,6 +220,8 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
       }
     }
   }
+  }  // query tiles
+  idx_fill_upper2<kTileQ>(scores, tile, b, S, T, nkt, vec);
 }
 
 // Few queries per call: MFMA M = index heads (NHB blocks of 32), N = 32 keys.
@@ -339,10 +352,16 @@ __global__ __launch_bounds__(256) void idx_f32_kernel(const float* __restrict__ 
 template <int DI, int QG, int MODE>
 hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
                         int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
-  const IdxGrid g = idx_grid(S, T, P, 16 * QG);
+  // Long contexts (many key tiles per query tile) share each key tile between
+  // the pair's two query tiles. Measured with one 4096-query chunk after
+  // 524288 keys (32 heads): 14.97 -> 13.97 ms; at S = T (32768 and 4096) it
+  // gained nothing or lost 7%, so those keep one unit per workgroup.
+  const bool two = (int64_t)T >= 8 * (int64_t)S;
+  const IdxGrid g = idx_grid2(S, T, P, 16 * QG, two);
   if (g.gx > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((idx_tile_kernel<DI, QG, MODE>), dim3((unsigned)g.gx, B), dim3(256), 0, st, q,
-                     k, w, scores, S, T, P, HI, scale, g.nqt, g.nkt, g.npairs, g.maxlen);
+                     k, w, scores, S, T, P, HI, scale, g.nqt, g.nkt, g.npairs, g.maxlen,
+                     two ? 1 : 0);
   return hipGetLastError();
 }
 

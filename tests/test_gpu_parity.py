@@ -88,6 +88,8 @@ INDEX_CASES = [
     (1, 700, 100, 4, 64, 0), (2, 150, 600, 8, 32, 2), (1, 1100, 0, 8, 64, 1),
     # few heads at dim 128 (one query group)
     (2, 150, 600, 4, 128, 2),
+    # T >= 8 S: one workgroup multiplies a key tile with both query tiles of its pair
+    (1, 100, 3000, 8, 128, 0), (2, 37, 700, 3, 64, 1), (1, 50, 900, 70, 128, 2),
 ]
 
 
