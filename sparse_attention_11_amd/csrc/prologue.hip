@@ -9,10 +9,11 @@
 //
 // Kernels
 //  gemm_bf16_kernel   C[M,N] = A[M,K] W[N,K]^T (nn.Linear weights), bf16 in,
-//                     fp32 accumulate, bf16 out. 128 x 128 tiles, 4 waves of
-//                     64 x 64, v_mfma_f32_32x32x16_bf16 with both operands
-//                     read K-contiguous from LDS (K steps of 64,
-//                     double-buffered, the next step loaded into registers
+//                     fp32 accumulate, bf16 out. Tiles of 128 x 128 (K steps
+//                     of 64) or, for wide outputs, 256 x 128 (K steps of 32),
+//                     4 waves of 64 x 64 or 128 x 64, v_mfma_f32_32x32x16_bf16
+//                     with both operands read K-contiguous from LDS
+//                     (double-buffered, the next step loaded into registers
 //                     under the current MFMAs); the MFMA forms C^T so that a
 //                     lane stores four consecutive columns at once.
 //  rope_q_kernel      half-split RoPE on the last rope_dim dims of every
@@ -26,9 +27,13 @@
 namespace dsa {
 namespace {
 
-constexpr int kGBM = 128, kGBN = 128, kGBK = 64;
-constexpr int kGPad = kGBK + 8;  // bf16 per LDS row (144 bytes: conflict-free 16-byte reads)
-constexpr int kGLd = kGBM * kGBK / 8 / 256;  // 16-byte chunks per thread per operand tile
+constexpr int kGBN = 128;  // output columns per workgroup
+// rows per workgroup (BM) and K step (BK): 128 x 64 for skinny outputs, 256
+// x 32 for wide ones (half the L2 -> CU operand bytes per flop of the square
+// tile, same LDS footprint). LDS rows are padded by 8 bf16 (16 bytes), which
+// keeps the 16-byte operand reads of 32 consecutive rows conflict-free.
+template <int BM>
+constexpr int gemm_bk() { return BM == 256 ? 32 : 64; }
 constexpr int kGroupedTiles = 8;  // column tiles up to which a row tile stays on one XCD
 
 // Two weight / output pairs share one pass over A (the key and head-weight
@@ -53,10 +58,16 @@ struct GemmRope {
 
 // RHALF: half the rotary width (16 or 32) for the RoPE epilogue, 0 for none;
 // a compile-time constant so that every rotary pair's registers are fixed.
-template <int RHALF>
+template <int RHALF, int BM>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                            GemmOut o1, GemmOut o2, int M, int K,
                                                            int ntiles_n, int nt1, GemmRope rp) {
+  constexpr int kGBM = BM, kGBK = gemm_bk<BM>(), kGPad = kGBK + 8;
+  constexpr int kWM = BM / 2;                  // rows per wave (2 x 2 waves)
+  constexpr int kWI = kWM / 32;                // 32-row MFMA blocks per wave
+  constexpr int kCPR = kGBK / 8;               // 16-byte chunks per tile row
+  constexpr int kGLdA = kGBM * kCPR / 256;     // A chunks per thread
+  constexpr int kGLdW = kGBN * kCPR / 256;     // W chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGBM * kGPad];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGBN * kGPad];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,30 +90,40 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   const int N = second ? o2.N : o1.N, ldc = second ? o2.ldc : o1.ldc;
   const int n0 = (second ? nt - nt1 : nt) * kGBN;
 
-  // global -> register staging: 1024 16-byte chunks per operand tile, 4 per thread
-  u32x4_t ra[kGLd], rw[kGLd];
+  // global -> register staging of the next K step (16-byte chunks)
+  u32x4_t ra[kGLdA], rw[kGLdW];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < kGLd; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = 8 * (c & 7);
-      const int m = m0 + r, n = n0 + r;
+    for (int i = 0; i < kGLdA; ++i) {
+      const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
+      const int m = m0 + r;
       const bool kin = k0 + kc < K;  // K % 32 == 0: a chunk is all in or all out
       ra[i] = (m < M && kin) ? load16(A + (int64_t)m * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kGLdW; ++i) {
+      const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
+      const int n = n0 + r;
+      const bool kin = k0 + kc < K;
       rw[i] = (n < N && kin) ? load16(W + (int64_t)n * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kGLd; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = 8 * (c & 7);
+    for (int i = 0; i < kGLdA; ++i) {
+      const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
       *(u32x4_t*)(&As[buf][r * kGPad + kc]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kGLdW; ++i) {
+      const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
       *(u32x4_t*)(&Ws[buf][r * kGPad + kc]) = rw[i];
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[kWI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
@@ -115,10 +136,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     if (kt + 1 < nk) load_tile((kt + 1) * kGBK);
 #pragma unroll
     for (int s = 0; s < kGBK / 16; ++s) {
-      bf16x8_t a[2], b[2];
+      bf16x8_t a[kWI], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + 32 * i + (lane & 31);
+      for (int i = 0; i < kWI; ++i) {
+        const int r = wm * kWM + 32 * i + (lane & 31);
         a[i] = as_bf16x8(*(const u32x4_t*)(&As[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
       }
 #pragma unroll
@@ -127,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
         b[j] = as_bf16x8(*(const u32x4_t*)(&Ws[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kWI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     }
@@ -146,8 +167,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     constexpr int half = RHALF;
     const int hd0 = (n0 + wn * 64) % rp.D;  // head dim of the wave's first column
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+    for (int i = 0; i < kWI; ++i) {
+      const int m = m0 + wm * kWM + 32 * i + (lane & 31);
       const int p = rp.P + (m < M ? m : M - 1) % rp.S;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -170,10 +191,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+      const int m = m0 + wm * kWM + 32 * i + (lane & 31);
       if (m >= M) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -284,18 +305,30 @@ hipError_t gemm_launch(const void* A, GemmOut o1, GemmOut o2, int M, int K, cons
   if (K % 32 != 0) return hipErrorInvalidValue;
   const int nt1 = (o1.N + kGBN - 1) / kGBN, nt2 = o2.N > 0 ? (o2.N + kGBN - 1) / kGBN : 0;
   const int ntn = nt1 + nt2;
-  const int64_t mtiles = (M + kGBM - 1) / kGBM;
+  // wide outputs: 256-row tiles (still >= 2 workgroups per CU at M = 32768)
+  const int bm = (ntn > kGroupedTiles && (int64_t)((M + 255) / 256) * ntn >= 2048) ? 256 : 128;
+  const int64_t mtiles = (M + bm - 1) / bm;
   const int64_t g = (ntn <= kGroupedTiles ? (mtiles + 7) / 8 * 8 : mtiles) * ntn;
   if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (rp && rp->R == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<32>), dim3((unsigned)g), dim3(256), 0, st,
-                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, *rp);
-  else if (rp && rp->R == 32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<16>), dim3((unsigned)g), dim3(256), 0, st,
-                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, *rp);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<0>), dim3((unsigned)g), dim3(256), 0, st,
-                       (const uint16_t*)A, o1, o2, M, K, ntn, nt1, GemmRope{});
+#define DSA_GEMM_LAUNCH(RH, BMV, RP)                                                             \
+  hipLaunchKernelGGL((gemm_bf16_kernel<RH, BMV>), dim3((unsigned)g), dim3(256), 0, st,          \
+                     (const uint16_t*)A, o1, o2, M, K, ntn, nt1, RP)
+  if (bm == 256) {
+    if (rp && rp->R == 64)
+      DSA_GEMM_LAUNCH(32, 256, *rp);
+    else if (rp && rp->R == 32)
+      DSA_GEMM_LAUNCH(16, 256, *rp);
+    else
+      DSA_GEMM_LAUNCH(0, 256, GemmRope{});
+  } else {
+    if (rp && rp->R == 64)
+      DSA_GEMM_LAUNCH(32, 128, *rp);
+    else if (rp && rp->R == 32)
+      DSA_GEMM_LAUNCH(16, 128, *rp);
+    else
+      DSA_GEMM_LAUNCH(0, 128, GemmRope{});
+  }
+#undef DSA_GEMM_LAUNCH
   return hipGetLastError();
 }
 }  // namespace

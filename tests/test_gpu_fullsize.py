@@ -367,11 +367,14 @@ def test_spark_swa_chunk_and_decode():
 
 
 # -------------------------------------------------------- prologue-s32k
-def test_prologue_s32k_sampled_rows():
+@pytest.mark.parametrize("S", [32768, 8100])
+def test_prologue_s32k_sampled_rows(S):
     """The indexer's projections at full size (three GEMMs + LayerNorm / RoPE in
-    the benchmark's launch configuration), sampled tokens against the oracle."""
+    the benchmark's launch configuration), sampled tokens against the oracle.
+    S = 8100 still takes the 256-row tiles of the wide q projection (32 row
+    tiles x 64 column tiles) and ends in a ragged row tile of 164 rows."""
     wl = WORKLOADS["prologue-s32k"]
-    S, HI, D, Q, Hd, R = wl.S, wl.HI, wl.DI, wl.q_lora, wl.hidden, wl.rope_idx
+    HI, D, Q, Hd, R = wl.HI, wl.DI, wl.q_lora, wl.hidden, wl.rope_idx
     E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=DEV)
     gen = lambda t, tid, sc: datagen.normal_device(t, wl.seed, tid, sc)
     q_lora, hidden = gen(E(1, S, Q), 20, 1.0), gen(E(1, S, Hd), 21, 1.0)
@@ -387,6 +390,8 @@ def test_prologue_s32k_sampled_rows():
         "wq_b", "wk", "k_norm_w", "k_norm_b", "weights_proj")], to_dev(cos), to_dev(sin),
         q_idx, k_cache, w, 0)
     rows = sample_rows(S, 2048, n=8, seed=3)
+    if S % 256:
+        rows = sorted(set(rows) | {S // 256 * 256, S - 2})  # first and late rows of the ragged tile
     got_q, got_k, got_w = from_dev(q_idx[0, rows]), from_dev(k_cache[0, rows]), from_dev(w[0, rows])
     del q_lora, hidden, q_idx, k_cache, w
     _free()
