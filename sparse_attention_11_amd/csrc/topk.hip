@@ -15,7 +15,7 @@
 // the causal half of every prefill row out of the histograms, where its
 // identical keys would serialise the LDS atomics.)
 //
-// One 256-thread workgroup per (row, segment):
+// One workgroup (256, 512 or 1024 threads) per (row, segment):
 //  1. count the valid keys; k' = min(k, count);
 //  2. radix select of the k'-th largest key, most significant digit first,
 //     11/11/10-bit digits per 32-bit half, one shared LDS histogram per
@@ -119,7 +119,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
 // EPT > 0 keeps the elements in registers (range <= NT*EPT); EPT == 0 streams.
 // E: sort elements per thread (the sort covers max(k, NT) = NT*E keys).
 // Stages with at most 16 keys per thread are held to 64 registers so that
-// 2048 threads (8 waves per SIMD) fit a CU; the 64-key stages need more.
+// 2048 threads (8 waves per SIMD) fit a CU; the 32-key stages need more.
 template <int NT, int SRC, int DST, int EPT, int E>
 __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(const void* __restrict__ src,
                                                         int32_t* __restrict__ out_idx,
@@ -415,27 +415,34 @@ template <int NT, int SRC, int DST, int EPT>
 hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T, int k,
                     int seg_len, int nseg, hipStream_t st) {
   const dim3 g((unsigned)blocks), b(NT);
-  // sort width NT*E >= max(k, NT)
+  // sort width NT*E >= max(k, NT); k <= kMaxK = 8 * 256, so 1024 threads
+  // need E <= 2 and 512 threads E <= 4
+  constexpr int E4 = NT >= 1024 ? 2 : 4, E8 = NT >= 1024 ? 2 : (NT >= 512 ? 4 : 8);
   if (DST == 1 || k <= NT)
     hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
   else if (k <= 2 * NT)
     hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
-  else if (NT == 256 && k <= 1024)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, (NT == 256 ? 4 : 2)>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+  else if (k <= 4 * NT)
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
   else
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, (NT == 256 ? 8 : 2)>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
   return hipGetLastError();
 }
 
 // A stage with few workgroups (few rows: decode, one long sequence) uses
 // 1024-thread workgroups so that each row gets four times the lanes; a
 // stage whose elements per workgroup are at most `range` keeps them in
-// registers (range / NT each).
+// registers (range / NT each). Ranges of 16384 take 512 threads (32 keys
+// each, 80 registers, 6 waves per SIMD) rather than 256 threads of 64 keys
+// (150 registers, 3 waves per SIMD): measured on 16384-score segments of a
+// 528384-key row, 4.23 -> 3.55 ms for 4096 rows, bit-identical.
 template <int SRC, int DST, int RANGE>
 hipError_t launch_stage(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T,
                         int k, int seg_len, int nseg, hipStream_t st) {
   if (blocks < 256)
     return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
+  if (RANGE / 256 > 16)
+    return launch_e<512, SRC, DST, RANGE / 512>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
   return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
 }
 
