@@ -501,7 +501,9 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
     in = outb;
     outb = tmp;
   }
-  // final selection and sort among at most kCand candidates per row
+  // final selection and sort among at most kCand candidates per row (rows of
+  // two segments have at most 4096: 16 per thread of a 256-thread workgroup)
+  if (C <= 4096) return launch_stage<1, 0, 4096>(in, indices, nullptr, rows, C, topk, C, 1, st);
   return launch_stage<1, 0, kCand>(in, indices, nullptr, rows, C, topk, C, 1, st);
 }
 
