@@ -9,7 +9,9 @@ inputs already resident in HBM:
                      both SWA layers
   *-pas              the same with 128 attention sinks per layer
 Every stage is a C-ABI call of libdsa.so; stage times come from HIP events
-recorded on the same stream the library launches on.
+recorded on the same stream the library launches on. The top-k stage is
+dsa_topk_unsorted: the same selection as dsa_topk without the final sort by
+score, since the attention calls take the selection as a set.
 
 Prints ONE JSON line. `value` is prefill tokens/s of the named workload
 (default mla-s4k, the DeepSeek-V2-shaped 4096-token prefill); the other
@@ -176,7 +178,7 @@ class Layer:
         else:
             st = [("K1 index_scores", lambda: dsa.dsa_index_scores(
                 self.q_idx, self.k_idx[:, : wl.T] if wl.B == 1 else self.k_idx, self.w, self.scores, P))]
-        st.append(("K2 topk", lambda: dsa.dsa_topk(self.scores, self.idx, self.tk_ws)))
+        st.append(("K2 topk", lambda: dsa.dsa_topk_unsorted(self.scores, self.idx, self.tk_ws)))
         kc = self.k if self.T_alloc == wl.T else self.k[:, : wl.T]
         vc = self.v if self.T_alloc == wl.T else self.v[:, : wl.T]
         if S > 1:
@@ -193,7 +195,7 @@ class Layer:
             Td = wl.T + 1
             st += [
                 ("D K1 index_scores", lambda: dsa.dsa_index_scores(self.qd_idx, self.k_idx, self.wd, self.sd, Td - 1)),
-                ("D K2 topk", lambda: dsa.dsa_topk(self.sd, self.idd, self.tk_wsd)),
+                ("D K2 topk", lambda: dsa.dsa_topk_unsorted(self.sd, self.idd, self.tk_wsd)),
                 ("D K4 sparse_attn_decode", lambda: self._decode(
                     self.qd, self.k, self.v, self.idd, self.gd, self.od, self.wsd)),
             ]

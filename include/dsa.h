@@ -143,6 +143,18 @@ int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int top
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same selection as dsa_topk ([AXK2] §1) without the final ordering:
+ * indices[b,s,0..n) hold the n = min(topk, finite scores in the row)
+ * selected positions in an unspecified order that is identical from run to
+ * run, and the remaining slots hold -1. The attention calls take index lists
+ * as sets, so a layer may use either call; this one skips the sort. Same
+ * arguments, limits, workspace (dsa_topk_workspace_size) and status codes as
+ * dsa_topk.
+ */
+int dsa_topk_unsorted(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sparse MLA attention over the selected expanded K/V rows, prefill
  * ([AXK2] "MLA + explicit sparse mask" steps 3-5: the cache holds expanded
  * K/V; the indexer's positions form an additive mask, combined with the

@@ -27,7 +27,7 @@ RELU_PER_HEAD, RELU_NONE, RELU_POST_SUM = 0, 1, 2
 MAX_TOPK = 2048
 
 _EXPORTS = [
-    "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk",
+    "dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_unsorted",
     "dsa_sparse_attn_prefill_workspace_size", "dsa_sparse_attn_prefill",
     "dsa_sparse_attn_decode_workspace_size", "dsa_sparse_attn_decode",
     "swa_attn_workspace_size", "swa_attn", "dsa_status_string", "dsa_last_error",
@@ -64,6 +64,7 @@ def lib():
         L.dsa_topk_workspace_size.argtypes = [i32, i32, i32, i32]
         L.dsa_topk_workspace_size.restype = sz
         L.dsa_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
+        L.dsa_topk_unsorted.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
         L.dsa_sparse_attn_prefill_workspace_size.argtypes = [i32] * 8
         L.dsa_sparse_attn_prefill_workspace_size.restype = sz
         L.dsa_sparse_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -100,7 +101,7 @@ def lib():
         L.swa_attn_gqa_workspace_size.restype = sz
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, i32, i32, vp, sz, vp]
-        for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_attn_prefill",
+        for fn in ("dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
                    "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
                    "dsa_index_quant_fp8", "dsa_index_scores_fp8", "dsa_indexer_prologue"):
@@ -172,16 +173,24 @@ def dsa_topk_workspace_size(B: int, S: int, T: int, topk: int) -> int:
     return int(lib().dsa_topk_workspace_size(B, S, T, topk))
 
 
-def dsa_topk(scores, indices, workspace=None, stream=None):
+def _topk_call(name, scores, indices, workspace, stream):
     B, S, T = scores.shape
     topk = indices.shape[-1]
     need = dsa_topk_workspace_size(B, S, T, topk)
     if workspace is None:
         workspace = _workspace(need, scores)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dsa_topk", lib().dsa_topk(_ptr(scores), _ptr(indices), B, S, T, topk,
+    _check(name, getattr(lib(), name)(_ptr(scores), _ptr(indices), B, S, T, topk,
                                       _ptr(workspace), nbytes, _stream(stream)))
     return indices
+
+
+def dsa_topk(scores, indices, workspace=None, stream=None):
+    return _topk_call("dsa_topk", scores, indices, workspace, stream)
+
+
+def dsa_topk_unsorted(scores, indices, workspace=None, stream=None):
+    return _topk_call("dsa_topk_unsorted", scores, indices, workspace, stream)
 
 
 def dsa_sparse_attn_prefill_workspace_size(B, S, T, H, qk_dim, v_dim, topk, dtype) -> int:

@@ -334,9 +334,9 @@ size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
   return dsa::topk_workspace_bytes(B, S, T, topk);
 }
 
-int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "dsa_topk";
+static int topk_impl(const char* fn, const float* scores, int32_t* indices, int B, int S, int T,
+                     int topk, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                     int order) {
   g_err.clear();
   if (!scores || !indices) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || S < 1 || T < 1) return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1", fn);
@@ -346,7 +346,20 @@ int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int top
     return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
   int st = check_ws(fn, workspace, workspace_bytes, dsa::topk_workspace_bytes(B, S, T, topk));
   if (st) return st;
-  return hip_status(dsa::launch_topk(scores, indices, B, S, T, topk, workspace, stream), fn);
+  return hip_status(dsa::launch_topk(scores, indices, B, S, T, topk, workspace, stream, order),
+                    fn);
+}
+
+int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl("dsa_topk", scores, indices, B, S, T, topk, workspace, workspace_bytes, stream,
+                   0);
+}
+
+int dsa_topk_unsorted(const float* scores, int32_t* indices, int B, int S, int T, int topk,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl("dsa_topk_unsorted", scores, indices, B, S, T, topk, workspace,
+                   workspace_bytes, stream, 1);
 }
 
 size_t dsa_sparse_attn_prefill_workspace_size(int B, int S, int T, int H, int qk_dim, int v_dim,

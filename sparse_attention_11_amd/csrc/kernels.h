@@ -36,8 +36,10 @@ hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const
 
 // Per-row top-k (topk.hip).
 size_t topk_workspace_bytes(int B, int S, int T, int topk);
+// order 0: by score descending (ties: lower position first); 1: the same
+// selection unsorted (a fixed, repeatable order), -1 slots last.
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void* workspace, hipStream_t stream);
+                       void* workspace, hipStream_t stream, int order = 0);
 
 // Selection bitmap + MFMA flash attention with a bitmap or window mask
 // (attn_prefill.hip). Requires bf16 and a (Dqk, Dv) pair that

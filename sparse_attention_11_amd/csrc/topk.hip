@@ -26,7 +26,8 @@
 //  4. either a bitonic sort (descending; strides inside a thread run in
 //     registers, inside a wave via lane swaps, only the widest through LDS)
 //     and the index output, or, for the first stage of a long row, the
-//     unsorted keys of the segment (padded with 0) for a second pass.
+//     unsorted keys of the segment (padded with 0) for a second pass, or,
+//     when the caller asks for no ordering, the compacted list itself.
 // Rows longer than 16384 are split: segments of 16384 scores are reduced to
 // k candidate keys each, groups of 16384 candidates are reduced again until
 // at most 16384 remain, then one workgroup per row selects and sorts the
@@ -124,7 +125,7 @@ template <int NT, int SRC, int DST, int EPT, int E>
 __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(const void* __restrict__ src,
                                                         int32_t* __restrict__ out_idx,
                                                         uint64_t* __restrict__ out_keys, int T,
-                                                        int k, int seg_len, int nseg) {
+                                                        int k, int seg_len, int nseg, int order) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
   // selected keys: k of them for a candidate stage, at most NT*E >= k for a
@@ -354,6 +355,15 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
     for (int i = tid; i < k; i += NT) o[i] = (i < kk) ? sel[i] : 0ull;
     return;
   }
+  // unsorted output: the compacted list as it stands (its order is fixed by
+  // the thread layout, so it repeats from run to run)
+  static_assert(EPT > 0, "a repeatable order needs the ordered (register) compaction");
+  if (order != 0) {
+    int32_t* orow = out_idx + row * (int64_t)k;
+    for (int i = tid; i < k; i += NT)
+      orow[i] = (i < kk) ? (int32_t)(0xFFFFFFFFu - (uint32_t)sel[i]) : -1;
+    return;
+  }
 
   // ---- bitonic sort (descending) of N = NT*E keys, padded with 0. Keys are
   // unique apart from the 0 padding, so one compare decides each exchange:
@@ -413,19 +423,19 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
 
 template <int NT, int SRC, int DST, int EPT>
 hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T, int k,
-                    int seg_len, int nseg, hipStream_t st) {
+                    int seg_len, int nseg, hipStream_t st, int order) {
   const dim3 g((unsigned)blocks), b(NT);
   // sort width NT*E >= max(k, NT); k <= kMaxK = 8 * 256, so 1024 threads
   // need E <= 2 and 512 threads E <= 4
   constexpr int E4 = NT >= 1024 ? 2 : 4, E8 = NT >= 1024 ? 2 : (NT >= 512 ? 4 : 8);
   if (DST == 1 || k <= NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
   else if (k <= 2 * NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
   else if (k <= 4 * NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
   else
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
   return hipGetLastError();
 }
 
@@ -438,12 +448,12 @@ hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t block
 // 528384-key row, 4.23 -> 3.55 ms for 4096 rows, bit-identical.
 template <int SRC, int DST, int RANGE>
 hipError_t launch_stage(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T,
-                        int k, int seg_len, int nseg, hipStream_t st) {
+                        int k, int seg_len, int nseg, hipStream_t st, int order = 0) {
   if (blocks < 256)
-    return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
+    return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
   if (RANGE / 256 > 16)
-    return launch_e<512, SRC, DST, RANGE / 512>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
-  return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st);
+    return launch_e<512, SRC, DST, RANGE / 512>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
+  return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
 }
 
 constexpr int kCand = 16384;  // candidate keys one register-resident workgroup takes
@@ -475,11 +485,11 @@ size_t topk_workspace_bytes(int B, int S, int T, int topk) {
 }
 
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void* workspace, hipStream_t st) {
+                       void* workspace, hipStream_t st, int order) {
   const int64_t rows = (int64_t)B * S;
   if (T <= kSegLen) {  // one register-resident workgroup per row
-    if (T <= 4096) return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st);
-    return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st);
+    if (T <= 4096) return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
+    return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
   }
   int groups[8];
   const int lv = stage_groups(T, topk, groups, 8);
@@ -503,8 +513,8 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
   }
   // final selection and sort among at most kCand candidates per row (rows of
   // two segments have at most 4096: 16 per thread of a 256-thread workgroup)
-  if (C <= 4096) return launch_stage<1, 0, 4096>(in, indices, nullptr, rows, C, topk, C, 1, st);
-  return launch_stage<1, 0, kCand>(in, indices, nullptr, rows, C, topk, C, 1, st);
+  if (C <= 4096) return launch_stage<1, 0, 4096>(in, indices, nullptr, rows, C, topk, C, 1, st, order);
+  return launch_stage<1, 0, kCand>(in, indices, nullptr, rows, C, topk, C, 1, st, order);
 }
 
 }  // namespace dsa

@@ -60,18 +60,21 @@ def test_index_scores_validation(kw, code):
     assert dsa.dsa_last_error().startswith("dsa_index_scores")
 
 
-def topk(**kw):
+def topk(fn="dsa_topk", **kw):
     a = dict(s=P, i=P, B=1, S=2, T=100, k=10, ws=None, nb=0)
     a.update(kw)
-    return dsa.lib().dsa_topk(a["s"], a["i"], a["B"], a["S"], a["T"], a["k"], a["ws"], a["nb"], None)
+    return getattr(dsa.lib(), fn)(a["s"], a["i"], a["B"], a["S"], a["T"], a["k"], a["ws"], a["nb"],
+                                  None)
 
 
+@pytest.mark.parametrize("fn", ["dsa_topk", "dsa_topk_unsorted"])
 @pytest.mark.parametrize("kw,code", [
     (dict(s=None), 1), (dict(i=None), 1), (dict(k=0), 1), (dict(k=101), 1), (dict(T=0), 1),
     (dict(T=5000, k=2049), 2),
 ])
-def test_topk_validation(kw, code):
-    assert topk(**kw) == code
+def test_topk_validation(fn, kw, code):
+    assert topk(fn, **kw) == code
+    assert dsa.dsa_last_error().startswith(fn + ":")
 
 
 def prefill(**kw):

@@ -128,23 +128,30 @@ def test_dsa_s32k_fp8_indexer_sampled_rows():
         assert_rows_close(got[i], ref, 1e-3, what=f"dsa-s32k fp8 scores row {s}")
 
 
-def _topk_full(wl, S, T, P, k, mode, rows, seed_off=0):
+def _topk_full(wl, S, T, P, k, mode, rows, seed_off=0, order=0):
     sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
     datagen.scores_device(sc.view(S, T), 0, S, P, wl.seed + seed_off, mode=mode)
     idx = torch.empty(1, S, k, dtype=torch.int32, device=DEV)
-    dsa.dsa_topk(sc, idx)
+    (dsa.dsa_topk_unsorted if order else dsa.dsa_topk)(sc, idx)
     got = idx[0, rows].cpu().numpy()
     del sc, idx
     _free()
     for i, s in enumerate(rows):
         ref_sc = datagen.scores_host(s, 1, S, T, P, wl.seed + seed_off, mode=mode)
-        np.testing.assert_array_equal(got[i], oracle.topk(ref_sc, k)[0], err_msg=f"row {s}")
+        ref = oracle.topk(ref_sc, k)[0]
+        g = got[i]
+        if order:  # unsorted: the same set, -1 slots last
+            nv = int((ref >= 0).sum())
+            assert (g[nv:] == -1).all(), f"row {s}: -1 slots not last"
+            g, ref = np.sort(g[:nv]), np.sort(ref[:nv])
+        np.testing.assert_array_equal(g, ref, err_msg=f"row {s}")
 
 
-@pytest.mark.parametrize("mode", [0, 2])
-def test_dsa_s32k_topk_full_tensor(mode):
+@pytest.mark.parametrize("mode,order", [(0, 0), (2, 0), (0, 1)])
+def test_dsa_s32k_topk_full_tensor(mode, order):
     wl = WORKLOADS["dsa-s32k"]
-    _topk_full(wl, wl.S, wl.T, 0, wl.topk, mode, sample_rows(wl.S, wl.topk, n=12, seed=2))
+    _topk_full(wl, wl.S, wl.T, 0, wl.topk, mode, sample_rows(wl.S, wl.topk, n=12, seed=2),
+               order=order)
 
 
 def test_dsa_s32k_prefill_sampled_rows():
@@ -271,6 +278,8 @@ def test_hybrid_512k_chunk_and_decode():
     # top-k on synthetic chunk-shaped and decode-shaped score rows
     _topk_full(wl, S, T, P, wl.topk, 1, [0, 7, S - 1], seed_off=50)
     _topk_full(wl, 1, Ta, T, wl.topk, 2, [0], seed_off=51)
+    _topk_full(wl, S, T, P, wl.topk, 1, [3, S - 2], seed_off=50, order=1)
+    _topk_full(wl, 1, Ta, T, wl.topk, 2, [0], seed_off=51, order=1)
 
     # DSA attention: chunk (MFMA path) and decode (gather path)
     k = dev_normal((1, Ta, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)

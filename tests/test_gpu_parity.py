@@ -117,12 +117,24 @@ def test_index_scores_custom_scale_and_longer_cache():
 
 
 # ----------------------------------------------------------------- top-k
-def _run_topk(scores32: np.ndarray, k: int) -> np.ndarray:
+def _run_topk(scores32: np.ndarray, k: int, order: int = 0) -> np.ndarray:
     B, S, T = scores32.shape
     idx = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
-    dsa.dsa_topk(to_dev(scores32), idx)
+    (dsa.dsa_topk_unsorted if order else dsa.dsa_topk)(to_dev(scores32), idx)
     _sync()
     return idx.cpu().numpy()
+
+
+def as_set(x: np.ndarray) -> np.ndarray:
+    """Index lists in canonical form: the selected positions ascending, then
+    the -1 slots. Unsorted results must also hold their -1 slots last."""
+    out = np.full_like(x, -1)
+    for r in np.ndindex(x.shape[:-1]):
+        valid = x[r] >= 0
+        assert not np.any(valid[1:] & ~valid[:-1]), f"row {r}: a -1 slot before a selected one"
+        sel = np.sort(x[r][valid])
+        out[r][:len(sel)] = sel
+    return out
 
 
 def test_topk_on_oracle_scores_tiny_and_mla():
@@ -142,31 +154,37 @@ def test_topk_on_oracle_scores_tiny_and_mla():
     (4096, 4000, 512, 1), (4096, 3990, 256, 2), (3000, 2900, 300, 1), (1000, 976, 512, 0),
     (4096, 4072, 129, 0),
 ])
-def test_topk_synthetic_rows(T, P, k, mode):
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_synthetic_rows(T, P, k, mode, order):
     S = T - P
     rows = min(S, 24)
     sc = datagen.scores_host(0, rows, S, T, P, seed=T + k, mode=mode)
-    got = _run_topk(sc[None], k)[0]
-    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+    got = _run_topk(sc[None], k, order)[0]
+    ref = oracle.topk(sc, k)
+    np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
 
 
 # Enough rows that every stage runs 256-thread workgroups (few-row calls use
 # 1024-thread ones): a mid-length single-stage row and a two-stage row.
 @pytest.mark.parametrize("rows,T,k,mode", [(300, 6000, 1024, 1), (96, 33000, 2048, 0)])
-def test_topk_many_rows(rows, T, k, mode):
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_many_rows(rows, T, k, mode, order):
     P = T - rows
     sc = datagen.scores_host(0, rows, rows, T, P, seed=rows + T, mode=mode)
-    got = _run_topk(sc[None], k)[0]
-    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+    got = _run_topk(sc[None], k, order)[0]
+    ref = oracle.topk(sc, k)
+    np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
 
 
 @pytest.mark.parametrize("T,k", [(3000, 2048), (2000, 500), (4096, 512)])
-def test_topk_constant_and_all_masked_tail(T, k):
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_constant_and_all_masked_tail(T, k, order):
     sc = np.zeros((2, T), np.float32)
     sc[1, 5:] = -np.inf
     sc[0, ::2] = -0.0
-    got = _run_topk(sc[None], k)[0]
-    np.testing.assert_array_equal(got, oracle.topk(sc, k))
+    got = _run_topk(sc[None], k, order)[0]
+    ref = oracle.topk(sc, k)
+    np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
     assert got[1, 5:].tolist() == [-1] * (k - 5)
 
 
