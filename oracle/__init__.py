@@ -25,14 +25,19 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   index_quant_fp8
                 pinned: closed forms (a unit vector rotates to all ones),
                 torch's float8_e4m3fn conversion of the same scaled values,
-                scipy's Hadamard matrix within FP8 rounding, the scale rule.
+                scipy's Hadamard matrix within FP8 rounding, the scale rule;
+                against E4M3 of the exact fp64 rotation: equal on Gaussian
+                rows, elsewhere different only at rounding midpoints within
+                the fp32 rotation's error bound.
   index_scores_fp8
                 pinned: index_scores on the dequantised rows with scale / D;
                 Hadamard invariance of index_scores (H q . H k = D q . k).
   indexer_prologue
                 pinned: torch's linear and layer_norm, RoPE closed forms
                 (position 0 is the identity, pair norms are kept, rotating by
-                a and then by -a restores the input, the angle-sum identity).
+                a and then by -a restores the input, the angle-sum identity),
+                the direction by a quarter turn and the textbook
+                x cos + rotate_half(x) sin form.
 Parity unpinned by the pages (fixed by convention, tested in every mode):
 ReLU placement (per head by default), the two scale constants, and the
 inclusive window boundary.

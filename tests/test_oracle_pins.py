@@ -714,3 +714,101 @@ def test_prologue_rope_rotation_group():
     np.testing.assert_allclose(rot(ya, -a).reshape(B, S, Q), xq, rtol=1e-6, atol=1e-6)
     ab = rot(rot(xq, a).reshape(B, S, Q), b)
     np.testing.assert_allclose(ab, rot(xq, a + b), rtol=1e-5, atol=1e-5)
+
+
+def test_prologue_rope_quarter_turn_and_rotate_half():
+    # Direction of the half-split rotation (A.X-K2 page, "two RoPE layouts": the
+    # indexer rotates pair (j, j + R/2)). At a quarter turn (cos 0, sin 1) the pair
+    # (x_j, x_{j+R/2}) must become (-x_{j+R/2}, x_j); at any angle the result is the
+    # textbook half-split form x cos + rotate_half(x) sin, rotate_half(x) = (-x2, x1),
+    # with the same angle on both halves. Rotating by -theta fails both.
+    B, S, HI, D, R, P = 1, 3, 2, 16, 8, 2
+    Q, Hd = HI * D, 32
+    rng = np.random.default_rng(14)
+    xq = rng.standard_normal((B, S, Q)).astype(np.float32)
+    hid = rng.standard_normal((B, S, Hd)).astype(np.float32)
+    wk = (rng.standard_normal((D, Hd)) / np.sqrt(Hd)).astype(np.float32)
+    kn_w, kn_b = np.ones(D, np.float32), np.zeros(D, np.float32)
+    wp = np.ones((HI, Hd), np.float32)
+    eye = np.eye(Q, dtype=np.float32)
+    h = R // 2
+
+    def run(c, s):
+        return oracle.indexer_prologue(xq, hid, eye, wk, kn_w, kn_b, wp, c, s, P, HI, 1e-5)
+
+    q0, k0, _ = run(np.ones((P + S, h), np.float32), np.zeros((P + S, h), np.float32))
+    q1, k1, _ = run(np.zeros((P + S, h), np.float32), np.ones((P + S, h), np.float32))
+    for a1, a0 in ((q1, q0), (k1, k0)):
+        lo, hi = a0[..., D - R: D - h], a0[..., D - h:]
+        np.testing.assert_array_equal(a1[..., D - R: D - h], -hi)
+        np.testing.assert_array_equal(a1[..., D - h:], lo)
+    ang = rng.uniform(-np.pi, np.pi, (P + S, h))
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    q2, k2, _ = run(c, s)
+    cc = np.concatenate([c, c], -1)[P:].astype(np.float64)
+    ss = np.concatenate([s, s], -1)[P:].astype(np.float64)
+    for a2, a0 in ((q2, q0.reshape(B, S, HI, D)), (k2, k0)):
+        x = torch.from_numpy(np.ascontiguousarray(a0[..., D - R:]))
+        rot_half = torch.cat([-x[..., h:], x[..., :h]], dim=-1).numpy()
+        shp = (1, S, 1, R) if a0.ndim == 4 else (1, S, R)
+        ref = a0[..., D - R:] * cc.reshape(shp) + rot_half * ss.reshape(shp)
+        np.testing.assert_allclose(a2[..., D - R:], ref, rtol=1e-12, atol=1e-12)
+
+
+def _fp8_codes_vs_exact_rotation(xb):
+    """Oracle codes of bf16 rows and E4M3 of the exact (fp64) Hadamard product
+    scaled by the oracle's own row scale; rows whose exact-rotation scale differs
+    are checked and dropped."""
+    from scipy.linalg import hadamard
+    D = xb.shape[1]
+    x = _bf16_value(xb).astype(np.float64)
+    y = x @ hadamard(D).T.astype(np.float64)  # exact: bf16 inputs, +-1 entries
+    codes, scales = oracle.index_quant_fp8(xb)
+    bound = np.log2(D) * 2.0 ** -24 * np.abs(x).sum(axis=1)
+    amax = np.abs(y).max(axis=1)
+    # the scale rule on the exact rotation; a row whose amax sits within the bound
+    # of the rule's boundary may take the neighbouring scale
+    e_exact = np.ceil(np.log2(amax / 448.0))
+    same = np.log2(scales.astype(np.float64)) == e_exact
+    assert np.all(same | (np.abs(amax - 448.0 * 2.0 ** e_exact) <= bound))
+    assert same.mean() > 0.99
+    ys = y[same] / scales[same, None]
+    bs = np.broadcast_to((bound[same] / scales[same])[:, None], ys.shape)
+    # (ys is exact in fp64 and its fp32 rounding cannot cross an E4M3 midpoint,
+    # which has at most 5 significant bits)
+    return codes[same], _torch_e4m3(ys.astype(np.float32)), ys, bs
+
+
+def test_fp8_codes_equal_exact_rotation_on_gaussian_rows():
+    # on rows drawn like the workloads' (bf16 Gaussians) every fp32 butterfly sum
+    # is exact, so the codes are E4M3 of the exact Hadamard product everywhere
+    rng = np.random.default_rng(31)
+    xb = _bf16_bits(rng.standard_normal((4000, 128)))
+    got, ref, _, _ = _fp8_codes_vs_exact_rotation(xb)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8_codes_against_exact_rotation_differ_only_at_midpoints():
+    # The codes are defined by the rotation as computed in fp32 (reading of the
+    # A.X-K2 implementation notes). Rows with a wide exponent spread make fp32
+    # partial sums round; against E4M3 of the EXACT Hadamard product (same
+    # power-of-two scale) a code may then differ only where the fp32 rotation and
+    # the exact one lie on two sides of an E4M3 rounding midpoint, and by one code
+    # step. fp32 rotation error bound: log2(D) roundings, each at most 2^-24 of
+    # sum|x|.
+    rng = np.random.default_rng(31)
+    xb = _bf16_bits(rng.standard_normal((4000, 128)) * 2.0 ** rng.integers(-12, 13, (4000, 128)))
+    got, ref, ys, bs = _fp8_codes_vs_exact_rotation(xb)
+    diff = got != ref
+    assert diff.any()  # the case this pin is about occurs at this size
+    assert diff.mean() < 1e-4, diff.mean()
+    cv, vals = _e4m3_table()
+    table = np.zeros(256)
+    table[cv] = vals
+    gi, ri = got[diff].astype(np.int64), ref[diff].astype(np.int64)
+    # one code step: neighbouring magnitudes of one sign (or +-0 around zero)
+    step = np.abs((gi & 0x7F) - (ri & 0x7F))
+    assert np.all((step == 1) & (((gi ^ ri) & 0x80) == 0) | ((gi & 0x7F) == 0) & ((ri & 0x7F) == 0))
+    # the midpoint between the two codes' values lies within the bound of the exact value
+    mid = (table[gi] + table[ri]) / 2.0
+    assert np.all(np.abs(mid - ys[diff]) <= bs[diff])
