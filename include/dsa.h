@@ -71,6 +71,15 @@ extern "C" {
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_HEAD_DIM 256
 #define DSA_MAX_SINKS 256
+/* Size limits every call applies (DSA_ERR_UNSUPPORTED beyond them): query
+ * rows B * S <= DSA_MAX_ROWS; keys T, and positions past_len + S, <=
+ * DSA_MAX_KEYS; attention heads <= DSA_MAX_HEADS; index heads <=
+ * DSA_MAX_INDEX_HEADS. The *_workspace_size queries return 0 for sizes their
+ * calls reject. */
+#define DSA_MAX_ROWS (0x7FFFFFFF / 64)
+#define DSA_MAX_KEYS (1 << 30)
+#define DSA_MAX_HEADS 65535
+#define DSA_MAX_INDEX_HEADS 1024
 
 /*
  * Lightning-indexer scores with causal mask ([AXK2] §1: per-head dot products
@@ -86,7 +95,7 @@ extern "C" {
  *        triangle).
  * scale  > 0 and finite; the conventional value is idx_dim^-1/2.
  * relu_mode one of DSA_RELU_*.
- * Supported: idx_dim in {32, 64, 128}; any n_idx_heads >= 1.
+ * Supported: idx_dim in {32, 64, 128}; 1 <= n_idx_heads <= DSA_MAX_INDEX_HEADS.
  */
 int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
                      int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
@@ -136,7 +145,8 @@ int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const ui
  * indices [B,S,topk] int32
  * 1 <= topk <= min(T, DSA_MAX_TOPK).
  * workspace: at least dsa_topk_workspace_size(...) bytes (may be 0 bytes, in
- * which case workspace may be NULL).
+ * which case workspace may be NULL; the size query returns 0 for sizes the
+ * call rejects).
  */
 size_t dsa_topk_workspace_size(int B, int S, int T, int topk);
 int dsa_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
@@ -318,6 +328,24 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
                          int past_len, int q_lora_rank, int hidden_dim, int n_idx_heads,
                          int idx_dim, int rope_dim, float ln_eps, int dtype, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The work plan the MFMA prefill path (bf16, S >= 16) launches for a call
+ * with these sizes, for inspection; host arithmetic only, no GPU call. A
+ * query tile is 128 consecutive queries; tile qt sees the 64-key blocks of
+ * its causal range (DSA, window <= 0) or of its window range. When the grid
+ * would be small, long tiles are split into work items of at most
+ * *max_blocks blocks each (*max_blocks = INT_MAX when nothing is split).
+ * Outputs: *n_tiles, *n_items (workgroups per head and batch row) and, when
+ * cap >= *n_tiles + 1 and item_start is not NULL, item_start[o] = the first
+ * item of the o-th longest tile (tile n_tiles - 1 - o), item_start[n_tiles] =
+ * n_items (items of a tile are its consecutive key ranges, first to last).
+ * The prefill workspace is sized from the plan of past_len = T - S, which
+ * has the most items any call with this T can have.
+ * Returns DSA_OK, or DSA_ERR_INVALID_ARG for null outputs or bad sizes.
+ */
+int dsa_prefill_work_plan(int B, int S, int T, int past_len, int H, int kv_offset, int window,
+                          int* n_tiles, int* n_items, int* max_blocks, int* item_start, int cap);
 
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);

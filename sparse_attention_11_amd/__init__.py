@@ -37,6 +37,7 @@ _EXPORTS = [
     "swa_attn_gqa_workspace_size", "swa_attn_gqa",
     "dsa_index_quant_fp8", "dsa_index_scores_fp8",
     "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
+    "dsa_prefill_work_plan",
 ]
 MAX_SINKS = 256
 
@@ -101,7 +102,8 @@ def lib():
         L.swa_attn_gqa_workspace_size.restype = sz
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, i32, i32, vp, sz, vp]
-        for fn in ("dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
+        L.dsa_prefill_work_plan.argtypes = [i32] * 7 + [vp] * 4 + [i32]
+        for fn in ("dsa_prefill_work_plan", "dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
                    "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
                    "dsa_index_quant_fp8", "dsa_index_scores_fp8", "dsa_indexer_prologue"):
@@ -171,6 +173,23 @@ def dsa_index_scores(q_idx, k_idx, w, scores, past_len: int, scale: float | None
 
 def dsa_topk_workspace_size(B: int, S: int, T: int, topk: int) -> int:
     return int(lib().dsa_topk_workspace_size(B, S, T, topk))
+
+
+def dsa_prefill_work_plan(B: int, S: int, T: int, past_len: int, H: int, kv_offset: int = 0,
+                          window: int = 0):
+    """The MFMA prefill path's launch plan (host arithmetic only): returns
+    (n_tiles, n_items, max_blocks, item_start) with item_start[o] the first
+    work item of the o-th longest 128-query tile and item_start[n_tiles] =
+    n_items."""
+    import numpy as np
+    nqt = (S + 127) // 128
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    start = np.zeros(nqt + 1, np.int32)
+    _check("dsa_prefill_work_plan",
+           lib().dsa_prefill_work_plan(B, S, T, past_len, H, kv_offset, window, ctypes.byref(a),
+                                       ctypes.byref(b), ctypes.byref(c),
+                                       start.ctypes.data_as(ctypes.c_void_p), nqt + 1))
+    return a.value, b.value, c.value, start
 
 
 def _topk_call(name, scores, indices, workspace, stream):

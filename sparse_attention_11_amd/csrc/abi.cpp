@@ -33,6 +33,20 @@ bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 bool head_dim_ok(int d) { return d >= 16 && d <= DSA_MAX_HEAD_DIM && d % 16 == 0; }
 
+// Query rows (B * S) any call takes: grids index rows (times a small factor)
+// in 32 bits. 33.5 M rows is far beyond one GPU's HBM for these layers.
+constexpr long long kMaxRows = DSA_MAX_ROWS;
+bool rows_ok(int B, int S) { return (long long)B * S <= kMaxRows; }
+// Attention heads: the prefill grid's second dimension holds one per head.
+constexpr int kMaxHeads = DSA_MAX_HEADS;
+// Keys and positions: kernels index keys in 32 bits with small offsets
+// added, so T and past_len + S stay at or below 2^30 (2000x the longest
+// context here).
+constexpr int kMaxKeys = DSA_MAX_KEYS;
+bool keys_ok(long long T) { return T <= kMaxKeys; }
+// Index heads: products with the head count and dim stay in 32 bits.
+constexpr int kMaxIndexHeads = DSA_MAX_INDEX_HEADS;
+
 // Common checks of the attention entry points. Returns DSA_OK or a status.
 int check_attn(const char* fn, const void* q, const void* k, const void* v, const void* gate,
                const void* out, int B, int S, int T, int H, int nope, int rope, int v_dim,
@@ -41,11 +55,18 @@ int check_attn(const char* fn, const void* q, const void* k, const void* v, cons
   if (B < 1 || S < 1 || T < 1 || H < 1)
     return fail(DSA_ERR_INVALID_ARG, "%s: B, S, T and H must be >= 1 (got %d, %d, %d, %d)", fn, B,
                 S, T, H);
-  if (nope < 0 || rope < 0 || nope + rope < 1 || v_dim < 1)
+  if (nope < 0 || rope < 0 || nope + (long long)rope < 1 || v_dim < 1)
     return fail(DSA_ERR_INVALID_ARG, "%s: bad head dims (nope %d, rope %d, v %d)", fn, nope, rope,
                 v_dim);
+  if (nope > DSA_MAX_HEAD_DIM || rope > DSA_MAX_HEAD_DIM)  // (keeps nope + rope in range)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: head dims must be at most %d (nope %d, rope %d)", fn,
+                DSA_MAX_HEAD_DIM, nope, rope);
   if (dtype != DSA_F32 && dtype != DSA_BF16)
     return fail(DSA_ERR_INVALID_ARG, "%s: dtype must be DSA_F32 or DSA_BF16 (got %d)", fn, dtype);
+  if (!rows_ok(B, S))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (H > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d heads", fn, kMaxHeads);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   if (!finite_pos(sm_scale))
     return fail(DSA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
   if (gate_dim != 0 && gate_dim != 1 && gate_dim != v_dim)
@@ -72,12 +93,19 @@ size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, i
                   int n_sink) {
   if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim))
     return dsa::prefill_mfma_workspace_bytes(B, S, T, H, v_dim);
-  return dsa::gather_workspace_bytes(B * S, H, v_dim, topk + n_sink);
+  return dsa::gather_workspace_bytes((int64_t)B * S, H, v_dim, (int64_t)topk + n_sink);
 }
 
 size_t swa_ws(int B, int S, int H, int qk_dim, int v_dim, int window, int dtype, int n_sink) {
   if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return 0;
-  return dsa::gather_workspace_bytes(B * S, H, v_dim, window + n_sink);
+  return dsa::gather_workspace_bytes((int64_t)B * S, H, v_dim, (int64_t)window + n_sink);
+}
+
+// Size queries return 0 for arguments their calls reject (those calls fail
+// before they look at the workspace), and otherwise the exact requirement.
+bool attn_sizes_ok(int B, int S, int H, int qk_dim, int v_dim, int n_sink, int dtype) {
+  return B >= 1 && S >= 1 && H >= 1 && H <= kMaxHeads && rows_ok(B, S) && head_dim_ok(qk_dim) && head_dim_ok(v_dim) &&
+         n_sink >= 0 && n_sink <= DSA_MAX_SINKS && (dtype == DSA_F32 || dtype == DSA_BF16);
 }
 
 int check_sinks(const char* fn, const void* sink_k, const void* sink_v, int n_sink) {
@@ -143,7 +171,7 @@ int decode_impl(const char* fn, const void* q, const void* k_cache, const void* 
   if (topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
   st = check_ws(fn, workspace, workspace_bytes,
-                dsa::gather_workspace_bytes(B, H, v_dim, topk + n_sink));
+                dsa::gather_workspace_bytes(B, H, v_dim, (int64_t)topk + n_sink));
   if (st) return st;
   return hip_status(dsa::launch_gather(q, k_cache, v_cache, sink_k, sink_v, n_sink, indices, gate,
                                        out, B, 1, T, T - 1, 0, H, H, qk_nope_dim + qk_rope_dim, v_dim,
@@ -168,6 +196,8 @@ int swa_impl(const char* fn, const void* q, const void* k_buf, const void* v_buf
   if (window < 1) return fail(DSA_ERR_INVALID_ARG, "%s: window must be >= 1", fn);
   if (past_len < 0 || kv_offset < 0)
     return fail(DSA_ERR_INVALID_ARG, "%s: past_len and kv_offset must be >= 0", fn);
+  if (!keys_ok((long long)past_len + S))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: positions past_len + S above %d", fn, kMaxKeys);
   const long long lim = std::max(0LL, (long long)past_len - window + 1);
   if (kv_offset > lim)
     return fail(DSA_ERR_INVALID_ARG,
@@ -181,6 +211,9 @@ int swa_impl(const char* fn, const void* q, const void* k_buf, const void* v_buf
   if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
   if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
     return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);
+  // A window wider than the context selects the same keys as one of exactly
+  // past_len + S: every query's window then starts at or before position 0.
+  window = (int)std::min<long long>(window, (long long)past_len + S);
   st = check_ws(fn, workspace, workspace_bytes,
                 swa_ws(B, S, H, dqk, v_dim, window, dtype, n_sink));
   if (st) return st;
@@ -232,6 +265,10 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float*
     return fail(DSA_ERR_UNSUPPORTED, "%s: idx_dim must be 32, 64 or 128 (got %d)", fn, idx_dim);
   if ((long long)B * S > 65535 && dtype == DSA_F32)
     return fail(DSA_ERR_UNSUPPORTED, "%s: fp32 path limited to B*S <= 65535", fn);
+  if (!rows_ok(B, S)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (n_idx_heads > kMaxIndexHeads)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d index heads", fn, kMaxIndexHeads);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
   return hip_status(dsa::launch_index_scores(q_idx, k_idx, w, scores, B, S, T, past_len,
                                              n_idx_heads, idx_dim, scale, relu_mode, dtype,
@@ -274,6 +311,10 @@ int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const ui
   if (idx_dim != 128)
     return fail(DSA_ERR_UNSUPPORTED, "%s: idx_dim must be 128 (got %d)", fn, idx_dim);
   if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  if (!rows_ok(B, S)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (n_idx_heads > kMaxIndexHeads)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d index heads", fn, kMaxIndexHeads);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   return hip_status(dsa::launch_index_scores_fp8(q_codes, q_scales, k_codes, k_scales, w, scores,
                                                  B, S, T, past_len, n_idx_heads, idx_dim, scale,
                                                  relu_mode, stream),
@@ -281,7 +322,7 @@ int dsa_index_scores_fp8(const uint8_t* q_codes, const float* q_scales, const ui
 }
 
 size_t dsa_indexer_prologue_workspace_size(int B, int S, int idx_dim) {
-  if (B < 1 || S < 1 || idx_dim < 1) return 0;
+  if (B < 1 || S < 1 || (idx_dim != 64 && idx_dim != 128) || !rows_ok(B, S)) return 0;
   return (size_t)B * S * idx_dim * 2;  // the key projection before its LayerNorm (bf16)
 }
 
@@ -318,6 +359,9 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
                 fn);
   if ((long long)B * S > 0x7FFFFFFF / 128 || (long long)n_idx_heads * idx_dim > 0x7FFFFFFF / 128)
     return fail(DSA_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  if (n_idx_heads > kMaxIndexHeads)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d index heads", fn, kMaxIndexHeads);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   int st = check_ws(fn, workspace, workspace_bytes,
                     dsa_indexer_prologue_workspace_size(B, S, idx_dim));
   if (st) return st;
@@ -330,7 +374,10 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
 }
 
 size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
-  if (B < 1 || S < 1 || T < 1 || topk < 1) return 0;
+  // (sizes the call itself rejects need no workspace)
+  if (B < 1 || S < 1 || T < 1 || topk < 1 || topk > T || topk > DSA_MAX_TOPK || !rows_ok(B, S) ||
+      !keys_ok(T))
+    return 0;
   return dsa::topk_workspace_bytes(B, S, T, topk);
 }
 
@@ -344,6 +391,8 @@ static int topk_impl(const char* fn, const float* scores, int32_t* indices, int 
     return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
   if (topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  if (!rows_ok(B, S)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   int st = check_ws(fn, workspace, workspace_bytes, dsa::topk_workspace_bytes(B, S, T, topk));
   if (st) return st;
   return hip_status(dsa::launch_topk(scores, indices, B, S, T, topk, workspace, stream, order),
@@ -369,7 +418,8 @@ size_t dsa_sparse_attn_prefill_workspace_size(int B, int S, int T, int H, int qk
 
 size_t dsa_sparse_attn_prefill_pas_workspace_size(int B, int S, int T, int H, int qk_dim,
                                                   int v_dim, int topk, int n_sink, int dtype) {
-  if (B < 1 || S < 1 || T < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || topk < 1 || n_sink < 0)
+  if (!attn_sizes_ok(B, S, H, qk_dim, v_dim, n_sink, dtype) || T < S || !keys_ok(T) ||
+      topk < 1 || topk > T || topk > DSA_MAX_TOPK)
     return 0;
   return prefill_ws(B, S, T, H, qk_dim, v_dim, topk, dtype, n_sink);
 }
@@ -395,13 +445,30 @@ int dsa_sparse_attn_prefill_pas(const void* q, const void* k_cache, const void* 
                       topk, sm_scale, gate_dim, dtype, workspace, workspace_bytes, stream);
 }
 
+int dsa_prefill_work_plan(int B, int S, int T, int past_len, int H, int kv_offset, int window,
+                          int* n_tiles, int* n_items, int* max_blocks, int* item_start, int cap) {
+  const char* fn = "dsa_prefill_work_plan";
+  g_err.clear();
+  if (!n_tiles || !n_items || !max_blocks) return fail(DSA_ERR_INVALID_ARG, "%s: null output", fn);
+  if (B < 1 || S < 1 || T < 1 || H < 1 || past_len < 0 || kv_offset < 0 ||
+      (long long)past_len + S - kv_offset > T || (long long)past_len + S > 0x7FFFFFFF)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!rows_ok(B, S)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (!keys_ok(T) || !keys_ok((long long)past_len + S))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
+  dsa::prefill_work_plan(B, S, T, past_len, H, kv_offset, window, n_tiles, n_items, max_blocks,
+                         item_start, cap);
+  return DSA_OK;
+}
+
 size_t dsa_sparse_attn_decode_workspace_size(int B, int H, int v_dim, int topk) {
   return dsa_sparse_attn_decode_pas_workspace_size(B, H, v_dim, topk, 0);
 }
 
 size_t dsa_sparse_attn_decode_pas_workspace_size(int B, int H, int v_dim, int topk, int n_sink) {
-  if (B < 1 || H < 1 || v_dim < 1 || topk < 1 || n_sink < 0) return 0;
-  return dsa::gather_workspace_bytes(B, H, v_dim, topk + n_sink);
+  if (!attn_sizes_ok(B, 1, H, 16, v_dim, n_sink, DSA_BF16) || topk < 1 || topk > DSA_MAX_TOPK)
+    return 0;
+  return dsa::gather_workspace_bytes(B, H, v_dim, (int64_t)topk + n_sink);
 }
 
 int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -432,7 +499,7 @@ size_t swa_attn_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int w
 
 size_t swa_attn_pas_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
                                    int n_sink, int dtype) {
-  if (B < 1 || S < 1 || H < 1 || qk_dim < 1 || v_dim < 1 || window < 1 || n_sink < 0) return 0;
+  if (!attn_sizes_ok(B, S, H, qk_dim, v_dim, n_sink, dtype) || window < 1) return 0;
   return swa_ws(B, S, H, qk_dim, v_dim, window, dtype, n_sink);
 }
 
@@ -457,7 +524,7 @@ int swa_attn_pas(const void* q, const void* k_buf, const void* v_buf, const void
 
 size_t swa_attn_gqa_workspace_size(int B, int S, int H, int qk_dim, int v_dim, int window,
                                    int dtype) {
-  return swa_ws(B, S, H, qk_dim, v_dim, window, dtype, 0);
+  return swa_attn_pas_workspace_size(B, S, H, qk_dim, v_dim, window, 0, dtype);
 }
 
 int swa_attn_gqa(const void* q, const void* k_buf, const void* v_buf, const void* gate, void* out,

@@ -326,10 +326,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 
 struct Plan {
   int nsplit, per_split;
+  int nsplit_bound;  // splits the workspace is sized for (>= nsplit, monotone in nent)
 };
 
-Plan make_plan(int64_t rows, int H, int nent) {
-  const int64_t hgroups = (H + 31) / 32;
+Plan make_plan(int64_t rows, int H, int64_t nent_in) {
+  // (callers clamp the entry count to the visible positions; the clamp here
+  // only keeps the arithmetic in range)
+  const int nent = (int)std::min<int64_t>(nent_in, 0x3FFFFFFF);
+  const int64_t hgroups = ((int64_t)H + 31) / 32;
   const int64_t base = rows * hgroups;
   // about 512 workgroups: enough to keep HBM busy, while fewer splits mean
   // less partial-state traffic through the merge
@@ -338,17 +342,20 @@ Plan make_plan(int64_t rows, int H, int nent) {
   // decode: 16 entries per split 15.7 us, 8 12.1, 4 11.4)
   const int max_split = std::max(1, (nent + kG - 1) / kG);
   nsplit = std::min(std::min(nsplit, max_split), kMaxSplit);
+  const int bound = nsplit;  // never decreases as nent grows
   int per = (nent + nsplit - 1) / nsplit;
   per = (per + kG - 1) / kG * kG;
   nsplit = (nent + per - 1) / per;
-  return {nsplit, per};
+  return {nsplit, per, bound};
 }
 
 }  // namespace
 
-size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries) {
+size_t gather_workspace_bytes(int64_t rows, int H, int Dv, int64_t nentries) {
+  // sized for the bound, so a call with fewer entries (a window clamped to the
+  // visible positions) never needs more than a query with more entries
   const Plan pl = make_plan(rows, H, nentries);
-  return (size_t)rows * pl.nsplit * H * (size_t)(Dv + 4) * sizeof(float);
+  return (size_t)rows * pl.nsplit_bound * H * (size_t)(Dv + 4) * sizeof(float);
 }
 
 hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,

@@ -543,7 +543,7 @@ struct SplitPlan {
 // calls with more than kMaxSplitTiles query tiles (their grid is large).
 SplitPlan make_split_plan(int B, int S, int T, int P, int H, int kv_offset, int window) {
   SplitPlan pl;
-  pl.nqt = (S + kBQ - 1) / kBQ;
+  pl.nqt = (int)(((int64_t)S + kBQ - 1) / kBQ);
   pl.M = 0x7FFFFFFF;  // no split
   if (window <= 0 && kv_offset == 0 && (int64_t)B * H * pl.nqt < 1024 &&
       pl.nqt <= kMaxSplitTiles) {
@@ -605,8 +605,23 @@ bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv) {
          (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64) || (Dqk == 256 && Dv == 256);
 }
 
+void prefill_work_plan(int B, int S, int T, int P, int H, int kv_offset, int window, int* n_tiles,
+                       int* n_items, int* max_blocks, int* item_start, int cap) {
+  const SplitPlan pl = make_split_plan(B, S, T, P, H, kv_offset, window);
+  *n_tiles = pl.nqt;
+  *n_items = pl.items;
+  *max_blocks = pl.M;
+  if (item_start && cap >= pl.nqt + 1) {
+    if (pl.nqt <= kMaxSplitTiles) {
+      for (int o = 0; o <= pl.nqt; ++o) item_start[o] = pl.tab.start[o];
+    } else {  // never split: one item per tile, longest first
+      for (int o = 0; o <= pl.nqt; ++o) item_start[o] = o;
+    }
+  }
+}
+
 size_t bitmap_bytes(int B, int S, int T) {
-  return (size_t)B * (size_t)S * (size_t)((T + 31) / 32) * sizeof(uint32_t);
+  return (size_t)B * (size_t)S * (size_t)(((int64_t)T + 31) / 32) * sizeof(uint32_t);
 }
 
 size_t prefill_mfma_workspace_bytes(int B, int S, int T, int H, int Dv) {
@@ -622,7 +637,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const void* gate, void* out, int B, int S, int T, int past_len,
                                int kv_offset, int H, int Hkv, int Dqk, int Dv, int topk, int window,
                                float sm_scale, int gate_dim, void* workspace, hipStream_t st) {
-  const int W32 = (T + 31) / 32;
+  const int W32 = (int)(((int64_t)T + 31) / 32);
   uint32_t* bm = (uint32_t*)workspace;
   // partial states follow the (256-byte aligned) bitmap; only DSA calls have them
   float* part = nullptr;

@@ -163,8 +163,8 @@ struct IdxGrid {
 
 inline IdxGrid idx_grid(int S, int T, int P, int tq) {
   IdxGrid g;
-  g.nqt = (S + tq - 1) / tq;
-  g.nkt = (T + kIdxTileK - 1) / kIdxTileK;
+  g.nqt = (int)(((int64_t)S + tq - 1) / tq);
+  g.nkt = (int)(((int64_t)T + kIdxTileK - 1) / kIdxTileK);
   g.npairs = (g.nqt + 1) / 2;
   g.maxlen = 1;
   for (int j = 0; j < g.npairs; ++j) {

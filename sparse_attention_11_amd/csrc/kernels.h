@@ -56,11 +56,16 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                int window, float sm_scale, int gate_dim, void* workspace,
                                hipStream_t stream);
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv);
+// The launch plan of launch_prefill_mfma (host only): query tiles, work items,
+// blocks per item, and the first item of each tile (longest tile first) when
+// cap allows; returns false if the table does not fit (tiles are not split).
+void prefill_work_plan(int B, int S, int T, int P, int H, int kv_offset, int window, int* n_tiles,
+                       int* n_items, int* max_blocks, int* item_start, int cap);
 
 // Split-K row-gather attention + merge (attn_gather.hip); any dtype, any S.
 // window > 0 selects the implicit window list, else `indices` is used; the
 // n_sink sink rows are entries in front of that list. Cache heads as above.
-size_t gather_workspace_bytes(int rows, int H, int Dv, int nentries);
+size_t gather_workspace_bytes(int64_t rows, int H, int Dv, int64_t nentries);
 hipError_t launch_gather(const void* q, const void* k, const void* v, const void* sink_k,
                          const void* sink_v, int n_sink, const int32_t* indices,
                          const void* gate, void* out, int B, int S, int T, int past_len,

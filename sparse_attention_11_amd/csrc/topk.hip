@@ -459,13 +459,15 @@ hipError_t launch_stage(const void* src, int32_t* idx, uint64_t* keys, int64_t b
 constexpr int kCand = 16384;  // candidate keys one register-resident workgroup takes
 
 // number of candidate-reduction passes and their group counts for a row of T scores
+// (k <= 2048 < kCand, so every pass shrinks the candidate count)
 int stage_groups(int T, int k, int* groups, int max_levels) {
-  const int nseg = (T + kSegLen - 1) / kSegLen;
-  int C = nseg * k, lv = 0;
-  groups[lv++] = nseg;
+  const int64_t nseg = ((int64_t)T + kSegLen - 1) / kSegLen;
+  int64_t C = nseg * k;
+  int lv = 0;
+  groups[lv++] = (int)nseg;
   while (C > kCand && lv < max_levels) {
-    const int g = (C + kCand - 1) / kCand;
-    groups[lv++] = g;
+    const int64_t g = (C + kCand - 1) / kCand;
+    groups[lv++] = (int)g;
     C = g * k;
   }
   return lv;

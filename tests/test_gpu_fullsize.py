@@ -35,6 +35,36 @@ def sample_rows(S, k, n=12, seed=0):
     return sorted(base | set(extra))
 
 
+def strat_rows(S, k, block, seed):
+    """One seeded row in every block of `block` consecutive query rows (so every
+    query tile of that size, and every pair of tiles the indexer schedules
+    together, holds a sampled row), plus s = 0, k - 1, k and S - 1."""
+    rng = np.random.default_rng(seed)
+    rows = {min(b * block + int(rng.integers(0, block)), S - 1) for b in range((S + block - 1) // block)}
+    return sorted(rows | {0, min(k - 1, S - 1), min(k, S - 1), S - 1})
+
+
+def host_stream(wl, shape, tid, scale, start=0):
+    """A whole bf16 stream (e.g. a K or V cache) generated once on the host."""
+    return datagen.normal_host(shape, "bf16", wl.seed, tid, scale, start)
+
+
+def check_attn_rows_full(wl, out, idx, rows, kh, vh, b=0, qtid=datagen.TID_Q,
+                         gtid=datagen.TID_GATE, S_stream=None, P=0):
+    """Compare out[s] (s in rows, query row b*S_stream + s at position P + s)
+    against the oracle over the whole host caches kh / vh [B, T, H, D] with the
+    row's own index list."""
+    S_stream = wl.S if S_stream is None else S_stream
+    H, Dqk, Dv = wl.H, wl.Dqk, wl.v
+    for s in rows:
+        r = b * S_stream + s
+        q = host_row(wl, qtid, wl.scale_q, r, H * Dqk).reshape(1, 1, H, Dqk)
+        g = host_row(wl, gtid, wl.scale_gate, r, H).reshape(1, 1, H)
+        ir = np.ascontiguousarray(idx[s].reshape(1, 1, -1))
+        ref = oracle.sparse_attn(q, kh[b:b + 1], vh[b:b + 1], ir, g, P + s, wl.nope, wl.rope)[0, 0]
+        assert_rows_close(out[s].reshape(H, Dv), ref, 2e-2, what=f"{wl.name} attn row {s}")
+
+
 def dev_normal(shape, wl, tid, scale, start=0):
     t = torch.empty(*shape, dtype=torch.bfloat16, device=DEV)
     return datagen.normal_device(t, wl.seed, tid, scale, start)
@@ -80,7 +110,7 @@ def test_dsa_s32k_indexer_sampled_rows():
     w = dev_normal((1, S, wl.HI), wl, datagen.TID_W, wl.scale_w)
     sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
     dsa.dsa_index_scores(q_idx, k_idx, w, sc, 0)
-    rows = sample_rows(S, wl.topk, n=10, seed=1)
+    rows = strat_rows(S, wl.topk, 128, seed=1)  # every 128-query tile
     got = sc[0, rows].cpu().numpy()
     del sc, q_idx, w
     _free()
@@ -108,7 +138,7 @@ def test_dsa_s32k_fp8_indexer_sampled_rows():
     dsa.dsa_index_quant_fp8(k_idx, kc, ks)
     sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
     dsa.dsa_index_scores_fp8(qc, qs, kc, ks, w, sc, 0)
-    rows = sample_rows(S, wl.topk, n=10, seed=2)
+    rows = strat_rows(S, wl.topk, 512, seed=2)
     got = sc[0, rows].cpu().numpy()
     got_qc, got_qs = qc[0, rows].cpu().numpy(), qs[0, rows].cpu().numpy()
     got_kc, got_ks = kc.cpu().numpy(), ks.cpu().numpy()
@@ -150,7 +180,7 @@ def _topk_full(wl, S, T, P, k, mode, rows, seed_off=0, order=0):
 @pytest.mark.parametrize("mode,order", [(0, 0), (2, 0), (0, 1)])
 def test_dsa_s32k_topk_full_tensor(mode, order):
     wl = WORKLOADS["dsa-s32k"]
-    _topk_full(wl, wl.S, wl.T, 0, wl.topk, mode, sample_rows(wl.S, wl.topk, n=12, seed=2),
+    _topk_full(wl, wl.S, wl.T, 0, wl.topk, mode, strat_rows(wl.S, wl.topk, 128, seed=2),
                order=order)
 
 
@@ -165,12 +195,14 @@ def test_dsa_s32k_prefill_sampled_rows():
     datagen.indices_device(idx.view(S, wl.topk), 0, S, 0, seed=wl.seed)
     out = torch.empty(1, S, H, wl.v, dtype=torch.bfloat16, device=DEV)
     dsa.dsa_sparse_attn_prefill(q, k, v, idx, g, out, 0, wl.nope, wl.rope)
-    rows = sample_rows(S, wl.topk, n=8, seed=3)
+    rows = strat_rows(S, wl.topk, 128, seed=3)  # one row in every 128-query tile
     got = from_dev(out[0, rows])
     idx_h = datagen.indices_host(0, S, S, 0, wl.topk, seed=wl.seed)
     del q, k, v, g, idx, out
     _free()
-    check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, T)
+    kh = host_stream(wl, (1, T, H, wl.Dqk), datagen.TID_K, wl.scale_k)
+    vh = host_stream(wl, (1, T, H, wl.v), datagen.TID_V, wl.scale_v)
+    check_attn_rows_full(wl, dict(zip(rows, got)), idx_h, rows, kh, vh)
 
 
 # ------------------------------------------------- mla-s4k with sinks
@@ -245,26 +277,37 @@ def test_decode_b8_full_layer():
 
 
 # --------------------------------------------------------- hybrid-512k
-def test_hybrid_512k_chunk_and_decode():
+def _hybrid_rows(wl):
+    return strat_rows(wl.S, wl.topk, 16, seed=7)  # one row in every 16-query indexer tile
+
+
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_hybrid_512k_indexer_sampled_rows(part):
+    """Chunk scores (4096 queries after 524 288 cached keys: the key-stationary
+    schedule that pairs query tiles) on a quarter of the 256+ sampled rows per
+    part (the oracle's 2.2 G multiply-adds per row are the cost), and the
+    decode token's row in part 0."""
     wl = WORKLOADS["hybrid-512k"]
-    S, P, T, H = wl.S, wl.past_len, wl.T, wl.H
+    S, P, T = wl.S, wl.past_len, wl.T
     Ta = T + 1
-    # indexer over the chunk and for the decode token (row S of the query streams)
+    rows = _hybrid_rows(wl)[part::4]
     k_idx = dev_normal((1, Ta, wl.DI), wl, datagen.TID_KIDX, wl.scale_kidx)
     q_idx = dev_normal((1, S + 1, wl.HI, wl.DI), wl, datagen.TID_QIDX, wl.scale_qidx)
     w = dev_normal((1, S + 1, wl.HI), wl, datagen.TID_W, wl.scale_w)
     sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
     dsa.dsa_index_scores(q_idx[:, :S], k_idx[:, :T].contiguous(), w[:, :S], sc, P)
-    rows = [0, 1, S // 2, S - 1]
     got = sc[0, rows].cpu().numpy()
     del sc
-    scd = torch.empty(1, 1, Ta, dtype=torch.float32, device=DEV)
-    dsa.dsa_index_scores(q_idx[:, S:].contiguous(), k_idx, w[:, S:].contiguous(), scd, T)
-    got_d = scd[0, 0].cpu().numpy()
-    del scd, q_idx, k_idx, w
+    got_d = None
+    if part == 0:
+        scd = torch.empty(1, 1, Ta, dtype=torch.float32, device=DEV)
+        dsa.dsa_index_scores(q_idx[:, S:].contiguous(), k_idx, w[:, S:].contiguous(), scd, T)
+        got_d = scd[0, 0].cpu().numpy()
+        del scd
+    del q_idx, k_idx, w
     _free()
-    kh = datagen.normal_host((1, Ta, wl.DI), "bf16", wl.seed, datagen.TID_KIDX, wl.scale_kidx)
-    for i, s in enumerate(rows + [S]):
+    kh = host_stream(wl, (1, Ta, wl.DI), datagen.TID_KIDX, wl.scale_kidx)
+    for i, s in enumerate(rows + ([S] if part == 0 else [])):
         qh = host_row(wl, datagen.TID_QIDX, wl.scale_qidx, s, wl.HI * wl.DI).reshape(1, 1, wl.HI, wl.DI)
         wh = host_row(wl, datagen.TID_W, wl.scale_w, s, wl.HI).reshape(1, 1, wl.HI)
         if s < S:
@@ -273,15 +316,28 @@ def test_hybrid_512k_chunk_and_decode():
         else:
             ref = oracle.index_scores(qh, kh, wh, T)[0, 0]
             assert_rows_close(got_d, ref, 2e-2, what="hybrid decode scores")
-    del kh
 
-    # top-k on synthetic chunk-shaped and decode-shaped score rows
-    _topk_full(wl, S, T, P, wl.topk, 1, [0, 7, S - 1], seed_off=50)
-    _topk_full(wl, 1, Ta, T, wl.topk, 2, [0], seed_off=51)
-    _topk_full(wl, S, T, P, wl.topk, 1, [3, S - 2], seed_off=50, order=1)
-    _topk_full(wl, 1, Ta, T, wl.topk, 2, [0], seed_off=51, order=1)
 
-    # DSA attention: chunk (MFMA path) and decode (gather path)
+def test_hybrid_512k_topk():
+    """Top-k on synthetic chunk-shaped (4096 rows of up to 528 384 keys) and
+    decode-shaped (one row of 528 385 keys) score tensors, sorted and unsorted."""
+    wl = WORKLOADS["hybrid-512k"]
+    S, P, T = wl.S, wl.past_len, wl.T
+    rows = _hybrid_rows(wl)
+    _topk_full(wl, S, T, P, wl.topk, 1, rows, seed_off=50)
+    _topk_full(wl, 1, T + 1, T, wl.topk, 2, [0], seed_off=51)
+    _topk_full(wl, S, T, P, wl.topk, 1, rows[1::4], seed_off=50, order=1)
+    _topk_full(wl, 1, T + 1, T, wl.topk, 2, [0], seed_off=51, order=1)
+
+
+def test_hybrid_512k_chunk_and_decode_attention():
+    """DSA attention of the 4096-token chunk (the bench's launch configuration)
+    on 256+ sampled rows (every 16-query tile) and of the decode token, against
+    the oracle over the whole 528 385-row caches."""
+    wl = WORKLOADS["hybrid-512k"]
+    S, P, T, H = wl.S, wl.past_len, wl.T, wl.H
+    Ta = T + 1
+    rows = _hybrid_rows(wl)
     k = dev_normal((1, Ta, H, wl.Dqk), wl, datagen.TID_K, wl.scale_k)
     v = dev_normal((1, Ta, H, wl.v), wl, datagen.TID_V, wl.scale_v)
     q = dev_normal((1, S + 1, H, wl.Dqk), wl, datagen.TID_Q, wl.scale_q)
@@ -299,13 +355,19 @@ def test_hybrid_512k_chunk_and_decode():
     del k, v, q, g, idx, out, od
     _free()
     idx_h = datagen.indices_host(0, S + 1, S + 1, P, wl.topk, seed=wl.seed)
-    check_attn_rows(wl, dict(zip(rows, got)), idx_h, rows, 0, Ta, S_stream=0)
-    check_attn_rows(wl, {S: got_d}, idx_h, [S], 0, Ta, S_stream=0)
+    kh = host_stream(wl, (1, Ta, H, wl.Dqk), datagen.TID_K, wl.scale_k)
+    vh = host_stream(wl, (1, Ta, H, wl.v), datagen.TID_V, wl.scale_v)
+    check_attn_rows_full(wl, dict(zip(rows, got)), idx_h, rows, kh, vh, S_stream=0, P=P)
+    check_attn_rows_full(wl, {S: got_d}, idx_h, [S], kh, vh, S_stream=0, P=P)
 
 
 def test_hybrid_512k_swa_layers():
+    """Both SWA layers: the chunk through the MFMA path on 256+ sampled rows
+    and the decode token through the gather path, against the oracle on the
+    window buffers."""
     wl = WORKLOADS["hybrid-512k"]
     S, P, H, W = wl.S, wl.past_len, wl.H, wl.window
+    rows = _hybrid_rows(wl)
     for j in (1, 2):
         tid = lambda base: base + datagen.SWA_TID_STRIDE * j
         off = P - W + 1
@@ -322,19 +384,18 @@ def test_hybrid_512k_swa_layers():
         dsa.swa_attn(q[:, S:].contiguous(), kb[:, offd - off:].contiguous(),
                      vb[:, offd - off:].contiguous(), g[:, S:].contiguous(), od, P + S, offd, W,
                      wl.nope, wl.rope)
-        rows = [0, 1, 511, 2047, S - 1]
         got = from_dev(out[0, rows])
         got_d = from_dev(od[0, 0])
         del kb, vb, q, g, out, od
         _free()
+        kh = host_stream(wl, (1, Tb + 1, H, wl.Dqk), tid(datagen.TID_K), wl.scale_k, off * H * wl.Dqk)
+        vh = host_stream(wl, (1, Tb + 1, H, wl.v), tid(datagen.TID_V), wl.scale_v, off * H * wl.v)
         for s, o in list(zip(rows, got)) + [(S, got_d)]:
             p = P + s
-            pos = list(range(p - W + 1, p + 1))
-            kc = compact_cache(wl, pos, 0, 0, H, wl.Dqk, tid(datagen.TID_K), wl.scale_k)
-            vc = compact_cache(wl, pos, 0, 0, H, wl.v, tid(datagen.TID_V), wl.scale_v)
             qh = host_row(wl, tid(datagen.TID_Q), wl.scale_q, s, H * wl.Dqk).reshape(1, 1, H, wl.Dqk)
             gh = host_row(wl, tid(datagen.TID_GATE), wl.scale_gate, s, H).reshape(1, 1, H)
-            ref = oracle.swa_attn(qh, kc, vc, gh, p, p - W + 1, W, wl.nope, wl.rope)[0, 0]
+            nb = p + 1 - off  # the buffer rows up to this query's position
+            ref = oracle.swa_attn(qh, kh[:, :nb], vh[:, :nb], gh, p, off, W, wl.nope, wl.rope)[0, 0]
             assert_rows_close(o.reshape(H, wl.v), ref, 2e-2, what=f"swa layer {j} row {s}")
 
 

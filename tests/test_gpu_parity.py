@@ -188,6 +188,30 @@ def test_topk_constant_and_all_masked_tail(T, k, order):
     assert got[1, 5:].tolist() == [-1] * (k - 5)
 
 
+# Run-to-run determinism: both top-k calls must return the same array twice,
+# order and -1 slots included (the unsorted call's order is its compaction
+# order, which depends only on the scores). Shapes: single-stage rows
+# (T <= 16384), two-segment rows and one 528 385-key row (two reduction passes).
+@pytest.mark.parametrize("R,T,k,mode", [(64, 12000, 2048, 1), (48, 30000, 2048, 2),
+                                        (1, 528385, 2048, 1), (1, 528385, 2048, 0)])
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_deterministic_run_to_run(R, T, k, mode, order):
+    P = T - R
+    sc = torch.empty(R, T, dtype=torch.float32, device=DEV)
+    datagen.scores_device(sc, 0, R, P, seed=T + R, mode=mode)
+    fn = dsa.dsa_topk_unsorted if order else dsa.dsa_topk
+    a = torch.full((1, R, k), -7, dtype=torch.int32, device=DEV)
+    b = torch.full((1, R, k), -9, dtype=torch.int32, device=DEV)
+    fn(sc.view(1, R, T), a)
+    fn(sc.view(1, R, T), b)
+    _sync()
+    np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+    # and the selection is the oracle's
+    ref = oracle.topk(datagen.scores_host(0, R, R, T, P, seed=T + R, mode=mode), k)
+    got = a.cpu().numpy()[0]
+    np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
+
+
 # ----------------------------------------------------- sparse attention
 def _attn_dev(hi):
     return {k_: to_dev(v_) for k_, v_ in hi.items()}
