@@ -347,6 +347,28 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
 int dsa_prefill_work_plan(int B, int S, int T, int past_len, int H, int kv_offset, int window,
                           int* n_tiles, int* n_items, int* max_blocks, int* item_start, int cap);
 
+/*
+ * dsa_sparse_attn_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, layouts, results and status
+ * codes are those of dsa_sparse_attn_decode minus the workspace; the split
+ * partial states live in a static device buffer of DSA_STATIC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends (its
+ * address is looked up once per device; no call allocates or frees memory).
+ * A call whose partial states need more than that buffer (see
+ * dsa_sparse_attn_decode_workspace_size) returns DSA_ERR_UNSUPPORTED. Every
+ * call on one GPU uses the same buffer: calls that may overlap on one GPU
+ * (different streams, or host threads) race and must be ordered by the
+ * caller. Each call writes all the scratch it reads, so nothing carries over
+ * from the previous call.
+ */
+#define DSA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int dsa_sparse_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* indices, const void* gate, void* out, int B,
+                                   int T, int H, int qk_nope_dim, int qk_rope_dim, int v_dim,
+                                   int topk, float sm_scale, int gate_dim, int dtype,
+                                   hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */

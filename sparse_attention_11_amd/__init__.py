@@ -37,7 +37,7 @@ _EXPORTS = [
     "swa_attn_gqa_workspace_size", "swa_attn_gqa",
     "dsa_index_quant_fp8", "dsa_index_scores_fp8",
     "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
-    "dsa_prefill_work_plan",
+    "dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc",
 ]
 MAX_SINKS = 256
 
@@ -103,7 +103,8 @@ def lib():
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, i32, i32, vp, sz, vp]
         L.dsa_prefill_work_plan.argtypes = [i32] * 7 + [vp] * 4 + [i32]
-        for fn in ("dsa_prefill_work_plan", "dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
+        L.dsa_sparse_attn_decode_noalloc.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, vp]
+        for fn in ("dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc", "dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
                    "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
                    "dsa_index_quant_fp8", "dsa_index_scores_fp8", "dsa_indexer_prologue"):
@@ -260,6 +261,25 @@ def dsa_sparse_attn_decode(q, k_cache, v_cache, indices, gate, out, qk_nope_dim:
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate), _ptr(out), B, T, H,
         qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale, _gate_dim(gate, Dv), _dtype(q),
         _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def dsa_sparse_attn_decode_noalloc(q, k_cache, v_cache, indices, gate, out, qk_nope_dim: int,
+                                   qk_rope_dim: int, sm_scale: float | None = None, stream=None):
+    """dsa_sparse_attn_decode with its partial states in the library's static
+    device scratch: no workspace, no allocation."""
+    B, _, H, Dqk = q.shape
+    T, Dv = k_cache.shape[1], v_cache.shape[3]
+    topk = indices.shape[-1]
+    if sm_scale is None:
+        sm_scale = Dqk ** -0.5
+    _check("dsa_sparse_attn_decode_noalloc", lib().dsa_sparse_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(indices), _ptr(gate), _ptr(out), B, T, H,
+        qk_nope_dim, qk_rope_dim, Dv, topk, sm_scale, _gate_dim(gate, Dv), _dtype(q),
+        _stream(stream)))
     return out
 
 

@@ -10,6 +10,9 @@
 #include "dsa.h"
 #include "kernels.h"
 
+static_assert(DSA_STATIC_SCRATCH_BYTES == dsa::kStaticScratchBytes,
+              "the header's scratch size is the library's");
+
 namespace {
 
 thread_local std::string g_err;
@@ -479,6 +482,36 @@ int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cac
   return decode_impl("dsa_sparse_attn_decode", q, k_cache, v_cache, nullptr, nullptr, 0, indices,
                      gate, out, B, T, H, qk_nope_dim, qk_rope_dim, v_dim, topk, sm_scale,
                      gate_dim, dtype, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* indices, const void* gate, void* out, int B,
+                                   int T, int H, int qk_nope_dim, int qk_rope_dim, int v_dim,
+                                   int topk, float sm_scale, int gate_dim, int dtype,
+                                   hipStream_t stream) {
+  const char* fn = "dsa_sparse_attn_decode_noalloc";
+  g_err.clear();
+  int st = check_attn(fn, q, k_cache, v_cache, gate, out, B, 1, T, H, qk_nope_dim, qk_rope_dim,
+                      v_dim, sm_scale, gate_dim, dtype);
+  if (st) return st;
+  if (!indices) return fail(DSA_ERR_INVALID_ARG, "%s: indices is NULL", fn);
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  const size_t need = dsa::gather_workspace_bytes(B, H, v_dim, topk);
+  if (need > DSA_STATIC_SCRATCH_BYTES)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "%s: this call's partial states need %zu bytes; the static scratch holds %zu "
+                "(use dsa_sparse_attn_decode with a workspace)",
+                fn, need, (size_t)DSA_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  hipError_t e = dsa::static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(dsa::launch_gather(q, k_cache, v_cache, nullptr, nullptr, 0, indices, gate, out,
+                                       B, 1, T, T - 1, 0, H, H, qk_nope_dim + qk_rope_dim, v_dim,
+                                       topk, 0, sm_scale, gate_dim, dtype, ws, stream),
+                    fn);
 }
 
 int dsa_sparse_attn_decode_pas(const void* q, const void* k_cache, const void* v_cache,

@@ -73,4 +73,10 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
                          float sm_scale, int gate_dim, int dtype, void* workspace,
                          hipStream_t stream);
 
+// Static device scratch (scratch.hip) for dsa_sparse_attn_decode_noalloc:
+// kStaticScratchBytes per GPU, held from module load to process exit. Returns
+// the current device's address of it (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr);
+
 }  // namespace dsa

@@ -230,3 +230,18 @@ def test_swa_gqa_workspace_sizes():
                  (2, 5, 4, 48, 32, 16, 0)]:
         assert L.swa_attn_gqa_workspace_size(*args) == L.swa_attn_workspace_size(*args)
     assert L.swa_attn_gqa_workspace_size(1, 4096, 8, 256, 256, 512, 1) == 0
+
+
+def test_noalloc_decode_rejects_calls_beyond_the_static_scratch():
+    # 300 sequences x 128 heads x (256 + 4) floats of partial state > 32 MiB:
+    # rejected on the host before any HIP call
+    L = dsa.lib()
+    need = dsa.dsa_sparse_attn_decode_workspace_size(300, 128, 256, 2048)
+    assert need > dsa.STATIC_SCRATCH_BYTES
+    st = L.dsa_sparse_attn_decode_noalloc(P, P, P, P, P, P, 300, 4096, 128, 128, 64, 256, 2048,
+                                          0.07, 1, 1, None)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+    assert "static scratch" in dsa.dsa_last_error()
+    # invalid arguments are still INVALID_ARG
+    assert L.dsa_sparse_attn_decode_noalloc(None, P, P, P, P, P, 1, 4096, 8, 128, 64, 128, 64,
+                                            0.07, 1, 1, None) == dsa.DSA_ERR_INVALID_ARG
