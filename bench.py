@@ -14,7 +14,10 @@ dsa_topk_unsorted: the same selection as dsa_topk without the final sort by
 score, since the attention calls take the selection as a set.
 
 Prints ONE JSON line. `value` is prefill tokens/s of the named workload
-(default mla-s4k, the DeepSeek-V2-shaped 4096-token prefill); the other
+(default dsa-s32k: a 32768-token causal prefill with 128 heads, indexer 64 x
+128, top-k 2048) over whole timed steps; `decode_us_per_step` is the decode
+step of the decode workload (default decode-b8: 8 sequences x 131072 cached
+tokens), and `decode` holds its roofline and CPU baseline. The other
 workloads are measured in the same run and reported under "also".
 """
 from __future__ import annotations
@@ -42,8 +45,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mla-s4k")
-    ap.add_argument("--also", default="dsa-s32k,decode-b8,hybrid-512k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8,prologue-s32k",
+    ap.add_argument("--workload", default="dsa-s32k",
+                    help="the prefill workload whose tokens/s is `value`")
+    ap.add_argument("--decode-workload", default="decode-b8",
+                    help="decode workload whose us/step goes in the same line ('' for none)")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--also", default="hybrid-512k,mla-s4k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8,prologue-s32k",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -429,50 +436,120 @@ def counted_traffic(wl_name):
 
 
 # ------------------------------------------------------------ CPU baseline
-def cpu_baseline(wl, budget_s):
-    """The fp64 oracle (as it stands) on a bounded sample of query rows of the
-    same workload, timed on this host's cores: indexer -> top-k -> attention
-    for blocks of consecutive query rows spread over the sequence."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _bitrev_order(n):
+    bits = max(1, int(math.log2(n)))
+    return [int(format(i, f"0{bits}b")[::-1], 2) for i in range(n)]
+
+
+def cpu_prefill_baseline(wl, budget_s, threads=0, nblk=64, block=8):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload's
+    query rows, on this host's cores: indexer -> top-k -> sparse attention +
+    gate for blocks of `block` consecutive query rows, the blocks taken from an
+    `nblk`-block grid over the sequence in bit-reversed order (any prefix mixes
+    short and long causal contexts). Every input is generated before the timed
+    region; blocks run until the time budget is spent."""
     import datagen
     import oracle
 
     oracle.build(force=False)
-    B, S, P = wl.B, wl.S, wl.past_len
-    T = wl.T
+    S, P, T = wl.S, wl.past_len, wl.T
     dt = wl.dtype_name
     g = lambda shape, tid, sc, start=0: datagen.normal_host(shape, dt, wl.seed, tid, sc, start)
     k_idx = g((1, T, wl.DI), datagen.TID_KIDX, wl.scale_kidx)
     kc = g((1, T, wl.H, wl.Dqk), datagen.TID_K, wl.scale_k)
     vc = g((1, T, wl.H, wl.v), datagen.TID_V, wl.scale_v)
-    # blocks of 8 consecutive query rows; visited in bit-reversed order of a
-    # 256-block grid over the sequence so that any prefix of the visit order
-    # samples early and late rows (short and long causal contexts) alike.
-    # Passes over the grid repeat until the time budget is spent.
-    block, nblk = 8, 256
-    grid = np.linspace(0, max(S - block, 0), nblk).astype(int)
-    order = [int(format(i, "08b")[::-1], 2) for i in range(nblk)]
-    rows, nb_done = 0, 0
-    t0 = time.perf_counter()
-    for oi in order * 64:
-        s0 = int(grid[oi])
+    whole = S <= nblk * block // 2  # short prefills: the whole layer per pass, repeated
+    if whole:
+        starts = [0]
+        block = S
+    else:
+        grid = np.linspace(0, S - block, nblk).astype(int)
+        starts = [int(grid[o]) for o in _bitrev_order(nblk)]
+    inp = []
+    for s0 in starts:
         n = min(block, S - s0)
-        q_idx = g((1, n, wl.HI, wl.DI), datagen.TID_QIDX, wl.scale_qidx, s0 * wl.HI * wl.DI)
-        w = g((1, n, wl.HI), datagen.TID_W, wl.scale_w, s0 * wl.HI)
-        q = g((1, n, wl.H, wl.Dqk), datagen.TID_Q, wl.scale_q, s0 * wl.H * wl.Dqk)
-        gate = g((1, n, wl.H), datagen.TID_GATE, wl.scale_gate, s0 * wl.H)
-        Tn = P + s0 + n
-        sc = oracle.index_scores(q_idx, k_idx[:, :Tn], w, P + s0)
-        idx = oracle.topk(sc.astype(np.float32), wl.topk)
-        oracle.sparse_attn(q, kc[:, :Tn], vc[:, :Tn], idx, gate, P + s0, wl.nope, wl.rope)
-        rows += n
-        nb_done += 1
-        if time.perf_counter() - t0 > budget_s or S <= block:
+        inp.append((s0, n,
+                    g((1, n, wl.HI, wl.DI), datagen.TID_QIDX, wl.scale_qidx, s0 * wl.HI * wl.DI),
+                    g((1, n, wl.HI), datagen.TID_W, wl.scale_w, s0 * wl.HI),
+                    g((1, n, wl.H, wl.Dqk), datagen.TID_Q, wl.scale_q, s0 * wl.H * wl.Dqk),
+                    g((1, n, wl.H), datagen.TID_GATE, wl.scale_gate, s0 * wl.H)))
+    full = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    used = oracle.num_threads()
+    rows, done = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for s0, n, q_idx, w, q, gate in inp:
+            Tn = P + s0 + n
+            sc = oracle.index_scores(q_idx, k_idx[:, :Tn], w, P + s0)
+            idx = oracle.topk(sc.astype(np.float32), wl.topk)
+            oracle.sparse_attn(q, kc[:, :Tn], vc[:, :Tn], idx, gate, P + s0, wl.nope, wl.rope)
+            rows += n
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if not whole or time.perf_counter() - t0 > min(budget_s, 2.0):
             break
     el = time.perf_counter() - t0
-    return {"value": rows / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows} query rows of {wl.name} ({nb_done} blocks of {block} consecutive "
-                      f"rows spread over the {S}-token prefill, B=1): indexer + top-k + sparse "
-                      f"attention + gate in fp64, {el:.1f} s"}
+    oracle.set_num_threads(full)
+    what = (f"the whole {S}-token prefill, {done} passes" if whole else
+            f"{done} blocks of {block} consecutive rows spread over the {S}-token prefill")
+    return {"value": rows / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{rows} query rows of {wl.name} ({what}, B=1): indexer + top-k + sparse "
+                      f"attention + gate in fp64, {el:.1f} s; inputs generated before timing"}
+
+
+def cpu_decode_baseline(wl, reps=3):
+    """The oracle's decode step for one of the B sequences (indexer over its
+    T cached keys -> top-k -> sparse attention + gate), times B: the B
+    sequences are independent and alike, and their expanded caches (tens of
+    GB) need not be generated on the host. Attention runs on the sequence's
+    selected cache rows (the rows of its top-k, generated before timing;
+    attention depends only on the selected set, so this is the same result)."""
+    import datagen
+    import oracle
+
+    oracle.build(force=False)
+    T, P, k = wl.T, wl.past_len, wl.topk
+    dt = wl.dtype_name
+    b = 0
+    g = lambda shape, tid, sc, start=0: datagen.normal_host(shape, dt, wl.seed, tid, sc, start)
+    k_idx = g((1, T, wl.DI), datagen.TID_KIDX, wl.scale_kidx, b * T * wl.DI)
+    q_idx = g((1, 1, wl.HI, wl.DI), datagen.TID_QIDX, wl.scale_qidx, b * wl.HI * wl.DI)
+    w = g((1, 1, wl.HI), datagen.TID_W, wl.scale_w, b * wl.HI)
+    q = g((1, 1, wl.H, wl.Dqk), datagen.TID_Q, wl.scale_q, b * wl.H * wl.Dqk)
+    gate = g((1, 1, wl.H), datagen.TID_GATE, wl.scale_gate, b * wl.H)
+    idx = oracle.topk(oracle.index_scores(q_idx, k_idx, w, P).astype(np.float32), k)[0, 0]
+    sel = [int(t) for t in idx if t >= 0]
+    row = lambda tid, sc, t, D: g((wl.H * D,), tid, sc, (b * T + t) * wl.H * D)
+    kc = np.stack([row(datagen.TID_K, wl.scale_k, t, wl.Dqk) for t in sel]).reshape(1, len(sel), wl.H, wl.Dqk)
+    vc = np.stack([row(datagen.TID_V, wl.scale_v, t, wl.v) for t in sel]).reshape(1, len(sel), wl.H, wl.v)
+    ci = np.arange(len(sel), dtype=np.int32).reshape(1, 1, -1)
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        sc = oracle.index_scores(q_idx, k_idx, w, P)
+        got = oracle.topk(sc.astype(np.float32), k)
+        oracle.sparse_attn(q, kc, vc, ci, gate, len(sel) - 1, wl.nope, wl.rope)
+        ts.append(time.perf_counter() - t0)
+        assert np.array_equal(got[0, 0], idx)
+    one = float(np.median(ts))
+    return {"value": one * wl.B * 1e6, "unit": "us/step", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"sequence 0 of {wl.B} ({T} cached keys, top-{k}): indexer + top-k + sparse "
+                      f"attention + gate in fp64, median of {reps} runs {one * 1e3:.1f} ms, times "
+                      f"{wl.B} sequences; its selected cache rows generated before timing"}
 
 
 def main():
@@ -496,23 +573,51 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    log = lambda msg: print(f"# {msg}", file=sys.stderr, flush=True)
+
+    # ---- prefill headline
     wl = WORKLOADS[args.workload]
     layer = make_layer(wl, torch, dsa, datagen)
     per_stage, total_ms, wall = time_layer(layer, args.steps, args.warmup, torch)
     main_r = summarize(wl, per_stage, total_ms)
     del layer
     torch.cuda.empty_cache()
+    log(f"{wl.name}: {total_ms:.3f} ms/step")
+
+    # ---- decode in the same line
+    dec = None
+    if args.decode_workload:
+        dwl = WORKLOADS[args.decode_workload]
+        dlay = make_layer(dwl, torch, dsa, datagen)
+        dps, dtm, _ = time_layer(dlay, args.decode_steps, args.warmup, torch)
+        dec_r = summarize(dwl, dps, dtm)
+        del dlay
+        torch.cuda.empty_cache()
+        log(f"{dwl.name}: {dtm * 1e3:.1f} us/step")
+        dw = work(dwl)
+        t4 = dps["K4 sparse_attn_decode"]["mean_us"] * 1e-6
+        ach = dw["attn"]["bytes_gather"] / t4 / 1e9
+        droof = {"kernel": "K4 sparse_attn_decode (split-K row gather + merge)", "bound": "hbm",
+                 "achieved": ach, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                 "frac": ach * 1e9 / PEAK_HBM, "traffic": None,
+                 "algorithmic_bytes_per_launch": dw["attn"]["bytes_gather"],
+                 "mean_launch_us": t4 * 1e6}
+        droof["traffic"], droof["traffic_source"] = counted_traffic(dwl.name)
+        dec = {"workload": dwl.name, "us_per_step": dtm * 1e3, "steps": args.decode_steps,
+               "config": {"B": dwl.B, "T": dwl.T, "heads": dwl.H, "qk": dwl.Dqk, "v": dwl.v,
+                          "index_heads": dwl.HI, "index_dim": dwl.DI, "topk": dwl.topk},
+               "stages": dec_r, "roofline": droof, "cpu_baseline": None}
 
     also = {}
     for name in [s for s in args.also.split(",") if s]:
-        if name == wl.name:
+        if name in (wl.name, args.decode_workload):
             continue
         lay = make_layer(WORKLOADS[name], torch, dsa, datagen)
         ps, tm, _ = time_layer(lay, args.also_steps, 2, torch)
         also[name] = summarize(WORKLOADS[name], ps, tm)
         del lay
         torch.cuda.empty_cache()
-        print(f"# {name}: {tm:.3f} ms/step", file=sys.stderr, flush=True)
+        log(f"{name}: {tm:.3f} ms/step")
 
     w = work(wl)
     t3 = (per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6
@@ -534,11 +639,12 @@ def main():
                 "algorithmic_flops_per_launch": w["K5"]["flops"], "mean_launch_us": t5 * 1e6}
     elif t3 is not None:
         ach = w["attn"]["flops"] / t3 / 1e12
-        roof = {"kernel": "K3 sparse_attn_prefill (bitmap + MFMA flash)", "bound": "mfma",
-                "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+        roof = {"kernel": "K3 sparse_attn_prefill (selection bitmap + dense-masked MFMA flash)",
+                "bound": "mfma", "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
                 "algorithmic_flops_per_launch": w["attn"]["flops"],
                 "issued_dense_flops_per_launch": w["attn"]["dense_flops"],
+                "issued_frac": w["attn"]["dense_flops"] / t3 / PEAK_BF16,
                 "mean_launch_us": t3 * 1e6}
     else:
         t4 = per_stage["K4 sparse_attn_decode"]["mean_us"] * 1e-6
@@ -547,9 +653,19 @@ def main():
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM,
                 "traffic": None, "mean_launch_us": t4 * 1e6}
     roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
+
+    # ---- the oracle on this host's cores (after every GPU measurement)
     cpu = None
     if not args.no_cpu and not wl.swa_only and not wl.prologue_only:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log("cpu baseline (oracle)")
+        cpu = cpu_prefill_baseline(wl, args.cpu_seconds)
+        cpu["cpu_model"] = cpu_model()
+        cpu["one_thread"] = {
+            name: cpu_prefill_baseline(WORKLOADS[name], args.cpu_seconds / 3, threads=1)
+            for name in ("tiny-fp32", "mla-s4k")}
+        if dec is not None:
+            dec["cpu_baseline"] = cpu_decode_baseline(WORKLOADS[args.decode_workload])
+            dec["cpu_baseline"]["cpu_model"] = cpu["cpu_model"]
     line = {
         "metric": METRIC,
         "value": main_r.get("step_tokens_per_s", main_r.get("prefill_tokens_per_s",
@@ -563,10 +679,11 @@ def main():
                    "heads": wl.H, "qk_nope": wl.nope, "qk_rope": wl.rope, "v": wl.v,
                    "index_heads": wl.HI, "index_dim": wl.DI, "topk": wl.topk,
                    "parallelism": "single GPU"},
-        "decode_us_per_step": main_r.get("decode_us_per_step"),
+        "decode_us_per_step": dec["us_per_step"] if dec else main_r.get("decode_us_per_step"),
         "stages": main_r,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "decode": dec,
         "also": also,
     }
     print(json.dumps(line))

@@ -81,6 +81,8 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             dbl, i32, vp]
         lib.oracle_index_scores.restype = None
@@ -118,6 +120,11 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _dtype_of(*arrs) -> int:

@@ -119,6 +119,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops that follow (the CPU-baseline timing's
+ * one-thread figure); results do not depend on it. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Lightning-indexer scores [A.X-K2 page, SGA: the score formula and the
  * causal mask]:

@@ -92,9 +92,24 @@ int check_ws(const char* fn, void* ws, size_t have, size_t need) {
 
 // (the gather path lists the n_sink sinks as extra entries; the MFMA path
 // runs them as extra key blocks and needs no more workspace)
+// Path of a DSA prefill call. The dense-masked MFMA tiles cost in proportion
+// to the keys each query can see (about T - S/2 when the caches end with the
+// chunk); the row gather costs in proportion to the topk rows each query
+// selects, at about 1 flop per byte. Measured on one MI355X (4096-query
+// chunks, 32 heads, dims 192/128, topk 2048): 131072 cached keys 12.8 ms
+// dense vs 23.7 ms gather, 262144 keys 25.8 vs 24.1 ms, 524288 keys 52.0 vs
+// 25.8 ms; the ratio does not depend on the head count or dims. So the gather
+// takes calls whose visible keys per query exceed 128 x topk. The rule reads
+// only (S, T, topk) so that the size query and the call always agree.
+constexpr double kGatherKeysPerSelected = 128.0;
+bool prefill_uses_mfma(int dtype, int S, int T, int qk_dim, int v_dim, int topk) {
+  if (!dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim)) return false;
+  return (double)T - 0.5 * S < kGatherKeysPerSelected * topk;
+}
+
 size_t prefill_ws(int B, int S, int T, int H, int qk_dim, int v_dim, int topk, int dtype,
                   int n_sink) {
-  if (dsa::prefill_mfma_supported(dtype, S, qk_dim, v_dim))
+  if (prefill_uses_mfma(dtype, S, T, qk_dim, v_dim, topk))
     return dsa::prefill_mfma_workspace_bytes(B, S, T, H, v_dim);
   return dsa::gather_workspace_bytes((int64_t)B * S, H, v_dim, (int64_t)topk + n_sink);
 }
@@ -139,7 +154,7 @@ int prefill_impl(const char* fn, const void* q, const void* k_cache, const void*
   if (topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
   const int dqk = qk_nope_dim + qk_rope_dim;
-  const bool mfma = dsa::prefill_mfma_supported(dtype, S, dqk, v_dim);
+  const bool mfma = prefill_uses_mfma(dtype, S, T, dqk, v_dim, topk);
   if (mfma && B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
   if (!mfma && (long long)B * S > 0x7FFFFFFF / 64)
     return fail(DSA_ERR_UNSUPPORTED, "%s: B*S too large for the gather path", fn);

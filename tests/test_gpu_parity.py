@@ -269,6 +269,10 @@ PREFILL_CASES = [
     (1, 1, 40, 3, 64, 64, 128, 41), (1, 300, 1800, 1, 128, 64, 128, 2048),
     # head dims 256 / 256 (one workgroup per CU, long tiles split and merged)
     (1, 150, 100, 2, 128, 128, 256, 64),
+    # bf16 chunks whose visible keys per query exceed 128 x topk take the row
+    # gather: more than 32 heads (two head groups), ragged heads, small topk
+    (1, 64, 20000, 2, 128, 64, 128, 64), (2, 40, 9000, 3, 64, 64, 128, 32),
+    (1, 20, 12000, 40, 64, 32, 64, 48), (1, 17, 70000, 1, 128, 64, 128, 500),
 ]
 
 
@@ -438,6 +442,8 @@ PAS_PREFILL_CASES = [
     (1, 200, 50, 3, 128, 64, 128, 64, 128), (2, 130, 100, 2, 64, 64, 128, 200, 1),
     (1, 77, 300, 4, 32, 32, 64, 33, 100), (1, 300, 1800, 1, 128, 64, 128, 2048, 256),
     (2, 8, 500, 5, 128, 64, 128, 128, 65), (1, 40, 30, 3, 32, 16, 32, 20, 7),
+    # the row-gather path of long bf16 chunks, with sinks
+    (1, 50, 20000, 2, 128, 64, 128, 100, 7),
 ]
 
 
