@@ -38,6 +38,12 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                 a and then by -a restores the input, the angle-sum identity),
                 the direction by a quarter turn and the textbook
                 x cos + rotate_half(x) sin form.
+  mla_prologue  pinned: torch's linear compositions (q_gate_proj on the
+                concatenation, kv_a_proj, kv_b_proj of the latent) without
+                RoPE, the interleaved RoPE as complex multiplication (a
+                quarter turn maps (x_2j, x_2j+1) to (-x_2j+1, x_2j)), equal to
+                the half-split rotation on de-interleaved dims, relative-
+                position invariance of q.k, the rope key shared by all heads.
 Parity unpinned by the pages (fixed by convention, tested in every mode):
 ReLU placement (per head by default), the two scale constants, and the
 inclusive window boundary.
@@ -81,6 +87,8 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_mla_prologue.argtypes = [vp] * 8 + [i32] * 12 + [vp] * 4
+        lib.oracle_mla_prologue.restype = None
         lib.oracle_set_num_threads.argtypes = [i32]
         lib.oracle_set_num_threads.restype = None
         lib.oracle_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -331,3 +339,34 @@ def indexer_prologue(q_lora, hidden, wq_b, wk, k_norm_w, k_norm_b, weights_proj,
         _dtype_of(q_lora, hidden, wq_b, wk, k_norm_w, k_norm_b, weights_proj), B, S, past_len,
         Q, Hd, HI, D, R, float(eps), _ptr(oq), _ptr(ok), _ptr(ow))
     return oq, ok, ow
+
+
+def mla_prologue(q_resid, q_comp, hidden, wq_gate, wkv_a, wkv_b, rope_cos, rope_sin,
+                 past_len: int, H: int, nope: int, rope: int, v_dim: int):
+    """The main attention's projections (q_gate_proj split, kv_a_proj_with_mqa,
+    expand_kv, interleaved RoPE). q_resid [B,S,Qr], q_comp [B,S,Qc], hidden
+    [B,S,Hd], wq_gate [H*(nope+rope+v), Qr+Qc], wkv_a [L+rope, Hd], wkv_b
+    [H*(nope+v), L], rope tables [T, rope/2] fp32 or None (rope 0) ->
+    (q [B,S,H,nope+rope], gate [B,S,H,v], k_rows [B,S,H,nope+rope],
+    v_rows [B,S,H,v]) float64."""
+    q_resid, q_comp, hidden = _c(q_resid), _c(q_comp), _c(hidden)
+    wq_gate, wkv_a, wkv_b = _c(wq_gate), _c(wkv_a), _c(wkv_b)
+    B, S, Qr = q_resid.shape
+    Qc, Hd = q_comp.shape[2], hidden.shape[2]
+    Dqk = nope + rope
+    L = wkv_a.shape[0] - rope
+    assert wq_gate.shape == (H * (Dqk + v_dim), Qr + Qc)
+    assert wkv_a.shape == (L + rope, Hd) and wkv_b.shape == (H * (nope + v_dim), L)
+    if rope > 0:
+        rope_cos = _c(np.asarray(rope_cos, np.float32))
+        rope_sin = _c(np.asarray(rope_sin, np.float32))
+        assert rope_cos.shape[1] == rope // 2 and rope_cos.shape[0] >= past_len + S
+    else:
+        rope_cos = rope_sin = None
+    outs = (np.empty((B, S, H, Dqk)), np.empty((B, S, H, v_dim)), np.empty((B, S, H, Dqk)),
+            np.empty((B, S, H, v_dim)))
+    _load().oracle_mla_prologue(_ptr(q_resid), _ptr(q_comp), _ptr(hidden), _ptr(wq_gate),
+                                _ptr(wkv_a), _ptr(wkv_b), _ptr(rope_cos), _ptr(rope_sin),
+                                _dtype_of(q_resid, q_comp, hidden, wq_gate, wkv_a, wkv_b), B, S,
+                                past_len, Qr, Qc, Hd, L, H, nope, rope, v_dim, *[_ptr(o) for o in outs])
+    return outs

@@ -38,6 +38,14 @@
  *                           state (wk) through a LayerNorm, per-head weights
  *                           (weights_proj), half-split RoPE on q and k
  *                           [A.X-K2 page, SGA bullets and "two RoPE layouts"]
+ *   oracle_mla_prologue  -- the main attention's projections: q_gate_proj on
+ *                           [q_resid, q_compressed] split per head into the
+ *                           query and the output gate, kv_a_proj_with_mqa to
+ *                           the latent and the shared rope key, expand_kv
+ *                           (kv_b_proj) of the latent into per-head k_nope and
+ *                           v, interleaved RoPE on the rope slices
+ *                           [A.X-K2 page, "MLA + explicit sparse mask" steps
+ *                           1-3, "Attention output gate", "two RoPE layouts"]
  *   oracle_swa_attn_gqa  -- sliding-window attention whose K/V buffers hold
  *                           fewer heads than q (grouped KV heads)
  *                           [Spark-X2.5 page, "why the gate": 8 query heads,
@@ -75,6 +83,16 @@
  *    and of the key: pair (j, j + rope_dim/2) of that slice rotates by the
  *    caller's (cos, sin) of position p and frequency j. The pages' bf16
  *    modules round each projection to bf16; the oracle keeps fp64 throughout.
+ *  - MLA prologue: q_gate_proj reads the concatenation [q_resid, q_compressed]
+ *    and its output for head h is the query (Dqk values, nope slice then rope
+ *    slice) followed by the gate (Dv values); kv_a_proj_with_mqa's output is
+ *    the latent (kv_lora_rank values) followed by the rope key (qk_rope
+ *    values, one for all heads); expand_kv is kv_b_proj applied to the latent
+ *    (no normalisation between: the page names none), whose output for head
+ *    h is k_nope (qk_nope values) followed by v (Dv values). The interleaved
+ *    RoPE rotates the pair (x_2j, x_2j+1) of a rope slice in place by the
+ *    caller's (cos, sin) of position p and frequency j. The expanded key of
+ *    head h is [k_nope_h | rotated rope key].
  *  - FP8 indexer (the page names the steps, not their details): the rotation
  *    is the Sylvester-ordered Walsh-Hadamard matrix with entries +-1 (no
  *    normalisation; scores divide by D instead), computed by the fast
@@ -362,6 +380,90 @@ void oracle_indexer_prologue(const void *q_lora, const void *hidden,
                rd(weights_proj, dtype, (int64_t)o * Hd + i);
       out_w[bs * HI + o] = acc;
     }
+  }
+}
+
+/*
+ * The main attention's projections for S tokens at positions past_len + s
+ * [A.X-K2 page, "MLA + explicit sparse mask" steps 1-3: q_gate_proj produces
+ * the query and the attention output gate together, kv_a_proj_with_mqa
+ * compresses K/V to the kv_lora_rank latent plus the shared RoPE key, and
+ * expand_kv expands the latent into full per-head keys and values (the cache
+ * holds these expanded rows); "Attention output gate": the fused projection
+ * reads [q_resid, q_compressed] and its output splits into a qk_head_dim
+ * query and a v_head_dim gate; "two RoPE layouts": the main attention uses
+ * the interleaved layout].
+ *   q_resid [B,S,Qr], q_comp [B,S,Qc], hidden [B,S,Hd]        (dtype)
+ *   wq_gate [H*(N+R+Dv), Qr+Qc], wkv_a [L+R, Hd], wkv_b [H*(N+Dv), L]
+ *   rope_cos / rope_sin [T, R/2] fp32 (unused when R = 0)
+ *   out_q [B,S,H,N+R], out_gate [B,S,H,Dv], out_k [B,S,H,N+R], out_v [B,S,H,Dv]
+ *   (double; out_k / out_v are the cache rows of the S new tokens)
+ */
+static void rope_interleaved(double *x, int R, const float *cs, const float *sn) {
+  for (int j = 0; j < R / 2; ++j) {
+    double a = x[2 * j], b = x[2 * j + 1], c = cs[j], s = sn[j];
+    x[2 * j] = a * c - b * s;
+    x[2 * j + 1] = b * c + a * s;
+  }
+}
+
+void oracle_mla_prologue(const void *q_resid, const void *q_comp, const void *hidden,
+                         const void *wq_gate, const void *wkv_a, const void *wkv_b,
+                         const float *rope_cos, const float *rope_sin, int dtype, int B,
+                         int S, int past_len, int Qr, int Qc, int Hd, int L, int H, int N,
+                         int R, int Dv, double *out_q, double *out_gate, double *out_k,
+                         double *out_v) {
+  int64_t n = (int64_t)B * S;
+  int Dqk = N + R, Wq = Dqk + Dv, Wkv = N + Dv, Qin = Qr + Qc;
+  int half = R / 2;
+#pragma omp parallel
+  {
+    double *lat = (double *)malloc(sizeof(double) * (size_t)(L + R + 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bs = 0; bs < n; ++bs) {
+      int64_t p = past_len + bs % S;
+      const float *cs = R > 0 ? rope_cos + p * half : NULL;
+      const float *sn = R > 0 ? rope_sin + p * half : NULL;
+      /* q_gate_proj on [q_resid, q_compressed]; head h: query then gate */
+      for (int h = 0; h < H; ++h) {
+        for (int c = 0; c < Wq; ++c) {
+          int64_t o = (int64_t)h * Wq + c;
+          double acc = 0.0;
+          for (int i = 0; i < Qin; ++i) {
+            double a = i < Qr ? rd(q_resid, dtype, bs * Qr + i)
+                              : rd(q_comp, dtype, bs * Qc + (i - Qr));
+            acc += a * rd(wq_gate, dtype, o * Qin + i);
+          }
+          if (c < Dqk)
+            out_q[(bs * H + h) * Dqk + c] = acc;
+          else
+            out_gate[(bs * H + h) * Dv + (c - Dqk)] = acc;
+        }
+        if (R > 0) rope_interleaved(out_q + (bs * H + h) * Dqk + N, R, cs, sn);
+      }
+      /* kv_a_proj_with_mqa: latent, then the shared rope key */
+      for (int c = 0; c < L + R; ++c) {
+        double acc = 0.0;
+        for (int i = 0; i < Hd; ++i)
+          acc += rd(hidden, dtype, bs * Hd + i) * rd(wkv_a, dtype, (int64_t)c * Hd + i);
+        lat[c] = acc;
+      }
+      if (R > 0) rope_interleaved(lat + L, R, cs, sn);
+      /* expand_kv: kv_b_proj of the latent; head h: k_nope then v */
+      for (int h = 0; h < H; ++h) {
+        for (int c = 0; c < Wkv; ++c) {
+          double acc = 0.0;
+          for (int i = 0; i < L; ++i)
+            acc += lat[i] * rd(wkv_b, dtype, ((int64_t)h * Wkv + c) * L + i);
+          if (c < N)
+            out_k[(bs * H + h) * Dqk + c] = acc;
+          else
+            out_v[(bs * H + h) * Dv + (c - N)] = acc;
+        }
+        for (int r = 0; r < R; ++r) out_k[(bs * H + h) * Dqk + N + r] = lat[L + r];
+      }
+    }
+    free(lat);
   }
 }
 

@@ -812,3 +812,114 @@ def test_fp8_codes_against_exact_rotation_differ_only_at_midpoints():
     # the midpoint between the two codes' values lies within the bound of the exact value
     mid = (table[gi] + table[ri]) / 2.0
     assert np.all(np.abs(mid - ys[diff]) <= bs[diff])
+
+
+# ------------------------------------------------------- MLA prologue
+def _mla_inputs(B, S, Qr, Qc, Hd, L, H, N, R, Dv, seed):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    d = dict(q_resid=f(B, S, Qr), q_comp=f(B, S, Qc), hidden=f(B, S, Hd),
+             wq_gate=f(H * (N + R + Dv), Qr + Qc) / np.sqrt(Qr + Qc),
+             wkv_a=f(L + R, Hd) / np.sqrt(Hd), wkv_b=f(H * (N + Dv), L) / np.sqrt(L))
+    return {n: a.astype(np.float32) for n, a in d.items()}
+
+
+def _mla(x, cos, sin, P, H, N, R, Dv):
+    return oracle.mla_prologue(x["q_resid"], x["q_comp"], x["hidden"], x["wq_gate"], x["wkv_a"],
+                               x["wkv_b"], cos, sin, P, H, N, R, Dv)
+
+
+def test_mla_prologue_without_rope_matches_torch_linear():
+    # A.X-K2 page, "MLA + explicit sparse mask" steps 1-3 and "Attention output
+    # gate": q_gate_proj on the concatenation [q_resid, q_compressed], split per
+    # head into the query and the gate; kv_a_proj_with_mqa to the latent; expand_kv
+    # = kv_b_proj of the latent, split per head into k_nope and v
+    B, S, Qr, Qc, Hd, L, H, N, Dv = 2, 3, 32, 16, 40, 24, 3, 16, 8
+    x = _mla_inputs(B, S, Qr, Qc, Hd, L, H, N, 0, Dv, 1)
+    q, g, k, v = _mla(x, None, None, 0, H, N, 0, Dv)
+    t = {n: torch.from_numpy(a.astype(np.float64)) for n, a in x.items()}
+    F = torch.nn.functional
+    qg = F.linear(torch.cat([t["q_resid"], t["q_comp"]], -1), t["wq_gate"]).reshape(B, S, H, N + Dv)
+    lat = F.linear(t["hidden"], t["wkv_a"])
+    kv = F.linear(lat, t["wkv_b"]).reshape(B, S, H, N + Dv)
+    np.testing.assert_allclose(q, qg[..., :N].numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g, qg[..., N:].numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(k, kv[..., :N].numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(v, kv[..., N:].numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_mla_prologue_interleaved_rope_closed_forms():
+    # "two RoPE layouts": the main attention rotates the interleaved pairs
+    # (x_2j, x_2j+1). As complex numbers x_2j + i x_2j+1 the rotation is a
+    # multiplication by e^(i theta_j); a quarter turn maps (x_2j, x_2j+1) to
+    # (-x_2j+1, x_2j). The rope key (after kv_a_proj) is one slice shared by all
+    # heads; the nope dims, the gate and v do not move.
+    B, S, Qr, Qc, Hd, L, H, N, R, Dv, P = 1, 4, 32, 32, 48, 32, 3, 16, 8, 16, 3
+    x = _mla_inputs(B, S, Qr, Qc, Hd, L, H, N, R, Dv, 2)
+    T, h = P + S, R // 2
+    q0, g0, k0, v0 = _mla(x, np.ones((T, h), np.float32), np.zeros((T, h), np.float32), P, H, N, R, Dv)
+    q1, g1, k1, v1 = _mla(x, np.zeros((T, h), np.float32), np.ones((T, h), np.float32), P, H, N, R, Dv)
+    for a1, a0 in ((q1, q0), (k1, k0)):
+        np.testing.assert_array_equal(a1[..., :N], a0[..., :N])
+        np.testing.assert_array_equal(a1[..., N::2], -a0[..., N + 1::2])
+        np.testing.assert_array_equal(a1[..., N + 1::2], a0[..., N::2])
+    np.testing.assert_array_equal(g1, g0)
+    np.testing.assert_array_equal(v1, v0)
+    # the rope key is the same in every head
+    for hh in range(1, H):
+        np.testing.assert_array_equal(k1[:, :, hh, N:], k1[:, :, 0, N:])
+    rng = np.random.default_rng(7)
+    ang = rng.uniform(-np.pi, np.pi, (T, h))
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    q2, _, k2, _ = _mla(x, c, s, P, H, N, R, Dv)
+    rot = (c + 1j * s).astype(np.complex128)[P:]  # rows of the S tokens
+    for a2, a0 in ((q2, q0), (k2, k0)):
+        z0 = a0[..., N::2] + 1j * a0[..., N + 1::2]
+        z2 = z0 * rot[None, :, None, :]
+        np.testing.assert_allclose(a2[..., N::2], z2.real, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(a2[..., N + 1::2], z2.imag, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_interleaved_rope_is_half_split_on_deinterleaved_dims():
+    # the interleaved rotation equals the indexer's half-split rotation applied to
+    # the dims reordered (even dims first, then odd) and reordered back
+    R, S, P = 16, 3, 2
+    h = R // 2
+    rng = np.random.default_rng(8)
+    xr = rng.standard_normal((1, S, R)).astype(np.float32)
+    ang = rng.uniform(-np.pi, np.pi, (P + S, h))
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    # MLA: the rope key with wkv_a = identity on the hidden state (L = 0 is not
+    # allowed, so a 16-wide latent of zeros sits in front)
+    L, H, N, Dv = 16, 1, 16, 16
+    hid = np.concatenate([np.zeros((1, S, L), np.float32), xr], -1)
+    x = dict(q_resid=np.zeros((1, S, 32), np.float32), q_comp=np.zeros((1, S, 32), np.float32),
+             hidden=hid, wq_gate=np.zeros((H * (N + R + Dv), 64), np.float32),
+             wkv_a=np.eye(L + R, dtype=np.float32), wkv_b=np.zeros((H * (N + Dv), L), np.float32))
+    _, _, k, _ = _mla(x, c, s, P, H, N, R, Dv)
+    inter = k[0, :, 0, N:]
+    # indexer prologue with wq_b = identity: q_idx = half-split RoPE of q_lora
+    perm = np.concatenate([np.arange(0, R, 2), np.arange(1, R, 2)])
+    ones = lambda *sh: np.ones(sh, np.float32)
+    qi, _, _ = oracle.indexer_prologue(xr[..., perm], ones(1, S, 32), np.eye(R, dtype=np.float32),
+                                       ones(R, 32), ones(R), np.zeros(R, np.float32), ones(1, 32),
+                                       c, s, P, 1)
+    back = np.empty_like(qi[0, :, 0])
+    back[:, perm] = qi[0, :, 0]
+    np.testing.assert_allclose(inter, back, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_rope_dot_products_depend_on_relative_position():
+    # with angles p * w_j, the rope part of q(s) . k(s') depends only on the
+    # distance of the two positions: moving every token by the same offset keeps
+    # every such product (q and k rotate the same way)
+    B, S, Qr, Qc, Hd, L, H, N, R, Dv = 1, 5, 32, 32, 32, 16, 2, 16, 16, 16
+    x = _mla_inputs(B, S, Qr, Qc, Hd, L, H, N, R, Dv, 9)
+    w = 10000.0 ** (-np.arange(R // 2) * 2.0 / R)
+    out = []
+    for P in (0, 37):
+        ang = np.arange(P + S)[:, None] * w[None, :]
+        q, _, k, _ = _mla(x, np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32), P,
+                          H, N, R, Dv)
+        out.append(np.einsum("shd,thd->hst", q[0, ..., N:], k[0, ..., N:]))
+    np.testing.assert_allclose(out[0], out[1], rtol=1e-5, atol=1e-5)  # fp32 tables
