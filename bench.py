@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--decode-workload", default="decode-b8",
                     help="decode workload whose us/step goes in the same line ('' for none)")
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--also", default="hybrid-512k,mla-s4k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8,prologue-s32k",
+    ap.add_argument("--also", default="hybrid-512k,mla-s4k,mla-s4k-pas,hybrid-512k-pas,spark-swa,dsa-s32k-fp8,prologue-s32k,mla-prologue-s32k",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--also-steps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -286,7 +286,43 @@ class PrologueLayer:
             self.sin, self.q_idx, self.k_cache, self.w, self.wl.past_len, workspace=self.ws))]
 
 
+class MlaPrologueLayer:
+    """The main attention's projections for S tokens (one stage)."""
+
+    def __init__(self, wl, torch, dsa, datagen):
+        self.wl, self.dsa = wl, dsa
+        dev = torch.device("cuda")
+        B, S, P, H = wl.B, wl.S, wl.past_len, wl.H
+        Qr, Qc, Hd, L, N, R, Dv = wl.q_lora, wl.q_comp, wl.hidden, wl.kv_lora, wl.nope, wl.rope, wl.v
+        E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=dev)
+        gen = lambda t, tid, sc: datagen.normal_device(t, wl.seed, tid, sc)
+        self.qr, self.qc, self.hd = gen(E(B, S, Qr), 40, 1.0), gen(E(B, S, Qc), 41, 1.0), gen(E(B, S, Hd), 42, 1.0)
+        self.wq = gen(E(H * (N + R + Dv), Qr + Qc), 43, (Qr + Qc) ** -0.5)
+        self.wa = gen(E(L + R, Hd), 44, Hd ** -0.5)
+        self.wb = gen(E(H * (N + Dv), L), 45, L ** -0.5)
+        pos = torch.arange(P + S, device=dev, dtype=torch.float64)[:, None]
+        freq = 10000.0 ** (-2.0 * torch.arange(R // 2, device=dev, dtype=torch.float64) / R)
+        self.cos, self.sin = torch.cos(pos * freq).float(), torch.sin(pos * freq).float()
+        self.q, self.g = E(B, S, H, N + R), E(B, S, H, Dv)
+        self.kc, self.vc = E(B, P + S, H, N + R), E(B, P + S, H, Dv)
+        self.ws = torch.empty(dsa.dsa_mla_prologue_workspace_size(B, S, L), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def stages(self):
+        return [("K0m mla_prologue", lambda: self.dsa.dsa_mla_prologue(
+            self.qr, self.qc, self.hd, self.wq, self.wa, self.wb, self.cos, self.sin, self.q,
+            self.g, self.kc, self.vc, self.wl.past_len, workspace=self.ws))]
+
+
+def mla_prologue_flops(wl):
+    M, H, N, R, Dv = wl.B * wl.S, wl.H, wl.nope, wl.rope, wl.v
+    return 2.0 * M * ((wl.q_lora + wl.q_comp) * H * (N + R + Dv) + wl.hidden * (wl.kv_lora + R)
+                      + wl.kv_lora * H * (N + Dv))
+
+
 def make_layer(wl, torch, dsa, datagen):
+    if wl.mla_prologue_only:
+        return MlaPrologueLayer(wl, torch, dsa, datagen)
     if wl.prologue_only:
         return PrologueLayer(wl, torch, dsa, datagen)
     return (SwaLayer if wl.swa_only else Layer)(wl, torch, dsa, datagen)
@@ -374,6 +410,13 @@ def summarize(wl, per_stage, total_ms):
     g = lambda name: per_stage[name]["mean_us"] * 1e-6
     r = {"workload": wl.name, "ms_per_step": total_ms,
          "stages_us": {k: round(v["mean_us"], 2) for k, v in per_stage.items()}}
+    if wl.mla_prologue_only:  # the main attention's projections: three GEMMs, fused epilogues
+        t0 = g("K0m mla_prologue")
+        fl = mla_prologue_flops(wl)
+        r["prefill_tokens_per_s"] = wl.B * wl.S / t0
+        r["K0m_mfma_frac"] = fl / t0 / PEAK_BF16
+        r["K0m_tflops"] = fl / t0 / 1e12
+        return r
     if wl.prologue_only:  # the indexer's projections: three GEMMs + LayerNorm / RoPE
         t0 = g("K0 indexer_prologue")
         M = wl.B * wl.S

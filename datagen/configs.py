@@ -29,6 +29,14 @@ N(0, scale^2) stream keyed by (seed, tensor id). Seed = workload number - 1.
                 hidden state, RoPE on 64 dims) for 32768 tokens; inputs N(0,1),
                 weights N(0,1) / sqrt(fan-in), LayerNorm weight N(0,1) and
                 bias N(0,1) / 10, RoPE angles p * 10000^(-2j/64).
+  mla-prologue-s32k
+                the main attention's projections for the dsa-s32k tokens and
+                heads: q_gate_proj on [q_resid 1536, q_compressed 1536] to 128
+                heads of (query 192, gate 128), kv_a_proj_with_mqa from a
+                7168-wide hidden state to a 512-wide latent and the 64-dim
+                rope key, expand_kv to (k_nope 128, v 128) per head,
+                interleaved RoPE with angles p * 10000^(-2j/64); inputs
+                N(0,1), weights N(0,1) / sqrt(fan-in), tensor ids 40-45.
   spark-swa     one sliding-window layer with grouped KV heads (Spark-X2.5
                 page: 8 query heads over 2 KV heads, head_dim 256, window 512,
                 one gate logit per head): a 4096-token chunk after 131072
@@ -74,6 +82,9 @@ class Workload:
     q_lora: int = 0            # query LoRA rank (prologue input width)
     hidden: int = 0            # hidden size (prologue input width)
     rope_idx: int = 0          # rotary dims of each index head and key
+    mla_prologue_only: bool = False  # the main attention's projections alone
+    q_comp: int = 0            # q_compressed width (the second q_gate_proj input)
+    kv_lora: int = 0           # kv_lora_rank (the latent of kv_a_proj_with_mqa)
     scale_q: float = 1.0
     scale_k: float = 1.0
     scale_v: float = 1.0
@@ -128,9 +139,17 @@ WORKLOADS["dsa-s32k-fp8"] = dataclasses.replace(WORKLOADS["dsa-s32k"], name="dsa
 WORKLOADS["prologue-s32k"] = Workload("prologue-s32k", BF16, B=1, S=32768, past_len=0, H=0, nope=0,
                                       rope=0, v=0, HI=64, DI=128, topk=0, seed=6,
                                       prologue_only=True, q_lora=1536, hidden=7168, rope_idx=64)
+# The main attention's projections for the dsa-s32k tokens and heads:
+# q_gate_proj on [q_resid (1536), q_compressed (1536)], kv_a_proj_with_mqa from
+# a 7168-wide hidden state to a 512-wide latent plus the 64-dim rope key,
+# expand_kv to 128 heads of (nope 128, v 128); interleaved RoPE on 64 dims.
+WORKLOADS["mla-prologue-s32k"] = Workload("mla-prologue-s32k", BF16, B=1, S=32768, past_len=0, H=128,
+                                          nope=128, rope=64, v=128, HI=0, DI=0, topk=0, seed=7,
+                                          mla_prologue_only=True, q_lora=1536, q_comp=1536,
+                                          hidden=7168, kv_lora=512)
 WORKLOADS["spark-swa"] = Workload("spark-swa", BF16, B=1, S=4096, past_len=131072, H=8, nope=128,
                                   rope=128, v=256, HI=0, DI=0, topk=0, seed=5, n_swa=1,
                                   decode_after=True, H_kv=2, swa_only=True)
 
 ORDER = ["tiny-fp32", "mla-s4k", "dsa-s32k", "decode-b8", "hybrid-512k", "mla-s4k-pas",
-         "hybrid-512k-pas", "spark-swa", "dsa-s32k-fp8", "prologue-s32k"]
+         "hybrid-512k-pas", "spark-swa", "dsa-s32k-fp8", "prologue-s32k", "mla-prologue-s32k"]

@@ -330,6 +330,51 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The main attention's projections, in front of the sparse attention calls
+ * ([AXK2] "MLA + explicit sparse mask" steps 1-3: q_gate_proj produces the
+ * query and the attention output gate together, kv_a_proj_with_mqa
+ * compresses K/V to the kv_lora_rank latent plus one RoPE key shared by all
+ * heads, expand_kv expands the latent into the full per-head K/V that the
+ * caches hold; "Attention output gate": the fused projection reads
+ * [q_resid, q_compressed] and splits its output into a qk_head_dim query and
+ * a v_head_dim gate; "two RoPE layouts": the main attention's rotary layout
+ * is interleaved). For the S tokens of a call (positions past_len + s), with
+ * Dqk = qk_nope_dim + qk_rope_dim (N + R):
+ *   [qry_h | gate_h]      = ([q_resid, q_compressed] . wq_gate^T)[h*(Dqk+Dv) ...]
+ *   [latent | rope key]   = hidden . wkv_a^T
+ *   [k_nope_h | v_h]      = (latent . wkv_b^T)[h*(N+Dv) ...]
+ *   q[b,s,h,:]                    = [qry_h[:N] | RoPE_p(qry_h[N:])]
+ *   gate[b,s,h,:]                 = gate_h        (use gate_dim = v_dim)
+ *   k_cache[b,past_len+s,h,:]     = [k_nope_h | RoPE_p(rope key)]
+ *   v_cache[b,past_len+s,h,:]     = v_h
+ * RoPE_p rotates each interleaved pair (x_2j, x_2j+1) of a rope slice to
+ * (x_2j c - x_2j+1 s, x_2j+1 c + x_2j s), c = rope_cos[p * R/2 + j],
+ * s = rope_sin[p * R/2 + j] (fp32 tables [T, R/2], the caller's schedule).
+ * Weights use the nn.Linear layout [out, in]: wq_gate [H*(Dqk+v_dim),
+ * q_resid_dim + q_comp_dim], wkv_a [kv_lora_rank + R, hidden_dim], wkv_b
+ * [H*(N+v_dim), kv_lora_rank]. q_resid [B,S,q_resid_dim], q_compressed
+ * [B,S,q_comp_dim], hidden [B,S,hidden_dim]; q [B,S,H,Dqk], gate
+ * [B,S,H,v_dim], k_cache [B,T,H,Dqk], v_cache [B,T,H,v_dim] (rows past_len ..
+ * past_len + S - 1 are written, no other). All bf16 (DSA_F32 is
+ * DSA_ERR_UNSUPPORTED); each projection is accumulated in fp32 and rounded
+ * once to bf16, after its RoPE where it has one. No normalisation sits between
+ * kv_a_proj_with_mqa and expand_kv (none is named on the page).
+ * Supported: q_resid_dim, q_comp_dim, hidden_dim, kv_lora_rank multiples of
+ * 32; N, R, v_dim multiples of 16 with N + R and v_dim at most
+ * DSA_MAX_HEAD_DIM (R = 0: no RoPE, the tables may be NULL).
+ * workspace: at least dsa_mla_prologue_workspace_size(B, S, kv_lora_rank)
+ * bytes (the latent).
+ */
+size_t dsa_mla_prologue_workspace_size(int B, int S, int kv_lora_rank);
+int dsa_mla_prologue(const void* q_resid, const void* q_compressed, const void* hidden,
+                     const void* wq_gate, const void* wkv_a, const void* wkv_b,
+                     const float* rope_cos, const float* rope_sin, void* q, void* gate,
+                     void* k_cache, void* v_cache, int B, int S, int T, int past_len,
+                     int q_resid_dim, int q_comp_dim, int hidden_dim, int kv_lora_rank, int H,
+                     int qk_nope_dim, int qk_rope_dim, int v_dim, int dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The work plan the MFMA prefill path (bf16, S >= 16) launches for a call
  * with these sizes, for inspection; host arithmetic only, no GPU call. A
  * query tile is 128 consecutive queries; tile qt sees the 64-key blocks of

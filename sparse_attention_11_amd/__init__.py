@@ -38,6 +38,7 @@ _EXPORTS = [
     "dsa_index_quant_fp8", "dsa_index_scores_fp8",
     "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
     "dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc",
+    "dsa_mla_prologue_workspace_size", "dsa_mla_prologue",
 ]
 MAX_SINKS = 256
 
@@ -103,8 +104,11 @@ def lib():
         L.swa_attn_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, i32, i32, vp, sz, vp]
         L.dsa_prefill_work_plan.argtypes = [i32] * 7 + [vp] * 4 + [i32]
+        L.dsa_mla_prologue_workspace_size.argtypes = [i32] * 3
+        L.dsa_mla_prologue_workspace_size.restype = sz
+        L.dsa_mla_prologue.argtypes = [vp] * 12 + [i32] * 13 + [vp, sz, vp]
         L.dsa_sparse_attn_decode_noalloc.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, vp]
-        for fn in ("dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc", "dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
+        for fn in ("dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc", "dsa_mla_prologue", "dsa_index_scores", "dsa_topk", "dsa_topk_unsorted", "dsa_sparse_attn_prefill",
                    "dsa_sparse_attn_decode", "swa_attn", "dsa_sparse_attn_prefill_pas",
                    "dsa_sparse_attn_decode_pas", "swa_attn_pas", "swa_attn_gqa",
                    "dsa_index_quant_fp8", "dsa_index_scores_fp8", "dsa_indexer_prologue"):
@@ -469,3 +473,30 @@ def dsa_status_string(status: int) -> str:
 
 def dsa_last_error() -> str:
     return lib().dsa_last_error().decode()
+
+
+def dsa_mla_prologue_workspace_size(B: int, S: int, kv_lora_rank: int) -> int:
+    return int(lib().dsa_mla_prologue_workspace_size(B, S, kv_lora_rank))
+
+
+def dsa_mla_prologue(q_resid, q_compressed, hidden, wq_gate, wkv_a, wkv_b, rope_cos, rope_sin,
+                     q, gate, k_cache, v_cache, past_len: int, workspace=None, stream=None):
+    """The main attention's projections (q_gate_proj split, kv_a_proj_with_mqa,
+    expand_kv, interleaved RoPE); sizes are read from the tensors:
+    q [B,S,H,Dqk], gate [B,S,H,Dv], rope tables [T, R/2] (None: R = 0)."""
+    B, S, Qr = q_resid.shape
+    Qc, Hd = q_compressed.shape[2], hidden.shape[2]
+    H, Dqk = q.shape[2], q.shape[3]
+    Dv = gate.shape[3]
+    R = 0 if rope_cos is None else 2 * rope_cos.shape[1]
+    L = wkv_a.shape[0] - R
+    T = k_cache.shape[1]
+    if workspace is None:
+        workspace = _workspace(dsa_mla_prologue_workspace_size(B, S, L), q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_mla_prologue", lib().dsa_mla_prologue(
+        _ptr(q_resid), _ptr(q_compressed), _ptr(hidden), _ptr(wq_gate), _ptr(wkv_a), _ptr(wkv_b),
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(q), _ptr(gate), _ptr(k_cache), _ptr(v_cache), B, S, T,
+        past_len, Qr, Qc, Hd, L, H, Dqk - R, R, Dv, _dtype(q), _ptr(workspace), nbytes,
+        _stream(stream)))
+    return q, gate, k_cache, v_cache

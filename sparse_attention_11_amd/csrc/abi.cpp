@@ -391,6 +391,62 @@ int dsa_indexer_prologue(const void* q_lora, const void* hidden, const void* wq_
                     fn);
 }
 
+size_t dsa_mla_prologue_workspace_size(int B, int S, int kv_lora_rank) {
+  if (B < 1 || S < 1 || kv_lora_rank < 32 || kv_lora_rank % 32 != 0 || !rows_ok(B, S)) return 0;
+  return (size_t)B * S * kv_lora_rank * 2;  // the latent (bf16)
+}
+
+int dsa_mla_prologue(const void* q_resid, const void* q_compressed, const void* hidden,
+                     const void* wq_gate, const void* wkv_a, const void* wkv_b,
+                     const float* rope_cos, const float* rope_sin, void* q, void* gate,
+                     void* k_cache, void* v_cache, int B, int S, int T, int past_len,
+                     int q_resid_dim, int q_comp_dim, int hidden_dim, int kv_lora_rank, int H,
+                     int qk_nope_dim, int qk_rope_dim, int v_dim, int dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_mla_prologue";
+  g_err.clear();
+  if (!q_resid || !q_compressed || !hidden || !wq_gate || !wkv_a || !wkv_b || !q || !gate ||
+      !k_cache || !v_cache)
+    return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (qk_rope_dim > 0 && (!rope_cos || !rope_sin))
+    return fail(DSA_ERR_INVALID_ARG, "%s: rope tables are NULL with qk_rope_dim %d", fn,
+                qk_rope_dim);
+  if (B < 1 || S < 1 || T < 1 || past_len < 0 || q_resid_dim < 1 || q_comp_dim < 1 ||
+      hidden_dim < 1 || kv_lora_rank < 1 || H < 1 || qk_nope_dim < 0 || qk_rope_dim < 0 ||
+      v_dim < 1 || qk_nope_dim + (long long)qk_rope_dim < 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1 (nope, rope >= 0) and past_len >= 0",
+                fn);
+  if ((long long)past_len + S > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: T (%d) < past_len + S (%d + %d)", fn, T, past_len, S);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (q_resid_dim % 32 || q_comp_dim % 32 || hidden_dim % 32 || kv_lora_rank % 32)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "%s: q_resid_dim, q_comp_dim, hidden_dim and kv_lora_rank must be multiples of 32",
+                fn);
+  if (qk_nope_dim % 16 || qk_rope_dim % 16 || v_dim % 16 ||
+      qk_nope_dim + qk_rope_dim > DSA_MAX_HEAD_DIM || v_dim > DSA_MAX_HEAD_DIM)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "%s: head dims must be multiples of 16 with nope + rope and v at most %d", fn,
+                DSA_MAX_HEAD_DIM);
+  if (!rows_ok(B, S)) return fail(DSA_ERR_UNSUPPORTED, "%s: B*S above %lld", fn, kMaxRows);
+  if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
+  if (H > kMaxHeads) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d heads", fn, kMaxHeads);
+  if ((long long)q_resid_dim + q_comp_dim > 0x7FFFFFFF / 256 || hidden_dim > 0x7FFFFFFF / 256 ||
+      kv_lora_rank > 0x7FFFFFFF / 256)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: input widths too large", fn);
+  int st = check_ws(fn, workspace, workspace_bytes,
+                    dsa_mla_prologue_workspace_size(B, S, kv_lora_rank));
+  if (st) return st;
+  return hip_status(dsa::launch_mla_prologue(q_resid, q_compressed, hidden, wq_gate, wkv_a, wkv_b,
+                                             rope_cos, rope_sin, q, gate, k_cache, v_cache, B, S,
+                                             T, past_len, q_resid_dim, q_comp_dim, hidden_dim,
+                                             kv_lora_rank, H, qk_nope_dim, qk_rope_dim, v_dim,
+                                             workspace, stream),
+                    fn);
+}
+
 size_t dsa_topk_workspace_size(int B, int S, int T, int topk) {
   // (sizes the call itself rejects need no workspace)
   if (B < 1 || S < 1 || T < 1 || topk < 1 || topk > T || topk > DSA_MAX_TOPK || !rows_ok(B, S) ||

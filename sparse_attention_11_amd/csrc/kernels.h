@@ -34,6 +34,18 @@ hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const
                                    int q_lora_rank, int hidden_dim, int HI, int DI, int R,
                                    float eps, void* workspace, hipStream_t stream);
 
+// The main attention's projections (prologue.hip): kv_a_proj_with_mqa (latent
+// into the workspace [B*S, L] bf16, rotated rope key into every head's cache
+// row), expand_kv (k_nope and v into the cache rows), q_gate_proj on
+// [q_resid, q_comp] (query with its rope slice rotated, gate). Widths: Qr, Qc,
+// Hd, L multiples of 32; N, R, Dv multiples of 16.
+hipError_t launch_mla_prologue(const void* q_resid, const void* q_comp, const void* hidden,
+                               const void* wq_gate, const void* wkv_a, const void* wkv_b,
+                               const float* rope_cos, const float* rope_sin, void* q, void* gate,
+                               void* k_cache, void* v_cache, int B, int S, int T, int past_len,
+                               int Qr, int Qc, int Hd, int L, int H, int N, int R, int Dv,
+                               void* workspace, hipStream_t stream);
+
 // Per-row top-k (topk.hip).
 size_t topk_workspace_bytes(int B, int S, int T, int topk);
 // order 0: by score descending (ties: lower position first); 1: the same

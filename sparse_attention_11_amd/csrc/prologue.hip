@@ -16,11 +16,30 @@
 //                     (double-buffered, the next step loaded into registers
 //                     under the current MFMAs); the MFMA forms C^T so that a
 //                     lane stores four consecutive columns at once.
+//                     The A operand may be two row-major matrices side by
+//                     side (a concatenation along K read in place), and the
+//                     epilogue may scatter columns into the main attention's
+//                     tensors (the MLA side below).
 //  rope_q_kernel      half-split RoPE on the last rope_dim dims of every
 //                     index head, in place.
 //  ln_rope_k_kernel   LayerNorm over idx_dim (fp32 statistics), then the
 //                     same RoPE, written into the key cache rows
 //                     past_len .. past_len + S - 1.
+//
+// The main attention's projections (A.X-K2 page, "MLA + explicit sparse
+// mask" steps 1-3 and "Attention output gate"; interleaved RoPE, "two RoPE
+// layouts") run as three GEMMs whose epilogues write the attention's inputs
+// directly:
+//   kv_a_proj_with_mqa  hidden -> [latent | rope key]: the latent to the
+//                       workspace, the rope key rotated and written into the
+//                       rope slice of every head's cache row
+//   expand_kv           latent -> per head [k_nope | v]: into the nope slice of
+//                       the key cache rows and the value cache rows
+//   q_gate_proj         [q_resid | q_compressed] -> per head [query | gate]:
+//                       the query (rope slice rotated) and the gate
+// A lane holds four consecutive output columns, so every interleaved rotary
+// pair (2j, 2j + 1) is in one lane and no group of four straddles a head or
+// a slice (every width is a multiple of 16).
 #include "common.h"
 #include "kernels.h"
 
@@ -56,12 +75,87 @@ struct GemmRope {
   int D, R, S, P;
 };
 
+// The A operand: rows of A1 (K1 wide) followed, along K, by rows of A2 (K -
+// K1 wide; unused when K1 = K). K1 is a multiple of 32, so a 16-byte chunk
+// lies in one of the two.
+struct GemmA {
+  const uint16_t* A1;
+  const uint16_t* A2;
+  int K1;
+};
+// Epilogues of the main attention's projections (EPI 1..3 below): token row
+// m = b * S + s sits at position P + s of caches with T rows.
+struct GemmMla {
+  uint16_t* q;     // [M, H, N + R]       (EPI 1)
+  uint16_t* gate;  // [M, H, Dv]          (EPI 1)
+  uint16_t* kc;    // [B, T, H, N + R]    (EPI 2: rope slices, EPI 3: nope slices)
+  uint16_t* vc;    // [B, T, H, Dv]       (EPI 3)
+  uint16_t* lat;   // [M, L]              (EPI 2)
+  const float* cosb;
+  const float* sinb;  // [T, R / 2]
+  int H, N, R, Dv, L, S, T, P;
+};
+
+__device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float c, float d) {
+  uint2 pk;
+  pk.x = pack_bf16x2(a, b);
+  pk.y = pack_bf16x2(c, d);
+  *(uint2*)p = pk;
+}
+
+// Interleaved RoPE of the two pairs (x0, x1), (x2, x3) at rotary indices j0,
+// j0 + 1 of position p.
+__device__ __forceinline__ void rope_interleaved4(float* x, const GemmMla& e, int p, int j0) {
+  const int half = e.R / 2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float c = e.cosb[(int64_t)p * half + j0 + u], s = e.sinb[(int64_t)p * half + j0 + u];
+    const float a = x[2 * u], b = x[2 * u + 1];
+    x[2 * u] = a * c - b * s;
+    x[2 * u + 1] = b * c + a * s;
+  }
+}
+
+// Columns n .. n + 3 of token row m, scattered by the MLA epilogues.
+template <int EPI>
+__device__ __forceinline__ void mla_store4(const GemmMla& e, int m, int n, float* x) {
+  const int b = m / e.S, s = m - b * e.S, p = e.P + s;
+  const int Dqk = e.N + e.R;
+  if (EPI == 1) {  // q_gate_proj: head h = [query (Dqk) | gate (Dv)]
+    const int W = Dqk + e.Dv, h = n / W, c = n - h * W;
+    if (c < Dqk) {
+      if (c >= e.N) rope_interleaved4(x, e, p, (c - e.N) >> 1);
+      store4_bf16(e.q + ((int64_t)m * e.H + h) * Dqk + c, x[0], x[1], x[2], x[3]);
+    } else {
+      store4_bf16(e.gate + ((int64_t)m * e.H + h) * e.Dv + (c - Dqk), x[0], x[1], x[2], x[3]);
+    }
+  } else if (EPI == 2) {  // kv_a_proj_with_mqa: [latent (L) | rope key (R)]
+    if (n < e.L) {
+      store4_bf16(e.lat + (int64_t)m * e.L + n, x[0], x[1], x[2], x[3]);
+    } else {
+      const int r = n - e.L;
+      rope_interleaved4(x, e, p, r >> 1);
+      uint16_t* row = e.kc + ((int64_t)b * e.T + p) * e.H * Dqk + e.N + r;
+      for (int h = 0; h < e.H; ++h) store4_bf16(row + (int64_t)h * Dqk, x[0], x[1], x[2], x[3]);
+    }
+  } else {  // expand_kv: head h = [k_nope (N) | v (Dv)]
+    const int W = e.N + e.Dv, h = n / W, c = n - h * W;
+    const int64_t cr = ((int64_t)b * e.T + p) * e.H + h;
+    if (c < e.N)
+      store4_bf16(e.kc + cr * Dqk + c, x[0], x[1], x[2], x[3]);
+    else
+      store4_bf16(e.vc + cr * e.Dv + (c - e.N), x[0], x[1], x[2], x[3]);
+  }
+}
+
 // RHALF: half the rotary width (16 or 32) for the RoPE epilogue, 0 for none;
 // a compile-time constant so that every rotary pair's registers are fixed.
-template <int RHALF, int BM>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                           GemmOut o1, GemmOut o2, int M, int K,
-                                                           int ntiles_n, int nt1, GemmRope rp) {
+// EPI 0: C = A W^T into (o1, o2); EPI 1..3: the MLA epilogues above (o1.N is
+// the output width).
+template <int RHALF, int BM, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1, GemmOut o2,
+                                                           int M, int K, int ntiles_n, int nt1,
+                                                           GemmRope rp, GemmMla mla) {
   constexpr int kGBM = BM, kGBK = gemm_bk<BM>(), kGPad = kGBK + 8;
   constexpr int kWM = BM / 2;                  // rows per wave (2 x 2 waves)
   constexpr int kWI = kWM / 32;                // 32-row MFMA blocks per wave
@@ -97,8 +191,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     for (int i = 0; i < kGLdA; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
       const int m = m0 + r;
-      const bool kin = k0 + kc < K;  // K % 32 == 0: a chunk is all in or all out
-      ra[i] = (m < M && kin) ? load16(A + (int64_t)m * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+      const int k = k0 + kc;
+      const bool kin = k < K;  // K % 32 == 0: a chunk is all in or all out
+      // (only q_gate_proj reads two matrices; the other instantiations see one)
+      const uint16_t* src = (EPI != 1 || k < ga.K1)
+                                ? ga.A1 + (int64_t)m * (EPI == 1 ? ga.K1 : K) + k
+                                : ga.A2 + (int64_t)m * (K - ga.K1) + (k - ga.K1);
+      ra[i] = (m < M && kin) ? load16(src) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < kGLdW; ++i) {
@@ -189,6 +288,24 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
             acc[i][j2][4 * g2 + r] = x2 * cs + x1 * sn;
           }
     }
+  }
+  if (EPI > 0) {
+#pragma unroll
+    for (int i = 0; i < kWI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm * kWM + 32 * i + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 64 + 32 * j + 8 * g + 4 * (lane >> 5);
+          if (n >= N) continue;  // (widths are multiples of 4)
+          float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          mla_store4<EPI>(mla, m, n, x);
+        }
+      }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < kWI; ++i)
@@ -300,9 +417,9 @@ __global__ __launch_bounds__(256) void ln_rope_k_kernel(const uint16_t* __restri
 }  // namespace
 
 namespace {
-hipError_t gemm_launch(const void* A, GemmOut o1, GemmOut o2, int M, int K, const GemmRope* rp,
-                       hipStream_t st) {
-  if (K % 32 != 0) return hipErrorInvalidValue;
+hipError_t gemm_launch(GemmA ga, GemmOut o1, GemmOut o2, int M, int K, const GemmRope* rp,
+                       hipStream_t st, int epi = 0, const GemmMla* mla = nullptr) {
+  if (K % 32 != 0 || ga.K1 % 32 != 0 || ga.K1 > K) return hipErrorInvalidValue;
   const int nt1 = (o1.N + kGBN - 1) / kGBN, nt2 = o2.N > 0 ? (o2.N + kGBN - 1) / kGBN : 0;
   const int ntn = nt1 + nt2;
   // wide outputs: 256-row tiles (still >= 2 workgroups per CU at M = 32768)
@@ -310,32 +427,40 @@ hipError_t gemm_launch(const void* A, GemmOut o1, GemmOut o2, int M, int K, cons
   const int64_t mtiles = (M + bm - 1) / bm;
   const int64_t g = (ntn <= kGroupedTiles ? (mtiles + 7) / 8 * 8 : mtiles) * ntn;
   if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-#define DSA_GEMM_LAUNCH(RH, BMV, RP)                                                             \
-  hipLaunchKernelGGL((gemm_bf16_kernel<RH, BMV>), dim3((unsigned)g), dim3(256), 0, st,          \
-                     (const uint16_t*)A, o1, o2, M, K, ntn, nt1, RP)
-  if (bm == 256) {
-    if (rp && rp->R == 64)
-      DSA_GEMM_LAUNCH(32, 256, *rp);
-    else if (rp && rp->R == 32)
-      DSA_GEMM_LAUNCH(16, 256, *rp);
-    else
-      DSA_GEMM_LAUNCH(0, 256, GemmRope{});
-  } else {
-    if (rp && rp->R == 64)
-      DSA_GEMM_LAUNCH(32, 128, *rp);
-    else if (rp && rp->R == 32)
-      DSA_GEMM_LAUNCH(16, 128, *rp);
-    else
-      DSA_GEMM_LAUNCH(0, 128, GemmRope{});
+  const GemmMla ml = mla ? *mla : GemmMla{};
+#define DSA_GEMM_LAUNCH(RH, BMV, EP, RP)                                                         \
+  hipLaunchKernelGGL((gemm_bf16_kernel<RH, BMV, EP>), dim3((unsigned)g), dim3(256), 0, st, ga,  \
+                     o1, o2, M, K, ntn, nt1, RP, ml)
+#define DSA_GEMM_BM(BMV)                                           \
+  if (epi == 1) {                                                  \
+    DSA_GEMM_LAUNCH(0, BMV, 1, GemmRope{});                        \
+  } else if (epi == 2) {                                           \
+    DSA_GEMM_LAUNCH(0, BMV, 2, GemmRope{});                        \
+  } else if (epi == 3) {                                           \
+    DSA_GEMM_LAUNCH(0, BMV, 3, GemmRope{});                        \
+  } else if (rp && rp->R == 64) {                                  \
+    DSA_GEMM_LAUNCH(32, BMV, 0, *rp);                              \
+  } else if (rp && rp->R == 32) {                                  \
+    DSA_GEMM_LAUNCH(16, BMV, 0, *rp);                              \
+  } else {                                                         \
+    DSA_GEMM_LAUNCH(0, BMV, 0, GemmRope{});                        \
   }
+  if (bm == 256) {
+    DSA_GEMM_BM(256)
+  } else {
+    DSA_GEMM_BM(128)
+  }
+#undef DSA_GEMM_BM
 #undef DSA_GEMM_LAUNCH
   return hipGetLastError();
 }
+
+GemmA one_a(const void* A, int K) { return GemmA{(const uint16_t*)A, nullptr, K}; }
 }  // namespace
 
 hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int ldc,
                             hipStream_t st) {
-  return gemm_launch(A, GemmOut{(const uint16_t*)W, (uint16_t*)C, N, ldc},
+  return gemm_launch(one_a(A, K), GemmOut{(const uint16_t*)W, (uint16_t*)C, N, ldc},
                      GemmOut{nullptr, nullptr, 0, 0}, M, K, nullptr, st);
 }
 
@@ -351,13 +476,14 @@ hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const
   // sits in one lane (idx_dim 64 or 128, rope_dim 32 or 64)
   const bool fused = (DI == 64 || DI == 128) && (R == 32 || R == 64);
   const GemmRope rp{rope_cos, rope_sin, DI, R, S, past_len};
-  hipError_t e = gemm_launch(q_lora, GemmOut{(const uint16_t*)wq_b, (uint16_t*)q_idx, HI * DI,
+  hipError_t e = gemm_launch(one_a(q_lora, q_lora_rank),
+                             GemmOut{(const uint16_t*)wq_b, (uint16_t*)q_idx, HI * DI,
                                              HI * DI},
                              GemmOut{nullptr, nullptr, 0, 0}, M, q_lora_rank, fused ? &rp : nullptr,
                              st);
   if (e != hipSuccess) return e;
   // the key and head-weight projections in one pass over the hidden state
-  e = gemm_launch(hidden, GemmOut{(const uint16_t*)wk, (uint16_t*)workspace, DI, DI},
+  e = gemm_launch(one_a(hidden, hidden_dim), GemmOut{(const uint16_t*)wk, (uint16_t*)workspace, DI, DI},
                   GemmOut{(const uint16_t*)weights_proj, (uint16_t*)w, HI, HI}, M, hidden_dim,
                   nullptr, st);
   if (e != hipSuccess) return e;
@@ -373,6 +499,32 @@ hipError_t launch_indexer_prologue(const void* q_lora, const void* hidden, const
                      (const uint16_t*)k_norm_bias, rope_cos, rope_sin, (uint16_t*)k_idx_cache,
                      (int64_t)M, S, T, past_len, DI, R, eps);
   return hipGetLastError();
+}
+
+hipError_t launch_mla_prologue(const void* q_resid, const void* q_comp, const void* hidden,
+                               const void* wq_gate, const void* wkv_a, const void* wkv_b,
+                               const float* rope_cos, const float* rope_sin, void* q, void* gate,
+                               void* k_cache, void* v_cache, int B, int S, int T, int past_len,
+                               int Qr, int Qc, int Hd, int L, int H, int N, int R, int Dv,
+                               void* workspace, hipStream_t st) {
+  const int M = B * S;
+  GemmMla e{(uint16_t*)q,          (uint16_t*)gate, (uint16_t*)k_cache, (uint16_t*)v_cache,
+            (uint16_t*)workspace, rope_cos,        rope_sin,           H,
+            N,                    R,               Dv,                 L,
+            S,                    T,               past_len};
+  const GemmOut none{nullptr, nullptr, 0, 0};
+  // kv_a_proj_with_mqa: the latent (workspace) and the rotated rope key
+  hipError_t err = gemm_launch(one_a(hidden, Hd), GemmOut{(const uint16_t*)wkv_a, nullptr, L + R, 0},
+                               none, M, Hd, nullptr, st, 2, &e);
+  if (err != hipSuccess) return err;
+  // expand_kv: per-head k_nope and v from the latent
+  err = gemm_launch(one_a(workspace, L), GemmOut{(const uint16_t*)wkv_b, nullptr, H * (N + Dv), 0},
+                    none, M, L, nullptr, st, 3, &e);
+  if (err != hipSuccess) return err;
+  // q_gate_proj on [q_resid, q_compressed]: query (rope slice rotated) and gate
+  return gemm_launch(GemmA{(const uint16_t*)q_resid, (const uint16_t*)q_comp, Qr},
+                     GemmOut{(const uint16_t*)wq_gate, nullptr, H * (N + R + Dv), 0}, none, M,
+                     Qr + Qc, nullptr, st, 1, &e);
 }
 
 }  // namespace dsa

@@ -138,6 +138,11 @@ int main() {
                                 (const float*)P(2), VP(0), VP(1), VP(2), B, S, T, past, iv(), iv(),
                                 iv(), iv(), iv(), fv(), dt, VP(0), wsb, nullptr),
            "dsa_indexer_prologue");
+    (void)dsa_mla_prologue_workspace_size(iv(), iv(), iv());
+    expect(dsa_mla_prologue(P(0), P(1), P(2), P(0), P(1), P(2), (const float*)P(0),
+                            (const float*)P(1), VP(2), VP(0), VP(1), VP(2), B, S, T, past, iv(),
+                            iv(), iv(), iv(), H, iv(), iv(), iv(), dt, VP(0), wsb, nullptr),
+           "dsa_mla_prologue");
   }
   for (int s = -2; s < 8; ++s) (void)dsa_status_string(s);
   if (bad) return 3;

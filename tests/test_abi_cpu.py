@@ -245,3 +245,34 @@ def test_noalloc_decode_rejects_calls_beyond_the_static_scratch():
     # invalid arguments are still INVALID_ARG
     assert L.dsa_sparse_attn_decode_noalloc(None, P, P, P, P, P, 1, 4096, 8, 128, 64, 128, 64,
                                             0.07, 1, 1, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def mla(**kw):
+    a = dict(qr=P, qc=P, hd=P, wq=P, wa=P, wb=P, cos=P, sin=P, q=P, g=P, kc=P, vc=P, B=1, S=4,
+             T=8, past=0, Qr=64, Qc=32, Hd=96, L=64, H=2, N=64, R=32, Dv=64, dt=1, ws=P,
+             wsb=1 << 30)
+    a.update(kw)
+    return dsa.lib().dsa_mla_prologue(a["qr"], a["qc"], a["hd"], a["wq"], a["wa"], a["wb"],
+                                      a["cos"], a["sin"], a["q"], a["g"], a["kc"], a["vc"], a["B"],
+                                      a["S"], a["T"], a["past"], a["Qr"], a["Qc"], a["Hd"], a["L"],
+                                      a["H"], a["N"], a["R"], a["Dv"], a["dt"], a["ws"], a["wsb"],
+                                      None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qr=None), 1), (dict(wb=None), 1), (dict(kc=None), 1), (dict(cos=None), 1),
+    (dict(B=0), 1), (dict(T=3), 1), (dict(past=-1), 1), (dict(N=0, R=0), 1), (dict(dt=2), 1),
+    (dict(dt=0), 2), (dict(Qr=48), 2), (dict(L=40), 2), (dict(N=24), 2), (dict(R=8), 2),
+    (dict(N=192, R=128), 2), (dict(Dv=272), 2), (dict(ws=None), 3), (dict(wsb=100), 3),
+])
+def test_mla_prologue_validation(kw, code):
+    assert mla(**kw) == code
+    assert dsa.dsa_last_error().startswith("dsa_mla_prologue")
+
+
+def test_mla_prologue_rope_tables_optional_without_rope():
+    # R = 0: no rotation, the tables may be NULL; the call then fails only on the
+    # workspace (checked last), so validation passed
+    assert mla(R=0, cos=None, sin=None, wsb=0) == dsa.DSA_ERR_WORKSPACE
+    assert dsa.dsa_mla_prologue_workspace_size(2, 5, 64) == 2 * 5 * 64 * 2
+    assert dsa.dsa_mla_prologue_workspace_size(2, 5, 40) == 0

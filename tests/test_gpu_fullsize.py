@@ -474,3 +474,39 @@ def test_prologue_s32k_sampled_rows(S):
         assert_rows_close(got_q[i], rq[0, 0], 2e-2, what=f"prologue q_idx row {s}")
         assert_rows_close(got_k[i], rk[0, 0], 2e-2, what=f"prologue k row {s}")
         assert_rows_close(got_w[i], rw[0, 0], 2e-2, what=f"prologue w row {s}")
+
+
+# ---------------------------------------------------- mla-prologue-s32k
+@pytest.mark.parametrize("S", [32768, 8100])
+def test_mla_prologue_s32k_sampled_rows(S):
+    """The main attention's projections at full size (three GEMMs with the
+    query/gate split, the latent, the rope key broadcast and expand_kv in
+    their epilogues), sampled tokens against the oracle. S = 8100 ends in a
+    ragged row tile."""
+    wl = WORKLOADS["mla-prologue-s32k"]
+    H, N, R, Dv = wl.H, wl.nope, wl.rope, wl.v
+    Qr, Qc, Hd, L = wl.q_lora, wl.q_comp, wl.hidden, wl.kv_lora
+    E = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=DEV)
+    gen = lambda t, tid, sc: datagen.normal_device(t, wl.seed, tid, sc)
+    qr, qc, hd = gen(E(1, S, Qr), 40, 1.0), gen(E(1, S, Qc), 41, 1.0), gen(E(1, S, Hd), 42, 1.0)
+    host = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", wl.seed, tid, sc)
+    wq = host((H * (N + R + Dv), Qr + Qc), 43, (Qr + Qc) ** -0.5)
+    wa = host((L + R, Hd), 44, Hd ** -0.5)
+    wb = host((H * (N + Dv), L), 45, L ** -0.5)
+    pos = np.arange(S, dtype=np.float64)[:, None]
+    ang = pos * 10000.0 ** (-2.0 * np.arange(R // 2) / R)
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    q, g, kc, vc = E(1, S, H, N + R), E(1, S, H, Dv), E(1, S, H, N + R), E(1, S, H, Dv)
+    dsa.dsa_mla_prologue(qr, qc, hd, to_dev(wq), to_dev(wa), to_dev(wb), to_dev(cos), to_dev(sin),
+                         q, g, kc, vc, 0)
+    rows = strat_rows(S, 2048, 512, seed=4)
+    if S % 256:
+        rows = sorted(set(rows) | {S // 256 * 256, S - 2})
+    got = [from_dev(t[0, rows]) for t in (q, g, kc, vc)]
+    del qr, qc, hd, q, g, kc, vc
+    _free()
+    for i, s in enumerate(rows):
+        args = [host_row(wl, tid, 1.0, s, w).reshape(1, 1, w) for tid, w in ((40, Qr), (41, Qc), (42, Hd))]
+        ref = oracle.mla_prologue(*args, wq, wa, wb, cos, sin, s, H, N, R, Dv)
+        for name, a, r in zip(("q", "gate", "k", "v"), got, ref):
+            assert_rows_close(a[i], r[0, 0], 2e-2, what=f"mla prologue {name} row {s}")

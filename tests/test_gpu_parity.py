@@ -637,3 +637,48 @@ def test_indexer_prologue_cases(B, S, P, Q, Hd, HI, D, R):
     assert_rows_close(got_k[:, P:P + S], rk, 2e-2, what=what + " k")
     assert np.all(got_k[:, :P] == 7.0) and np.all(got_k[:, P + S:] == 7.0), "rows outside the call changed"
     assert_rows_close(from_dev(wd), rw, 2e-2, what=what + " w")
+
+
+# ------------------------------------------------------- MLA prologue
+MLA_PROLOGUE_CASES = [
+    # B, S, P, Qr, Qc, Hd, L, H, N, R, Dv
+    (1, 200, 0, 64, 32, 96, 64, 4, 64, 32, 64),
+    (2, 130, 70, 96, 64, 160, 128, 5, 128, 64, 128),   # ragged row tiles, odd head count
+    (1, 1, 999, 32, 32, 64, 32, 3, 128, 64, 128),      # one decode token
+    (1, 300, 17, 128, 128, 256, 512, 8, 128, 64, 128),  # latent rank 512
+    (3, 7, 5, 64, 64, 32, 64, 2, 64, 0, 64),           # no RoPE
+    (1, 50, 3, 64, 64, 64, 96, 3, 32, 16, 48),         # small dims
+]
+
+
+@pytest.mark.parametrize("B,S,P,Qr,Qc,Hd,L,H,N,R,Dv", MLA_PROLOGUE_CASES)
+def test_mla_prologue_cases(B, S, P, Qr, Qc, Hd, L, H, N, R, Dv):
+    seed = S + H
+    Dqk, T = N + R, P + S + 3  # three cache rows past the call stay untouched
+    g = lambda shape, tid, sc: datagen.normal_host(shape, "bf16", seed, tid, sc)
+    qr, qc, hd = g((B, S, Qr), 30, 1.0), g((B, S, Qc), 31, 1.0), g((B, S, Hd), 32, 1.0)
+    wq = g((H * (Dqk + Dv), Qr + Qc), 33, (Qr + Qc) ** -0.5)
+    wa = g((L + R, Hd), 34, Hd ** -0.5)
+    wb = g((H * (N + Dv), L), 35, L ** -0.5)
+    cos = sin = None
+    if R:
+        ang = np.random.default_rng(seed).uniform(-np.pi, np.pi, (T, R // 2))
+        cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    q = torch.full((B, S, H, Dqk), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gate = torch.full((B, S, H, Dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kc = torch.full((B, T, H, Dqk), 7.0, dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((B, T, H, Dv), 7.0, dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_mla_prologue(to_dev(qr), to_dev(qc), to_dev(hd), to_dev(wq), to_dev(wa), to_dev(wb),
+                         None if cos is None else to_dev(cos), None if sin is None else to_dev(sin),
+                         q, gate, kc, vc, P)
+    _sync()
+    rq, rg, rk, rv = oracle.mla_prologue(qr, qc, hd, wq, wa, wb, cos, sin, P, H, N, R, Dv)
+    what = f"mla prologue {B, S, P, Qr, Qc, Hd, L, H, N, R, Dv}"
+    assert_rows_close(from_dev(q), rq, 2e-2, what=what + " q")
+    assert_rows_close(from_dev(gate), rg, 2e-2, what=what + " gate")
+    kh, vh = from_dev(kc), from_dev(vc)
+    assert_rows_close(kh[:, P:P + S], rk, 2e-2, what=what + " k rows")
+    assert_rows_close(vh[:, P:P + S], rv, 2e-2, what=what + " v rows")
+    outside = np.ones(T, bool)
+    outside[P:P + S] = False
+    assert (kh[:, outside] == 7.0).all() and (vh[:, outside] == 7.0).all(), "rows outside the call"
