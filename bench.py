@@ -371,6 +371,33 @@ def time_layer(layer, steps, warmup, torch):
     return per_stage, total_ms, wall
 
 
+def time_graph(stages, steps, torch):
+    """Mean time of one replay of the stages captured in a HIP graph (kernels
+    only: the library's calls enqueue kernels and nothing else)."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for _, fn in stages:
+            fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _, fn in stages:
+                fn()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 # ------------------------------------------------------ algorithmic work
 def work(wl):
     """Algorithmic flops / bytes per stage (the dense work DSA avoids is not counted)."""
@@ -634,6 +661,7 @@ def main():
         dlay = make_layer(dwl, torch, dsa, datagen)
         dps, dtm, _ = time_layer(dlay, args.decode_steps, args.warmup, torch)
         dec_r = summarize(dwl, dps, dtm)
+        dgraph = time_graph(dlay.stages(), args.decode_steps, torch)
         del dlay
         torch.cuda.empty_cache()
         log(f"{dwl.name}: {dtm * 1e3:.1f} us/step")
@@ -647,6 +675,7 @@ def main():
                  "mean_launch_us": t4 * 1e6}
         droof["traffic"], droof["traffic_source"] = counted_traffic(dwl.name)
         dec = {"workload": dwl.name, "us_per_step": dtm * 1e3, "steps": args.decode_steps,
+               "us_per_step_graph": dgraph * 1e3,
                "config": {"B": dwl.B, "T": dwl.T, "heads": dwl.H, "qk": dwl.Dqk, "v": dwl.v,
                           "index_heads": dwl.HI, "index_dim": dwl.DI, "topk": dwl.topk},
                "stages": dec_r, "roofline": droof, "cpu_baseline": None}
@@ -658,6 +687,9 @@ def main():
         lay = make_layer(WORKLOADS[name], torch, dsa, datagen)
         ps, tm, _ = time_layer(lay, args.also_steps, 2, torch)
         also[name] = summarize(WORKLOADS[name], ps, tm)
+        dst = [st for st in lay.stages() if st[0].startswith("D ")]
+        if dst:  # the decode token's stages replayed from a HIP graph
+            also[name]["decode_us_per_step_graph"] = time_graph(dst, 20, torch) * 1e3
         del lay
         torch.cuda.empty_cache()
         log(f"{name}: {tm:.3f} ms/step")

@@ -199,13 +199,17 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   // ---- register prefetch of one key block. A K row of KCH 16-byte chunks is
   // covered by one or two power-of-two parts (24 = 16 + 8), so that a thread
   // keeps one byte offset per part and successive loads of a part add a
-  // fixed row step. Loads go through a buffer resource that ends at the
+  // fixed row step (24 = 16 + 8, 12 = 8 + 4). Loads go through a buffer resource that ends at the
   // last row of this batch's buffer: rows past it read as zeros.
-  constexpr int KP1 = (KCH == 24) ? 16 : KCH;  // chunks per row, part 1
+  constexpr int KP1 = (KCH == 24) ? 16 : (KCH == 12) ? 8 : KCH;  // chunks per row, part 1
   constexpr int KP2 = KCH - KP1;               // part 2 (0 or 8)
   constexpr int R1 = 256 / KP1, N1 = kBN / R1;  // rows per load, loads
   constexpr int R2 = KP2 ? 256 / KP2 : 1, N2 = KP2 ? kBN / R2 : 0;
   static_assert(N1 + N2 == KLD && (VLD == 1 || VUN == 256 * VLD), "load split");
+  static_assert(256 % KP1 == 0 && (KP2 == 0 || 256 % KP2 == 0) && N1 * R1 == kBN &&
+                    (KP2 == 0 || N2 * R2 == kBN),
+                "every K row chunk is loaded exactly once");
+  static_assert(VCH == 8 || VCH == 16 || VCH == 32, "the V swizzle keeps chunks inside a row");
   const int krow1 = tid / KP1, kc1 = tid % KP1;
   const int krow2 = KP2 ? tid / KP2 : 0, kc2 = KP2 ? KP1 + tid % KP2 : 0;
   const uint32_t rowb = (uint32_t)HKV * DQK * 2u;  // bytes between key rows
@@ -601,8 +605,10 @@ constexpr int kBitmapLdsMaxWords = 12288;  // 48 KiB of LDS
 
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv) {
   if (dtype != 1 || S < 16) return false;
+  // (96: A.X-K2-Light's qk_head_dim, nope 64 + rope 32)
   return (Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128) ||
-         (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64) || (Dqk == 256 && Dv == 256);
+         (Dqk == 256 && Dv == 128) || (Dqk == 128 && Dv == 64) || (Dqk == 256 && Dv == 256) ||
+         (Dqk == 96 && Dv == 64) || (Dqk == 96 && Dv == 128);
 }
 
 void prefill_work_plan(int B, int S, int T, int P, int H, int kv_offset, int window, int* n_tiles,
@@ -669,6 +675,8 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                              bm, gg, oo, B, S, T, past_len, kv_offset, H, Hkv, W32, window,    \
                              sl2, gate_dim, part, st);
   DSA_PREFILL_CASE(64, 64)
+  DSA_PREFILL_CASE(96, 64)
+  DSA_PREFILL_CASE(96, 128)
   DSA_PREFILL_CASE(128, 64)
   DSA_PREFILL_CASE(128, 128)
   DSA_PREFILL_CASE(192, 128)

@@ -273,6 +273,8 @@ PREFILL_CASES = [
     # gather: more than 32 heads (two head groups), ragged heads, small topk
     (1, 64, 20000, 2, 128, 64, 128, 64), (2, 40, 9000, 3, 64, 64, 128, 32),
     (1, 20, 12000, 40, 64, 32, 64, 48), (1, 17, 70000, 1, 128, 64, 128, 500),
+    # qk 96 (A.X-K2-Light: nope 64 + rope 32) on the MFMA path, v 64 and 128
+    (1, 150, 40, 3, 64, 32, 64, 48), (2, 90, 0, 2, 64, 32, 128, 64), (1, 300, 200, 1, 64, 32, 64, 300),
 ]
 
 
@@ -352,6 +354,7 @@ def test_decode_cases(B, T, H, nope, rope, Dv, k, dt):
     (1, 300, 700, 128, 2, 128, 64, 128, "bf16", True), (2, 200, 0, 64, 3, 64, 64, 128, "bf16", False),
     (1, 150, 40, 512, 2, 128, 64, 128, "bf16", True), (1, 1, 900, 512, 4, 128, 64, 128, "bf16", True),
     (2, 6, 100, 32, 3, 64, 64, 64, "bf16", True), (1, 50, 20, 16, 2, 32, 16, 32, "f32", True),
+    (1, 200, 300, 64, 2, 64, 32, 64, "bf16", True), (1, 130, 0, 40, 3, 64, 32, 128, "bf16", False),
 ])
 def test_swa_cases(B, S, P, W, H, nope, rope, Dv, dt, offset):
     kv_off = max(0, P - W + 1) if offset else 0
@@ -444,6 +447,8 @@ PAS_PREFILL_CASES = [
     (2, 8, 500, 5, 128, 64, 128, 128, 65), (1, 40, 30, 3, 32, 16, 32, 20, 7),
     # the row-gather path of long bf16 chunks, with sinks
     (1, 50, 20000, 2, 128, 64, 128, 100, 7),
+    # qk 96 with sinks on the MFMA path
+    (1, 100, 60, 2, 64, 32, 64, 40, 33),
 ]
 
 
