@@ -111,6 +111,67 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t* red, 
   }
 }
 
+// Bitonic sort (descending) of the kk keys in sel[0..kk), padded with 0 to
+// N = NT*E slots, then the positions of the first k to orow (-1 for padding).
+// Strides inside a thread run in registers, inside a wave via lane swaps,
+// only the widest through LDS (sel holds N keys). Keys are unique apart from
+// the 0 padding, so one compare decides each exchange: a slot keeps its own
+// key iff (own > partner) equals "this slot keeps the larger key"; both
+// conditions are lane masks and meet in one mask XOR. Callers have published
+// sel[0..kk) with a barrier.
+template <int NT, int E>
+__device__ __forceinline__ void sort_store(uint64_t* sel, int kk, int k, int32_t* orow) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int N = NT * E;
+  uint64_t a[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    a[e] = (i < kk) ? sel[i] : 0ull;
+  }
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pe = e ^ stride;
+          if (pe > e) {
+            const int i = tid * E + e;
+            const bool desc = (i & size) == 0;  // larger key to the lower slot
+            const uint64_t lo = a[e], hi = a[pe];
+            const bool sw = (hi > lo) == desc;
+            a[e] = sw ? hi : lo;
+            a[pe] = sw ? lo : hi;
+          }
+        }
+      } else {
+        if (stride >= 64 * E) {
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) sel[tid * E + e] = a[e];
+          __syncthreads();
+        }
+        // the slot's role depends on tid bits only (stride, size >= E)
+        const int i0 = tid * E;
+        const bool keep_max = ((i0 & stride) == 0) == ((i0 & size) == 0);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t other =
+              stride < 64 * E ? lane_xor_u64(a[e], stride / E, lane) : sel[(tid * E + e) ^ stride];
+          a[e] = ((a[e] > other) == keep_max) ? a[e] : other;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < k) orow[i] = (a[e] == 0ull) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)a[e]);
+  }
+}
+
 // Workgroup blockIdx.x handles elements [seg*seg_len, min(T, (seg+1)*seg_len))
 // of row blockIdx.x / nseg (seg = blockIdx.x % nseg), where a row holds
 // SRC 0: T fp32 scores; SRC 1: T 64-bit candidate keys (0 = empty).
@@ -365,60 +426,7 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
     return;
   }
 
-  // ---- bitonic sort (descending) of N = NT*E keys, padded with 0. Keys are
-  // unique apart from the 0 padding, so one compare decides each exchange:
-  // a slot keeps its own key iff (own > partner) equals "this slot keeps the
-  // larger key"; both conditions are lane masks and meet in one mask XOR.
-  constexpr int N = NT * E;
-  uint64_t a[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    a[e] = (i < kk) ? sel[i] : 0ull;
-  }
-#pragma unroll
-  for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int pe = e ^ stride;
-          if (pe > e) {
-            const int i = tid * E + e;
-            const bool desc = (i & size) == 0;  // larger key to the lower slot
-            const uint64_t lo = a[e], hi = a[pe];
-            const bool sw = (hi > lo) == desc;
-            a[e] = sw ? hi : lo;
-            a[pe] = sw ? lo : hi;
-          }
-        }
-      } else {
-        if (stride >= 64 * E) {
-          __syncthreads();
-#pragma unroll
-          for (int e = 0; e < E; ++e) sel[tid * E + e] = a[e];
-          __syncthreads();
-        }
-        // the slot's role depends on tid bits only (stride, size >= E)
-        const int i0 = tid * E;
-        const bool keep_max = ((i0 & stride) == 0) == ((i0 & size) == 0);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint64_t other =
-              stride < 64 * E ? lane_xor_u64(a[e], stride / E, lane) : sel[(tid * E + e) ^ stride];
-          a[e] = ((a[e] > other) == keep_max) ? a[e] : other;
-        }
-      }
-    }
-  }
-
-  int32_t* orow = out_idx + row * (int64_t)k;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    if (i < k) orow[i] = (a[e] == 0ull) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)a[e]);
-  }
+  sort_store<NT, E>(sel, kk, k, out_idx + row * (int64_t)k);
 }
 
 template <int NT, int SRC, int DST, int EPT>
@@ -473,11 +481,358 @@ int stage_groups(int T, int k, int* groups, int max_levels) {
   return lv;
 }
 
+// ------------------------------------------------------------ few long rows
+// Decode calls have a few rows of many scores. Instead of reducing every
+// 16384-score segment to k candidates (k = 2048 is an eighth of a segment, so
+// two or three passes over k-candidate sets), the threshold comes from one
+// histogram of the whole row: the top 11 bits of every valid key (sign,
+// exponent, two mantissa bits), summed over the row's chunks. The bin holding
+// the k-th largest key bounds the selection from below, so the keys in that
+// bin and above -- on indexer scores k plus a few hundred to a few thousand --
+// are the only candidates.
+//   row_hist_zero_kernel  clears the rows' histograms
+//   row_hist_kernel       one workgroup per 2048-score chunk: LDS histogram,
+//                         non-zero bins added to the row's
+//   row_filter_kernel     per chunk: the threshold bin from the row's
+//                         histogram, then the chunk's keys in that bin and
+//                         above, in position order, into the chunk's own slots
+//   row_select_kernel     one workgroup per row: the first digit of the radix
+//                         select is that same bin (read off the row histogram),
+//                         the rest runs on the candidates (held in registers
+//                         when there are at most 16384, streamed otherwise),
+//                         then an ordered compaction (position order) and
+//                         either the bitonic sort (dsa_topk) or the compacted
+//                         list itself (dsa_topk_unsorted).
+constexpr int kRowChunk = 2048;      // scores per chunk: 256 threads x 8
+constexpr int kRowMaxChunks = 1024;  // rows up to 2M scores take this path
+constexpr int kRowRegKeys = 16;      // candidates per select thread kept in registers
+
+__global__ __launch_bounds__(256) void row_hist_zero_kernel(uint32_t* __restrict__ h, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) h[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void row_hist_kernel(const float* __restrict__ scores,
+                                                       uint32_t* __restrict__ ghist, int T,
+                                                       int nc) {
+  constexpr int EPT = kRowChunk / 256;
+  __shared__ uint32_t h[kBins];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / nc;
+  const int c = blockIdx.x % nc;
+  const int t0 = c * kRowChunk, n = min(T - t0, kRowChunk);
+  for (int i = tid; i < kBins; i += 256) h[i] = 0u;
+  const float* sr = scores + row * (int64_t)T + t0;
+  float f[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + 256 * j;
+    f[j] = e < n ? sr[e] : -INFINITY;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if (f[j] != -INFINITY) atomicAdd(&h[orderable_key(f[j]) >> 21], 1u);
+  __syncthreads();
+  uint32_t* gr = ghist + row * kBins;
+  for (int i = tid; i < kBins; i += 256)
+    if (h[i]) atomicAdd(&gr[i], h[i]);
+}
+
+__global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict__ scores,
+                                                         const uint32_t* __restrict__ ghist,
+                                                         uint64_t* __restrict__ cand,
+                                                         uint32_t* __restrict__ cnt, int T,
+                                                         int nc, int k) {
+  constexpr int NT = 256, NW = 4, EPT = kRowChunk / 256;
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t s_red[NW];
+  __shared__ uint32_t s_col[EPT * NW];
+  __shared__ int s_krem, s_done, s_digit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x / nc;
+  const int c = blockIdx.x % nc;
+  const int t0 = c * kRowChunk, n = min(T - t0, kRowChunk);
+  // this chunk's scores first: their loads overlap the histogram work
+  const float* sr = scores + row * (int64_t)T + t0;
+  uint32_t hi[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + NT * j;
+    const float f = e < n ? sr[e] : -INFINITY;
+    hi[j] = f == -INFINITY ? 0u : orderable_key(f);
+  }
+  uint32_t tot = 0;
+  for (int i = tid; i < kBins; i += NT) {
+    const uint32_t v = ghist[row * kBins + i];
+    h[i] = v;
+    tot += v;
+  }
+  tot = block_sum<NW>(tot, s_red);  // (its barriers also publish h)
+  const int kk = (int)min((uint32_t)k, tot);
+  uint32_t bmin = 0xFFFFFFFFu;  // no candidates when the row has no valid key
+  if (kk > 0) {
+    __syncthreads();  // every thread has read s_red before pick_digit reuses it
+    pick_digit<NT>(h, s_red, kk, tid, lane, wave, &s_krem, &s_done, &s_digit);
+    __syncthreads();
+    bmin = (uint32_t)s_digit;
+  }
+  // keys in the threshold bin and above, in position order: positions t0 +
+  // 256 j + 64 wave + lane are ordered (j, wave, lane)
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const bool take = hi[j] != 0u && (hi[j] >> 21) >= bmin;
+    const uint64_t bal = __ballot(take);
+    if (lane == 0) s_col[j * NW + wave] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefix over the EPT x NW column counts
+    constexpr int PER = (EPT * NW + 63) / 64;
+    uint32_t v[PER];
+    uint32_t loc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = lane * PER + q;
+      v[q] = i < EPT * NW ? s_col[i] : 0u;
+      loc += v[q];
+    }
+    const uint32_t x = wave_scan_incl_u32(loc);
+    uint32_t run = x - loc;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int i = lane * PER + q;
+      if (i < EPT * NW) s_col[i] = run;
+      run += v[q];
+    }
+    if (lane == 63) cnt[row * nc + c] = x;
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t* cr = cand + (row * nc + c) * (int64_t)kRowChunk;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const bool take = hi[j] != 0u && (hi[j] >> 21) >= bmin;
+    const uint64_t bal = __ballot(take);
+    if (take) {
+      const uint32_t pos = s_col[j * NW + wave] + (uint32_t)__popcll(bal & lt_mask);
+      const uint32_t t = (uint32_t)(t0 + tid + NT * j);
+      cr[pos] = ((uint64_t)hi[j] << 32) | (uint64_t)(0xFFFFFFFFu - t);
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void row_select_kernel(const uint64_t* __restrict__ cand,
+                                                          const uint32_t* __restrict__ cnt,
+                                                          const uint32_t* __restrict__ ghist,
+                                                          int32_t* __restrict__ out, int nc, int k,
+                                                          int order) {
+  constexpr int NT = 1024, NW = 16, EPT = kRowRegKeys;
+  static_assert(kRowMaxChunks <= NT, "one thread per chunk offset");
+  static_assert(kMaxK == 2 * NT, "the sort covers kMaxK slots with two per thread");
+  __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
+  __shared__ uint64_t sel[kMaxK];
+  __shared__ uint32_t off[kRowMaxChunks + 1];
+  __shared__ uint32_t s_red[NW];
+  __shared__ uint32_t s_col[EPT * NW];
+  __shared__ int s_krem, s_done, s_digit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  // start of each chunk's candidates in the concatenation (chunk order =
+  // position order), and the row histogram
+  const uint32_t cv = tid < nc ? cnt[row * nc + tid] : 0u;
+  const uint32_t xi = wave_scan_incl_u32(cv);
+  if (lane == 63) s_red[wave] = xi;
+  uint32_t tot = 0;
+  for (int i = tid; i < kBins; i += NT) {
+    const uint32_t v = ghist[row * kBins + i];
+    hist[i] = v;
+    tot += v;
+  }
+  __syncthreads();
+  uint32_t wbase = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w < wave) wbase += s_red[w];
+  if (tid < nc) off[tid] = wbase + xi - cv;
+  if (tid == nc - 1) off[nc] = wbase + xi;
+  tot = block_sum<NW>(tot, s_red);  // (its barriers also publish off and hist)
+  const int C = (int)off[nc];
+  const int kk = (int)min((uint32_t)k, tot);  // <= C: every key of the top k is a candidate
+  auto slot = [&](int g) -> int64_t {  // the g-th candidate's slot: last chunk with off <= g
+    int lo = 0, hi = nc;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= (uint32_t)g) lo = mid;
+      else hi = mid;
+    }
+    return (row * nc + lo) * (int64_t)kRowChunk + (g - (int)off[lo]);
+  };
+  // first digit: the threshold bin, from the row histogram (the candidates
+  // are exactly the keys in that bin and above)
+  uint64_t prefix = 0, mask = 0;
+  int krem = kk;
+  bool done = kk == 0;
+  if (kk > 0) {
+    __syncthreads();  // every thread has read s_red before pick_digit reuses it
+    pick_digit<NT>(hist, s_red, kk, tid, lane, wave, &s_krem, &s_done, &s_digit);
+    __syncthreads();
+    prefix = (uint64_t)s_digit << digit_shift(0);
+    mask = (uint64_t)digit_mask(0) << digit_shift(0);
+    krem = s_krem;
+    done = s_done != 0;
+  }
+  if (C <= NT * EPT) {
+    // candidates g = tid + NT j in registers; their order (j, wave, lane) is
+    // the candidate order
+    uint64_t kreg[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int g = tid + NT * j;
+      kreg[j] = g < C ? cand[slot(g)] : 0ull;
+    }
+    for (int pass = 1; pass < 6 && !done; ++pass) {
+      const int shift = digit_shift(pass);
+      const uint32_t dmask = digit_mask(pass);
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        // non-matching keys count into a per-lane spare bin instead of branching
+        const bool m = kreg[j] != 0ull && (kreg[j] & mask) == prefix;
+        atomicAdd(&hist[m ? ((uint32_t)(kreg[j] >> shift) & dmask) : (uint32_t)(kBins + lane)], 1u);
+      }
+      __syncthreads();
+      pick_digit<NT>(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+      __syncthreads();
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= (uint64_t)dmask << shift;
+      krem = s_krem;
+      done = s_done != 0;
+    }
+    // the kk keys >= prefix, in candidate order (ballot column counts, then
+    // an exclusive prefix over them)
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const uint64_t bal = __ballot(kreg[j] != 0ull && kreg[j] >= prefix);
+      if (lane == 0) s_col[j * NW + wave] = (uint32_t)__popcll(bal);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int PER = (EPT * NW + 63) / 64;
+      uint32_t v[PER];
+      uint32_t loc = 0;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        v[q] = s_col[lane * PER + q];
+        loc += v[q];
+      }
+      const uint32_t x = wave_scan_incl_u32(loc);
+      uint32_t run = x - loc;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        s_col[lane * PER + q] = run;
+        run += v[q];
+      }
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const bool take = kreg[j] != 0ull && kreg[j] >= prefix;
+      const uint64_t bal = __ballot(take);
+      if (take) {
+        const uint32_t pos = s_col[j * NW + wave] + (uint32_t)__popcll(bal & lt_mask);
+        if (pos < (uint32_t)kMaxK) sel[pos] = kreg[j];
+      }
+    }
+  } else {
+    // many candidates (ties or a flat row): the same steps streaming from memory
+    for (int pass = 1; pass < 6 && !done; ++pass) {
+      const int shift = digit_shift(pass);
+      const uint32_t dmask = digit_mask(pass);
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (int g = tid; g < C; g += NT) {
+        const uint64_t key = cand[slot(g)];
+        if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      pick_digit<NT>(hist, s_red, krem, tid, lane, wave, &s_krem, &s_done, &s_digit);
+      __syncthreads();
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= (uint64_t)dmask << shift;
+      krem = s_krem;
+      done = s_done != 0;
+    }
+    uint32_t base = 0;
+    for (int g0 = 0; g0 < C; g0 += NT) {
+      const int g = g0 + tid;
+      const uint64_t key = g < C ? cand[slot(g)] : 0ull;
+      const bool take = key != 0ull && key >= prefix;
+      const uint32_t x = wave_scan_incl_u32((uint32_t)take);
+      if (lane == 63) s_red[wave] = x;
+      __syncthreads();
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w < wave) before += s_red[w];
+        all += s_red[w];
+      }
+      const uint32_t pos = base + before + x - (uint32_t)take;
+      if (take && pos < (uint32_t)kMaxK) sel[pos] = key;
+      base += all;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  int32_t* orow = out + row * (int64_t)k;
+  if (order != 0) {  // the compacted list: position order, -1 slots last
+    for (int i = tid; i < k; i += NT)
+      orow[i] = (i < kk) ? (int32_t)(0xFFFFFFFFu - (uint32_t)sel[i]) : -1;
+    return;
+  }
+  sort_store<NT, kMaxK / NT>(sel, kk, k, orow);
+}
+
+// the histogram-threshold path: few rows (every stage of the segmented path
+// would run fewer than 256 workgroups) of more than one segment
+bool use_row_path(int64_t rows, int T) {
+  if (T <= kSegLen) return false;
+  const int64_t nseg = ((int64_t)T + kSegLen - 1) / kSegLen;
+  const int64_t nc = ((int64_t)T + kRowChunk - 1) / kRowChunk;
+  return rows * nseg < 256 && nc <= kRowMaxChunks;
+}
+
+size_t row_path_bytes(int64_t rows, int T) {
+  const int64_t nc = ((int64_t)T + kRowChunk - 1) / kRowChunk;
+  // candidates (one chunk's worth of slots per chunk), histograms, counts
+  return (size_t)rows * nc * kRowChunk * sizeof(uint64_t) + (size_t)rows * kBins * 4 +
+         (size_t)rows * nc * 4;
+}
+
+hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, int T, int k,
+                           void* workspace, hipStream_t st, int order) {
+  const int nc = (int)(((int64_t)T + kRowChunk - 1) / kRowChunk);
+  uint64_t* cand = (uint64_t*)workspace;
+  uint32_t* ghist = (uint32_t*)(cand + rows * nc * (int64_t)kRowChunk);
+  uint32_t* cnt = ghist + rows * kBins;
+  const int nh = (int)(rows * kBins);
+  hipLaunchKernelGGL(row_hist_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, ghist, nh);
+  hipLaunchKernelGGL(row_hist_kernel, dim3((unsigned)(rows * nc)), dim3(256), 0, st, scores, ghist,
+                     T, nc);
+  hipLaunchKernelGGL(row_filter_kernel, dim3((unsigned)(rows * nc)), dim3(256), 0, st, scores,
+                     ghist, cand, cnt, T, nc, k);
+  hipLaunchKernelGGL(row_select_kernel, dim3((unsigned)rows), dim3(1024), 0, st, cand, cnt, ghist,
+                     indices, nc, k, order);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int S, int T, int topk) {
   if (T <= kSegLen) return 0;
   const int64_t rows = (int64_t)B * S;
+  if (use_row_path(rows, T)) return row_path_bytes(rows, T);
   int groups[8];
   const int lv = stage_groups(T, topk, groups, 8);
   // two ping-pong candidate buffers: the first stage output and the largest later one
@@ -493,6 +848,8 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
     if (T <= 4096) return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
     return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
   }
+  if (use_row_path(rows, T))
+    return launch_row_path(scores, indices, rows, T, topk, workspace, st, order);
   int groups[8];
   const int lv = stage_groups(T, topk, groups, 8);
   uint64_t* bufa = (uint64_t*)workspace;

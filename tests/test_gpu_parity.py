@@ -188,6 +188,30 @@ def test_topk_constant_and_all_masked_tail(T, k, order):
     assert got[1, 5:].tolist() == [-1] * (k - 5)
 
 
+# Few rows longer than one segment take the histogram-threshold path
+# (threshold bin from the row's top-11-bit histogram, candidates in and above
+# it, exact selection among them): constant rows (every key in the tie bin,
+# the candidates are the whole row), +-0 ties, -inf tails, rows with fewer
+# valid keys than k, chunk-boundary lengths.
+@pytest.mark.parametrize("R,T,k", [(3, 40000, 2048), (1, 16385, 700), (2, 8192 * 5, 2048),
+                                   (5, 70001, 129)])
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_row_path_edge_rows(R, T, k, order):
+    rng = np.random.default_rng(T + k)
+    sc = rng.standard_normal((R, T)).astype(np.float32)
+    sc[0, :] = 0.25                      # constant row
+    if R > 1:
+        sc[1, ::3] = -0.0                # signed zeros among positives and negatives
+        sc[1, ::2] = 0.0
+    if R > 2:
+        sc[2, 100:] = -np.inf            # 100 valid keys (fewer than k when k > 100)
+    if R > 3:
+        sc[3, :] = np.round(sc[3, :] * 4) / 4  # many exact ties
+    got = _run_topk(sc[None], k, order)[0]
+    ref = oracle.topk(sc, k)
+    np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
+
+
 # Run-to-run determinism: both top-k calls must return the same array twice,
 # order and -1 slots included (the unsorted call's order is its compaction
 # order, which depends only on the scores). Shapes: single-stage rows
