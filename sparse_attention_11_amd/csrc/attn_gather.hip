@@ -28,7 +28,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kG = 4;          // tokens in flight per step
+constexpr int kG = 4;          // tokens in flight per step (G = 8 when a split holds 8 entries)
 constexpr int kMaxSplit = 256;  // splits of one row's selection (merge weights live in LDS)
 
 template <int DT>
@@ -55,8 +55,9 @@ struct Elem<1> {  // bf16
 
 // WIN 0: indices list; WIN 1: window p, p-1, ..., p-window+1.
 // KC / VC: 16-byte chunks per lane of a head's K / V row (chunk c of a row
-// belongs to lane c % 8 of the head's 8 lanes).
-template <int DT, int WIN, int KC, int VC>
+// belongs to lane c % 8 of the head's 8 lanes). G: tokens whose loads are in
+// flight together (a split of G entries waits on a single round of loads).
+template <int DT, int WIN, int KC, int VC, int G>
 __global__ __launch_bounds__(256) void gather_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
     const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
@@ -117,16 +118,16 @@ __global__ __launch_bounds__(256) void gather_kernel(
     if (WIN) return p - le;
     return (ent < e1 && le >= 0) ? irow[le] : -1;
   };
-  int tn[kG];  // positions of the next group (index loads run one group ahead)
+  int tn[G];  // positions of the next group (index loads run one group ahead)
 #pragma unroll
-  for (int g = 0; g < kG; ++g) tn[g] = pos_of(e0 + g);
+  for (int g = 0; g < G; ++g) tn[g] = pos_of(e0 + g);
 
-  for (int base = e0; base < e1; base += kG) {
-    int jrow[kG];
-    bool ok[kG];
-    bool snk[kG];  // wave-uniform: entries are the same for every lane
+  for (int base = e0; base < e1; base += G) {
+    int jrow[G];
+    bool ok[G];
+    bool snk[G];  // wave-uniform: entries are the same for every lane
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int ent = base + g;
       const int t = tn[g];
       const int j = t - kv_offset;
@@ -137,9 +138,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
       jrow[g] = snk[g] ? ent : (ok[g] ? j : 0);
     }
     // all K and V chunks of the group in flight at once
-    u32x4_t kr[kG][KC], vr[kG][VC];
+    u32x4_t kr[G][KC], vr[G][VC];
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
+    for (int g = 0; g < G; ++g) {
       const char* krow =
           snk[g] ? skb + (((int64_t)jrow[g] * HKV + hk) * (int64_t)DQK) * esz
                  : kb + (((kvrow0 + jrow[g]) * HKV + hk) * (int64_t)DQK) * esz;
@@ -158,12 +159,12 @@ __global__ __launch_bounds__(256) void gather_kernel(
       }
     }
 #pragma unroll
-    for (int g = 0; g < kG; ++g) tn[g] = pos_of(base + kG + g);
+    for (int g = 0; g < G; ++g) tn[g] = pos_of(base + G + g);
 
     // logits
-    float x[kG];
+    float x[G];
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
+    for (int g = 0; g < G; ++g) {
       float dot = 0.0f;
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
@@ -180,14 +181,14 @@ __global__ __launch_bounds__(256) void gather_kernel(
     }
     float mx = m;
 #pragma unroll
-    for (int g = 0; g < kG; ++g) mx = fmaxf(mx, x[g]);
+    for (int g = 0; g < G; ++g) mx = fmaxf(mx, x[g]);
     const float muse = (mx == -INFINITY) ? 0.0f : mx;
     const float alpha = exp2_hw(m - muse);
     m = mx;
-    float pg[kG];
+    float pg[G];
     float ps = 0.0f;
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
+    for (int g = 0; g < G; ++g) {
       pg[g] = exp2_hw(x[g] - muse);  // 0 for a skipped slot (x = -inf)
       ps += pg[g];
     }
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
 #pragma unroll
       for (int e = 0; e < EP; ++e) o[i][e] *= alpha;
 #pragma unroll
-    for (int g = 0; g < kG; ++g) {
+    for (int g = 0; g < G; ++g) {
       if (!ok[g]) continue;  // never multiply a skipped row (it may hold anything)
 #pragma unroll
       for (int i = 0; i < VC; ++i) {
@@ -246,6 +247,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int h = (int)(rh % H);
   const int64_t sstride = (int64_t)H * (DV + 4);
   const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 4);
+  // columns: group j of G sums splits j, j + G, ...; thread (j, cg) owns
+  // output columns 4 cg .. 4 cg + 3. Its first kPre splits' columns are
+  // loaded before anything else, together with the (m, l) pairs, so the
+  // workgroup waits on one round of loads; longer lists loop after.
+  const int ncg = DV / 4, G = 256 / ncg;
+  const int cg = tid % ncg, j = tid / ncg;
+  const float* pc = pbase + 4 * cg;
+  // the gate values this thread applies, loaded up front with the rest
+  float graw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (gate_dim == 1) {
+    graw[0] = DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh];
+  } else if (gate_dim > 1 && tid < ncg) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t gi = rh * DV + 4 * tid + c;
+      graw[c] = DT ? bf16_to_f32(((const uint16_t*)gate)[gi]) : ((const float*)gate)[gi];
+    }
+  }
+  constexpr int kPre = 32;
+  float4 x[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int sp = j + G * u;
+    x[u] = (j < G && sp < nsplit) ? *(const float4*)(pc + sp * sstride)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float mt = -INFINITY, lt = 0.0f;
   if (tid < nsplit) {
     mt = pbase[tid * sstride + DV];
@@ -264,32 +291,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
   if (lane == 0) red[1][wave] = L;
-  // columns: group j of G sums splits j, j + G, ...; thread (j, cg) owns
-  // output columns 4 cg .. 4 cg + 3
-  const int ncg = DV / 4, G = 256 / ncg;
-  const int cg = tid % ncg, j = tid / ncg;
   __syncthreads();
   L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (j < G) {
-    const float* pc = pbase + 4 * cg;
-    constexpr int kU = 8;
-    for (int s0 = j; s0 < nsplit; s0 += G * kU) {
-      float4 x[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int sp = s0 + G * u;
-        x[u] = sp < nsplit ? *(const float4*)(pc + sp * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int sp = s0 + G * u;
-        const float ww = sp < nsplit ? wsh[sp] : 0.0f;
-        acc.x = fmaf(x[u].x, ww, acc.x);
-        acc.y = fmaf(x[u].y, ww, acc.y);
-        acc.z = fmaf(x[u].z, ww, acc.z);
-        acc.w = fmaf(x[u].w, ww, acc.w);
-      }
+    for (int u = 0; u < kPre; ++u) {
+      const int sp = j + G * u;
+      const float ww = sp < nsplit ? wsh[sp] : 0.0f;
+      acc.x = fmaf(x[u].x, ww, acc.x);
+      acc.y = fmaf(x[u].y, ww, acc.y);
+      acc.z = fmaf(x[u].z, ww, acc.z);
+      acc.w = fmaf(x[u].w, ww, acc.w);
+    }
+    for (int sp = j + G * kPre; sp < nsplit; sp += G) {
+      const float4 y = *(const float4*)(pc + sp * sstride);
+      const float ww = wsh[sp];
+      acc.x = fmaf(y.x, ww, acc.x);
+      acc.y = fmaf(y.y, ww, acc.y);
+      acc.z = fmaf(y.z, ww, acc.z);
+      acc.w = fmaf(y.w, ww, acc.w);
     }
   }
   accsh[tid] = acc;
@@ -304,18 +325,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     t.w += y.w;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float g1 = 1.0f;
-  if (gate_dim == 1)
-    g1 = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
   const float tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d = 4 * tid + c;
-    float gg = g1;
-    if (gate_dim > 1) {
-      const int64_t gi = rh * DV + d;
-      gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[gi]) : ((const float*)gate)[gi]);
-    }
+    float gg = 1.0f;
+    if (gate_dim == 1) gg = sigmoid_f32(graw[0]);
+    if (gate_dim > 1) gg = sigmoid_f32(graw[c]);
     const float r = tv[c] * inv * gg;
     if (DT)
       ((uint16_t*)out)[rh * DV + d] = f32_to_bf16(r);
@@ -371,10 +387,18 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
   const dim3 grid((unsigned)(rows * pl.nsplit), (H + 31) / 32);
   if (rows * pl.nsplit > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float sl2 = sm_scale * DSA_LOG2E;
-#define DSA_GATHER(DT, WIN, KC, VC)                                                            \
-  hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC>), grid, dim3(256), 0, st, q, k, v, sink_k,  \
-                     sink_v, n_sink, indices, part, S, T, past_len, kv_offset, H, Hkv, Dqk, Dv,  \
+  // splits of 8 entries (few rows: one long selection spread over the GPU)
+  // load all 8 tokens at once; bf16 only (fp32 rows are twice the registers)
+  const bool g8 = dtype == 1 && pl.per_split == 2 * kG;
+#define DSA_GATHER_G(DT, WIN, KC, VC, GG)                                                          \
+  hipLaunchKernelGGL((gather_kernel<DT, WIN, KC, VC, GG>), grid, dim3(256), 0, st, q, k, v, sink_k, \
+                     sink_v, n_sink, indices, part, S, T, past_len, kv_offset, H, Hkv, Dqk, Dv,    \
                      nent, pl.per_split, pl.nsplit, window, sl2)
+#define DSA_GATHER(DT, WIN, KC, VC)              \
+  if (DT == 1 && g8)                             \
+    DSA_GATHER_G(DT, WIN, KC, VC, (DT == 1 ? 2 * kG : kG)); \
+  else                                           \
+    DSA_GATHER_G(DT, WIN, KC, VC, kG)
 #define DSA_GATHER_VC(DT, WIN, KC)            \
   switch (vc) {                               \
     case 1: DSA_GATHER(DT, WIN, KC, 1); break; \
@@ -414,6 +438,7 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
 #undef DSA_GATHER_KC
 #undef DSA_GATHER_VC
 #undef DSA_GATHER
+#undef DSA_GATHER_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nrh = rows * H;

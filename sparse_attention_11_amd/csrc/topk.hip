@@ -506,6 +506,13 @@ int stage_groups(int T, int k, int* groups, int max_levels) {
 constexpr int kRowChunk = 2048;      // scores per chunk: 256 threads x 8
 constexpr int kRowMaxChunks = 1024;  // rows up to 2M scores take this path
 constexpr int kRowRegKeys = 16;      // candidates per select thread kept in registers
+// Copies of each row's histogram: chunk c adds into copy c % kRowHistCopies,
+// and readers sum the copies. Spreads the device-scope atomics of a row's
+// chunks (a single 528385-key row has 259) over more addresses.
+#ifndef DSA_ROW_HIST_COPIES
+#define DSA_ROW_HIST_COPIES 4
+#endif
+constexpr int kRowHistCopies = DSA_ROW_HIST_COPIES;
 
 __global__ __launch_bounds__(256) void row_hist_zero_kernel(uint32_t* __restrict__ h, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -534,9 +541,17 @@ __global__ __launch_bounds__(256) void row_hist_kernel(const float* __restrict__
   for (int j = 0; j < EPT; ++j)
     if (f[j] != -INFINITY) atomicAdd(&h[orderable_key(f[j]) >> 21], 1u);
   __syncthreads();
-  uint32_t* gr = ghist + row * kBins;
+  uint32_t* gr = ghist + (row * kRowHistCopies + c % kRowHistCopies) * kBins;
   for (int i = tid; i < kBins; i += 256)
     if (h[i]) atomicAdd(&gr[i], h[i]);
+}
+
+// bin i of a row's histogram: the sum of its copies
+__device__ __forceinline__ uint32_t row_bin(const uint32_t* __restrict__ ghist, int64_t row, int i) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int cp = 0; cp < kRowHistCopies; ++cp) v += ghist[(row * kRowHistCopies + cp) * kBins + i];
+  return v;
 }
 
 __global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict__ scores,
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict
   }
   uint32_t tot = 0;
   for (int i = tid; i < kBins; i += NT) {
-    const uint32_t v = ghist[row * kBins + i];
+    const uint32_t v = row_bin(ghist, row, i);
     h[i] = v;
     tot += v;
   }
@@ -644,7 +659,7 @@ __global__ __launch_bounds__(1024) void row_select_kernel(const uint64_t* __rest
   if (lane == 63) s_red[wave] = xi;
   uint32_t tot = 0;
   for (int i = tid; i < kBins; i += NT) {
-    const uint32_t v = ghist[row * kBins + i];
+    const uint32_t v = row_bin(ghist, row, i);
     hist[i] = v;
     tot += v;
   }
@@ -806,8 +821,8 @@ bool use_row_path(int64_t rows, int T) {
 size_t row_path_bytes(int64_t rows, int T) {
   const int64_t nc = ((int64_t)T + kRowChunk - 1) / kRowChunk;
   // candidates (one chunk's worth of slots per chunk), histograms, counts
-  return (size_t)rows * nc * kRowChunk * sizeof(uint64_t) + (size_t)rows * kBins * 4 +
-         (size_t)rows * nc * 4;
+  return (size_t)rows * nc * kRowChunk * sizeof(uint64_t) +
+         (size_t)rows * kRowHistCopies * kBins * 4 + (size_t)rows * nc * 4;
 }
 
 hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, int T, int k,
@@ -815,8 +830,8 @@ hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, 
   const int nc = (int)(((int64_t)T + kRowChunk - 1) / kRowChunk);
   uint64_t* cand = (uint64_t*)workspace;
   uint32_t* ghist = (uint32_t*)(cand + rows * nc * (int64_t)kRowChunk);
-  uint32_t* cnt = ghist + rows * kBins;
-  const int nh = (int)(rows * kBins);
+  uint32_t* cnt = ghist + rows * kRowHistCopies * kBins;
+  const int nh = (int)(rows * kRowHistCopies * kBins);
   hipLaunchKernelGGL(row_hist_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, ghist, nh);
   hipLaunchKernelGGL(row_hist_kernel, dim3((unsigned)(rows * nc)), dim3(256), 0, st, scores, ghist,
                      T, nc);
