@@ -163,9 +163,27 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * DV];
 
+  // XCD-aware order (selection-mask calls). Workgroups are dealt to the 8
+  // XCDs round-robin by their linear id; this maps XCD x's share to one
+  // contiguous range of the logical (item fastest, then head, then batch)
+  // order, so the tiles running together on an XCD are mostly of one head and
+  // stream the same K/V blocks (from key 0 up) through that XCD's L2 instead
+  // of each XCD pulling every head's K/V from memory (dsa-s32k: 285 -> 152 GB
+  // fetched per launch, 49.6 -> 46.2 ms). Window tiles read short, different
+  // key ranges and keep the plain order.
+  int item = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (MASK == 0) {
+    const int64_t nx = gridDim.x, ny = gridDim.y;
+    const int64_t N = nx * ny * gridDim.z;
+    const int64_t L = blockIdx.x + nx * (blockIdx.y + ny * (int64_t)blockIdx.z);
+    const int64_t x = L % 8, q8 = N / 8, r8 = N % 8;
+    const int64_t lg = x * q8 + (x < r8 ? x : r8) + L / 8;
+    item = (int)(lg % nx);
+    h = (int)((lg / nx) % ny);
+    b = (int)(lg / (nx * ny));
+  }
   int qt, split, nsplit;
-  if (!item_tile(blockIdx.x, nqt, M, tab, &qt, &split, &nsplit)) return;
-  const int h = blockIdx.y, b = blockIdx.z;
+  if (!item_tile(item, nqt, M, tab, &qt, &split, &nsplit)) return;
   const int hk = h / (H / HKV);  // cache head: query heads come in groups of H / HKV
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
@@ -415,7 +433,7 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   // ---- normalise, gate, store
   const float ltot = l + shfl_xor_f(l, 32);
   if (nsplit > 1) {  // partial state (unnormalised O, max, sum) for the merge kernel
-    float* pp = part + ((((int64_t)b * H + h) * gridDim.x + blockIdx.x) * kBQ + 32 * wave + ln) *
+    float* pp = part + ((((int64_t)b * H + h) * gridDim.x + item) * kBQ + 32 * wave + ln) *
                            (DV + 4);
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
