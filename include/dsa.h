@@ -57,6 +57,7 @@ extern "C" {
 #define DSA_ERR_UNSUPPORTED 2 /* valid but not implemented (head dims, topk > DSA_MAX_TOPK) */
 #define DSA_ERR_WORKSPACE 3   /* workspace pointer null or smaller than the *_workspace_size */
 #define DSA_ERR_HIP 4         /* a HIP launch failed; dsa_last_error() holds the message */
+#define DSA_ERR_CHECK 5       /* debug builds only: a device-side check failed (see below) */
 
 /* dtype */
 #define DSA_F32 0
@@ -413,6 +414,19 @@ int dsa_sparse_attn_decode_noalloc(const void* q, const void* k_cache, const voi
                                    int T, int H, int qk_nope_dim, int qk_rope_dim, int v_dim,
                                    int topk, float sm_scale, int gate_dim, int dtype,
                                    hipStream_t stream);
+
+/* Debug builds. libdsa_debug.so is the same library compiled with
+ * -DDSA_DEBUG: its kernels also check the invariants they rely on (indices
+ * inside their buffers, the number of keys a selection must hold, work items
+ * inside the launch plan). A failed check does not stop the kernel; it is
+ * counted in device memory, and every call of a debug build then
+ * synchronizes the device (so it must not be captured into a graph) and
+ * returns DSA_ERR_CHECK, with dsa_last_error() naming the source file, line
+ * and two values of the first failure. Outputs of a debug build are
+ * bit-identical to the release build's. Returns 1 in a debug build, else 0.
+ * Callers: tests and tools that want the checks; production code links the
+ * release build. */
+int dsa_debug_build(void);
 
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int status);

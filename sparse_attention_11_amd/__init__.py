@@ -21,7 +21,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
-DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP, DSA_ERR_CHECK = range(6)
 DSA_F32, DSA_BF16 = 0, 1
 RELU_PER_HEAD, RELU_NONE, RELU_POST_SUM = 0, 1, 2
 MAX_TOPK = 2048
@@ -38,7 +38,7 @@ _EXPORTS = [
     "dsa_index_quant_fp8", "dsa_index_scores_fp8",
     "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
     "dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc",
-    "dsa_mla_prologue_workspace_size", "dsa_mla_prologue",
+    "dsa_mla_prologue_workspace_size", "dsa_mla_prologue", "dsa_debug_build",
 ]
 MAX_SINKS = 256
 
@@ -50,6 +50,18 @@ class DsaError(RuntimeError):
 
 
 _lib = None
+
+# The same library compiled with -DDSA_DEBUG (device-side checks; include/dsa.h).
+DEBUG_LIB_PATH = os.path.join(_PKG, "libdsa_debug.so")
+
+
+def use_library(path: str) -> str:
+    """Make later calls go to the library at `path` (for example
+    DEBUG_LIB_PATH); returns the path in use before."""
+    global LIB_PATH, _lib
+    prev = LIB_PATH
+    LIB_PATH, _lib = path, None
+    return prev
 
 
 def lib():
@@ -117,6 +129,8 @@ def lib():
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.argtypes = []
         L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_debug_build.argtypes = []
+        L.dsa_debug_build.restype = i32
         _lib = L
     return _lib
 
@@ -473,6 +487,10 @@ def dsa_status_string(status: int) -> str:
 
 def dsa_last_error() -> str:
     return lib().dsa_last_error().decode()
+
+
+def dsa_debug_build() -> bool:
+    return bool(lib().dsa_debug_build())
 
 
 def dsa_mla_prologue_workspace_size(B: int, S: int, kv_lora_rank: int) -> int:

@@ -27,9 +27,45 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+#ifdef DSA_DEBUG
+// Debug builds: wait for the call's kernels, then read (and clear) every
+// kernel file's device check record; the first failure found is reported.
+int debug_check(const char* fn) {
+  const hipError_t se = hipDeviceSynchronize();
+  if (se != hipSuccess)
+    return fail(DSA_ERR_HIP, "%s: HIP error %d (%s) while running", fn, (int)se, hipGetErrorString(se));
+  struct Src {
+    const char* file;
+    int (*take)(dsa::DebugRecord*);
+  };
+  const Src srcs[] = {{"attn_gather.hip", dsa::debug_take_attn_gather},
+                      {"attn_prefill.hip", dsa::debug_take_attn_prefill},
+                      {"index_fp8.hip", dsa::debug_take_index_fp8},
+                      {"index_scores.hip", dsa::debug_take_index_scores},
+                      {"prologue.hip", dsa::debug_take_prologue},
+                      {"topk.hip", dsa::debug_take_topk}};
+  int status = DSA_OK;
+  for (const Src& s : srcs) {  // every record is read, so none carries over to the next call
+    dsa::DebugRecord r;
+    const int t = s.take(&r);
+    if (status != DSA_OK) continue;
+    if (t < 0) status = fail(DSA_ERR_HIP, "%s: reading the check record of %s failed", fn, s.file);
+    if (t > 0)
+      status = fail(DSA_ERR_CHECK, "%s: device check failed in %s line %d (values %lld, %lld); %u failed checks",
+                    fn, s.file, r.line, r.a, r.b, r.count);
+  }
+  return status;
+}
+#endif
+
 int hip_status(hipError_t e, const char* fn) {
-  if (e == hipSuccess) return DSA_OK;
-  return fail(DSA_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  if (e != hipSuccess)
+    return fail(DSA_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+#ifdef DSA_DEBUG
+  return debug_check(fn);
+#else
+  return DSA_OK;
+#endif
 }
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -258,11 +294,20 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
     case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    case DSA_ERR_CHECK: return "DSA_ERR_CHECK";
     default: return "DSA_ERR_UNKNOWN";
   }
 }
 
 const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int dsa_debug_build(void) {
+#ifdef DSA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
                      int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
       if (WIN) ok[g] = ok[g] && ent - n_sink < window;
       if (snk[g]) ok[g] = ent < e1;
       jrow[g] = snk[g] ? ent : (ok[g] ? j : 0);
+      DSA_CHECK(!ok[g] || (jrow[g] >= 0 && jrow[g] < (snk[g] ? n_sink : Tbuf)), jrow[g], ent);
     }
     // all K and V chunks of the group in flight at once
     u32x4_t kr[G][KC], vr[G][VC];
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int h = (int)(rh % H);
   const int64_t sstride = (int64_t)H * (DV + 4);
   const float* pbase = part + (row * nsplit * H + h) * (int64_t)(DV + 4);
+  if (threadIdx.x == 0) DSA_CHECK(nsplit >= 1 && nsplit <= kMaxSplit, nsplit, kMaxSplit);
   // columns: group j of G sums splits j, j + G, ...; thread (j, cg) owns
   // output columns 4 cg .. 4 cg + 3. Its first kPre splits' columns are
   // loaded before anything else, together with the (m, l) pairs, so the
@@ -366,6 +368,10 @@ Plan make_plan(int64_t rows, int H, int64_t nent_in) {
 }
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(attn_gather)
+#endif
 
 size_t gather_workspace_bytes(int64_t rows, int H, int Dv, int64_t nentries) {
   // sized for the bound, so a call with fewer entries (a window clamped to the

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void bitmap_lds_kernel(const int32_t* __restri
   extern __shared__ uint32_t sbits[];
   const int64_t row = blockIdx.x;
   const int p = P + (int)(row % S);
+  if (threadIdx.x == 0) DSA_CHECK(p < T && (int64_t)W32 * 32 >= T, p, T);  // the query's row exists
   for (int i = threadIdx.x; i < W32; i += blockDim.x) sbits[i] = 0;
   __syncthreads();
   const int32_t* ir = idx + row * topk;
@@ -184,6 +185,8 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   }
   int qt, split, nsplit;
   if (!item_tile(item, nqt, M, tab, &qt, &split, &nsplit)) return;
+  DSA_CHECK(qt >= 0 && qt < nqt && split >= 0 && split < nsplit, qt, split);
+  DSA_CHECK(h < H && (nsplit == 1 || part != nullptr), h, nsplit);
   const int hk = h / (H / HKV);  // cache head: query heads come in groups of H / HKV
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
@@ -207,6 +210,7 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   // (64-bit: M is INT_MAX when tiles are not split)
   const int jlo = (int)((int64_t)tjlo + (int64_t)split * M * kBN);
   const int jhi = (int)std::min<int64_t>(tjhi, (int64_t)jlo + (int64_t)M * kBN - 1);
+  DSA_CHECK(jlo >= 0 && jhi < Tbuf, jlo, jhi);  // the item's key blocks lie in the buffer
   const int64_t kvrow0 = (int64_t)b * Tbuf;
   // Blocks of this item: first the attention-sink rows (split 0 only, every
   // query sees all of them, no position), then the cache rows jlo .. jhi.
@@ -497,6 +501,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
   // first item of this tile and its number of splits
   const int base = tab.start[nqt - 1 - qt];
   const int c = tab.start[nqt - qt] - base;
+  DSA_CHECK(c >= 1 && base + c <= items, base, c);
   if (c <= 1 || (int)threadIdx.x >= TPR * kMergeRows) return;
   const int qi = rg * kMergeRows + threadIdx.x / TPR, dv0 = 4 * (threadIdx.x % TPR);
   const int s = qt * kBQ + qi;
@@ -620,6 +625,10 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 constexpr int kBitmapLdsMaxWords = 12288;  // 48 KiB of LDS
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(attn_prefill)
+#endif
 
 bool prefill_mfma_supported(int dtype, int S, int Dqk, int Dv) {
   if (dtype != 1 || S < 16) return false;

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"  // (struct DebugRecord)
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // MFMA bf16 operand (16 B / lane)
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -196,3 +198,40 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int m, int lane) {
 
 // Lane-swap helpers (wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// ---------------------------------------------------------------- checks
+// -DDSA_DEBUG builds: DSA_CHECK(cond, a, b) asserts an invariant a kernel
+// relies on (an index inside its buffer, a count the algorithm fixes). A
+// failure neither traps nor stops the kernel: it counts into this file's
+// device record (struct DebugRecord, kernels.h) and keeps the first failure's
+// line and the two values; the C ABI of a debug build synchronizes after each
+// call and reports a non-zero count as DSA_ERR_CHECK. Release builds compile
+// every check out. DSA_DEBUG_TAKE(name) defines the host function that reads
+// and clears the record of the file it is placed in.
+#ifdef DSA_DEBUG
+static __device__ dsa::DebugRecord g_debug_record;
+__device__ __noinline__ static void debug_fail(int line, long long a, long long b) {
+  if (atomicAdd(&g_debug_record.count, 1u) == 0u) {
+    g_debug_record.line = line;
+    g_debug_record.a = a;
+    g_debug_record.b = b;
+  }
+}
+#define DSA_CHECK(cond, a, b)                                          \
+  do {                                                                 \
+    if (!(cond)) debug_fail(__LINE__, (long long)(a), (long long)(b)); \
+  } while (0)
+#define DSA_DEBUG_TAKE(name)                                                                    \
+  int debug_take_##name(DebugRecord* out) {                                                     \
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_debug_record), sizeof(DebugRecord)) != hipSuccess) \
+      return -1;                                                                                \
+    if (out->count == 0u) return 0;                                                             \
+    const DebugRecord zero = {0u, 0, 0, 0};                                                     \
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_debug_record), &zero, sizeof(DebugRecord)) ==         \
+                   hipSuccess                                                                   \
+               ? 1                                                                              \
+               : -1;                                                                            \
+  }
+#else
+#define DSA_CHECK(cond, a, b) ((void)0)
+#endif

@@ -137,6 +137,7 @@ __global__ __launch_bounds__(256, 2) void idx8_tile_kernel(
   IdxTile tile;
   if (!idx_tile_of(blockIdx.x, 16, S, P, nqt, nkt, npairs, maxlen, &tile)) return;
   const int qt = tile.qt, kt = tile.kt;
+  DSA_CHECK(qt >= 0 && qt < nqt && kt >= 0 && kt < nkt, qt, kt);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,6 +268,10 @@ __global__ __launch_bounds__(256, 2) void idx8_tile_kernel(
 }
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(index_fp8)
+#endif
 
 hipError_t launch_quant_fp8(const void* x, uint8_t* codes, float* scales, int64_t rows, int dim,
                             hipStream_t st) {

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
   IdxTile2 tile;
   if (!idx_tile2_of(blockIdx.x, kTileQ, S, P, nqt, nkt, npairs, maxlen, two != 0, &tile)) return;
   const int kt = tile.kt;
+  DSA_CHECK(tile.q1 >= 0 && tile.q1 < nqt && kt >= 0 && kt < nkt, tile.q1, kt);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 31, lh = lane >> 5;
   const int tbase = (blockIdx.x * 4 + wave) * KPW;
+  DSA_CHECK(p < T, p, T);  // the query's own key exists
   float* orow = scores + row * T;
   if (tbase >= T) return;
 
@@ -425,6 +427,10 @@ hipError_t dispatch_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* w
 }
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(index_scores)
+#endif
 
 hipError_t launch_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores,
                                int B, int S, int T, int past_len, int HI, int DI, float scale,

@@ -91,4 +91,23 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 hipError_t static_scratch(void** ptr);
 
+// Device-side checks of -DDSA_DEBUG builds (common.h: DSA_CHECK). Each kernel
+// file keeps one record in device memory: the number of failed checks since it
+// was last read, and the first failure's source line and two values.
+struct DebugRecord {
+  unsigned int count;
+  int line;
+  long long a, b;
+};
+#ifdef DSA_DEBUG
+// Copy a file's record to *out and clear it (synchronous). Returns 1 if a
+// check failed, 0 if none did, -1 if the copy failed.
+int debug_take_attn_gather(DebugRecord* out);
+int debug_take_attn_prefill(DebugRecord* out);
+int debug_take_index_fp8(DebugRecord* out);
+int debug_take_index_scores(DebugRecord* out);
+int debug_take_prologue(DebugRecord* out);
+int debug_take_topk(DebugRecord* out);
+#endif
+
 }  // namespace dsa

@@ -121,6 +121,7 @@ template <int EPI>
 __device__ __forceinline__ void mla_store4(const GemmMla& e, int m, int n, float* x) {
   const int b = m / e.S, s = m - b * e.S, p = e.P + s;
   const int Dqk = e.N + e.R;
+  DSA_CHECK(p < e.T || EPI == 1, p, e.T);  // cache rows past_len + s exist
   if (EPI == 1) {  // q_gate_proj: head h = [query (Dqk) | gate (Dv)]
     const int W = Dqk + e.Dv, h = n / W, c = n - h * W;
     if (c < Dqk) {
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(256) void ln_rope_k_kernel(const uint16_t* __restri
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int b = (int)(m / S), s = (int)(m % S), p = P + s;
   const int half = R / 2, r0 = D - R;
+  DSA_CHECK(p < T, p, T);  // the key's cache row exists
   uint16_t* out = kcache + ((int64_t)b * T + p) * D;
   for (int c = 0; c < per; ++c) {
     const int d = lane + 64 * c;
@@ -415,6 +417,10 @@ __global__ __launch_bounds__(256) void ln_rope_k_kernel(const uint16_t* __restri
 }
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(prologue)
+#endif
 
 namespace {
 hipError_t gemm_launch(GemmA ga, GemmOut o1, GemmOut o2, int M, int K, const GemmRope* rp,

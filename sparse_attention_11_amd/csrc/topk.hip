@@ -241,6 +241,7 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
   }
   const int nvalid = (int)block_sum<NW>(valid, s_red);
   const int kk = min(k, nvalid);
+  DSA_CHECK(kk <= kSel, kk, kSel);
 
   // Register path on score input: the selection is decided on the 32-bit
   // score key alone; ties at the threshold are resolved by position rank.
@@ -327,6 +328,13 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       if (w < wave) base += s_red[w];
+#ifdef DSA_DEBUG
+    if (tid == 0) {  // the selection holds exactly kk keys
+      uint32_t tot = 0;
+      for (int w = 0; w < NW; ++w) tot += s_red[w];
+      DSA_CHECK(tot == (uint32_t)kk, tot, kk);
+    }
+#endif
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       if ((takebits >> j) & 1ull) {
@@ -391,6 +399,13 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
 #pragma unroll
         for (int w = 0; w < NW; ++w)
           if (w < wave) base += s_red[w];
+#ifdef DSA_DEBUG
+        if (tid == 0) {  // the keys >= the threshold are exactly kk
+          uint32_t tot = 0;
+          for (int w = 0; w < NW; ++w) tot += s_red[w];
+          DSA_CHECK(tot == (uint32_t)kk, tot, kk);
+        }
+#endif
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
           if ((takebits >> j) & 1ull) {
@@ -411,6 +426,7 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
     __syncthreads();
   }
 
+  if (EPT == 0 && SRC == 1 && tid == 0) DSA_CHECK(s_cnt == (uint32_t)kk || kk == 0, s_cnt, kk);
   if (DST == 1) {  // first stage of a long row: unsorted candidates
     uint64_t* o = out_keys + ((int64_t)row * nseg + seg) * k;
     for (int i = tid; i < k; i += NT) o[i] = (i < kk) ? sel[i] : 0ull;
@@ -619,7 +635,10 @@ __global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict
       if (i < EPT * NW) s_col[i] = run;
       run += v[q];
     }
-    if (lane == 63) cnt[row * nc + c] = x;
+    if (lane == 63) {
+      DSA_CHECK(x <= (uint32_t)n, x, n);
+      cnt[row * nc + c] = x;
+    }
   }
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -673,6 +692,7 @@ __global__ __launch_bounds__(1024) void row_select_kernel(const uint64_t* __rest
   tot = block_sum<NW>(tot, s_red);  // (its barriers also publish off and hist)
   const int C = (int)off[nc];
   const int kk = (int)min((uint32_t)k, tot);  // <= C: every key of the top k is a candidate
+  if (tid == 0) DSA_CHECK(kk <= C, kk, C);
   auto slot = [&](int g) -> int64_t {  // the g-th candidate's slot: last chunk with off <= g
     int lo = 0, hi = nc;
     while (hi - lo > 1) {
@@ -742,6 +762,7 @@ __global__ __launch_bounds__(1024) void row_select_kernel(const uint64_t* __rest
         loc += v[q];
       }
       const uint32_t x = wave_scan_incl_u32(loc);
+      if (lane == 63) DSA_CHECK(x == (uint32_t)kk, x, kk);  // exactly kk keys >= prefix
       uint32_t run = x - loc;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -798,6 +819,7 @@ __global__ __launch_bounds__(1024) void row_select_kernel(const uint64_t* __rest
       base += all;
       __syncthreads();
     }
+    if (tid == 0) DSA_CHECK(base == (uint32_t)kk, base, kk);
   }
   __syncthreads();
   int32_t* orow = out + row * (int64_t)k;
@@ -843,6 +865,10 @@ hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, 
 }
 
 }  // namespace
+
+#ifdef DSA_DEBUG
+DSA_DEBUG_TAKE(topk)
+#endif
 
 size_t topk_workspace_bytes(int B, int S, int T, int topk) {
   if (T <= kSegLen) return 0;

@@ -21,15 +21,32 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
-def test_library_exports_every_declared_symbol():
+@pytest.mark.parametrize("path", [dsa.LIB_PATH, dsa.DEBUG_LIB_PATH], ids=["release", "debug"])
+def test_library_exports_every_declared_symbol(path):
     names = declared_functions()
     assert set(names) == set(dsa._EXPORTS), names
-    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
         assert n in exported, n
         assert hasattr(dsa.lib(), n)
+
+
+def test_debug_build_flag_and_validation():
+    """libdsa_debug.so reports itself as the debug build and validates
+    arguments exactly as the release build does (before any HIP call)."""
+    rel, dbg = ctypes.CDLL(dsa.LIB_PATH), ctypes.CDLL(dsa.DEBUG_LIB_PATH)
+    assert rel.dsa_debug_build() == 0 and dbg.dsa_debug_build() == 1
+    for L in (rel, dbg):
+        L.dsa_topk.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + [ctypes.c_void_p,
+                                                                           ctypes.c_size_t,
+                                                                           ctypes.c_void_p]
+        assert L.dsa_topk(P, P, 1, 4, 100, 0, None, 0, None) == 1      # topk < 1
+        assert L.dsa_topk(P, P, 1, 4, 5000, 4096, None, 0, None) == 2  # topk > DSA_MAX_TOPK
+        assert L.dsa_topk(P, P, 1, 4, 50000, 2048, None, 0, None) == 3  # no workspace
+    dbg.dsa_status_string.restype = ctypes.c_char_p
+    assert dbg.dsa_status_string(5) == b"DSA_ERR_CHECK"
 
 
 def test_status_strings():
@@ -39,6 +56,7 @@ def test_status_strings():
     assert L.dsa_status_string(2) == b"DSA_ERR_UNSUPPORTED"
     assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
     assert L.dsa_status_string(4) == b"DSA_ERR_HIP"
+    assert L.dsa_status_string(5) == b"DSA_ERR_CHECK"
 
 
 def idx(**kw):
