@@ -166,6 +166,26 @@ int dsa_topk_unsorted(const float* scores, int32_t* indices, int B, int S, int T
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Indexer and top-k in one call ([AXK2] "Sparse Gated Attention": the
+ * indexer's scores exist only to choose each query's index_topk positions).
+ * indices[b,s,:] are exactly what dsa_index_scores followed by dsa_topk
+ * (sorted = 1) or dsa_topk_unsorted (sorted = 0) return on the same inputs.
+ * The scores live in the workspace, and only the causally visible part of
+ * each row (t <= past_len + s) is written and read: the -inf upper triangle
+ * of the two-call path is neither stored nor scanned.
+ * Arguments, limits and status codes: those of dsa_index_scores (without
+ * `scores`) and of dsa_topk; `sorted` must be 0 or 1. workspace: at least
+ * dsa_index_topk_workspace_size(B, S, T, topk) bytes (B*S*T fp32 scores,
+ * then the top-k's own workspace); the size query returns 0 for sizes the
+ * call rejects.
+ */
+size_t dsa_index_topk_workspace_size(int B, int S, int T, int topk);
+int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w, int32_t* indices, int B,
+                   int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
+                   int relu_mode, int dtype, int topk, int sorted, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sparse MLA attention over the selected expanded K/V rows, prefill
  * ([AXK2] "MLA + explicit sparse mask" steps 3-5: the cache holds expanded
  * K/V; the indexer's positions form an additive mask, combined with the

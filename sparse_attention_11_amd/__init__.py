@@ -39,6 +39,7 @@ _EXPORTS = [
     "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
     "dsa_prefill_work_plan", "dsa_sparse_attn_decode_noalloc",
     "dsa_mla_prologue_workspace_size", "dsa_mla_prologue", "dsa_debug_build",
+    "dsa_index_topk_workspace_size", "dsa_index_topk",
 ]
 MAX_SINKS = 256
 
@@ -129,6 +130,10 @@ def lib():
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.argtypes = []
         L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_index_topk_workspace_size.argtypes = [i32] * 4
+        L.dsa_index_topk_workspace_size.restype = sz
+        L.dsa_index_topk.argtypes = [vp] * 4 + [i32] * 6 + [f32] + [i32] * 4 + [vp, sz, vp]
+        L.dsa_index_topk.restype = i32
         L.dsa_debug_build.argtypes = []
         L.dsa_debug_build.restype = i32
         _lib = L
@@ -188,6 +193,30 @@ def dsa_index_scores(q_idx, k_idx, w, scores, past_len: int, scale: float | None
         _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, S, T, past_len, HI, DI, scale,
         relu_mode, _dtype(q_idx), _stream(stream)))
     return scores
+
+
+def dsa_index_topk_workspace_size(B: int, S: int, T: int, topk: int) -> int:
+    return int(lib().dsa_index_topk_workspace_size(B, S, T, topk))
+
+
+def dsa_index_topk(q_idx, k_idx, w, indices, past_len: int, scale: float | None = None,
+                   relu_mode: int = RELU_PER_HEAD, sorted: bool = True, workspace=None,
+                   stream=None):
+    """dsa_index_scores + dsa_topk (or dsa_topk_unsorted) in one call; the
+    scores stay in the workspace. indices [B,S,topk] int32."""
+    B, S, HI, DI = q_idx.shape
+    T = k_idx.shape[1]
+    topk = indices.shape[-1]
+    if scale is None:
+        scale = DI ** -0.5
+    if workspace is None:
+        workspace = _workspace(dsa_index_topk_workspace_size(B, S, T, topk), q_idx)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_index_topk", lib().dsa_index_topk(
+        _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(indices), B, S, T, past_len, HI, DI, scale,
+        relu_mode, _dtype(q_idx), topk, 1 if sorted else 0, _ptr(workspace), nbytes,
+        _stream(stream)))
+    return indices
 
 
 def dsa_topk_workspace_size(B: int, S: int, T: int, topk: int) -> int:

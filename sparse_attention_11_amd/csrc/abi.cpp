@@ -309,12 +309,11 @@ int dsa_debug_build(void) {
 #endif
 }
 
-int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
-                     int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
-                     int relu_mode, int dtype, hipStream_t stream) {
-  const char* fn = "dsa_index_scores";
-  g_err.clear();
-  if (!q_idx || !k_idx || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+// Checks of the indexer's arguments (dsa_index_scores, dsa_index_topk).
+static int check_index(const char* fn, const void* q_idx, const void* k_idx, const void* w,
+                       const void* out, int B, int S, int T, int past_len, int n_idx_heads,
+                       int idx_dim, float scale, int relu_mode, int dtype) {
+  if (!q_idx || !k_idx || !w || !out) return fail(DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || S < 1 || T < 1 || n_idx_heads < 1 || idx_dim < 1 || past_len < 0)
     return fail(DSA_ERR_INVALID_ARG, "%s: sizes must be >= 1 and past_len >= 0", fn);
   if ((long long)past_len + S > T)
@@ -333,9 +332,56 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float*
     return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d index heads", fn, kMaxIndexHeads);
   if (!keys_ok(T)) return fail(DSA_ERR_UNSUPPORTED, "%s: more than %d keys", fn, kMaxKeys);
   if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+  return DSA_OK;
+}
+
+int dsa_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores, int B,
+                     int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
+                     int relu_mode, int dtype, hipStream_t stream) {
+  const char* fn = "dsa_index_scores";
+  g_err.clear();
+  const int st = check_index(fn, q_idx, k_idx, w, scores, B, S, T, past_len, n_idx_heads, idx_dim,
+                             scale, relu_mode, dtype);
+  if (st) return st;
   return hip_status(dsa::launch_index_scores(q_idx, k_idx, w, scores, B, S, T, past_len,
                                              n_idx_heads, idx_dim, scale, relu_mode, dtype,
                                              stream),
+                    fn);
+}
+
+size_t dsa_index_topk_workspace_size(int B, int S, int T, int topk) {
+  if (B < 1 || S < 1 || T < 1 || topk < 1 || topk > T || topk > DSA_MAX_TOPK || !rows_ok(B, S) ||
+      !keys_ok(T))
+    return 0;
+  const size_t scores = ((size_t)B * S * T * sizeof(float) + 255) / 256 * 256;
+  return scores + dsa::topk_workspace_bytes(B, S, T, topk);
+}
+
+int dsa_index_topk(const void* q_idx, const void* k_idx, const void* w, int32_t* indices, int B,
+                   int S, int T, int past_len, int n_idx_heads, int idx_dim, float scale,
+                   int relu_mode, int dtype, int topk, int sorted, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_index_topk";
+  g_err.clear();
+  int st = check_index(fn, q_idx, k_idx, w, indices, B, S, T, past_len, n_idx_heads, idx_dim,
+                       scale, relu_mode, dtype);
+  if (st) return st;
+  if (topk < 1 || topk > T)
+    return fail(DSA_ERR_INVALID_ARG, "%s: topk must be in [1, T] (topk %d, T %d)", fn, topk, T);
+  if (topk > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "%s: topk %d > %d", fn, topk, DSA_MAX_TOPK);
+  if (sorted != 0 && sorted != 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: sorted must be 0 or 1 (got %d)", fn, sorted);
+  st = check_ws(fn, workspace, workspace_bytes, dsa_index_topk_workspace_size(B, S, T, topk));
+  if (st) return st;
+  float* scores = (float*)workspace;
+  void* tk = (char*)workspace + ((size_t)B * S * T * sizeof(float) + 255) / 256 * 256;
+  // scores of t <= past_len + s only; the top-k reads no further
+  const hipError_t e = dsa::launch_index_scores(q_idx, k_idx, w, scores, B, S, T, past_len,
+                                                n_idx_heads, idx_dim, scale, relu_mode, dtype,
+                                                stream, /*fill_masked=*/false);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(dsa::launch_topk(scores, indices, B, S, T, topk, tk, stream, sorted ? 0 : 1,
+                                     past_len),
                     fn);
 }
 

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
                                                           float* __restrict__ scores, int S,
                                                           int T, int P, int HI, float scale,
                                                           int nqt, int nkt, int npairs,
-                                                          int maxlen, int two) {
+                                                          int maxlen, int two, int fill) {
   constexpr int kQG = QG;
   constexpr int kTileQ = 16 * QG;                      // queries per workgroup (MFMA N axis)
   constexpr int KS = DI / 32;                          // 32-dim steps per head
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
     }
   }
   }  // query tiles
-  idx_fill_upper2<kTileQ>(scores, tile, b, S, T, nkt, vec);
+  if (fill) idx_fill_upper2<kTileQ>(scores, tile, b, S, T, nkt, vec);
 }
 
 // Few queries per call: MFMA M = index heads (NHB blocks of 32), N = 32 keys.
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ w,
                                                        float* __restrict__ scores, int S, int T,
-                                                       int P, int HI, float scale) {
+                                                       int P, int HI, float scale, int fill) {
   constexpr int KS = DI / 16;
   constexpr int NB = KPW / 32;
   const int64_t row = blockIdx.y;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
   if (tbase >= T) return;
 
   if (tbase > p) {  // the whole wave is above the diagonal
-    for (int kb = 0; kb < NB; ++kb) {
+    for (int kb = 0; kb < NB && fill; ++kb) {
       const int t = tbase + 32 * kb + ln;
       if (lh == 0 && t < T) orow[t] = -INFINITY;
     }
@@ -327,14 +327,14 @@ __global__ __launch_bounds__(256) void idx_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ w,
                                                       float* __restrict__ scores, int S, int T,
                                                       int P, int HI, int DI, float scale,
-                                                      int mode) {
+                                                      int mode, int fill) {
   const int64_t row = blockIdx.y;
   const int b = (int)(row / S), s = (int)(row % S);
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   float* out = scores + row * T + t;
   if (t > P + s) {
-    *out = -INFINITY;
+    if (fill) *out = -INFINITY;
     return;
   }
   const float* kp = k + ((int64_t)b * T + t) * DI;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void idx_f32_kernel(const float* __restrict__ 
 
 template <int DI, int QG, int MODE>
 hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
-                        int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
+                        int B, int S, int T, int P, int HI, float scale, int fill, hipStream_t st) {
   // Long contexts (many key tiles per query tile) share each key tile between
   // the pair's two query tiles. Measured with one 4096-query chunk after
   // 524288 keys (32 heads): 14.97 -> 13.97 ms; at S = T (32768 and 4096) it
@@ -363,18 +363,18 @@ hipError_t launch_tiles(const uint16_t* q, const uint16_t* k, const uint16_t* w,
   if (g.gx > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((idx_tile_kernel<DI, QG, MODE>), dim3((unsigned)g.gx, B), dim3(256), 0, st, q,
                      k, w, scores, S, T, P, HI, scale, g.nqt, g.nkt, g.npairs, g.maxlen,
-                     two ? 1 : 0);
+                     two ? 1 : 0, fill);
   return hipGetLastError();
 }
 
 template <int DI, int NHB, int MODE>
 hipError_t launch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
-                       int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
+                       int B, int S, int T, int P, int HI, float scale, int fill, hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
   auto waves = [&](int kpw) { return rows * ((T + kpw - 1) / kpw); };
 #define DSA_ROWS_LAUNCH(KPW)                                                                     \
   hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE, KPW>), dim3((T + 4 * KPW - 1) / (4 * KPW), \
-                     (unsigned)rows), dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale)
+                     (unsigned)rows), dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale, fill)
   if (waves(512) >= kRowsWaves)
     DSA_ROWS_LAUNCH(512);
   else
@@ -385,27 +385,27 @@ hipError_t launch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, 
 
 template <int DI, int MODE>
 hipError_t dispatch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
-                         int B, int S, int T, int P, int HI, float scale, hipStream_t st) {
+                         int B, int S, int T, int P, int HI, float scale, int fill, hipStream_t st) {
   const int nhb = (HI + 31) / 32;
   switch (nhb) {
-    case 1: return launch_rows<DI, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-    case 2: return launch_rows<DI, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-    case 3: return launch_rows<DI, 3, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-    default: return launch_rows<DI, 4, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
+    case 1: return launch_rows<DI, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+    case 2: return launch_rows<DI, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+    case 3: return launch_rows<DI, 3, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+    default: return launch_rows<DI, 4, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
   }
 }
 
 template <int MODE>
 hipError_t dispatch_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* w, float* scores,
-                         int B, int S, int T, int P, int HI, int DI, float scale,
+                         int B, int S, int T, int P, int HI, int DI, float scale, int fill,
                          hipStream_t st) {
   // few queries per sequence and at most 128 index heads: head-major MFMA
   const bool rows = S < 32 && HI <= 128 && (int64_t)B * S <= 65535;
   if (rows) {
     switch (DI) {
-      case 32: return dispatch_rows<32, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-      case 64: return dispatch_rows<64, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-      default: return dispatch_rows<128, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
+      case 32: return dispatch_rows<32, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+      case 64: return dispatch_rows<64, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+      default: return dispatch_rows<128, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
     }
   }
   // Light per-score work (few index heads x small dim): two 16-query groups
@@ -415,14 +415,14 @@ hipError_t dispatch_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* w
   // budget, so that dim always runs one group.)
   if (HI * DI <= 512 && DI <= 64) {
     switch (DI) {
-      case 32: return launch_tiles<32, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-      default: return launch_tiles<64, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
+      case 32: return launch_tiles<32, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+      default: return launch_tiles<64, 2, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
     }
   }
   switch (DI) {
-    case 32: return launch_tiles<32, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-    case 64: return launch_tiles<64, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
-    default: return launch_tiles<128, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, st);
+    case 32: return launch_tiles<32, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+    case 64: return launch_tiles<64, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
+    default: return launch_tiles<128, 1, MODE>(q, k, w, scores, B, S, T, P, HI, scale, fill, st);
   }
 }
 
@@ -434,20 +434,21 @@ DSA_DEBUG_TAKE(index_scores)
 
 hipError_t launch_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores,
                                int B, int S, int T, int past_len, int HI, int DI, float scale,
-                               int relu_mode, int dtype, hipStream_t stream) {
+                               int relu_mode, int dtype, hipStream_t stream, bool fill_masked) {
+  const int fill = fill_masked ? 1 : 0;
   if (dtype == 0) {
     hipLaunchKernelGGL(idx_f32_kernel, dim3((T + 255) / 256, B * S), dim3(256), 0, stream,
                        (const float*)q_idx, (const float*)k_idx, (const float*)w, scores, S, T,
-                       past_len, HI, DI, scale, relu_mode);
+                       past_len, HI, DI, scale, relu_mode, fill);
     return hipGetLastError();
   }
   const uint16_t* q = (const uint16_t*)q_idx;
   const uint16_t* k = (const uint16_t*)k_idx;
   const uint16_t* ww = (const uint16_t*)w;
   switch (relu_mode) {
-    case 0: return dispatch_bf16<0>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, stream);
-    case 1: return dispatch_bf16<1>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, stream);
-    default: return dispatch_bf16<2>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, stream);
+    case 0: return dispatch_bf16<0>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, fill, stream);
+    case 1: return dispatch_bf16<1>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, fill, stream);
+    default: return dispatch_bf16<2>(q, k, ww, scores, B, S, T, past_len, HI, DI, scale, fill, stream);
   }
 }
 

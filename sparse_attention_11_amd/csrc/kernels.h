@@ -8,9 +8,12 @@
 namespace dsa {
 
 // Lightning-indexer scores (index_scores.hip).
+// fill_masked = false leaves the entries above each row's causal bound
+// (t > past_len + s) unwritten, for callers that read only t <= past_len + s.
 hipError_t launch_index_scores(const void* q_idx, const void* k_idx, const void* w, float* scores,
                                int B, int S, int T, int past_len, int HI, int DI, float scale,
-                               int relu_mode, int dtype, hipStream_t stream);
+                               int relu_mode, int dtype, hipStream_t stream,
+                               bool fill_masked = true);
 
 // FP8 indexer (index_fp8.hip): Hadamard rotation + E4M3 codes with one
 // power-of-two scale per row (dim 32, 64 or 128, bf16 input); scores from
@@ -49,9 +52,11 @@ hipError_t launch_mla_prologue(const void* q_resid, const void* q_comp, const vo
 // Per-row top-k (topk.hip).
 size_t topk_workspace_bytes(int B, int S, int T, int topk);
 // order 0: by score descending (ties: lower position first); 1: the same
-// selection unsorted (a fixed, repeatable order), -1 slots last.
+// selection unsorted (a fixed, repeatable order), -1 slots last. causal_P >= 0:
+// row r = b S + s holds only min(T, causal_P + s + 1) valid scores (the rest
+// of its T are never read), which selects exactly what -inf there would.
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void* workspace, hipStream_t stream, int order = 0);
+                       void* workspace, hipStream_t stream, int order = 0, int causal_P = -1);
 
 // Selection bitmap + MFMA flash attention with a bitmap or window mask
 // (attn_prefill.hip). Requires bf16 and a (Dqk, Dv) pair that

@@ -186,7 +186,8 @@ template <int NT, int SRC, int DST, int EPT, int E>
 __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(const void* __restrict__ src,
                                                         int32_t* __restrict__ out_idx,
                                                         uint64_t* __restrict__ out_keys, int T,
-                                                        int k, int seg_len, int nseg, int order) {
+                                                        int k, int seg_len, int nseg, int order,
+                                                        int S, int P) {
   constexpr int NW = NT / 64;
   __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane
   // selected keys: k of them for a candidate stage, at most NT*E >= k for a
@@ -202,7 +203,9 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
   const int64_t row = blockIdx.x / nseg;
   const int seg = (int)(blockIdx.x % nseg);
   const int t0 = seg * seg_len;
-  const int n = min(T - t0, seg_len);
+  // valid length of a score row: T, or its causal bound when P >= 0
+  const int L = (SRC == 0 && P >= 0) ? min(T, P + (int)(row % S) + 1) : T;
+  const int n = max(0, min(L - t0, seg_len));
   const float* srow = (const float*)src + row * (int64_t)T;
   const uint64_t* krow = (const uint64_t*)src + row * (int64_t)T;
   auto load_key = [&](int j) -> uint64_t {
@@ -447,19 +450,19 @@ __global__ __launch_bounds__(NT, (EPT <= 16 ? 2048 / NT : 1)) void topk_kernel(c
 
 template <int NT, int SRC, int DST, int EPT>
 hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T, int k,
-                    int seg_len, int nseg, hipStream_t st, int order) {
+                    int seg_len, int nseg, hipStream_t st, int order, int S, int P) {
   const dim3 g((unsigned)blocks), b(NT);
   // sort width NT*E >= max(k, NT); k <= kMaxK = 8 * 256, so 1024 threads
   // need E <= 2 and 512 threads E <= 4
   constexpr int E4 = NT >= 1024 ? 2 : 4, E8 = NT >= 1024 ? 2 : (NT >= 512 ? 4 : 8);
   if (DST == 1 || k <= NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 1>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order, S, P);
   else if (k <= 2 * NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, 2>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order, S, P);
   else if (k <= 4 * NT)
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E4>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order, S, P);
   else
-    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order);
+    hipLaunchKernelGGL((topk_kernel<NT, SRC, DST, EPT, E8>), g, b, 0, st, src, idx, keys, T, k, seg_len, nseg, order, S, P);
   return hipGetLastError();
 }
 
@@ -472,12 +475,13 @@ hipError_t launch_e(const void* src, int32_t* idx, uint64_t* keys, int64_t block
 // 528384-key row, 4.23 -> 3.55 ms for 4096 rows, bit-identical.
 template <int SRC, int DST, int RANGE>
 hipError_t launch_stage(const void* src, int32_t* idx, uint64_t* keys, int64_t blocks, int T,
-                        int k, int seg_len, int nseg, hipStream_t st, int order = 0) {
+                        int k, int seg_len, int nseg, hipStream_t st, int order = 0, int S = 1,
+                        int P = -1) {
   if (blocks < 256)
-    return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
+    return launch_e<1024, SRC, DST, RANGE / 1024>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order, S, P);
   if (RANGE / 256 > 16)
-    return launch_e<512, SRC, DST, RANGE / 512>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
-  return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order);
+    return launch_e<512, SRC, DST, RANGE / 512>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order, S, P);
+  return launch_e<256, SRC, DST, RANGE / 256>(src, idx, keys, blocks, T, k, seg_len, nseg, st, order, S, P);
 }
 
 constexpr int kCand = 16384;  // candidate keys one register-resident workgroup takes
@@ -537,13 +541,14 @@ __global__ __launch_bounds__(256) void row_hist_zero_kernel(uint32_t* __restrict
 
 __global__ __launch_bounds__(256) void row_hist_kernel(const float* __restrict__ scores,
                                                        uint32_t* __restrict__ ghist, int T,
-                                                       int nc) {
+                                                       int nc, int S, int P) {
   constexpr int EPT = kRowChunk / 256;
   __shared__ uint32_t h[kBins];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / nc;
   const int c = blockIdx.x % nc;
-  const int t0 = c * kRowChunk, n = min(T - t0, kRowChunk);
+  const int L = P >= 0 ? min(T, P + (int)(row % S) + 1) : T;  // valid scores of the row
+  const int t0 = c * kRowChunk, n = max(0, min(L - t0, kRowChunk));
   for (int i = tid; i < kBins; i += 256) h[i] = 0u;
   const float* sr = scores + row * (int64_t)T + t0;
   float f[EPT];
@@ -574,7 +579,7 @@ __global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict
                                                          const uint32_t* __restrict__ ghist,
                                                          uint64_t* __restrict__ cand,
                                                          uint32_t* __restrict__ cnt, int T,
-                                                         int nc, int k) {
+                                                         int nc, int k, int S, int P) {
   constexpr int NT = 256, NW = 4, EPT = kRowChunk / 256;
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t s_red[NW];
@@ -583,7 +588,8 @@ __global__ __launch_bounds__(256) void row_filter_kernel(const float* __restrict
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x / nc;
   const int c = blockIdx.x % nc;
-  const int t0 = c * kRowChunk, n = min(T - t0, kRowChunk);
+  const int L = P >= 0 ? min(T, P + (int)(row % S) + 1) : T;  // valid scores of the row
+  const int t0 = c * kRowChunk, n = max(0, min(L - t0, kRowChunk));
   // this chunk's scores first: their loads overlap the histogram work
   const float* sr = scores + row * (int64_t)T + t0;
   uint32_t hi[EPT];
@@ -848,7 +854,7 @@ size_t row_path_bytes(int64_t rows, int T) {
 }
 
 hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, int T, int k,
-                           void* workspace, hipStream_t st, int order) {
+                           void* workspace, hipStream_t st, int order, int S, int P) {
   const int nc = (int)(((int64_t)T + kRowChunk - 1) / kRowChunk);
   uint64_t* cand = (uint64_t*)workspace;
   uint32_t* ghist = (uint32_t*)(cand + rows * nc * (int64_t)kRowChunk);
@@ -856,9 +862,9 @@ hipError_t launch_row_path(const float* scores, int32_t* indices, int64_t rows, 
   const int nh = (int)(rows * kRowHistCopies * kBins);
   hipLaunchKernelGGL(row_hist_zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, ghist, nh);
   hipLaunchKernelGGL(row_hist_kernel, dim3((unsigned)(rows * nc)), dim3(256), 0, st, scores, ghist,
-                     T, nc);
+                     T, nc, S, P);
   hipLaunchKernelGGL(row_filter_kernel, dim3((unsigned)(rows * nc)), dim3(256), 0, st, scores,
-                     ghist, cand, cnt, T, nc, k);
+                     ghist, cand, cnt, T, nc, k, S, P);
   hipLaunchKernelGGL(row_select_kernel, dim3((unsigned)rows), dim3(1024), 0, st, cand, cnt, ghist,
                      indices, nc, k, order);
   return hipGetLastError();
@@ -883,14 +889,17 @@ size_t topk_workspace_bytes(int B, int S, int T, int topk) {
 }
 
 hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int T, int topk,
-                       void* workspace, hipStream_t st, int order) {
+                       void* workspace, hipStream_t st, int order, int causal_P) {
   const int64_t rows = (int64_t)B * S;
   if (T <= kSegLen) {  // one register-resident workgroup per row
-    if (T <= 4096) return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
-    return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st, order);
+    if (T <= 4096)
+      return launch_stage<0, 0, 4096>(scores, indices, nullptr, rows, T, topk, T, 1, st, order, S,
+                                      causal_P);
+    return launch_stage<0, 0, kSegLen>(scores, indices, nullptr, rows, T, topk, T, 1, st, order, S,
+                                       causal_P);
   }
   if (use_row_path(rows, T))
-    return launch_row_path(scores, indices, rows, T, topk, workspace, st, order);
+    return launch_row_path(scores, indices, rows, T, topk, workspace, st, order, S, causal_P);
   int groups[8];
   const int lv = stage_groups(T, topk, groups, 8);
   uint64_t* bufa = (uint64_t*)workspace;
@@ -898,7 +907,7 @@ hipError_t launch_topk(const float* scores, int32_t* indices, int B, int S, int 
   if (rows * groups[0] > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   // stage 1: k candidate keys per 16384-score segment
   hipError_t e = launch_stage<0, 1, kSegLen>(scores, nullptr, bufa, rows * groups[0], T, topk,
-                                             kSegLen, groups[0], st);
+                                             kSegLen, groups[0], st, 0, S, causal_P);
   if (e != hipSuccess) return e;
   // candidate reductions: groups of kCand candidates -> k each
   int C = groups[0] * topk;

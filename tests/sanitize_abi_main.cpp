@@ -108,6 +108,10 @@ int main() {
     expect(dsa_topk(tsc, tix, iv(), iv(), iv(), iv(), tws, wsb, nullptr), "dsa_topk");
     expect(dsa_topk_unsorted(tsc, tix, iv(), iv(), iv(), iv(), tws, wsb, nullptr),
            "dsa_topk_unsorted");
+    (void)dsa_index_topk_workspace_size(iv(), iv(), iv(), iv());
+    expect(dsa_index_topk(P(0), P(1), P(2), tix, iv(), iv(), iv(), iv(), iv(), iv(), fv(),
+                          (int)(rnd() % 4), dt, iv(), (int)(rnd() % 3), tws, wsb, nullptr),
+           "dsa_index_topk");
     const int B = iv(), S = iv(), T = iv(), past = iv(), H = iv();
     expect(dsa_sparse_attn_prefill(P(0), P(1), P(2), (const int32_t*)P(0), P(1), VP(2), B, S, T,
                                    past, H, iv(), iv(), iv(), iv(), fv(), (int)(rnd() % 3), dt,

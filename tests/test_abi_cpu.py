@@ -95,6 +95,36 @@ def test_topk_validation(fn, kw, code):
     assert dsa.dsa_last_error().startswith(fn + ":")
 
 
+def index_topk(**kw):
+    a = dict(q=P, k=P, w=P, i=P, B=1, S=4, T=8, past=0, HI=2, DI=64, scale=0.125, relu=0, dt=1,
+             topk=4, sorted=1, ws=None, nb=0)
+    a.update(kw)
+    return dsa.lib().dsa_index_topk(a["q"], a["k"], a["w"], a["i"], a["B"], a["S"], a["T"],
+                                    a["past"], a["HI"], a["DI"], a["scale"], a["relu"], a["dt"],
+                                    a["topk"], a["sorted"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(i=None), 1), (dict(T=3), 1), (dict(past=5), 1), (dict(DI=48), 2),
+    (dict(topk=0), 1), (dict(topk=9), 1), (dict(T=5000, topk=4096), 2), (dict(sorted=2), 1),
+    (dict(scale=0.0), 1), (dict(relu=3), 1), (dict(dt=2), 1),
+    (dict(), 3),                                     # scores need a workspace
+    (dict(ws=P, nb=8 * 4 * 4 - 1), 3),               # one byte short of B*S*T fp32 scores
+])
+def test_index_topk_validation(kw, code):
+    assert index_topk(**kw) == code
+    assert dsa.dsa_last_error().startswith("dsa_index_topk:")
+
+
+def test_index_topk_workspace_size():
+    # B*S*T fp32 scores, 256-byte aligned, then the top-k's own workspace
+    assert dsa.dsa_index_topk_workspace_size(1, 4, 8, 4) == 256
+    assert dsa.dsa_index_topk_workspace_size(2, 100, 40000, 512) == \
+        (2 * 100 * 40000 * 4 + 255) // 256 * 256 + dsa.dsa_topk_workspace_size(2, 100, 40000, 512)
+    for bad in ((0, 4, 8, 4), (1, 4, 8, 9), (1, 4, 8, 0), (1, 4, 5000, 4096)):
+        assert dsa.dsa_index_topk_workspace_size(*bad) == 0
+
+
 def prefill(**kw):
     a = dict(q=P, k=P, v=P, i=P, g=P, o=P, B=1, S=32, T=64, past=0, H=2, nope=64, rope=64, v_dim=128,
              topk=16, sc=0.1, gd=1, dt=1, ws=None, nb=0)

@@ -184,6 +184,27 @@ def test_dsa_s32k_topk_full_tensor(mode, order):
                order=order)
 
 
+@pytest.mark.parametrize("srt", [False, True])
+def test_dsa_s32k_index_topk_full_tensor(srt):
+    """The fused indexer + top-k call on the whole dsa-s32k prefill: every
+    row's indices equal those of dsa_index_scores + dsa_topk(_unsorted)."""
+    wl = WORKLOADS["dsa-s32k"]
+    S, T = wl.S, wl.T
+    print(f"dsa-s32k index_topk sorted {srt}", flush=True)
+    qi = dev_normal((1, S, wl.HI, wl.DI), wl, datagen.TID_QIDX, wl.scale_qidx)
+    ki = dev_normal((1, T, wl.DI), wl, datagen.TID_KIDX, wl.scale_kidx)
+    w = dev_normal((1, S, wl.HI), wl, datagen.TID_W, wl.scale_w)
+    sc = torch.empty(1, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(qi, ki, w, sc, 0)
+    ref = torch.empty(1, S, wl.topk, dtype=torch.int32, device=DEV)
+    (dsa.dsa_topk if srt else dsa.dsa_topk_unsorted)(sc, ref)
+    del sc
+    got = torch.full((1, S, wl.topk), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_index_topk(qi, ki, w, got, 0, sorted=srt)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref), f"{int((got != ref).sum())} slots differ"
+
+
 def test_dsa_s32k_prefill_sampled_rows():
     wl = WORKLOADS["dsa-s32k"]
     S, T, H = wl.S, wl.T, wl.H

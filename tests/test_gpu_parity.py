@@ -236,6 +236,42 @@ def test_topk_deterministic_run_to_run(R, T, k, mode, order):
     np.testing.assert_array_equal(as_set(got) if order else got, as_set(ref) if order else ref)
 
 
+# ------------------------------------------------ fused indexer + top-k
+# dsa_index_topk against dsa_index_scores + dsa_topk / dsa_topk_unsorted on
+# the same inputs: bit-identical indices. Its workspace is filled with 0x7F
+# bytes (3.4e38 as fp32) first, so a read of any score above a row's causal
+# bound (which the fused call never writes) would be selected and show up.
+INDEX_TOPK_CASES = [  # B, S, T, P, HI, DI, k, dtype
+    (1, 600, 600, 0, 4, 64, 64, 1),          # tile indexer, one top-k stage, rows with < k visible
+    (2, 300, 20300, 20000, 8, 128, 512, 1),  # chunk after a long past: segmented top-k
+    (4, 1, 70001, 70000, 16, 128, 2048, 1),  # decode: rows indexer, long-row top-k
+    (1, 8, 9000, 8992, 4, 32, 100, 1),       # few queries: rows indexer with causal rows
+    (1, 3, 50000, 10000, 8, 64, 2048, 1),    # rows end long before T (long-row path, empty chunks)
+    (1, 100, 100, 0, 2, 32, 16, 0),          # fp32
+]
+
+
+@pytest.mark.parametrize("B,S,T,P,HI,DI,k,dt", INDEX_TOPK_CASES)
+@pytest.mark.parametrize("srt", [True, False])
+def test_index_topk_matches_two_calls(B, S, T, P, HI, DI, k, dt, srt):
+    print(f"index_topk B {B} S {S} T {T} P {P} HI {HI} DI {DI} k {k} dtype {dt} sorted {srt}",
+          flush=True)
+    tdt = torch.bfloat16 if dt == 1 else torch.float32
+    g = lambda shape, tid, sc=1.0: datagen.normal_device(torch.empty(*shape, dtype=tdt, device=DEV),
+                                                         17 + S, tid, sc)
+    qi, ki, w = g((B, S, HI, DI), 1), g((B, T, DI), 2), g((B, S, HI), 3, HI ** -0.5)
+    sc = torch.empty(B, S, T, dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(qi, ki, w, sc, P)
+    ref = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
+    (dsa.dsa_topk if srt else dsa.dsa_topk_unsorted)(sc, ref)
+    ws = torch.full((dsa.dsa_index_topk_workspace_size(B, S, T, k),), 0x7F, dtype=torch.uint8,
+                    device=DEV)
+    got = torch.full((B, S, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_index_topk(qi, ki, w, got, P, sorted=srt, workspace=ws)
+    _sync()
+    assert torch.equal(got, ref), f"{int((got != ref).sum())} of {got.numel()} slots differ"
+
+
 # ----------------------------------------------------- sparse attention
 def _attn_dev(hi):
     return {k_: to_dev(v_) for k_, v_ in hi.items()}
