@@ -622,6 +622,53 @@ def cpu_decode_baseline(wl, reps=3):
                       f"{wl.B} sequences; its selected cache rows generated before timing"}
 
 
+def headline_roofline(wl, per_stage):
+    """The roofline object of the main workload's dominant stage (K3, or the
+    stage a single-stage workload runs) from its mean stage time."""
+    w = work(wl)
+    t3 = (per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6
+          if wl.S > 1 and not (wl.swa_only or wl.prologue_only or wl.mla_prologue_only) else None)
+    if wl.mla_prologue_only:
+        t0 = per_stage["K0m mla_prologue"]["mean_us"] * 1e-6
+        fl = mla_prologue_flops(wl)
+        roof = {"kernel": "K0m mla_prologue (three bf16 GEMMs with scattering epilogues)",
+                "bound": "mfma", "achieved": fl / t0 / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": fl / t0 / PEAK_BF16, "traffic": None,
+                "algorithmic_flops_per_launch": fl, "mean_launch_us": t0 * 1e6}
+    elif wl.prologue_only:
+        t0 = per_stage["K0 indexer_prologue"]["mean_us"] * 1e-6
+        M = wl.B * wl.S
+        fl = 2.0 * M * (wl.q_lora * wl.HI * wl.DI + wl.hidden * wl.DI + wl.hidden * wl.HI)
+        roof = {"kernel": "K0 indexer_prologue (bf16 GEMMs + LayerNorm / RoPE)", "bound": "mfma",
+                "achieved": fl / t0 / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": fl / t0 / PEAK_BF16, "traffic": None, "algorithmic_flops_per_launch": fl,
+                "mean_launch_us": t0 * 1e6}
+    elif wl.swa_only:
+        t5 = per_stage["K5 swa_attn chunk"]["mean_us"] * 1e-6
+        ach = w["K5"]["flops"] / t5 / 1e12
+        roof = {"kernel": "K5 swa_attn_gqa chunk (MFMA flash, window mask)", "bound": "mfma",
+                "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
+                "algorithmic_flops_per_launch": w["K5"]["flops"], "mean_launch_us": t5 * 1e6}
+    elif t3 is not None:
+        ach = w["attn"]["flops"] / t3 / 1e12
+        roof = {"kernel": "K3 sparse_attn_prefill (selection bitmap + dense-masked MFMA flash)",
+                "bound": "mfma", "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
+                "algorithmic_flops_per_launch": w["attn"]["flops"],
+                "issued_dense_flops_per_launch": w["attn"]["dense_flops"],
+                "issued_frac": w["attn"]["dense_flops"] / t3 / PEAK_BF16,
+                "mean_launch_us": t3 * 1e6}
+    else:
+        t4 = per_stage["K4 sparse_attn_decode"]["mean_us"] * 1e-6
+        ach = w["attn"]["bytes_gather"] / t4 / 1e9
+        roof = {"kernel": "K4 sparse_attn_decode", "bound": "hbm", "achieved": ach,
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM,
+                "traffic": None, "mean_launch_us": t4 * 1e6}
+    roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
+    return roof
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -694,44 +741,11 @@ def main():
         torch.cuda.empty_cache()
         log(f"{name}: {tm:.3f} ms/step")
 
-    w = work(wl)
-    t3 = (per_stage["K3 sparse_attn_prefill"]["mean_us"] * 1e-6
-          if wl.S > 1 and not wl.swa_only and not wl.prologue_only else None)
-    if wl.prologue_only:
-        t0 = per_stage["K0 indexer_prologue"]["mean_us"] * 1e-6
-        M = wl.B * wl.S
-        fl = 2.0 * M * (wl.q_lora * wl.HI * wl.DI + wl.hidden * wl.DI + wl.hidden * wl.HI)
-        roof = {"kernel": "K0 indexer_prologue (bf16 GEMMs + LayerNorm / RoPE)", "bound": "mfma",
-                "achieved": fl / t0 / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": fl / t0 / PEAK_BF16, "traffic": None, "algorithmic_flops_per_launch": fl,
-                "mean_launch_us": t0 * 1e6}
-    elif wl.swa_only:
-        t5 = per_stage["K5 swa_attn chunk"]["mean_us"] * 1e-6
-        ach = w["K5"]["flops"] / t5 / 1e12
-        roof = {"kernel": "K5 swa_attn_gqa chunk (MFMA flash, window mask)", "bound": "mfma",
-                "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
-                "algorithmic_flops_per_launch": w["K5"]["flops"], "mean_launch_us": t5 * 1e6}
-    elif t3 is not None:
-        ach = w["attn"]["flops"] / t3 / 1e12
-        roof = {"kernel": "K3 sparse_attn_prefill (selection bitmap + dense-masked MFMA flash)",
-                "bound": "mfma", "achieved": ach, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": ach * 1e12 / PEAK_BF16, "traffic": None,
-                "algorithmic_flops_per_launch": w["attn"]["flops"],
-                "issued_dense_flops_per_launch": w["attn"]["dense_flops"],
-                "issued_frac": w["attn"]["dense_flops"] / t3 / PEAK_BF16,
-                "mean_launch_us": t3 * 1e6}
-    else:
-        t4 = per_stage["K4 sparse_attn_decode"]["mean_us"] * 1e-6
-        ach = w["attn"]["bytes_gather"] / t4 / 1e9
-        roof = {"kernel": "K4 sparse_attn_decode", "bound": "hbm", "achieved": ach,
-                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM,
-                "traffic": None, "mean_launch_us": t4 * 1e6}
-    roof["traffic"], roof["traffic_source"] = counted_traffic(wl.name)
+    roof = headline_roofline(wl, per_stage)
 
     # ---- the oracle on this host's cores (after every GPU measurement)
     cpu = None
-    if not args.no_cpu and not wl.swa_only and not wl.prologue_only:
+    if not args.no_cpu and not (wl.swa_only or wl.prologue_only or wl.mla_prologue_only):
         log("cpu baseline (oracle)")
         cpu = cpu_prefill_baseline(wl, args.cpu_seconds)
         cpu["cpu_model"] = cpu_model()

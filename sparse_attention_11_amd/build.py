@@ -25,6 +25,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
           # packed fp32 VALU forms are kept out of every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # multiply-adds are fused only within one source expression, never by
+          # the backend across statements: rounding then follows the source, and
+          # the checking build (whose extra branches regroup the code) computes
+          # the same bits as the release build
+          "-ffp-contract=on",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

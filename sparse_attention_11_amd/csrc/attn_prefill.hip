@@ -163,6 +163,13 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   static_assert((kBN * KCH) % 256 == 0, "K block must split evenly over 256 threads");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * DV];
+  // selection-mask calls start the logits' accumulators from the mask:
+  // entry n holds, for 4 consecutive accumulator elements, 0 where bit j of
+  // n is set (selected) and -inf where it is not; 0 + q.k is q.k exactly and
+  // -inf + q.k is -inf, so the MFMA chain ends with the masked logits
+  __shared__ __attribute__((aligned(16))) float mask_tab[16][4];
+  if (MASK == 0 && threadIdx.x < 64)
+    mask_tab[threadIdx.x >> 2][threadIdx.x & 3] = ((threadIdx.x >> 2) >> (threadIdx.x & 3)) & 1 ? 0.0f : -INFINITY;
 
   // XCD-aware order (selection-mask calls). Workgroups are dealt to the 8
   // XCDs round-robin by their linear id; this maps XCD x's share to one
@@ -353,6 +360,18 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
     // (the two halves' accumulation chains are interleaved, so consecutive
     // MFMAs never depend on each other)
     f32x16_t st[2] = {zero16(), zero16()};
+    if (MASK == 0) {  // accumulators start at 0 (selected) or -inf: 4 elements per table read
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t wbits = bits[i] >> (4 * lh);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_t m4 = *(const f32x4_t*)(&mask_tab[(wbits >> (8 * g)) & 0xFu][0]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st[i][4 * g + j] = m4[j];
+        }
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
@@ -364,12 +383,12 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
     // as a tree of three-input maxima (16 ops, 4 deep)
     float mx3[11];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2 && MASK != 0; ++i) {
       const uint32_t wbits = bits[i] >> (4 * lh);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x;
-        if (MASK == 0 || sinkb) {
+        if (sinkb) {
           x = keep_or_neg_inf(st[i][e], wbits, 8 * (e >> 2) + (e & 3));
         } else {
           const int jj = jb + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
@@ -379,13 +398,18 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
         st[i][e] = x;
       }
     }
+    // (the first level reads the logits themselves, which are MFMA results
+    // when the mask came in through the accumulators: that level uses the
+    // compiler's max, whose operands get the MFMA-to-VALU wait states; the
+    // inline-asm maxima only ever read VALU results)
 #pragma unroll
     for (int r = 0; r < 10; ++r) {  // 30 of the 32 logits
       const int e0 = 3 * r;
-      mx3[r] = max3_f32(st[e0 >> 4][e0 & 15], st[(e0 + 1) >> 4][(e0 + 1) & 15],
-                        st[(e0 + 2) >> 4][(e0 + 2) & 15]);
+      const float a = st[e0 >> 4][e0 & 15], b = st[(e0 + 1) >> 4][(e0 + 1) & 15],
+                  c = st[(e0 + 2) >> 4][(e0 + 2) & 15];
+      mx3[r] = MASK == 0 ? __builtin_fmaxf(__builtin_fmaxf(a, b), c) : max3_f32(a, b, c);
     }
-    mx3[10] = max_f32(st[1][14], st[1][15]);
+    mx3[10] = MASK == 0 ? __builtin_fmaxf(st[1][14], st[1][15]) : max_f32(st[1][14], st[1][15]);
     float mx = max3_f32(max3_f32(mx3[0], mx3[1], mx3[2]), max3_f32(mx3[3], mx3[4], mx3[5]),
                         max3_f32(mx3[6], mx3[7], mx3[8]));
     mx = max3_f32(mx, mx3[9], mx3[10]);

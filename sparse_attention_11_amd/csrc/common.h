@@ -67,13 +67,6 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
-// max(x, 0) as a single v_max_f32 (fmaxf also emits a NaN-quieting max, and
-// the compiler folds med3(x, 0, inf) back into fmaxf). Pure VALU op, no memory.
-__device__ __forceinline__ float relu_f32(float x) {
-  float r;
-  asm("v_max_f32_e32 %0, 0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
 // max(x, 0) as one signed-integer max on the bit pattern: every float with
 // the sign bit set (negatives, -0) maps to +0, everything else is unchanged.
 __device__ __forceinline__ float relu_bits(float x) {
@@ -109,7 +102,10 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), ones, acc, false);
 }
 
-// max of two floats as one v_max_f32 (no NaN-quieting of the inputs first)
+// max of two floats as one v_max_f32 (no NaN-quieting of the inputs first).
+// Like every inline-asm helper here it must only be given VALU results: the
+// compiler does not insert the MFMA-to-VALU wait states before inline asm, so
+// an MFMA result read here may be stale.
 __device__ __forceinline__ float max_f32(float a, float b) {
   float r;
   asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -132,7 +128,7 @@ __device__ __forceinline__ bf16x8_t lds_read_tr_pair(const uint16_t* lds, uint32
   const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
-// max of three floats as one v_max3_f32
+// max of three floats as one v_max3_f32 (VALU results only, as max_f32)
 __device__ __forceinline__ float max3_f32(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
