@@ -379,6 +379,18 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
         const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Ks[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
         st[i] = mfma32x32x16(a, bq[ks], st[i]);
       }
+    if (DQK <= 192) {
+      // K operand reads run about ten MFMAs ahead: the first twelve LDS reads
+      // (mask table and K) are issued first, then one per MFMA (dsa-s32k K3
+      // 44.6-44.9 -> 44.0-44.3 ms on one MI355X; 10 or 14 ahead were slower).
+      // Dims 256 have no registers to spare for it.
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+      for (int r = 0; r < 2 * KSQ; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
     // mask, then the running max on raw logits (scale > 0 keeps the order),
     // as a tree of three-input maxima (16 ops, 4 deep)
     float mx3[11];

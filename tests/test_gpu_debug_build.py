@@ -2,7 +2,8 @@
 kernels also check the invariants they rely on) against the release build.
 
 Every entry point runs once per library on the same inputs, at shapes that
-reach each kernel path: the indexer's tile and rows kernels, the FP8 indexer,
+reach each kernel path: the indexer's tile and rows kernels (alone and fused
+with the top-k), the FP8 indexer,
 the top-k's single-stage, segmented and long-row paths (sorted and
 unsorted), the MFMA prefill with and without split tiles, the row gather for
 short and long-context prefill, decode with and without sinks and through the
@@ -83,6 +84,12 @@ def test_debug_build_indexer_and_topk():
         s3 = torch.empty(1, 300, 300, dtype=torch.float32, device=DEV)
         dsa.dsa_index_scores_fp8(qc, qs, kc, ks, w, s3, 0)
         outs += [qc, qs, kc, ks, s3]
+        for srt in (True, False):  # fused indexer + top-k: tile rows and decode rows
+            f1 = torch.empty(1, 300, 64, dtype=torch.int32, device=DEV)
+            dsa.dsa_index_topk(qi, ki, w, f1, 0, sorted=srt)
+            f2 = torch.empty(2, 1, 2048, dtype=torch.int32, device=DEV)
+            dsa.dsa_index_topk(qd, kd, wd, f2, 4999, sorted=srt)
+            outs += [f1, f2]
         for sc, k in ((rows_short, 256), (rows_seg, 512), (rows_long, 2048)):
             for fn in (dsa.dsa_topk, dsa.dsa_topk_unsorted):
                 ix = torch.empty(1, sc.shape[0], k, dtype=torch.int32, device=DEV)
