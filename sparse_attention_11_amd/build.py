@@ -59,7 +59,8 @@ def build(jobs: int = 8, debug: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    jobs = int(sys.argv[1]) if len(sys.argv) > 1 else 8
+    nums = [a for a in sys.argv[1:] if not a.startswith("-")]
+    jobs = int(nums[0]) if nums else 8
     print(build(jobs))
     if "--no-debug" not in sys.argv:
         print(build(jobs, debug=True))

@@ -512,6 +512,337 @@ __global__ __launch_bounds__(256, (DV > 128 ? 1 : 2)) void prefill_kernel(
   }
 }
 
+// ------------------------------------------------- ping-pong flash kernel
+// Selection-mask calls without sinks or split tiles. One workgroup of 8
+// waves = one head x 256 queries: waves 0-3 (group A) own queries 0..127 of
+// the tile, waves 4-7 (group B) queries 128..255, so each SIMD runs one wave
+// of each group. The groups run half a block apart and alternate at every
+// workgroup barrier: while one group is in its MFMA phase (S(j) = K(j) Q^T
+// with the mask in the accumulators, then O += V(j-1)^T P(j-1)^T), the other
+// is in its VALU phase (the online softmax of its latest S, and staging the
+// next K block (A) or V block (B) from registers into LDS). The MFMA work of
+// one wave then runs under the VALU work of the other instead of after it.
+// K(j) and V(j-1) are read in the same phase, so both are double-buffered.
+// Per query the arithmetic is that of prefill_kernel, block by block; group A
+// also walks the tile's last (at most two) blocks, which its queries cannot
+// see: their bits are clear, so they add nothing.
+constexpr int kBQ2 = 256;  // queries per ping-pong workgroup
+// The ping-pong kernel runs when its grid has at least this many workgroups
+// (one per CU at a time): on smaller grids the prefill_kernel's twice as many
+// 128-query workgroups fill the GPU better.
+constexpr int64_t kPingPongMinGrid = 1024;
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint32_t* __restrict__ bm,
+    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int S, int Tbuf, int P, int H,
+    int HKV, int W32, float scale_log2, int gate_dim, int nqt) {
+  constexpr int KSQ = DQK / 16;
+  constexpr int NDB = DV / 32;
+  constexpr int KPAD = DQK + 8;
+  constexpr int KCH = DQK / 8;
+  constexpr int KLD = kBN * KCH / 256;   // K chunks per group-A thread per block
+  constexpr int VCH = DV / 8;
+  constexpr int VUN = (kBN / 4) * VCH;   // (4 keys x 8 dv) units per block
+  static_assert((kBN * KCH) % 256 == 0 && VUN <= 256, "one group of 256 threads stages a block");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * DV];
+  __shared__ __attribute__((aligned(16))) float mask_tab[16][4];  // as in prefill_kernel
+  if (threadIdx.x < 64)
+    mask_tab[threadIdx.x >> 2][threadIdx.x & 3] = ((threadIdx.x >> 2) >> (threadIdx.x & 3)) & 1 ? 0.0f : -INFINITY;
+
+  // XCD-aware order, as in prefill_kernel
+  int item, h, b;
+  {
+    const int64_t nx = gridDim.x, ny = gridDim.y;
+    const int64_t N = nx * ny * gridDim.z;
+    const int64_t L = blockIdx.x + nx * (blockIdx.y + ny * (int64_t)blockIdx.z);
+    const int64_t x = L % 8, q8 = N / 8, r8 = N % 8;
+    const int64_t lg = x * q8 + (x < r8 ? x : r8) + L / 8;
+    item = (int)(lg % nx);
+    h = (int)((lg / nx) % ny);
+    b = (int)(lg / (nx * ny));
+  }
+  const int qt = nqt - 1 - item;  // longest tiles first
+  DSA_CHECK(qt >= 0 && qt < nqt && h < H, qt, h);
+  const int hk = h / (H / HKV);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int tg = tid & 255;   // thread index inside the group
+  const int ln = lane & 31, lh = lane >> 5;
+  const int q0 = qt * kBQ2;
+  const int s = q0 + 32 * wave + ln;
+  const bool svalid = s < S;
+  const int sc = svalid ? s : S - 1;
+  const int64_t qrow = (int64_t)b * S + sc;
+
+  bf16x8_t bq[KSQ];
+  {
+    const uint16_t* qp = q + (qrow * H + h) * DQK + 8 * lh;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = as_bf16x8(load16(qp + 16 * ks));
+  }
+  // causal key range of the whole tile: rows 0 .. jhi
+  const int jhi = min(P + min(q0 + kBQ2 - 1, S - 1), Tbuf - 1);
+  const int nblk = jhi / kBN + 1;
+  DSA_CHECK(jhi >= 0 && jhi < Tbuf, jhi, Tbuf);
+  const int64_t kvrow0 = (int64_t)b * Tbuf;
+
+  // ---- K staging by group A (the chunk split of prefill_kernel, over 256 threads)
+  constexpr int KP1 = (KCH == 24) ? 16 : (KCH == 12) ? 8 : KCH;
+  constexpr int KP2 = KCH - KP1;
+  constexpr int R1 = 256 / KP1, N1 = kBN / R1;
+  constexpr int R2 = KP2 ? 256 / KP2 : 1, N2 = KP2 ? kBN / R2 : 0;
+  static_assert(N1 + N2 == KLD, "load split");
+  const int krow1 = tg / KP1, kc1 = tg % KP1;
+  const int krow2 = KP2 ? tg / KP2 : 0, kc2 = KP2 ? KP1 + tg % KP2 : 0;
+  const uint32_t rowb = (uint32_t)HKV * DQK * 2u;
+  const uint32_t kbo1 = krow1 * rowb + 16u * kc1, kbo2 = krow2 * rowb + 16u * kc2;
+  // ---- V staging by group B: unit tg = 4 key rows x 8 dv
+  const int vkg = tg / VCH, vdg = tg - (tg / VCH) * VCH;
+  const bool vact = tg < VUN;
+  const uint32_t vrowb = (uint32_t)HKV * DV * 2u;
+  const uint32_t vbo = 4 * vkg * vrowb + 16u * vdg;
+  // a wave stages only K (group A) or only V (group B): one register set
+  constexpr int NPRE = KLD > 4 ? KLD : 4;
+  u32x4_t pre[NPRE];
+  auto load_k = [&](int bi) {
+    const int jb = bi * kBN;
+    const auto kr = make_rsrc(k + ((kvrow0 + jb) * HKV + hk) * DQK,
+                              (int64_t)(Tbuf - jb) * rowb - (int64_t)hk * DQK * 2);
+#pragma unroll
+    for (int n = 0; n < N1; ++n) pre[n] = buffer_load16(kr, kbo1 + n * R1 * rowb);
+#pragma unroll
+    for (int n = 0; n < N2; ++n) pre[N1 + n] = buffer_load16(kr, kbo2 + n * R2 * rowb);
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < N1; ++n) *(u32x4_t*)(&Ks[buf][(krow1 + n * R1) * KPAD + 8 * kc1]) = pre[n];
+#pragma unroll
+    for (int n = 0; n < N2; ++n)
+      *(u32x4_t*)(&Ks[buf][(krow2 + n * R2) * KPAD + 8 * kc2]) = pre[N1 + n];
+  };
+  auto load_v = [&](int bi) {
+    const int jb = bi * kBN;
+    const auto vr = make_rsrc(v + ((kvrow0 + jb) * HKV + hk) * DV,
+                              (int64_t)(Tbuf - jb) * vrowb - (int64_t)hk * DV * 2);
+    if (vact) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pre[e] = buffer_load16(vr, vbo + e * vrowb);
+    }
+  };
+  auto store_v = [&](int buf) {
+    if (vact) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * vkg + e;
+        *(u32x4_t*)(&Vs[buf][r * DV + 8 * (vdg ^ vt_xor<VCH>(r))]) = pre[e];
+      }
+    }
+  };
+  // transposing-read offsets of the V operand, as in prefill_kernel
+  uint32_t vrd[NDB];
+  {
+    const int g16 = lane >> 4, jr = (lane >> 2) & 3, qr = lane & 3;
+    const int r = 4 * lh + jr;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int chunk = 4 * d + 2 * (g16 & 1) + (qr >> 1);
+      vrd[d] = (uint32_t)(r * DV * 2 + 16 * (chunk ^ vt_xor<VCH>(r)) + 8 * (qr & 1));
+    }
+  }
+
+  float m = -INFINITY, l = 0.0f;
+  const float lazy_thr = kLazyLog2 / scale_log2;
+  f32x16_t o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) o[d] = zero16();
+  f32x16_t st[2] = {zero16(), zero16()};
+  uint32_t pk[2][2][4] = {};
+  const uint32_t* bmrow = bm + qrow * (int64_t)W32;
+  uint32_t nbits[2];
+  auto load_bits = [&](int bi) {
+    const int w0 = 2 * bi;  // block bi covers bitmap words 2 bi, 2 bi + 1
+    nbits[0] = (w0 < W32) ? bmrow[w0] : 0u;
+    nbits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
+  };
+
+  // MFMA phase of block j: O += V(j-1)^T P(j-1)^T (j > 0), then S(j) (j < nblk);
+  // P and S are never live together
+  auto pv_part = [&](int j) {
+    const uint16_t* Vb = Vs[(j - 1) & 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t pb = as_bf16x8(u32x4_t{pk[i][c][0], pk[i][c][1], pk[i][c][2], pk[i][c][3]});
+        const uint32_t crow = (uint32_t)(16 * (2 * i + c) * DV * 2);
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const bf16x8_t va = lds_read_tr_pair(Vb, vrd[d] + crow, 8 * DV * 2);
+          o[d] = mfma32x32x16(va, pb, o[d]);
+        }
+      }
+  };
+  // the logits' accumulators start from the mask of block bi (0 where the
+  // key is selected, -inf where not; the table of prefill_kernel)
+  auto mask_init = [&](int bi) {
+    const uint32_t bits[2] = {nbits[0], nbits[1]};
+    if (bi + 1 < nblk) load_bits(bi + 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t wbits = bits[i] >> (4 * lh);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t m4 = *(const f32x4_t*)(&mask_tab[(wbits >> (8 * g)) & 0xFu][0]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) st[i][4 * g + jj] = m4[jj];
+      }
+    }
+  };
+  auto s_part = [&](int j) {
+    mask_init(j);
+    const uint16_t* Kb = Ks[j & 1];
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Kb[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
+        st[i] = mfma32x32x16(a, bq[ks], st[i]);
+      }
+  };
+  auto mfma_phase = [&](int j) {
+    if (j > 0) {
+      // each MFMA's operands (two transposing reads) are read about four
+      // MFMAs ahead: eight reads first, then two per MFMA (without the hint
+      // the compiler reads one operand ahead and every MFMA waits on LDS)
+      pv_part(j);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+    if (j < nblk) {
+      s_part(j);  // the K reads of prefill_kernel's hint: mask table and four K ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+      for (int r = 0; r < 2 * KSQ; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  // VALU phase: masked online softmax of the latest S into P (prefill_kernel's arithmetic)
+  auto softmax = [&]() {
+    float mx3[11];
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+      const int e0 = 3 * r;
+      const float a = st[e0 >> 4][e0 & 15], bb = st[(e0 + 1) >> 4][(e0 + 1) & 15],
+                  c = st[(e0 + 2) >> 4][(e0 + 2) & 15];
+      mx3[r] = __builtin_fmaxf(__builtin_fmaxf(a, bb), c);
+    }
+    mx3[10] = __builtin_fmaxf(st[1][14], st[1][15]);
+    float mx = max3_f32(max3_f32(mx3[0], mx3[1], mx3[2]), max3_f32(mx3[3], mx3[4], mx3[5]),
+                        max3_f32(mx3[6], mx3[7], mx3[8]));
+    mx = max3_f32(mx, mx3[9], mx3[10]);
+    mx = max_other_half(mx);
+    const bool bump = mx > m + lazy_thr;
+    const bool resc = bump && (m != -INFINITY);
+    const float mnew = bump ? mx : m;
+    const float nms = (mnew == -INFINITY) ? 0.0f : -mnew * scale_log2;
+    const float alpha = resc ? exp2_hw((m - mnew) * scale_log2) : 1.0f;
+    m = mnew;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = exp2_hw(fmaf(st[i][e], scale_log2, nms));
+        const float p1 = exp2_hw(fmaf(st[i][e + 1], scale_log2, nms));
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(pp, psum);
+        pk[i][e >> 3][(e & 7) >> 1] = pp;
+      }
+    l = l * alpha + psum;
+    if (__any(resc)) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
+  };
+
+  // Phase 2j: A computes block j on MFMA; B runs the softmax of block j-1 and
+  // stages V(j) (its buffer last held V(j-2), read up to phase 2j-1).
+  // Phase 2j+1: A runs the softmax of block j and stages K(j+1) (its buffer
+  // last held K(j-1), read up to phase 2j-1); B computes block j on MFMA.
+  // Each group runs its own loop (so that only its own state is live across
+  // iterations); both execute 2 nblk + 2 barriers.
+  load_bits(0);
+  if (grp == 0) {
+    load_k(0);
+    store_k(0);
+    if (nblk > 1) load_k(1);
+    __syncthreads();
+    for (int j = 0; j <= nblk; ++j) {
+      mfma_phase(j);
+      __syncthreads();
+      if (j < nblk) {
+        softmax();
+        if (j + 1 < nblk) {
+          store_k((j + 1) & 1);
+          if (j + 2 < nblk) load_k(j + 2);
+        }
+        __syncthreads();
+      }
+    }
+  } else {
+    load_v(0);
+    __syncthreads();
+    for (int j = 0; j <= nblk; ++j) {
+      if (j > 0) softmax();
+      if (j < nblk) {
+        store_v(j & 1);
+        if (j + 1 < nblk) load_v(j + 1);
+      }
+      __syncthreads();
+      mfma_phase(j);
+      if (j < nblk) __syncthreads();
+    }
+  }
+
+  // ---- normalise, gate, store
+  const float ltot = sum_other_half(l);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (!svalid) return;
+  float g1 = 1.0f;
+  if (gate_dim == 1) g1 = sigmoid_f32(bf16_to_f32(gate[qrow * H + h]));
+  uint16_t* orow = out + (qrow * H + h) * DV;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dv0 = 32 * d + 8 * g + 4 * lh;
+      float r4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float gg = g1;
+        if (gate_dim > 1) gg = sigmoid_f32(bf16_to_f32(gate[(qrow * H + h) * DV + dv0 + r]));
+        r4[r] = o[d][4 * g + r] * inv * gg;
+      }
+      uint2 pkd;
+      pkd.x = pack_bf16x2(r4[0], r4[1]);
+      pkd.y = pack_bf16x2(r4[2], r4[3]);
+      *(uint2*)(orow + dv0) = pkd;
+    }
+  }
+}
+
 // Combines the splits of each split tile: out = sum_s 2^(c(m_s - M)) O_s /
 // sum_s 2^(c(m_s - M)) l_s, then the gate. A workgroup covers 8 query rows
 // of one (tile, head, b), 32 threads per row and 4 output dims per thread,
@@ -634,6 +965,14 @@ hipError_t launch_dims(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        float scale_log2, int gate_dim, float* part, hipStream_t st) {
   const SplitPlan pl = make_split_plan(B, S, Tbuf, P, H, kv_offset, window);
   if (pl.items != pl.nqt && part == nullptr) return hipErrorInvalidValue;  // no partial buffer
+  if constexpr (DQK <= 192 && DV <= 128) {
+    const int nqt2 = (int)(((int64_t)S + kBQ2 - 1) / kBQ2);
+    if (window <= 0 && n_sink == 0 && pl.items == pl.nqt && (int64_t)B * H * nqt2 >= kPingPongMinGrid) {
+      hipLaunchKernelGGL((prefill_pp_kernel<DQK, DV>), dim3(nqt2, H, B), dim3(512), 0, st, q, k,
+                         v, bm, gate, out, S, Tbuf, P, H, Hkv, W32, scale_log2, gate_dim, nqt2);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(pl.items, H, B);
 #define DSA_FLASH_LAUNCH(MK, SK)                                                                 \
   hipLaunchKernelGGL((prefill_kernel<DQK, DV, MK, SK>), grid, dim3(256), 0, st, q, k, v, sk, sv,   \

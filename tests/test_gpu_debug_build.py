@@ -5,7 +5,8 @@ Every entry point runs once per library on the same inputs, at shapes that
 reach each kernel path: the indexer's tile and rows kernels (alone and fused
 with the top-k), the FP8 indexer,
 the top-k's single-stage, segmented and long-row paths (sorted and
-unsorted), the MFMA prefill with and without split tiles, the row gather for
+unsorted), the MFMA prefill with and without split tiles and its ping-pong
+form for large grids, the row gather for
 short and long-context prefill, decode with and without sinks and through the
 no-alloc entry, window attention (MFMA, gather, grouped heads, sinks) and both
 prologues. A failed device check makes the debug call return DSA_ERR_CHECK
@@ -115,6 +116,9 @@ def test_debug_build_attention():
     kd, vd = bf((3, 6000, H, Dqk), 26), bf((3, 6000, H, Dv), 27)
     ixd = sel(3, 1, 5999, 512, 28)
     kw, vw = bf((1, 400, 2, 256), 29), bf((1, 400, 2, 256), 30)                  # grouped KV, dims 256
+    # 128 heads x 8 tiles of 256 queries: the ping-pong prefill kernel, ragged
+    qP, kP, vP = bf((1, 2000, 128, Dqk), 33, Dqk ** -0.5), bf((1, 2000, 128, Dqk), 34), bf((1, 2000, 128, Dv), 35)
+    gP, ixP = bf((1, 2000, 128), 36), sel(1, 2000, 0, 128, 37)
     qw, gw = bf((1, 200, 8, 256), 31, 1 / 16), bf((1, 200, 8), 32)
 
     def run():
@@ -141,7 +145,9 @@ def test_debug_build_attention():
         dsa.swa_attn_gqa(qw, kw, vw, gw, o10, 200, 0, 128, 192, 64)       # grouped KV heads
         o11 = nan_like(1, 300, H, Dv)
         dsa.swa_attn_pas(q, kc, vc, sk, sv, g, o11, 0, 0, 64, N, R)
-        return [o, o2, o3, o4, o5, o6, o7, o8, o9, o10, o11]
+        o12 = nan_like(1, 2000, 128, Dv)
+        dsa.dsa_sparse_attn_prefill(qP, kP, vP, ixP, gP, o12, 0, N, R)     # ping-pong kernel
+        return [o, o2, o3, o4, o5, o6, o7, o8, o9, o10, o11, o12]
 
     ref, got = both(run)
     same(ref, got, "attention")

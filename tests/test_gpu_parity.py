@@ -347,6 +347,44 @@ def test_prefill_bf16_cases(B, S, P, H, nope, rope, Dv, k):
     _cmp_attn(got, ref, 2e-2, f"prefill {B, S, P, H, nope, rope, Dv, k}")
 
 
+# (B, S, P, H, nope, rope, Dv, k, gate): grids of at least 1024 workgroups of 256
+# queries (selection mask, no sinks, no split) take the ping-pong prefill kernel,
+# one case per head-dim pair it is built for; ragged last tiles, past context,
+# the elementwise gate. Checked rows: both 128-query groups of the first, a
+# middle and the last tile (their first, last and inner rows) plus random rows.
+PINGPONG_CASES = [
+    (1, 2085, 37, 128, 128, 64, 128, 256, "head"), (2, 1024, 0, 128, 64, 64, 128, 300, "head"),
+    (1, 2048, 100, 128, 64, 64, 64, 128, "elem"), (1, 2048, 0, 128, 32, 32, 64, 64, "head"),
+    (1, 1800, 5, 160, 64, 32, 64, 96, "head"), (1, 1800, 5, 160, 64, 32, 128, 96, "none"),
+]
+
+
+def _pp_rows(S, seed):
+    nt = (S + 255) // 256
+    rows = set()
+    for t in (0, nt // 2, nt - 1):
+        for r in (0, 31, 100, 127, 128, 159, 254, 255):
+            rows.add(min(t * 256 + r, S - 1))
+    rows |= set(np.random.default_rng(seed).integers(0, S, 16).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("B,S,P,H,nope,rope,Dv,k,gk", PINGPONG_CASES)
+def test_prefill_pingpong_cases(B, S, P, H, nope, rope, Dv, k, gk):
+    assert B * H * ((S + 255) // 256) >= 1024  # the grid that selects the ping-pong kernel
+    hi = _attn_case(B, S, P, H, nope, rope, Dv, seed=S + H + Dv)
+    idx = datagen.indices_host(0, B * S, S, P, k, seed=S + k).reshape(B, S, k)
+    gate = {"none": None, "head": hi["gate"],
+            "elem": datagen.normal_host((B, S, H, Dv), "bf16", 5, 8, 1.0)}[gk]
+    got = _run_prefill(hi, idx, P, nope, rope, gate)
+    for b in range(B):
+        for s in _pp_rows(S, seed=S + b):
+            g = None if gate is None else gate[b:b + 1, s:s + 1]
+            ref = oracle.sparse_attn(hi["q"][b:b + 1, s:s + 1], hi["k"][b:b + 1], hi["v"][b:b + 1],
+                                     idx[b:b + 1, s:s + 1], g, P + s, nope, rope)
+            _cmp_attn(got[b:b + 1, s:s + 1], ref, 2e-2, f"ping-pong {B, S, P, H, nope, rope, Dv, k} b{b} s{s}")
+
+
 @pytest.mark.parametrize("gate_kind", ["none", "elementwise", "limits"])
 def test_prefill_gate_modes(gate_kind):
     B, S, P, H, nope, rope, Dv, k = 1, 150, 20, 3, 128, 64, 128, 48
