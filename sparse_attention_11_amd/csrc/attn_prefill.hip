@@ -661,14 +661,22 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   for (int d = 0; d < NDB; ++d) o[d] = zero16();
   f32x16_t st[2] = {zero16(), zero16()};
   uint32_t pk[2][2][4] = {};
-  const uint32_t* bmrow = bm + qrow * (int64_t)W32;
+  // bitmap words of the next block, loaded unconditionally (clamped to the
+  // row) so that no control flow merges them; words past the row are
+  // cleared where they are used. They go through a buffer resource like the
+  // K and V loads: loads of one kind return in order, so the wait for these
+  // words skips the K or V prefetch issued after them.
+  // (the resource starts at the wave's first row, which is wave-uniform; each
+  // lane's row is an offset: a per-lane resource would serialise the loads)
+  const int rowbase = __builtin_amdgcn_readfirstlane(min(q0 + 32 * wave, S - 1));
+  const auto bmr = make_rsrc(bm + ((int64_t)b * S + rowbase) * W32, (int64_t)32 * W32 * 4);
+  const uint32_t boff = (uint32_t)(sc - rowbase) * (uint32_t)W32 * 4u;
   uint32_t nbits[2];
   auto load_bits = [&](int bi) {
-    const int w0 = 2 * bi;  // block bi covers bitmap words 2 bi, 2 bi + 1
-    nbits[0] = (w0 < W32) ? bmrow[w0] : 0u;
-    nbits[1] = (w0 + 1 < W32) ? bmrow[w0 + 1] : 0u;
+    const int w0 = min(2 * bi, W32 - 1), w1 = min(2 * bi + 1, W32 - 1);
+    nbits[0] = __builtin_amdgcn_raw_buffer_load_b32(bmr, boff + 4 * w0, 0, 0);
+    nbits[1] = __builtin_amdgcn_raw_buffer_load_b32(bmr, boff + 4 * w1, 0, 0);
   };
-
   // MFMA phase of block j: O += V(j-1)^T P(j-1)^T (j > 0), then S(j) (j < nblk);
   // P and S are never live together
   auto pv_part = [&](int j) {
@@ -689,8 +697,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   // the logits' accumulators start from the mask of block bi (0 where the
   // key is selected, -inf where not; the table of prefill_kernel)
   auto mask_init = [&](int bi) {
-    const uint32_t bits[2] = {nbits[0], nbits[1]};
-    if (bi + 1 < nblk) load_bits(bi + 1);
+    const uint32_t bits[2] = {2 * bi < W32 ? nbits[0] : 0u, 2 * bi + 1 < W32 ? nbits[1] : 0u};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t wbits = bits[i] >> (4 * lh);
@@ -712,34 +719,50 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
         const bf16x8_t a = as_bf16x8(*(const u32x4_t*)(&Kb[(32 * i + ln) * KPAD + 16 * ks + 8 * lh]));
         st[i] = mfma32x32x16(a, bq[ks], st[i]);
       }
+    load_bits(min(j + 1, nblk - 1));
   };
   // The wave in its MFMA phase runs at raised issue priority, so that when
   // both waves of a SIMD are ready the arbiter issues its MFMAs and operand
   // reads before the other wave's softmax (dsa-s32k 42.4 -> 39.6 ms; level 3
   // measures the same, raising the softmax phase instead gains nothing).
-  auto mfma_phase = [&](int j) {
+  // Each MFMA's PV operands (two transposing reads) are read about four MFMAs
+  // ahead: eight reads first, then two per MFMA (without the hint the compiler
+  // reads one operand ahead and every MFMA waits on LDS); the K reads follow
+  // prefill_kernel's hint (mask table and four K reads ahead).
+  auto pv_hint = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+  auto s_hint = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int r = 0; r < 2 * KSQ; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto mfma_first = [&]() {  // block 0: S only
     __builtin_amdgcn_s_setprio(1);
-    if (j > 0) {
-      // each MFMA's operands (two transposing reads) are read about four
-      // MFMAs ahead: eight reads first, then two per MFMA (without the hint
-      // the compiler reads one operand ahead and every MFMA waits on LDS)
-      pv_part(j);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-    if (j < nblk) {
-      s_part(j);  // the K reads of prefill_kernel's hint: mask table and four K ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-      for (int r = 0; r < 2 * KSQ; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
+    s_part(0);
+    s_hint();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto mfma_full = [&](int j) {  // 0 < j < nblk: PV(j-1), then S(j)
+    __builtin_amdgcn_s_setprio(1);
+    pv_part(j);
+    pv_hint();
+    s_part(j);
+    s_hint();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto mfma_last = [&]() {  // after the last block: PV(nblk-1) only
+    __builtin_amdgcn_s_setprio(1);
+    pv_part(nblk);
+    pv_hint();
     __builtin_amdgcn_s_setprio(0);
   };
   // VALU phase: masked online softmax of the latest S into P (prefill_kernel's arithmetic)
@@ -788,38 +811,53 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   // Phase 2j+1: A runs the softmax of block j and stages K(j+1) (its buffer
   // last held K(j-1), read up to phase 2j-1); B computes block j on MFMA.
   // Each group runs its own loop (so that only its own state is live across
-  // iterations); both execute 2 nblk + 2 barriers.
+  // iterations), with the first and last block peeled so that the loop body
+  // is straight-line code, and every prefetch is issued unconditionally
+  // (block index clamped to the last block; a stage past it lands in a buffer
+  // nobody reads again): no control flow merges in-flight registers, which
+  // would make the compiler wait for the loads. Both groups execute
+  // 2 nblk + 2 barriers.
   load_bits(0);
   if (grp == 0) {
     load_k(0);
     store_k(0);
-    if (nblk > 1) load_k(1);
+    load_k(min(1, nblk - 1));
     __syncthreads();
-    for (int j = 0; j <= nblk; ++j) {
-      mfma_phase(j);
+    mfma_first();
+    __syncthreads();
+    softmax();
+    store_k(1);
+    load_k(min(2, nblk - 1));
+    __syncthreads();
+    for (int j = 1; j < nblk; ++j) {
+      mfma_full(j);
       __syncthreads();
-      if (j < nblk) {
-        softmax();
-        if (j + 1 < nblk) {
-          store_k((j + 1) & 1);
-          if (j + 2 < nblk) load_k(j + 2);
-        }
-        __syncthreads();
-      }
+      softmax();
+      store_k((j + 1) & 1);
+      load_k(min(j + 2, nblk - 1));
+      __syncthreads();
     }
+    mfma_last();
+    __syncthreads();
   } else {
     load_v(0);
     __syncthreads();
-    for (int j = 0; j <= nblk; ++j) {
-      if (j > 0) softmax();
-      if (j < nblk) {
-        store_v(j & 1);
-        if (j + 1 < nblk) load_v(j + 1);
-      }
+    store_v(0);
+    load_v(min(1, nblk - 1));
+    __syncthreads();
+    mfma_first();
+    __syncthreads();
+    for (int j = 1; j < nblk; ++j) {
+      softmax();
+      store_v(j & 1);
+      load_v(min(j + 1, nblk - 1));
       __syncthreads();
-      mfma_phase(j);
-      if (j < nblk) __syncthreads();
+      mfma_full(j);
+      __syncthreads();
     }
+    softmax();
+    __syncthreads();
+    mfma_last();
   }
 
   // ---- normalise, gate, store
