@@ -177,10 +177,14 @@ __global__ __launch_bounds__(256, 2) void idx_tile_kernel(const uint16_t* __rest
           f32x4_t acc[8];
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) acc[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          // raised issue priority for the MFMA burst, so that the other wave
+          // of the SIMD fills it with its ReLU/weight work (dsa-s32k about 1%)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) acc[kb] = mfma16x16x32(a[kb][ks], bq[ks], acc[kb]);
+          __builtin_amdgcn_s_setprio(0);
           const float wh = (st * G + g < HI) ? bf16_to_f32(wc[qg][g]) * scale : 0.0f;
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb)
