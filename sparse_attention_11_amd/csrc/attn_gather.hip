@@ -3,11 +3,14 @@
 // For few queries (decode: one token per sequence) the work is a stream of
 // whole selected cache rows: with token-major caches one selected position is
 // one contiguous [H, D] row (A.X-K2 page: the cache holds expanded K/V; the
-// indexer's positions are shared by all heads). The selection is split into
-// chunks; a workgroup takes one chunk for 32 heads, keeps an online softmax
-// per head and writes a partial state (m, l, o[Dv]); the merge kernel
-// combines the chunks, applies the sigmoid gate (A.X-K2 page, "Attention
-// output gate"; Spark-X2.5 page, forward pass) and stores the output.
+// indexer's positions are shared by all heads). Split form: the selection is
+// split into chunks; a workgroup takes one chunk for 32 heads, keeps an
+// online softmax per head and writes a partial state (m, l, o[Dv]); the merge
+// kernel combines the chunks, applies the sigmoid gate (A.X-K2 page,
+// "Attention output gate"; Spark-X2.5 page, forward pass) and stores the
+// output. Whole-row form (bf16 grids of at least 256 (row, head) pairs):
+// one workgroup per (row, head) whose 32 lane groups take slices of the list
+// and are combined in LDS, with no partial states and no second launch.
 //
 // Lane layout: 8 lanes per head, 8 heads per wave, 4 waves = 32 heads. A
 // head's K row (Dqk elements) is read as 16-byte chunks, lane j of the head
@@ -53,66 +56,25 @@ struct Elem<1> {  // bf16
   }
 };
 
+// Online softmax over the entries [e0, e1) of one query row for one head:
+// the 8 lanes of the head (lane `sub` holds chunks sub, sub + 8, ...) load G
+// tokens' K and V chunks at once, reduce the logits over the 8 lanes and
+// update (m, l, o): o unnormalised, m in log2 units (qf is pre-scaled).
 // WIN 0: indices list; WIN 1: window p, p-1, ..., p-window+1.
 // KC / VC: 16-byte chunks per lane of a head's K / V row (chunk c of a row
 // belongs to lane c % 8 of the head's 8 lanes). G: tokens whose loads are in
-// flight together (a split of G entries waits on a single round of loads).
+// flight together.
 template <int DT, int WIN, int KC, int VC, int G>
-__global__ __launch_bounds__(256) void gather_kernel(
-    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
-    const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
-    const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
-    int kv_offset, int H, int HKV, int DQK, int DV, int nent, int per_split, int nsplit,
-    int window, float scale_log2) {
+__device__ __forceinline__ void gather_span(
+    const float (&qf)[KC][Elem<DT>::kPer16], const char* __restrict__ kb,
+    const char* __restrict__ vb, const char* __restrict__ skb, const char* __restrict__ svb,
+    int n_sink, const int32_t* __restrict__ irow, int e0, int e1, int p, int64_t kvrow0,
+    int Tbuf, int kv_offset, int window, int hk, int HKV, int DQK, int DV, int sub, int lane,
+    float& m, float& l, float (&o)[VC][Elem<DT>::kPer16]) {
   using E = Elem<DT>;
   constexpr int EP = E::kPer16;
   constexpr int esz = DT ? 2 : 4;
-  const int split = (int)(blockIdx.x % (unsigned)nsplit);
-  const int64_t row = blockIdx.x / (unsigned)nsplit;
-  const int b = (int)(row / S), s = (int)(row % S);
-  const int p = P + s;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane & 7;
-  const int h = 32 * blockIdx.y + 8 * wave + (lane >> 3);
-  const bool hvalid = h < H;
-  const int hh = hvalid ? h : H - 1;
-  const int hk = hh / (H / HKV);  // cache head: query heads come in groups of H / HKV
   const int nck = DQK / EP, ncv = DV / EP;
-
-  const char* qb = (const char*)qv;
-  const char* kb = (const char*)kv;
-  const char* vb = (const char*)vv;
-  const char* skb = (const char*)skv;
-  const char* svb = (const char*)svv;
-
-  float qf[KC][EP];
-#pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    const int c = sub + 8 * i;
-#pragma unroll
-    for (int e = 0; e < EP; ++e) qf[i][e] = 0.0f;
-    if (c < nck) {
-      const u32x4_t x = load16(qb + ((row * H + hh) * (int64_t)DQK + c * EP) * esz);
-      E::unpack(x, qf[i]);
-#pragma unroll
-      for (int e = 0; e < EP; ++e) qf[i][e] *= scale_log2;
-    }
-  }
-
-  float m = -INFINITY, l = 0.0f;
-  float o[VC][EP];
-#pragma unroll
-  for (int i = 0; i < VC; ++i)
-#pragma unroll
-    for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
-
-  // entries 0 .. n_sink-1 are the sinks, n_sink .. nent-1 the list
-  const int e0 = split * per_split;
-  const int e1 = min(nent, e0 + per_split);
-  const int nlist = nent - n_sink;
-  const int32_t* irow = idx + row * (int64_t)nlist;
-  const int64_t kvrow0 = (int64_t)b * Tbuf;
-
   auto pos_of = [&](int ent) -> int {  // (sink entries: unused)
     const int le = ent - n_sink;
     if (WIN) return p - le;
@@ -125,7 +87,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
   for (int base = e0; base < e1; base += G) {
     int jrow[G];
     bool ok[G];
-    bool snk[G];  // wave-uniform: entries are the same for every lane
+    bool snk[G];  // uniform over the head's 8 lanes: they share their entries
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int ent = base + g;
@@ -210,6 +172,68 @@ __global__ __launch_bounds__(256) void gather_kernel(
       }
     }
   }
+}
+
+// The query's chunks of one head, pre-scaled by scale * log2(e).
+template <int DT, int KC>
+__device__ __forceinline__ void load_q(const void* __restrict__ qv, int64_t row, int H, int hh,
+                                       int DQK, int sub, float scale_log2,
+                                       float (&qf)[KC][Elem<DT>::kPer16]) {
+  using E = Elem<DT>;
+  constexpr int EP = E::kPer16;
+  constexpr int esz = DT ? 2 : 4;
+  const int nck = DQK / EP;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = sub + 8 * i;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) qf[i][e] = 0.0f;
+    if (c < nck) {
+      const u32x4_t x = load16((const char*)qv + ((row * H + hh) * (int64_t)DQK + c * EP) * esz);
+      E::unpack(x, qf[i]);
+#pragma unroll
+      for (int e = 0; e < EP; ++e) qf[i][e] *= scale_log2;
+    }
+  }
+}
+
+// Split-K form: a workgroup takes entries split*per_split .. of one row for
+// 32 heads (8 per wave) and writes their partial states for merge_kernel.
+template <int DT, int WIN, int KC, int VC, int G>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
+    const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
+    const int32_t* __restrict__ idx, float* __restrict__ part, int S, int Tbuf, int P,
+    int kv_offset, int H, int HKV, int DQK, int DV, int nent, int per_split, int nsplit,
+    int window, float scale_log2) {
+  constexpr int EP = Elem<DT>::kPer16;
+  const int split = (int)(blockIdx.x % (unsigned)nsplit);
+  const int64_t row = blockIdx.x / (unsigned)nsplit;
+  const int b = (int)(row / S), s = (int)(row % S);
+  const int p = P + s;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 7;
+  const int h = 32 * blockIdx.y + 8 * wave + (lane >> 3);
+  const bool hvalid = h < H;
+  const int hh = hvalid ? h : H - 1;
+  const int hk = hh / (H / HKV);  // cache head: query heads come in groups of H / HKV
+  const int ncv = DV / EP;
+
+  float qf[KC][EP];
+  load_q<DT, KC>(qv, row, H, hh, DQK, sub, scale_log2, qf);
+  float m = -INFINITY, l = 0.0f;
+  float o[VC][EP];
+#pragma unroll
+  for (int i = 0; i < VC; ++i)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
+  // entries 0 .. n_sink-1 are the sinks, n_sink .. nent-1 the list
+  const int e0 = split * per_split;
+  const int e1 = min(nent, e0 + per_split);
+  const int32_t* irow = idx + row * (int64_t)(nent - n_sink);
+  gather_span<DT, WIN, KC, VC, G>(qf, (const char*)kv, (const char*)vv, (const char*)skv,
+                                  (const char*)svv, n_sink, irow, e0, e1, p, (int64_t)b * Tbuf,
+                                  Tbuf, kv_offset, window, hk, HKV, DQK, DV, sub, lane, m, l, o);
 
   if (!hvalid) return;
   // partial state: [row][split][h][DV + 4] = o[0..DV), m, l (16-byte rows)
@@ -226,6 +250,88 @@ __global__ __launch_bounds__(256) void gather_kernel(
     pr[DV] = m;
     pr[DV + 1] = l;
   }
+}
+
+// Whole-row form (no partial states, no merge launch): one workgroup per
+// (row, head); its 32 groups of 8 lanes take contiguous slices of the row's
+// entries, and their (m, l, o) are combined in LDS as merge_kernel combines
+// splits, then gated and stored.
+constexpr int kWgGroups = 32;
+template <int DT, int WIN, int KC, int VC, int G>
+__global__ __launch_bounds__(256) void gather_wg_kernel(
+    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
+    const void* __restrict__ skv, const void* __restrict__ svv, int n_sink,
+    const int32_t* __restrict__ idx, const void* __restrict__ gate, void* __restrict__ out,
+    int S, int Tbuf, int P, int kv_offset, int H, int HKV, int DQK, int DV, int nent,
+    int window, float scale_log2, int gate_dim) {
+  constexpr int EP = Elem<DT>::kPer16;
+  constexpr int kDVMax = 8 * VC * EP;  // largest DV this instantiation serves
+  __shared__ float gm[kWgGroups], gl[kWgGroups];
+  __shared__ float go[kWgGroups][kDVMax];
+  __shared__ float wsh[kWgGroups];
+  const int64_t rh = blockIdx.x;  // row * H + h
+  const int64_t row = rh / H;
+  const int h = (int)(rh % H);
+  const int b = (int)(row / S), s = (int)(row % S);
+  const int p = P + s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid >> 3, sub = lane & 7;
+  const int hk = h / (H / HKV);
+  const int ncv = DV / EP;
+
+  float qf[KC][EP];
+  load_q<DT, KC>(qv, row, H, h, DQK, sub, scale_log2, qf);
+  float m = -INFINITY, l = 0.0f;
+  float o[VC][EP];
+#pragma unroll
+  for (int i = 0; i < VC; ++i)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) o[i][e] = 0.0f;
+  const int per = (nent + kWgGroups - 1) / kWgGroups;
+  const int e0 = min(nent, grp * per), e1 = min(nent, e0 + per);
+  const int32_t* irow = idx + row * (int64_t)(nent - n_sink);
+  gather_span<DT, WIN, KC, VC, G>(qf, (const char*)kv, (const char*)vv, (const char*)skv,
+                                  (const char*)svv, n_sink, irow, e0, e1, p, (int64_t)b * Tbuf,
+                                  Tbuf, kv_offset, window, hk, HKV, DQK, DV, sub, lane, m, l, o);
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    const int c = sub + 8 * i;
+    if (c < ncv) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e) go[grp][c * EP + e] = o[i][e];
+    }
+  }
+  if (sub == 0) {
+    gm[grp] = m;
+    gl[grp] = l;
+  }
+  __syncthreads();
+  // weights 2^(m_g - M) over the groups (M = the largest m), as merge_kernel
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kWgGroups; ++g) M = fmaxf(M, gm[g]);
+  const float Muse = (M == -INFINITY) ? 0.0f : M;
+  if (tid < kWgGroups) wsh[tid] = gm[tid] != -INFINITY ? exp2f(gm[tid] - Muse) : 0.0f;
+  __syncthreads();
+  if (tid >= DV) return;
+  float L = 0.0f, acc = 0.0f;
+#pragma unroll
+  for (int g = 0; g < kWgGroups; ++g) {
+    L = fmaf(wsh[g], gl[g], L);
+    acc = fmaf(go[g][tid], wsh[g], acc);
+  }
+  float gg = 1.0f;
+  if (gate_dim == 1)
+    gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh]) : ((const float*)gate)[rh]);
+  else if (gate_dim > 1)
+    gg = sigmoid_f32(DT ? bf16_to_f32(((const uint16_t*)gate)[rh * DV + tid])
+                        : ((const float*)gate)[rh * DV + tid]);
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const float r = acc * inv * gg;
+  if (DT)
+    ((uint16_t*)out)[rh * DV + tid] = f32_to_bf16(r);
+  else
+    ((float*)out)[rh * DV + tid] = r;
 }
 
 // One workgroup per (row, head). Thread i < nsplit reads split i's (m, l) and
@@ -388,6 +494,43 @@ hipError_t launch_gather(const void* q, const void* k, const void* v, const void
                          hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
   const int nent = n_sink + (window > 0 ? window : topk);
+  const float sl2w = sm_scale * DSA_LOG2E;
+  // bf16 calls whose (row, head) grid fills the GPU take the whole-row kernel
+  // (no partial states, no merge launch): decode-b8 245 -> 239 us back to
+  // back. Few rows stay split across the GPU: one 2048-entry row of 32 heads
+  // takes 17.5 us split and 36 us whole-row (one CU's bandwidth per head);
+  // a 512-key window of 32 heads gains 1 us back to back but nothing inside
+  // the decode step, and dims 256 lose (14 -> 18 us at spark-swa).
+  if (dtype == 1 && Dv <= 256 && Dqk <= 256 && rows * H >= 256) {
+    if (rows * H > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+#define DSA_WG_LAUNCH(WIN, KC, VC)                                                                 \
+  hipLaunchKernelGGL((gather_wg_kernel<1, WIN, KC, VC, 2 * kG>), dim3((unsigned)(rows * H)), \
+                     dim3(256), 0, st, q, k, v, sink_k, sink_v, n_sink, indices, gate, out, S, T,   \
+                     past_len, kv_offset, H, Hkv, Dqk, Dv, nent, window, sl2w, gate_dim)
+#define DSA_WG_VC(WIN, KC)                       \
+  switch ((Dv + 63) / 64) {                      \
+    case 1: DSA_WG_LAUNCH(WIN, KC, 1); break;    \
+    case 2: DSA_WG_LAUNCH(WIN, KC, 2); break;    \
+    case 3: DSA_WG_LAUNCH(WIN, KC, 3); break;    \
+    default: DSA_WG_LAUNCH(WIN, KC, 4); break;   \
+  }
+#define DSA_WG_KC(WIN)                           \
+  switch ((Dqk + 63) / 64) {                     \
+    case 1: DSA_WG_VC(WIN, 1); break;            \
+    case 2: DSA_WG_VC(WIN, 2); break;            \
+    case 3: DSA_WG_VC(WIN, 3); break;            \
+    default: DSA_WG_VC(WIN, 4); break;           \
+  }
+    if (window > 0) {
+      DSA_WG_KC(1)
+    } else {
+      DSA_WG_KC(0)
+    }
+#undef DSA_WG_KC
+#undef DSA_WG_VC
+#undef DSA_WG_LAUNCH
+    return hipGetLastError();
+  }
   const Plan pl = make_plan(rows, H, nent);
   float* part = (float*)workspace;
   const dim3 grid((unsigned)(rows * pl.nsplit), (H + 31) / 32);

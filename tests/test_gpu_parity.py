@@ -430,9 +430,12 @@ def test_prefill_fp32_gather_path():
 
 
 # ---------------------------------------------------------------- decode
+# bf16 calls with rows x heads >= 256 take the whole-row decode kernel, the
+# others the split form and its merge
 @pytest.mark.parametrize("B,T,H,nope,rope,Dv,k,dt", [
     (3, 3000, 16, 128, 64, 128, 256, "bf16"), (2, 700, 4, 64, 64, 128, 700, "bf16"),
     (1, 5000, 8, 128, 64, 128, 2048, "bf16"), (2, 300, 4, 32, 16, 32, 64, "f32"),
+    (2, 4000, 160, 64, 32, 64, 1000, "bf16"),
 ])
 def test_decode_cases(B, T, H, nope, rope, Dv, k, dt):
     P = T - 1
@@ -584,6 +587,7 @@ def test_prefill_sinks_only_when_selection_is_empty():
 @pytest.mark.parametrize("B,T,H,nope,rope,Dv,k,n_sink,dt", [
     (3, 3000, 16, 128, 64, 128, 256, 128, "bf16"), (1, 5000, 8, 128, 64, 128, 2048, 200, "bf16"),
     (2, 300, 4, 32, 16, 32, 64, 3, "f32"),
+    (2, 3000, 128, 128, 64, 128, 300, 64, "bf16"),  # whole-row kernel (2 x 128 pairs)
 ])
 def test_decode_with_sinks(B, T, H, nope, rope, Dv, k, n_sink, dt):
     P = T - 1
