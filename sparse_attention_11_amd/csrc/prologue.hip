@@ -40,6 +40,8 @@
 // A lane holds four consecutive output columns, so every interleaved rotary
 // pair (2j, 2j + 1) is in one lane and no group of four straddles a head or
 // a slice (every width is a multiple of 16).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -185,9 +187,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
   const int N = second ? o2.N : o1.N, ldc = second ? o2.ldc : o1.ldc;
   const int n0 = (second ? nt - nt1 : nt) * kGBN;
 
-  // global -> register staging of the next K step (16-byte chunks)
-  u32x4_t ra[kGLdA], rw[kGLdW];
-  auto load_tile = [&](int k0) {
+  // global -> register staging, two K steps ahead: the data of step s is
+  // loaded at the start of step s - 2 into register set s & 1 and written to
+  // LDS at the end of step s - 1, so each load has two steps of MFMAs to land
+  u32x4_t ra[2][kGLdA], rw[2][kGLdW];
+  auto load_tile = [&](auto set_c, int k0) {
+    constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < kGLdA; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
@@ -198,26 +203,27 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
       const uint16_t* src = (EPI != 1 || k < ga.K1)
                                 ? ga.A1 + (int64_t)m * (EPI == 1 ? ga.K1 : K) + k
                                 : ga.A2 + (int64_t)m * (K - ga.K1) + (k - ga.K1);
-      ra[i] = (m < M && kin) ? load16(src) : u32x4_t{0, 0, 0, 0};
+      ra[SET][i] = (m < M && kin) ? load16(src) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < kGLdW; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
       const int n = n0 + r;
       const bool kin = k0 + kc < K;
-      rw[i] = (n < N && kin) ? load16(W + (int64_t)n * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+      rw[SET][i] = (n < N && kin) ? load16(W + (int64_t)n * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set_c, int buf) {
+    constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < kGLdA; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      *(u32x4_t*)(&As[buf][r * kGPad + kc]) = ra[i];
+      *(u32x4_t*)(&As[buf][r * kGPad + kc]) = ra[SET][i];
     }
 #pragma unroll
     for (int i = 0; i < kGLdW; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      *(u32x4_t*)(&Ws[buf][r * kGPad + kc]) = rw[i];
+      *(u32x4_t*)(&Ws[buf][r * kGPad + kc]) = rw[SET][i];
     }
   };
 
@@ -227,13 +233,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-  const int nk = (K + kGBK - 1) / kGBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * kGBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < kGBK / 16; ++s) {
       bf16x8_t a[kWI], b[2];
@@ -252,10 +252,30 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     }
+  };
+  const int nk = (K + kGBK - 1) / kGBK;
+  const std::integral_constant<int, 0> S0;
+  const std::integral_constant<int, 1> S1;
+  // one K step: loads of step kt + 2 into set kt & 1 (written to LDS at the
+  // end of step kt - 1, so free), MFMAs on buffer kt & 1, then step kt + 1's
+  // data (loaded two steps ago) into the other buffer (last read before the
+  // previous barrier)
+  auto step = [&](int kt, auto cur, auto nxt) {
+    if (kt + 2 < nk) load_tile(cur, (kt + 2) * kGBK);
+    compute(decltype(cur)::value);
     if (kt + 1 < nk) {
-      store_tile(buf ^ 1);  // the other buffer was last read before the previous barrier
+      store_tile(nxt, decltype(nxt)::value);
       __syncthreads();
     }
+  };
+
+  load_tile(S0, 0);
+  if (nk > 1) load_tile(S1, kGBK);
+  store_tile(S0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, S0, S1);
+    if (kt + 1 < nk) step(kt + 1, S1, S0);
   }
   // the MFMA computes C^T: lane l holds C[m][n] for m = 32 i + l % 32 and
   // n = 32 j + 8 g + 4 (l / 32) + r (e = 4 g + r) of the wave's tile, so each
