@@ -159,14 +159,19 @@ template <int RHALF, int BM, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1, GemmOut o2,
                                                            int M, int K, int ntiles_n, int nt1,
                                                            GemmRope rp, GemmMla mla) {
-  constexpr int kGBM = BM, kGBK = gemm_bk<BM>(), kGPad = kGBK + 8;
+  constexpr int kGBM = BM, kGBK = gemm_bk<BM>();
   constexpr int kWM = BM / 2;                  // rows per wave (2 x 2 waves)
   constexpr int kWI = kWM / 32;                // 32-row MFMA blocks per wave
   constexpr int kCPR = kGBK / 8;               // 16-byte chunks per tile row
   constexpr int kGLdA = kGBM * kCPR / 256;     // A chunks per thread
   constexpr int kGLdW = kGBN * kCPR / 256;     // W chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGBM * kGPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGBN * kGPad];
+  // tile rows of kGBK bf16 without padding; the 16-byte chunk c of row r is
+  // stored at chunk c ^ ((r / (16 / kCPR)) % kCPR), so that both the stores
+  // (kCPR lanes per row, 16 / kCPR rows per 16 lanes) and the MFMA operand
+  // reads (16 rows, one chunk) of a 16-lane phase hit 64 distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGBM * kGBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGBN * kGBK];
+  auto swz = [](int r, int c) { return c ^ ((r / (16 / kCPR)) % kCPR); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int pid = blockIdx.x;
@@ -218,12 +223,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
 #pragma unroll
     for (int i = 0; i < kGLdA; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      *(u32x4_t*)(&As[buf][r * kGPad + kc]) = ra[SET][i];
+      *(u32x4_t*)(&As[buf][r * kGBK + 8 * swz(r, kc / 8)]) = ra[SET][i];
     }
 #pragma unroll
     for (int i = 0; i < kGLdW; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      *(u32x4_t*)(&Ws[buf][r * kGPad + kc]) = rw[SET][i];
+      *(u32x4_t*)(&Ws[buf][r * kGBK + 8 * swz(r, kc / 8)]) = rw[SET][i];
     }
   };
 
@@ -240,12 +245,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
 #pragma unroll
       for (int i = 0; i < kWI; ++i) {
         const int r = wm * kWM + 32 * i + (lane & 31);
-        a[i] = as_bf16x8(*(const u32x4_t*)(&As[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
+        a[i] = as_bf16x8(*(const u32x4_t*)(&As[buf][r * kGBK + 8 * swz(r, 2 * s + (lane >> 5))]));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = wn * 64 + 32 * j + (lane & 31);
-        b[j] = as_bf16x8(*(const u32x4_t*)(&Ws[buf][r * kGPad + 16 * s + 8 * (lane >> 5)]));
+        b[j] = as_bf16x8(*(const u32x4_t*)(&Ws[buf][r * kGBK + 8 * swz(r, 2 * s + (lane >> 5))]));
       }
 #pragma unroll
       for (int i = 0; i < kWI; ++i)
