@@ -221,7 +221,9 @@ int dsa_sparse_attn_prefill(const void* q, const void* k_cache, const void* v_ca
  * q [B,1,H,Dqk], caches [B,T,H,*], indices [B,1,topk], gate [B,1,H(,Dv)],
  * out [B,1,H,Dv].
  * workspace: at least dsa_sparse_attn_decode_workspace_size(...) bytes
- * (per-split partial softmax states).
+ * (per-split partial softmax states; bf16 calls with B * H >= 256 combine
+ * their partial states on chip and leave the workspace untouched, but the
+ * required size is the same).
  */
 size_t dsa_sparse_attn_decode_workspace_size(int B, int H, int v_dim, int topk);
 int dsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -408,6 +410,11 @@ int dsa_mla_prologue(const void* q_resid, const void* q_compressed, const void* 
  * n_items (items of a tile are its consecutive key ranges, first to last).
  * The prefill workspace is sized from the plan of past_len = T - S, which
  * has the most items any call with this T can have.
+ * A selection-mask call (window <= 0) without sinks whose plan splits
+ * nothing, with qk dim <= 192 and v dim <= 128, runs instead as 256-query
+ * tiles (two 128-query halves per workgroup, same key ranges) when
+ * B * H * ceil(S / 256) >= 1024; this function reports the 128-query plan,
+ * whose tile ranges those workgroups cover in pairs.
  * Returns DSA_OK, or DSA_ERR_INVALID_ARG for null outputs or bad sizes.
  */
 int dsa_prefill_work_plan(int B, int S, int T, int past_len, int H, int kv_offset, int window,
