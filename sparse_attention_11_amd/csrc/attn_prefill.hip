@@ -671,6 +671,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(
   const int rowbase = __builtin_amdgcn_readfirstlane(min(q0 + 32 * wave, S - 1));
   const auto bmr = make_rsrc(bm + ((int64_t)b * S + rowbase) * W32, (int64_t)32 * W32 * 4);
   const uint32_t boff = (uint32_t)(sc - rowbase) * (uint32_t)W32 * 4u;
+  DSA_CHECK(sc >= rowbase && sc - rowbase < 32, sc, rowbase);  // the lane's row is in the resource
   uint32_t nbits[2];
   auto load_bits = [&](int bi) {
     const int w0 = min(2 * bi, W32 - 1), w1 = min(2 * bi + 1, W32 - 1);
