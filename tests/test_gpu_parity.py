@@ -90,6 +90,10 @@ INDEX_CASES = [
     (2, 150, 600, 4, 128, 2),
     # T >= 8 S: one workgroup multiplies a key tile with both query tiles of its pair
     (1, 100, 3000, 8, 128, 0), (2, 37, 700, 3, 64, 1), (1, 50, 900, 70, 128, 2),
+    # per-head ReLU with 16+ heads at every dim, with partial last LDS stages,
+    # ragged query and key tiles, and the key-stationary form (T >= 8 S)
+    (1, 600, 0, 16, 32, 0), (1, 300, 0, 33, 32, 0), (2, 333, 1200, 20, 64, 0),
+    (1, 1000, 500, 64, 128, 0), (1, 100, 3000, 18, 128, 0), (2, 70, 900, 17, 64, 0),
 ]
 
 
@@ -248,6 +252,7 @@ INDEX_TOPK_CASES = [  # B, S, T, P, HI, DI, k, dtype
     (1, 8, 9000, 8992, 4, 32, 100, 1),       # few queries: rows indexer with causal rows
     (1, 3, 50000, 10000, 8, 64, 2048, 1),    # rows end long before T (long-row path, empty chunks)
     (1, 100, 100, 0, 2, 32, 16, 0),          # fp32
+    (1, 700, 700, 0, 32, 128, 256, 1),       # tile indexer with the weighted-query pass
 ]
 
 
