@@ -20,9 +20,17 @@
 //                    only tiles on or below the causal diagonal are launched,
 //                    paired (j, last-j) so every pair costs the same, pairs
 //                    dealt to XCDs round-robin.
-//  idx_rows_kernel   few-query calls (decode): the index heads become the
-//                    MFMA M axis; a wave streams 128 or 512 keys of k in blocks
-//                    of 32.
+//  idx_rows_dma_kernel  few-query calls (decode) with up to 64 index heads:
+//                    the index heads become the MFMA M axis; a wave streams 128
+//                    or 512 keys of k in blocks of 32 through a two-slot LDS
+//                    ring filled by LDS-DMA, each copy instruction reading 1 KB
+//                    of whole key rows (32-byte pieces of 32 rows, as register
+//                    loads in the operand layout take them, streamed at about
+//                    4 TB/s; whole rows, swizzled in LDS for conflict-free
+//                    operand reads, at about 5.8).
+//  idx_rows_kernel   the same products with the keys loaded into registers
+//                    one block ahead (more than 64 heads: their operands then
+//                    need the register file at one wave per SIMD).
 //  idx_f32_kernel    fp32 inputs: plain fp32 loops (parity-size workloads).
 #include "common.h"
 #include "idx_tiles.h"
@@ -325,6 +333,216 @@ __global__ __launch_bounds__(256) void idx_rows_kernel(const uint16_t* __restric
   }
 }
 
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// The KS B operands of one 32-key ring slot: operand ks of lane (ln, lh) is
+// chunk 2 ks + lh of key ln, found at ln CH 16 + 16 ((2 ks + lh) ^ (ln % CH))
+// (the slot layout of idx_rows_dma_kernel). The reads are issued and waited for
+// in one asm statement: the slot was filled by LDS-DMA, whose completion the
+// caller has already awaited with an exact vmcnt, and an LDS read the compiler
+// can see would make it wait for every copy still in flight instead. Waiting
+// inside the statement leaves no read in flight behind the compiler's back.
+#define DSA_RB_READ(d, a) "ds_read_b128 %" #d ", %" #a "\n\t"
+template <int KS, int CH>
+__device__ __forceinline__ void read_block(const uint8_t* slot, int ln, int lh,
+                                           bf16x8_t (&o)[KS]) {
+  const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)slot +
+                        (uint32_t)(ln * CH * 16);
+  uint32_t a[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a[ks] = base + 16u * (uint32_t)((2 * ks + lh) ^ (ln % CH));
+  // outputs early-clobber: no result may land in an address not yet used
+  u32x4_t r[KS];
+  if constexpr (KS == 8) {
+    asm volatile(DSA_RB_READ(0, 8) DSA_RB_READ(1, 9) DSA_RB_READ(2, 10) DSA_RB_READ(3, 11)
+                     DSA_RB_READ(4, 12) DSA_RB_READ(5, 13) DSA_RB_READ(6, 14)
+                         DSA_RB_READ(7, 15) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                   "=&v"(r[6]), "=&v"(r[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+                   "v"(a[7])
+                 : "memory");
+  } else if constexpr (KS == 4) {
+    asm volatile(DSA_RB_READ(0, 4) DSA_RB_READ(1, 5) DSA_RB_READ(2, 6) DSA_RB_READ(3, 7)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                 : "memory");
+  } else {
+    static_assert(KS == 2, "idx_dim 32, 64 or 128");
+    asm volatile(DSA_RB_READ(0, 2) DSA_RB_READ(1, 3) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1])
+                 : "v"(a[0]), "v"(a[1])
+                 : "memory");
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) o[ks] = as_bf16x8(r[ks]);
+}
+#undef DSA_RB_READ
+
+// Few queries per call, the keys streamed through LDS: the products of
+// idx_rows_kernel (same operands, same MFMA order, the same bits out), but a
+// wave's keys arrive by LDS-DMA into a ring of two 32-key blocks, so that two
+// blocks per wave are in flight while one is multiplied (the register form
+// holds one), and its scores are kept in registers and stored at the end, so
+// that the loop's only vector-memory operations are the block copies and
+// vmcnt counts blocks exactly. The two slots are separate LDS arrays indexed
+// statically (the loop is unrolled), which lets the compiler tell a slot
+// being copied into from the one being read.
+template <int DI, int NHB, int MODE, int KPW>
+__global__ __launch_bounds__(256, 2) void idx_rows_dma_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ w,
+                                                              float* __restrict__ scores, int S,
+                                                              int T, int P, int HI, float scale,
+                                                              int fill) {
+  constexpr int KS = DI / 16;  // 1 KB copies per block (32 keys x 16 dims x 2 bytes)
+  constexpr int CH = DI / 8;   // 16-byte chunks per key row
+  constexpr int NB = KPW / 32;
+  static_assert(NB >= 2, "two blocks in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[4][KS * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[4][KS * 1024];
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / S), s = (int)(row % S);
+  const int p = P + s;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 31, lh = lane >> 5;
+  const int tbase = (blockIdx.x * 4 + wave) * KPW;
+  DSA_CHECK(p < T, p, T);  // the query's own key exists
+  float* orow = scores + row * T;
+  if (tbase >= T) return;
+
+  if (tbase > p) {  // the whole wave is above the diagonal
+    for (int kb = 0; kb < NB && fill; ++kb) {
+      const int t = tbase + 32 * kb + ln;
+      if (lh == 0 && t < T) orow[t] = -INFINITY;
+    }
+    return;
+  }
+  // blocks holding a key t <= p (every key of the others is masked)
+  const int nv = min(NB, (p - tbase) / 32 + 1);
+  DSA_CHECK(nv >= 1 && tbase + 32 * (nv - 1) <= p, nv, tbase);
+
+  // A slot holds its 32 keys row-major (CH 16-byte chunks per key), chunk c
+  // of key r in place c ^ (r % CH). Copy i brings rows 64/CH i .. : lane L
+  // fills place L % CH of row 64/CH i + L / CH, i.e. chunk (L % CH) ^ (row %
+  // CH), so every copy reads 1 KB of whole key rows (the lanes' 16-byte pieces
+  // permuted within each row). Keys past the bound are clamped to p (masked at
+  // the store).
+  auto issue = [&](int kb) {
+    uint8_t* dst = (kb & 1) ? &ring1[wave][0] : &ring0[wave][0];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int r = i * (64 / CH) + lane / CH;
+      const int t = min(tbase + 32 * kb + r, p);
+      const int c = (lane % CH) ^ (r % CH);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(k + ((int64_t)b * T + t) * DI + 8 * c),
+          (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+    }
+  };
+
+  // the first two blocks' copies go out before the query and weight loads
+  const bool full = nv == NB;
+  issue(0);
+  if (full) issue(1);
+
+  // query operands and head weights: every load issued unconditionally (heads
+  // past HI read the last head's and are zeroed after), all in flight together
+  // and converted only after the scheduling barrier, so one wait covers them
+  u32x4_t qr[NHB][KS];
+  uint16_t wr[NHB][16];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = 32 * hb + ln;
+    const uint16_t* qp = q + (row * HI + (hh < HI ? hh : HI - 1)) * DI + 8 * lh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qr[hb][ks] = load16(qp + 16 * ks);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 32 * hb + 8 * (e >> 2) + 4 * lh + (e & 3);
+      wr[hb][e] = w[row * HI + (m < HI ? m : HI - 1)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_t a[NHB][KS];
+  float wv[NHB][16];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const bool hv = 32 * hb + ln < HI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[hb][ks] = as_bf16x8(hv ? qr[hb][ks] : u32x4_t{0, 0, 0, 0});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 32 * hb + 8 * (e >> 2) + 4 * lh + (e & 3);
+      const float x = bf16_to_f32(wr[hb][e]) * scale;
+      wv[hb][e] = m < HI ? x : 0.0f;
+    }
+  }
+  // the products of one block: the weighted head sum of its 32 keys
+  auto block_scores = [&](const bf16x8_t (&bk)[KS]) {
+    float part = 0.0f;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      f32x16_t acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[hb][ks], bk[ks], acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = acc[e];
+        if (MODE == 0) x = relu_bits(x);
+        part = fmaf(wv[hb][e], x, part);
+      }
+    }
+    part = sum_other_half(part);
+    if (MODE == 2) part = relu_bits(part);
+    return part;
+  };
+
+  float res[NB];
+  if (full) {
+    // every block holds a visible key (all waves of a row but the one holding
+    // its bound): a branch-free pipeline, so every wait count is exact
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      // block kb has landed once only the copies issued after it (those of
+      // block kb + 1, when there is one) are outstanding
+      if (kb + 1 < NB)
+        wait_vmcnt<KS>();
+      else
+        wait_vmcnt<0>();
+      bf16x8_t bk[KS];
+      read_block<KS, CH>((kb & 1) ? &ring1[wave][0] : &ring0[wave][0], ln, lh, bk);
+      if (kb + 2 < NB) issue(kb + 2);  // the slot's reads completed inside read_block
+      res[kb] = block_scores(bk);
+    }
+  } else {
+    // the wave holding the bound: one block at a time
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      res[kb] = 0.0f;
+      if (kb < nv) {
+        if (kb > 0) issue(kb);  // (block 0 was issued above)
+        wait_vmcnt<0>();
+        bf16x8_t bk[KS];
+        read_block<KS, CH>((kb & 1) ? &ring1[wave][0] : &ring0[wave][0], ln, lh, bk);
+        res[kb] = block_scores(bk);
+      }
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+    const int t = tbase + 32 * kb + ln;
+    if (lh == 0 && t < T) orow[t] = (t <= p) ? res[kb] : -INFINITY;
+  }
+}
+
 // fp32 inputs: one thread per (row, key), plain loops in fp32.
 __global__ __launch_bounds__(256) void idx_f32_kernel(const float* __restrict__ q,
                                                       const float* __restrict__ k,
@@ -376,9 +594,16 @@ hipError_t launch_rows(const uint16_t* q, const uint16_t* k, const uint16_t* w, 
                        int B, int S, int T, int P, int HI, float scale, int fill, hipStream_t st) {
   const int64_t rows = (int64_t)B * S;
   auto waves = [&](int kpw) { return rows * ((T + kpw - 1) / kpw); };
+  // up to 64 heads the keys stream through LDS (idx_rows_dma_kernel); more
+  // heads keep their operands in registers at one wave per SIMD
 #define DSA_ROWS_LAUNCH(KPW)                                                                     \
-  hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE, KPW>), dim3((T + 4 * KPW - 1) / (4 * KPW), \
-                     (unsigned)rows), dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale, fill)
+  if constexpr (NHB <= 2)                                                                        \
+    hipLaunchKernelGGL((idx_rows_dma_kernel<DI, NHB, MODE, KPW>),                                \
+                       dim3((T + 4 * KPW - 1) / (4 * KPW), (unsigned)rows), dim3(256), 0, st, q, \
+                       k, w, scores, S, T, P, HI, scale, fill);                                  \
+  else                                                                                           \
+    hipLaunchKernelGGL((idx_rows_kernel<DI, NHB, MODE, KPW>), dim3((T + 4 * KPW - 1) / (4 * KPW), \
+                       (unsigned)rows), dim3(256), 0, st, q, k, w, scores, S, T, P, HI, scale, fill)
   if (waves(512) >= kRowsWaves)
     DSA_ROWS_LAUNCH(512);
   else

@@ -94,6 +94,9 @@ INDEX_CASES = [
     # ragged query and key tiles, and the key-stationary form (T >= 8 S)
     (1, 600, 0, 16, 32, 0), (1, 300, 0, 33, 32, 0), (2, 333, 1200, 20, 64, 0),
     (1, 1000, 500, 64, 128, 0), (1, 100, 3000, 18, 128, 0), (2, 70, 900, 17, 64, 0),
+    # few-query rows through the LDS-streamed form: waves whose keys are all
+    # visible and the wave holding each row's bound, ragged T, dims 64 and 32
+    (2, 31, 577, 64, 64, 0), (1, 17, 1300, 48, 32, 2),
 ]
 
 
