@@ -155,7 +155,9 @@ __device__ __forceinline__ void mla_store4(const GemmMla& e, int m, int n, float
 // a compile-time constant so that every rotary pair's registers are fixed.
 // EPI 0: C = A W^T into (o1, o2); EPI 1..3: the MLA epilogues above (o1.N is
 // the output width).
-template <int RHALF, int BM, int EPI>
+// KSTRAD (EPI 1 only): the concatenation point K1 is not a multiple of the K
+// step, so one step straddles the two A matrices.
+template <int RHALF, int BM, int EPI, bool KSTRAD = false>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1, GemmOut o2,
                                                            int M, int K, int ntiles_n, int nt1,
                                                            GemmRope rp, GemmMla mla) {
@@ -194,28 +196,48 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
 
   // global -> register staging, two K steps ahead: the data of step s is
   // loaded at the start of step s - 2 into register set s & 1 and written to
-  // LDS at the end of step s - 1, so each load has two steps of MFMAs to land
+  // LDS at the end of step s - 1, so each load has two steps of MFMAs to land.
+  // The loads are branch-free buffer loads over per-tile resources (rows past
+  // M or N read as zeros; a chunk past K is sent past the resource's end), so
+  // the compiler counts them exactly and the LDS write of step s - 1's data
+  // waits only for those loads, not for the ones step s has just issued (with
+  // a conditional load per chunk it waited for everything, a full memory
+  // latency per K step).
+  // (only q_gate_proj reads two A matrices; the other instantiations see one)
+  const int lda1 = EPI == 1 ? ga.K1 : K, lda2 = K - ga.K1;
+  const auto rA1 = make_rsrc(ga.A1 + (int64_t)m0 * lda1, (int64_t)(M - m0) * lda1 * 2);
+  const auto rA2 = make_rsrc(EPI == 1 ? ga.A2 + (int64_t)m0 * lda2 : ga.A1,
+                             EPI == 1 ? (int64_t)(M - m0) * lda2 * 2 : 0);
+  const auto rW = make_rsrc(W + (int64_t)n0 * K, (int64_t)(N - n0) * K * 2);
+  constexpr uint32_t kPast = 0xFFFFFFF0u;  // an offset past every resource
   u32x4_t ra[2][kGLdA], rw[2][kGLdW];
   auto load_tile = [&](auto set_c, int k0) {
     constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < kGLdA; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      const int m = m0 + r;
       const int k = k0 + kc;
-      const bool kin = k < K;  // K % 32 == 0: a chunk is all in or all out
-      // (only q_gate_proj reads two matrices; the other instantiations see one)
-      const uint16_t* src = (EPI != 1 || k < ga.K1)
-                                ? ga.A1 + (int64_t)m * (EPI == 1 ? ga.K1 : K) + k
-                                : ga.A2 + (int64_t)m * (K - ga.K1) + (k - ga.K1);
-      ra[SET][i] = (m < M && kin) ? load16(src) : u32x4_t{0, 0, 0, 0};
+      if constexpr (EPI == 1 && KSTRAD) {
+        // a step straddles K1 (K1 % 32 == 0, so a chunk does not), and a
+        // resource is uniform: each chunk reads both matrices, the side it is
+        // not in sent past the end
+        const bool in1 = k < ga.K1, in2 = !in1 && k < K;
+        ra[SET][i] = buffer_load16(rA1, in1 ? (uint32_t)(r * lda1 + k) * 2u : kPast) |
+                     buffer_load16(rA2, in2 ? (uint32_t)(r * lda2 + (k - ga.K1)) * 2u : kPast);
+      } else if constexpr (EPI == 1) {  // the whole step lies in A1 or in A2
+        const bool a2 = k0 >= ga.K1;
+        const uint32_t off = a2 ? (uint32_t)(r * lda2 + (k - ga.K1)) * 2u
+                                : (uint32_t)(r * lda1 + k) * 2u;
+        ra[SET][i] = buffer_load16(a2 ? rA2 : rA1, k < K ? off : kPast);
+      } else {
+        ra[SET][i] = buffer_load16(rA1, k < K ? (uint32_t)(r * lda1 + k) * 2u : kPast);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kGLdW; ++i) {
       const int c = tid + 256 * i, r = c / kCPR, kc = 8 * (c % kCPR);
-      const int n = n0 + r;
-      const bool kin = k0 + kc < K;
-      rw[SET][i] = (n < N && kin) ? load16(W + (int64_t)n * K + k0 + kc) : u32x4_t{0, 0, 0, 0};
+      const int k = k0 + kc;
+      rw[SET][i] = buffer_load16(rW, k < K ? (uint32_t)(r * K + k) * 2u : kPast);
     }
   };
   auto store_tile = [&](auto set_c, int buf) {
@@ -266,7 +288,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmA ga, GemmOut o1,
   // data (loaded two steps ago) into the other buffer (last read before the
   // previous barrier)
   auto step = [&](int kt, auto cur, auto nxt) {
-    if (kt + 2 < nk) load_tile(cur, (kt + 2) * kGBK);
+    // (past the last step every chunk lies past K and reads nothing: no branch,
+    // so the wait counts stay exact)
+    load_tile(cur, (kt + 2) * kGBK);
     compute(decltype(cur)::value);
     if (kt + 1 < nk) {
       store_tile(nxt, decltype(nxt)::value);
@@ -463,7 +487,10 @@ hipError_t gemm_launch(GemmA ga, GemmOut o1, GemmOut o2, int M, int K, const Gem
   hipLaunchKernelGGL((gemm_bf16_kernel<RH, BMV, EP>), dim3((unsigned)g), dim3(256), 0, st, ga,  \
                      o1, o2, M, K, ntn, nt1, RP, ml)
 #define DSA_GEMM_BM(BMV)                                           \
-  if (epi == 1) {                                                  \
+  if (epi == 1 && ga.K1 % gemm_bk<BMV>() != 0) {                   \
+    hipLaunchKernelGGL((gemm_bf16_kernel<0, BMV, 1, true>), dim3((unsigned)g), dim3(256), 0, st, \
+                       ga, o1, o2, M, K, ntn, nt1, GemmRope{}, ml);                          \
+  } else if (epi == 1) {                                           \
     DSA_GEMM_LAUNCH(0, BMV, 1, GemmRope{});                        \
   } else if (epi == 2) {                                           \
     DSA_GEMM_LAUNCH(0, BMV, 2, GemmRope{});                        \
