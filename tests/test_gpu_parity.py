@@ -659,6 +659,7 @@ def test_quant_fp8_bit_exact(R, D):
 FP8_CASES = [  # (B, S, P, HI, mode): idx_dim 128
     (1, 200, 0, 64, 0), (2, 130, 73, 5, 0), (1, 257, 600, 9, 1), (1, 1000, 500, 13, 2),
     (2, 1, 999, 64, 0), (1, 3, 40, 130, 0), (1, 600, 0, 17, 0),
+    (2, 333, 700, 24, 0),  # ReLU split (16+ heads): batched, ragged tiles, a past context
 ]
 
 
