@@ -371,6 +371,24 @@ def time_layer(layer, steps, warmup, torch):
     return per_stage, total_ms, wall
 
 
+def time_sorted_topk(layer, reps, torch):
+    """Mean time of the sorted top-k (dsa_topk) on the layer's own indexer
+    scores. The pipeline's K2 stage is dsa_topk_unsorted (the attention takes
+    index lists as sets); this reports the sorted call beside it, outside the
+    step."""
+    fn = lambda: layer.dsa.dsa_topk(layer.scores, layer.idx, layer.tk_ws)
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
 def time_graph(stages, steps, torch):
     """Mean time of one replay of the stages captured in a HIP graph (kernels
     only: the library's calls enqueue kernels and nothing else)."""
@@ -697,6 +715,8 @@ def main():
     layer = make_layer(wl, torch, dsa, datagen)
     per_stage, total_ms, wall = time_layer(layer, args.steps, args.warmup, torch)
     main_r = summarize(wl, per_stage, total_ms)
+    if "K2 topk" in per_stage:  # the sorted call, after the timed steps
+        main_r["K2_sorted_topk_us"] = time_sorted_topk(layer, 5, torch)
     del layer
     torch.cuda.empty_cache()
     log(f"{wl.name}: {total_ms:.3f} ms/step")
@@ -708,6 +728,7 @@ def main():
         dlay = make_layer(dwl, torch, dsa, datagen)
         dps, dtm, _ = time_layer(dlay, args.decode_steps, args.warmup, torch)
         dec_r = summarize(dwl, dps, dtm)
+        dec_r["K2_sorted_topk_us"] = time_sorted_topk(dlay, 20, torch)
         dgraph = time_graph(dlay.stages(), args.decode_steps, torch)
         del dlay
         torch.cuda.empty_cache()
